@@ -1,0 +1,388 @@
+"""Seeded synthetic inputs for the LSA indexer path.
+
+This module holds random draws and input construction only: storage casts
+(bf16, e4m3 with a per-entry scale), planted-key geometry and a counter-based
+hash for KV-pool contents.  It contains none of the method's arithmetic (no
+query projection, no scoring, no selection, no softmax or vote): the planting
+direction and the score bias are supplied by the caller, and the stored values
+of both for the named workloads are written by a calibration script that runs
+the CPU oracle.
+
+Every draw comes from ``numpy.random.PCG64`` seeded with
+``SeedSequence([seed, workload_id, request, layer, tag])``, so any tensor can
+be regenerated alone and in any order.
+
+Workloads follow the pages' context lengths (16K-1M tokens of context,
+4:1-compressed into entries) and the indexer layers 10/12/20; sizes, dtypes and
+fractions are listed in ``WORKLOADS``.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+GENERATOR_VERSION = 3
+
+_TAGS = {"h": 1, "wq": 2, "wg": 3, "plant": 4, "keys": 5, "logits": 6,
+         "student": 7, "misc": 8}
+_ALL = 0xFFFF  # "not per request / not per layer" slot in the seed tuple
+
+
+def stream(seed: int, wid: int, b: int, l: int, tag: str) -> np.random.Generator:
+    ss = np.random.SeedSequence([seed, wid, b, l, _TAGS[tag]])
+    return np.random.Generator(np.random.PCG64(ss))
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    wid: int
+    B: int          # concurrent decode requests
+    L: int          # indexer layers
+    N: int          # compressed entries per layer (context / 4)
+    H: int          # indexer heads
+    dI: int         # indexer head dim (key width)
+    D: int          # hidden size of h_t
+    key_dtype: str  # "bf16" or "e4m3"
+    k: int          # top-k over survivors
+    row_elems: int  # KV-pool row length in bf16 elements (0: no gather)
+    planted: tuple  # planted-relevant fraction per layer
+    core: float     # fraction planted in every layer (shared core)
+    sel_frac: tuple  # target fraction with I >= 0.5, per layer
+    layers: tuple = (10, 12, 20)
+    calib_rows: int = 0   # rows per (layer, request) used to set the bias; 0 = all
+    seed: int = 0
+
+    @property
+    def triples(self) -> int:
+        return self.B * self.L * self.N
+
+    @property
+    def key_bytes_per_entry(self) -> int:
+        return self.dI * (2 if self.key_dtype == "bf16" else 1) + (4 if self.key_dtype == "e4m3" else 0)
+
+
+def _sel(r):
+    # about 2% of the non-planted entries also pass the threshold
+    return tuple(x + 0.02 * (1.0 - x) for x in r)
+
+
+WORKLOADS = {
+    "tiny": Workload("tiny", 1, B=1, L=1, N=4096, H=8, dI=64, D=512, key_dtype="bf16",
+                     k=256, row_elems=512, planted=(0.10,), core=0.10, sel_frac=(0.12,),
+                     layers=(10,)),
+    "ctx128k": Workload("ctx128k", 2, B=1, L=3, N=32768, H=64, dI=128, D=4096,
+                        key_dtype="bf16", k=2048, row_elems=512,
+                        planted=(0.08, 0.12, 0.15), core=0.06,
+                        sel_frac=_sel((0.08, 0.12, 0.15))),
+    "ctx512k": Workload("ctx512k", 3, B=16, L=3, N=131072, H=64, dI=128, D=4096,
+                        key_dtype="bf16", k=2048, row_elems=512,
+                        planted=(0.10, 0.10, 0.10), core=0.05,
+                        sel_frac=_sel((0.10, 0.10, 0.10)), calib_rows=16384),
+    "ctx1m": Workload("ctx1m", 4, B=32, L=3, N=262144, H=64, dI=128, D=4096,
+                      key_dtype="e4m3", k=2048, row_elems=512,
+                      planted=(0.10, 0.10, 0.10), core=0.05,
+                      sel_frac=_sel((0.10, 0.10, 0.10)), calib_rows=8192),
+}
+
+
+def custom(name="custom", wid=90, **kw) -> Workload:
+    """A small ad-hoc workload (tests: ragged sizes, other seeds)."""
+    base = dict(B=1, L=1, N=1000, H=8, dI=64, D=256, key_dtype="bf16", k=64,
+                row_elems=64, planted=None, core=None, sel_frac=None,
+                layers=None, calib_rows=0, seed=0)
+    base.update(kw)
+    L = base["L"]
+    if base["planted"] is None:
+        base["planted"] = tuple([0.10] * L)
+    if base["core"] is None:
+        base["core"] = min(base["planted"]) / 2
+    if base["sel_frac"] is None:
+        base["sel_frac"] = _sel(base["planted"])
+    if base["layers"] is None:
+        base["layers"] = tuple(range(L))
+    return Workload(name, wid, **base)
+
+
+# ---------------------------------------------------------------------------
+# storage casts (library routines; no method arithmetic)
+# ---------------------------------------------------------------------------
+
+def to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> bf16 (round to nearest even), returned as uint16 bits."""
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+E4M3_MAX = 448.0
+
+
+def to_e4m3_rows(x: np.ndarray):
+    """Quantise rows of float32 to OCP e4m3 with one fp32 scale per row
+    (scale = max|row| / 448, nearest-even, saturating)."""
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    amax = t.abs().amax(dim=-1)
+    scale = torch.where(amax > 0, amax / E4M3_MAX, torch.ones_like(amax))
+    y = (t / scale.unsqueeze(-1)).clamp_(-E4M3_MAX, E4M3_MAX)
+    codes = y.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    return codes, scale.numpy().astype(np.float32)
+
+
+# ---------------------------------------------------------------------------
+# decode-time indexer inputs
+# ---------------------------------------------------------------------------
+
+def hidden(w: Workload) -> np.ndarray:
+    """h_t per request, ~N(0,1), stored bf16: uint16 [B][D]."""
+    out = np.empty((w.B, w.D), np.uint16)
+    for b in range(w.B):
+        x = stream(w.seed, w.wid, b, _ALL, "h").standard_normal(w.D, dtype=np.float32)
+        out[b] = to_bf16_bits(x)
+    return out
+
+
+def weights(w: Workload, l: int):
+    """Per-layer query-encoder weights ~N(0, 1/D), stored bf16:
+    Wq uint16 [H*dI][D] (row = head*dI + i), Wg uint16 [H][D]."""
+    sd = 1.0 / math.sqrt(w.D)
+    wq = stream(w.seed, w.wid, _ALL, l, "wq").standard_normal((w.H * w.dI, w.D), dtype=np.float32)
+    wg = stream(w.seed, w.wid, _ALL, l, "wg").standard_normal((w.H, w.D), dtype=np.float32)
+    return to_bf16_bits(wq * np.float32(sd)), to_bf16_bits(wg * np.float32(sd))
+
+
+def planted_sets(w: Workload, b: int):
+    """Planted-relevant entries of request b: bool [L][N] and the cosine of
+    each entry with the planting direction, float64 [L][N] (~U(0.5, 0.7))."""
+    r = stream(w.seed, w.wid, b, _ALL, "plant")
+    n_core = int(round(w.core * w.N))
+    perm = r.permutation(w.N)
+    core = perm[:n_core]
+    rest = perm[n_core:]
+    mask = np.zeros((w.L, w.N), bool)
+    for l in range(w.L):
+        mask[l, core] = True
+        n_extra = max(0, int(round((w.planted[l] - w.core) * w.N)))
+        extra = r.choice(rest, size=min(n_extra, rest.size), replace=False)
+        mask[l, extra] = True
+    cos = r.uniform(0.5, 0.7, size=(w.L, w.N))
+    return mask, cos
+
+
+def keys(w: Workload, b: int, l: int, u: np.ndarray, rows: int | None = None,
+         plant=None):
+    """Compressed indexer keys of (layer l, request b).
+
+    Non-planted keys ~N(0, I/dI).  A planted key k' ~N(0, I/dI) is moved to
+    cosine c with the unit direction u: k = k_perp + c/sqrt(1-c^2) |k_perp| u,
+    where k_perp is k' with its u component removed.  Returned in storage
+    format: bf16 -> (uint16 [rows][dI], None); e4m3 -> (uint8 [rows][dI],
+    fp32 scale [rows])."""
+    n = w.N if rows is None else min(rows, w.N)
+    x = stream(w.seed, w.wid, b, l, "keys").standard_normal((n, w.dI), dtype=np.float32)
+    x *= np.float32(1.0 / math.sqrt(w.dI))
+    mask, cos = plant if plant is not None else planted_sets(w, b)
+    sel = np.nonzero(mask[l, :n])[0]
+    if sel.size:
+        uu = np.asarray(u, np.float64)
+        uu = uu / np.linalg.norm(uu)
+        kp = x[sel].astype(np.float64)
+        kp -= np.outer(kp @ uu, uu)
+        c = cos[l, sel]
+        t = c / np.sqrt(1.0 - c * c) * np.linalg.norm(kp, axis=1)
+        x[sel] = (kp + np.outer(t, uu)).astype(np.float32)
+    if w.key_dtype == "bf16":
+        return to_bf16_bits(x), None
+    return to_e4m3_rows(x)
+
+
+# ---------------------------------------------------------------------------
+# KV pool contents: counter-based hash, identical on CPU and GPU
+# ---------------------------------------------------------------------------
+
+_M32 = 0xFFFFFFFF
+
+
+def _mix32(x):
+    # 32-bit integer finaliser (xor-shift / multiply, constants < 2^31 so the
+    # products stay inside int64 on every backend)
+    x = x ^ (x >> 16)
+    x = (x * 0x21F0AAAD) & _M32
+    x = x ^ (x >> 15)
+    x = (x * 0x735A2D97) & _M32
+    x = x ^ (x >> 15)
+    return x
+
+
+def _pool_words(wid, b, s, w):
+    """32-bit hash of (workload, request, entry, pair) for torch int64 tensors."""
+    hi = _mix32(((wid * 64 + b) * 0x10001 + (s >> 8)) & _M32)
+    lo = (((s & 0xFF) << 8) | w) & _M32
+    return _mix32(lo ^ hi)
+
+
+def pool_rows(w: Workload, b: int, s, device="cpu") -> torch.Tensor:
+    """KV-pool rows (bf16 bits as int16) for entries s of request b:
+    [len(s)][row_elems].  Each 32-bit hash gives two bf16 values; the top
+    exponent bit is cleared so every value is finite."""
+    s = torch.as_tensor(s, dtype=torch.int64, device=device).reshape(-1, 1)
+    pairs = torch.arange(w.row_elems // 2, dtype=torch.int64, device=device).reshape(1, -1)
+    h = _pool_words(w.wid, b, s, pairs)
+    lo = (h & 0xBFFF)
+    hi = ((h >> 16) & 0xBFFF)
+    out = torch.stack([lo, hi], dim=-1).reshape(s.shape[0], w.row_elems)
+    out = torch.where(out >= 0x8000, out - 0x10000, out)
+    return out.to(torch.int16)
+
+
+def pool_tensor(w: Workload, device) -> torch.Tensor:
+    """Whole KV pool [B][N][row_elems] (bf16 bits as int16) built on device."""
+    out = torch.empty((w.B, w.N, w.row_elems), dtype=torch.int16, device=device)
+    chunk = 1 << 16
+    for b in range(w.B):
+        for s0 in range(0, w.N, chunk):
+            s = torch.arange(s0, min(w.N, s0 + chunk), device=device)
+            out[b, s0:s0 + s.numel()] = pool_rows(w, b, s, device=device)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# calibration (planting direction + bias) written by the oracle-side script
+# ---------------------------------------------------------------------------
+
+DEFAULT_CALIBRATION = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                                   "tests", "golden", "calibration.json")
+
+
+@dataclass
+class Calibration:
+    u: np.ndarray          # float64 [L][B][dI] planting directions
+    bias: np.ndarray       # float32 [L]
+
+
+def load_calibration(w: Workload, path: str = DEFAULT_CALIBRATION) -> Calibration:
+    with open(path) as f:
+        data = json.load(f)
+    if data.get("generator_version") != GENERATOR_VERSION:
+        raise RuntimeError(f"{path} was written for generator version "
+                           f"{data.get('generator_version')}, this is {GENERATOR_VERSION}")
+    entry = data["workloads"][w.name]
+    u = np.array(entry["u"], dtype=np.float64).reshape(w.L, w.B, w.dI)
+    bias = np.array(entry["bias"], dtype=np.float32)
+    return Calibration(u=u, bias=bias)
+
+
+@dataclass
+class IndexerInputs:
+    w: Workload
+    h: np.ndarray            # uint16 [B][D]  (bf16 bits)
+    Wq: list                 # L x uint16 [H*dI][D]
+    Wg: list                 # L x uint16 [H][D]
+    keys: list               # L x ([B][N][dI] uint16 bf16 | uint8 e4m3)
+    scale: list              # L x (float32 [B][N] | None)
+    bias: np.ndarray         # float32 [L]
+    plant: np.ndarray        # bool [B][L][N]
+
+
+def indexer_inputs(w: Workload, calib: Calibration, threads: int = 8) -> IndexerInputs:
+    """All decode-time inputs of a workload, keys planted along calib.u."""
+    from concurrent.futures import ThreadPoolExecutor
+    h = hidden(w)
+    Wq, Wg = zip(*[weights(w, l) for l in range(w.L)])
+    plants = [planted_sets(w, b) for b in range(w.B)]
+    kdt = np.uint16 if w.key_dtype == "bf16" else np.uint8
+    keys_l = [np.empty((w.B, w.N, w.dI), kdt) for _ in range(w.L)]
+    scale_l = [None if w.key_dtype == "bf16" else np.empty((w.B, w.N), np.float32)
+               for _ in range(w.L)]
+
+    def one(lb):
+        l, b = lb
+        k, s = keys(w, b, l, calib.u[l, b], plant=plants[b])
+        keys_l[l][b] = k
+        if s is not None:
+            scale_l[l][b] = s
+
+    with ThreadPoolExecutor(max_workers=max(1, threads)) as ex:
+        list(ex.map(one, [(l, b) for l in range(w.L) for b in range(w.B)]))
+    plant = np.stack([p[0] for p in plants])
+    return IndexerInputs(w=w, h=h, Wq=list(Wq), Wg=list(Wg), keys=keys_l,
+                         scale=scale_l, bias=np.asarray(calib.bias, np.float32),
+                         plant=plant)
+
+
+def bias_from_sorted(v: np.ndarray, frac: float) -> float:
+    """Bias that puts a fraction `frac` of the pooled bias-free logits at or
+    above zero: minus the midpoint of the two order statistics around the
+    (1-frac) quantile."""
+    v = np.sort(np.asarray(v, np.float64))
+    M = v.size
+    m = int(round((1.0 - frac) * M))
+    m = min(max(m, 1), M - 1)
+    return float(np.float32(-(v[m - 1] + v[m]) / 2.0))
+
+
+# ---------------------------------------------------------------------------
+# offline label workload (teacher logits + student)
+# ---------------------------------------------------------------------------
+
+@dataclass(frozen=True)
+class LabelWorkload:
+    name: str = "labels128k"
+    wid: int = 5
+    Q: int = 64          # queries (decode positions) in the batch
+    L: int = 20          # teacher layers voting
+    N: int = 32768       # compressed entries (128K context / 4)
+    H: int = 64
+    dI: int = 128
+    D: int = 4096
+    top_p: float = 0.6
+    theta: int = 3
+    gamma: float = 2.0
+    relevant: float = 0.04     # per-query relevant pool
+    p_layer: float = 0.25      # chance a relevant entry is boosted in a layer
+    private: float = 0.01      # layer-private boosted noise
+    boost: float = 4.0
+    seed: int = 0
+
+
+LABELS = LabelWorkload()
+
+
+def teacher_logits(w: LabelWorkload, q: int) -> np.ndarray:
+    """Raw per-layer logits of query q, float32 [L][N]: N(0,1) plus `boost`
+    on boosted entries."""
+    r = stream(w.seed, w.wid, q, _ALL, "logits")
+    x = r.standard_normal((w.L, w.N), dtype=np.float32)
+    n_rel = int(round(w.relevant * w.N))
+    perm = r.permutation(w.N)
+    rel = perm[:n_rel]
+    outside = perm[n_rel:]
+    boost = np.zeros((w.L, w.N), bool)
+    hit = r.random((w.L, n_rel)) < w.p_layer
+    for l in range(w.L):
+        boost[l, rel[hit[l]]] = True
+        priv = r.choice(outside, size=int(round(w.private * w.N)), replace=False)
+        boost[l, priv] = True
+    x[boost] += np.float32(w.boost)
+    return x
+
+
+def student(w: LabelWorkload):
+    """Student inputs: h bf16 [Q][D], Wq f32 [H*dI][D], Wg f32 [H][D],
+    K bf16 [N][dI], bias 0."""
+    r = stream(w.seed, w.wid, _ALL, _ALL, "student")
+    h = to_bf16_bits(r.standard_normal((w.Q, w.D), dtype=np.float32))
+    sd = np.float32(1.0 / math.sqrt(w.D))
+    Wq = r.standard_normal((w.H * w.dI, w.D), dtype=np.float32) * sd
+    Wg = r.standard_normal((w.H, w.D), dtype=np.float32) * sd
+    K = to_bf16_bits(r.standard_normal((w.N, w.dI), dtype=np.float32)
+                     * np.float32(1.0 / math.sqrt(w.dI)))
+    return h, Wq, Wg, K, 0.0

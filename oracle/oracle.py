@@ -1,0 +1,264 @@
+"""ctypes wrapper of the plain CPU oracle (``lsa_oracle.c``).
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, by the smoke check and by the
+CPU-baseline leg of the benchmark.  The product library never imports it.
+
+Every function takes and returns numpy arrays.  Storage formats follow the
+boundary: bf16 is passed as ``uint16`` bit patterns, e4m3 as ``uint8`` codes.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "lsa_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liblsa_oracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (-O2, OpenMP, IEEE semantics kept)."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp"
+        cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared",
+               "-fno-fast-math", "-ffp-contract=off", _SRC, "-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        build()
+    lib = C.CDLL(_LIB_PATH)
+    P = C.c_void_p
+    i32, i64, f64 = C.c_int, C.c_int64, C.c_double
+    sig = {
+        "lsa_or_bf16_to_double": (f64, [C.c_uint16]),
+        "lsa_or_bf16_from_double": (C.c_uint16, [f64]),
+        "lsa_or_e4m3_to_double": (f64, [C.c_uint8]),
+        "lsa_or_softplus": (f64, [f64]),
+        "lsa_or_sigmoid": (f64, [f64]),
+        "lsa_or_project": (None, [i32, i32, i32, P, P, P, P, P, P]),
+        "lsa_or_query_collapse": (None, [i32, i32, P, P, P]),
+        "lsa_or_score": (None, [i32, i32, i32, i32, P, P, P, P, f64, P, i64, P]),
+        "lsa_or_threshold": (None, [i64, P, P]),
+        "lsa_or_merge_compact": (i64, [i32, i64, P, P, i64, P, P]),
+        "lsa_or_topk": (i64, [i64, P, P, i64, P]),
+        "lsa_or_gather": (None, [i64, i64, P, i64, P, P]),
+        "lsa_or_nucleus": (i64, [i64, P, f64, P, P]),
+        "lsa_or_vote": (None, [i32, i64, P, i32, P, P]),
+        "lsa_or_focal_bce_grad": (f64, [i32, i64, i32, i32, i32, f64, P, P, P, f64, P, P, P, P]),
+        "lsa_or_focal_bce_loss64": (f64, [i32, i64, i32, i32, i32, f64, P, P, P, f64, P, P]),
+        "lsa_or_num_threads": (i32, []),
+        "lsa_or_trigger_due": (i32, [i64, i32]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(C.c_void_p)
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+# ---- storage formats ------------------------------------------------------
+
+def bf16_to_double(bits) -> np.ndarray:
+    lib = _load()
+    b = np.asarray(bits, dtype=np.uint16).ravel()
+    return np.array([lib.lsa_or_bf16_to_double(int(v)) for v in b]).reshape(np.shape(bits))
+
+
+def bf16_from_double(a) -> np.ndarray:
+    lib = _load()
+    x = np.asarray(a, dtype=np.float64).ravel()
+    return np.array([lib.lsa_or_bf16_from_double(float(v)) for v in x],
+                    dtype=np.uint16).reshape(np.shape(a))
+
+
+def e4m3_to_double(codes) -> np.ndarray:
+    lib = _load()
+    c = np.asarray(codes, dtype=np.uint8).ravel()
+    return np.array([lib.lsa_or_e4m3_to_double(int(v)) for v in c]).reshape(np.shape(codes))
+
+
+def softplus(x: float) -> float:
+    return _load().lsa_or_softplus(float(x))
+
+
+def sigmoid(x: float) -> float:
+    return _load().lsa_or_sigmoid(float(x))
+
+
+def trigger_due(t: int, tau: int) -> bool:
+    return bool(_load().lsa_or_trigger_due(int(t), int(tau)))
+
+
+def num_threads() -> int:
+    return _load().lsa_or_num_threads()
+
+
+# ---- O1 projection ----------------------------------------------------------
+
+def project(h, Wq, Wg, H: int, dI: int, want_a: bool = False):
+    """One (layer, request): h bf16 [D], Wq bf16 [H*dI][D], Wg bf16 [H][D].
+    Returns q (uint16 [H][dI]), g (float32 [H]) and optionally a (fp64)."""
+    lib = _load()
+    h = _c(h, np.uint16)
+    Wq = _c(Wq, np.uint16)
+    Wg = _c(Wg, np.uint16)
+    D = h.shape[-1]
+    q = np.empty(H * dI, np.uint16)
+    g = np.empty(H, np.float32)
+    a = np.empty(H * dI, np.float64) if want_a else None
+    lib.lsa_or_project(D, H, dI, _p(h), _p(Wq), _p(Wg), _p(q), _p(g), _p(a))
+    q = q.reshape(H, dI)
+    return (q, g, a.reshape(H, dI)) if want_a else (q, g)
+
+
+def query_collapse(q, g) -> np.ndarray:
+    lib = _load()
+    q = _c(q, np.uint16)
+    g = _c(g, np.float32)
+    H, dI = q.shape
+    out = np.empty(dI, np.float64)
+    lib.lsa_or_query_collapse(H, dI, _p(q), _p(g), _p(out))
+    return out
+
+
+# ---- O3 score / O4 threshold / O5 merge ----------------------------------
+
+def score(keys, scale, q, g, bias: float, idx=None) -> np.ndarray:
+    """keys: uint16 [N][dI] (bf16) or uint8 [N][dI] (e4m3, with scale f32 [N]).
+    Returns fp64 z for all entries, or for the entries listed in idx."""
+    lib = _load()
+    key_dtype = 0 if keys.dtype == np.uint16 else 1
+    keys = np.ascontiguousarray(keys)
+    N, dI = keys.shape
+    q = _c(q, np.uint16)
+    g = _c(g, np.float32)
+    H = q.shape[0]
+    sc = _c(scale, np.float32) if scale is not None else None
+    if idx is not None:
+        idx = _c(idx, np.int64)
+        n = idx.shape[0]
+    else:
+        n = N
+    z = np.empty(n, np.float64)
+    lib.lsa_or_score(N, H, dI, key_dtype, _p(keys), _p(sc), _p(q), _p(g),
+                     float(bias), _p(idx), n, _p(z))
+    return z
+
+
+def threshold(z) -> np.ndarray:
+    lib = _load()
+    z = _c(z, np.float64)
+    sel = np.empty(z.shape, np.uint8)
+    lib.lsa_or_threshold(z.size, _p(z), _p(sel))
+    return sel
+
+
+def merge_compact(sel, z, cap: int | None = None):
+    """sel uint8 [L][N], z fp64 [L][N] -> (idx int32 [min(count,cap)],
+    zstar fp64, true count)."""
+    lib = _load()
+    sel = _c(sel, np.uint8)
+    z = _c(z, np.float64)
+    L, N = sel.shape
+    if cap is None:
+        cap = N
+    idx = np.empty(max(cap, 1), np.int32)
+    zs = np.empty(max(cap, 1), np.float64)
+    count = lib.lsa_or_merge_compact(L, N, _p(sel), _p(z), cap, _p(idx), _p(zs))
+    m = min(count, cap)
+    return idx[:m].copy(), zs[:m].copy(), int(count)
+
+
+def topk(surv_idx, surv_z, k: int):
+    lib = _load()
+    si = _c(surv_idx, np.int32)
+    sz = _c(surv_z, np.float64)
+    out = np.empty(max(k, 1), np.int32)
+    cnt = lib.lsa_or_topk(si.shape[0], _p(si), _p(sz), k, _p(out))
+    return out[:k].copy(), int(cnt)
+
+
+def gather(pool, idx) -> np.ndarray:
+    """pool: uint8 [N][row_bytes]; idx int32 [k] -> uint8 [k][row_bytes]."""
+    lib = _load()
+    pool = _c(pool, np.uint8)
+    idx = _c(idx, np.int32)
+    N, rb = pool.shape
+    hot = np.empty((idx.shape[0], rb), np.uint8)
+    lib.lsa_or_gather(N, rb, _p(pool), idx.shape[0], _p(idx), _p(hot))
+    return hot
+
+
+# ---- O8 labels -------------------------------------------------------------
+
+def nucleus(x, top_p: float, want_mass: bool = False):
+    lib = _load()
+    x = _c(x, np.float32)
+    N = x.shape[0]
+    sel = np.empty(N, np.uint8)
+    mass = np.empty(N, np.float64) if want_mass else None
+    n = lib.lsa_or_nucleus(N, _p(x), float(top_p), _p(sel), _p(mass))
+    return (sel, int(n), mass) if want_mass else (sel, int(n))
+
+
+def vote(sel, theta: int):
+    lib = _load()
+    sel = _c(sel, np.uint8)
+    L, N = sel.shape
+    count = np.empty(N, np.uint8)
+    label = np.empty(N, np.uint8)
+    lib.lsa_or_vote(L, N, _p(sel), int(theta), _p(count), _p(label))
+    return count, label
+
+
+# ---- O9 loss / gradient --------------------------------------------------
+
+def focal_bce_grad(h, Wq, Wg, bias: float, K, y, gamma: float, H: int, dI: int,
+                   want_grad: bool = True, want_z: bool = False):
+    """h bf16 [Q][D], Wq f32 [H*dI][D], Wg f32 [H][D], K bf16 [N][dI], y u8 [Q][N]."""
+    lib = _load()
+    h = _c(h, np.uint16)
+    Wq = _c(Wq, np.float32)
+    Wg = _c(Wg, np.float32)
+    K = _c(K, np.uint16)
+    y = _c(y, np.uint8)
+    Q, D = h.shape
+    N = K.shape[0]
+    dW = np.empty((H * dI, D), np.float64) if want_grad else None
+    z = np.empty((Q, N), np.float64) if want_z else None
+    loss = lib.lsa_or_focal_bce_grad(Q, N, D, H, dI, float(gamma), _p(h), _p(Wq),
+                                     _p(Wg), float(bias), _p(K), _p(y), _p(dW), _p(z))
+    return loss, dW, z
+
+
+def focal_bce_loss64(h, Wq, Wg, bias: float, K, y, gamma: float, H: int, dI: int) -> float:
+    lib = _load()
+    h = _c(h, np.float64)
+    Wq = _c(Wq, np.float64)
+    Wg = _c(Wg, np.float64)
+    K = _c(K, np.float64)
+    y = _c(y, np.uint8)
+    Q, D = h.shape
+    N = K.shape[0]
+    return lib.lsa_or_focal_bce_loss64(Q, N, D, H, dI, float(gamma), _p(h), _p(Wq),
+                                       _p(Wg), float(bias), _p(K), _p(y))

@@ -1,0 +1,222 @@
+/*
+ * lsa.h -- C ABI of liblsa.so, the MI355X (gfx950) Lookahead Sparse Attention
+ * indexer hot path.
+ *
+ * Sources (web pages on "FlashMemory-DeepSeek-V4: Lightning Index Ultra-Long
+ * Context via Lookahead Sparse Attention"):
+ *   [SUMMARY] gist.science technical summary: 2.1 architecture (trigger,
+ *             memory indexer, scoring, dynamic fetch, hierarchical
+ *             selection), 2.2 label curation, 2.3 decoupled training,
+ *             2.4 optimal configuration (layers 10/12/20, OR mode)
+ *   [REVIEW]  paper.oopus.info review: section 2 (core method), section 3
+ *             (resources)
+ *
+ * Conventions for every call:
+ *  - All tensor arguments are DEVICE pointers owned by the caller, except
+ *    where an argument is documented as a host array.  The library never
+ *    allocates persistent memory and keeps no global mutable state apart from
+ *    a thread-local error string.  Every call is reentrant.
+ *  - Every compute call enqueues its kernels on `stream` and returns without
+ *    synchronising.  Outputs are valid once the stream has reached that point.
+ *  - Argument, shape and dtype errors are detected on the host and returned
+ *    before anything is launched (nothing is written).  A launch failure
+ *    returns LSA_E_HIP.  lsa_last_error() then holds a message.
+ *  - Device pointers must be 16-byte aligned unless stated otherwise.
+ *  - bf16 tensors are passed as uint16_t bit patterns, e4m3 as uint8_t codes
+ *    (OCP 8-bit E4M3 "FN": bias 7, subnormals, no infinity, 0x7F/0xFF NaN).
+ *  - Notation: L indexer layers, B concurrent requests, N compressed entries
+ *    per layer and request, H indexer heads, dI indexer head dimension, D
+ *    hidden size, k top-k size.
+ */
+#ifndef LSA_H
+#define LSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  LSA_OK = 0,
+  LSA_E_ARG = 1,        /* null pointer, negative size, bad alignment, bad value */
+  LSA_E_SHAPE = 2,      /* a size outside what the kernels support */
+  LSA_E_DTYPE = 3,      /* unknown key dtype */
+  LSA_E_HIP = 4,        /* a HIP launch or runtime call failed */
+  LSA_E_WORKSPACE = 5   /* workspace missing or smaller than required */
+} lsa_status;
+
+typedef enum {
+  LSA_KEY_BF16 = 0,       /* keys bf16 [B][N][dI] */
+  LSA_KEY_FP8_E4M3 = 1    /* keys e4m3 [B][N][dI] + fp32 scale [B][N] */
+} lsa_key_dtype;
+
+#define LSA_MAX_LAYERS 8      /* indexer layers per lsa_score call */
+#define LSA_MAX_HEADS 64      /* indexer heads */
+#define LSA_MAX_VOTE_LAYERS 32
+
+/* Message describing the last non-OK status returned on this thread. */
+const char* lsa_last_error(void);
+
+/* Library version string. */
+const char* lsa_version(void);
+
+/* ---------------------------------------------------------------------------
+ * Trigger cadence ([SUMMARY] 2.1, periodic trigger; [REVIEW] section 2): the
+ * indexer runs at decode step t iff t >= 0 and t is a multiple of tau,
+ * counting from step 0.  Returns 1 or 0; tau <= 0 returns 0.  Host only.
+ */
+int lsa_trigger_due(int64_t decode_step, int tau);
+
+/* ---------------------------------------------------------------------------
+ * Query encoder ([SUMMARY] 2.1 memory-indexer bullet: the hidden state of the
+ * current token is mapped to a low-rank indexer query; 2.3: only this
+ * projection is trained).  For every layer l and request b:
+ *   a = Wq[l] . h[l][b]      (fp32 accumulation)      q[l][b] = bf16(a)
+ *   g[l][b][j] = softplus(Wg[l][j] . h[l][b])           (fp32)
+ * The head-gate form (softplus gates, one per head) is this library's reading
+ * of the scoring bullet's "gated, head-fused" match.
+ *
+ *   h        bf16 [L?][B][D]; layer l reads h + l * h_layer_stride
+ *            (h_layer_stride = 0: one h_t per request shared by all layers)
+ *   Wq       HOST array of L device pointers, each bf16 [H*dI][D]
+ *            (row index = head * dI + i)
+ *   Wg       HOST array of L device pointers, each bf16 [H][D]
+ *   q        out bf16 [L][B][H][dI]        g   out fp32 [L][B][H]
+ * Limits: 1 <= L <= LSA_MAX_LAYERS, B >= 1, D % 256 == 0, 1 <= H <= 64,
+ * dI in {64, 128}.
+ */
+lsa_status lsa_project_query(int L, int B, int D, int H, int dI,
+                             const uint16_t* h, int64_t h_layer_stride,
+                             const uint16_t* const* Wq,
+                             const uint16_t* const* Wg, uint16_t* q, float* g,
+                             hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Lookahead index score and threshold ([SUMMARY] 2.1 scoring bullet: a
+ * sigmoid, head-fused, gated match of the query against every earlier
+ * compressed entry; dynamic-fetch bullet: entries with I >= 0.5 are fetched).
+ * For every layer l, request b and entry s:
+ *   z[l][b][s] = sum_h g[l][b][h] * (q[l][b][h] . k_l[b][s]) * sigma + bias[l]
+ *   I = sigmoid(z);  selected  <=>  I >= 0.5  <=>  z >= 0 (NaN: not selected)
+ * with sigma = key_scale[l][b][s] for e4m3 keys and 1 for bf16 keys.
+ *
+ *   keys      HOST array of L device pointers, each [B][N][dI] (bf16 or e4m3)
+ *   key_scale HOST array of L device pointers, each fp32 [B][N]; required for
+ *             LSA_KEY_FP8_E4M3, ignored (may be NULL) for bf16
+ *   q, g      as written by lsa_project_query
+ *   bias      HOST array of L fp32 values
+ *   z         out fp32 [L][B][N]
+ *   I_opt     out fp32 [L][B][N] or NULL
+ *   sel_mask  out uint32 [L][B][ceil(N/32)]: bit (s % 32) of word s / 32;
+ *             bits past N are zero
+ * Limits: 1 <= L <= LSA_MAX_LAYERS, B >= 1, N >= 0 (N = 0 launches nothing),
+ * 1 <= H <= 64, dI in {64, 128}, L * B <= 65535.
+ */
+lsa_status lsa_score(int L, int B, int N, int H, int dI, lsa_key_dtype kdt,
+                     const void* const* keys, const float* const* key_scale,
+                     const uint16_t* q, const float* g, const float* bias,
+                     float* z, float* I_opt, uint32_t* sel_mask,
+                     hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Three-layer OR merge and survivor compaction ([SUMMARY] 2.4: the
+ * predictions of the indexer layers are combined by union; [REVIEW] section
+ * 2: an entry is fetched when any layer asks for it).  For every request b:
+ *   surv_idx[b]   = the entries s selected by at least one layer, ascending
+ *   surv_z[b][i]  = max over layers of z[l][b][s]  (NaN ignored)
+ *   surv_count[b] = the TRUE number of survivors, even when it exceeds cap;
+ *                   only the first cap are written
+ *
+ *   sel_mask  uint32 [L][B][ceil(N/32)]     z  fp32 [L][B][N]
+ *   surv_idx  out int32 [B][cap]  surv_z out fp32 [B][cap]  surv_count out int32 [B]
+ *   ws        device workspace of lsa_select_or_compact_workspace_bytes()
+ * Limits: 1 <= L <= LSA_MAX_VOTE_LAYERS, B >= 1, N >= 0, cap >= 0.
+ */
+size_t lsa_select_or_compact_workspace_bytes(int L, int B, int N);
+lsa_status lsa_select_or_compact(int L, int B, int N, const uint32_t* sel_mask,
+                                 const float* z, int cap, int32_t* surv_idx,
+                                 float* surv_z, int32_t* surv_count, void* ws,
+                                 size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Top-k inside the fetched set ([SUMMARY] 2.1 hierarchical-selection bullet:
+ * once the fetched subset is on the GPU, a fine-grained top-k runs inside
+ * it).  Ranking score: the merged logit surv_z (higher first); ties go to the
+ * lower entry index.  For every request b, with n = min(surv_count[b], cap):
+ *   topk_idx[b]   = the min(k, n) best survivors, in ASCENDING entry order,
+ *                   followed by -1 up to k
+ *   topk_count[b] = min(k, n)
+ *
+ *   surv_idx int32 [B][cap] (ascending), surv_z fp32 [B][cap], surv_count [B]
+ *   topk_idx out int32 [B][k]     topk_count out int32 [B]
+ *   ws       device workspace of lsa_topk_workspace_bytes()
+ * Limits: B >= 1, cap >= 0, k >= 0.
+ */
+size_t lsa_topk_workspace_bytes(int B, int cap, int k);
+lsa_status lsa_topk(int B, int cap, int k, const int32_t* surv_idx,
+                    const float* surv_z, const int32_t* surv_count,
+                    int32_t* topk_idx, int32_t* topk_count, void* ws,
+                    size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Hot-pool gather ([SUMMARY] 2.1 dynamic-fetch bullet: the selected
+ * compressed KV entries are brought into GPU memory).
+ *   hot[b][j] = pool[b][idx[b][j]]  (row_bytes bytes), zero row when
+ *   idx[b][j] < 0 or idx[b][j] >= N
+ *
+ *   pool  [B][N][row_bytes]   idx int32 [B][k]   hot out [B][k][row_bytes]
+ * Limits: row_bytes > 0 and a multiple of 16; pool and hot 16-byte aligned.
+ */
+lsa_status lsa_gather_hot(int B, int N, int k, int row_bytes, const void* pool,
+                          const int32_t* idx, void* hot, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Golden labels by cross-layer majority vote ([SUMMARY] 2.2 steps 1-3;
+ * [REVIEW] section 2, training labels).  For every query t and teacher
+ * layer l, over the N entries of the row logits[t][l]:
+ *   pi = softmax(row); walk entries in order (logit desc, index asc) and keep
+ *   each one while the mass already kept is < top_p (the entry crossing
+ *   top_p is kept);
+ * then count[t][s] = number of layers keeping s, label[t][s] = count >= theta.
+ *
+ *   logits          fp32 [Q][L][N] (finite values)
+ *   layer_mask_opt  out uint32 [Q][L][ceil(N/32)] or NULL
+ *   count           out uint8 [Q][N]        label  out uint8 [Q][N]
+ *   ws              device workspace of lsa_label_vote_workspace_bytes()
+ * Limits: Q >= 1, 1 <= L <= LSA_MAX_VOTE_LAYERS, 1 <= N <= 65536,
+ * 0 < top_p <= 1, theta >= 0.
+ */
+size_t lsa_label_vote_workspace_bytes(int Q, int L, int N);
+lsa_status lsa_label_vote(int Q, int L, int N, float top_p, int theta,
+                          const float* logits, uint32_t* layer_mask_opt,
+                          uint8_t* count, uint8_t* label, void* ws,
+                          size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Student loss and gradient ([SUMMARY] 2.3: keys frozen, only the query
+ * encoder's projection is trained, BCE combined with a focal loss; [REVIEW]
+ * section 2).  In fp32:
+ *   q_t = Wq h_t,  g_t = softplus(Wg h_t),  z_ts = sum_h g_th (q_th . K_s) + bias
+ *   loss = mean_ts BCE(z_ts, y_ts) + mean_ts (1 - p_t)^gamma BCE(z_ts, y_ts)
+ *   dWq  = d loss / d Wq
+ *
+ *   h     bf16 [Q][D]   Wq fp32 [H*dI][D]   Wg fp32 [H][D]   K bf16 [N][dI]
+ *   label uint8 [Q][N] (0 or 1)
+ *   loss  out fp32 [1]  dWq out fp32 [H*dI][D]
+ *   ws    device workspace of lsa_focal_bce_grad_workspace_bytes()
+ * Limits: 1 <= Q <= 64, N >= 1, D % 64 == 0, 1 <= H <= 64, dI in {64, 128}.
+ */
+size_t lsa_focal_bce_grad_workspace_bytes(int Q, int N, int D, int H, int dI);
+lsa_status lsa_focal_bce_grad(int Q, int N, int D, int H, int dI, float gamma,
+                              const uint16_t* h, const float* Wq,
+                              const float* Wg, float bias, const uint16_t* K,
+                              const uint8_t* label, float* loss, float* dWq,
+                              void* ws, size_t ws_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LSA_H */

@@ -8,7 +8,7 @@ direction and the score bias are supplied by the caller, and the stored values
 of both for the named workloads are written by a calibration script that runs
 the CPU oracle.
 
-Every draw comes from ``numpy.random.PCG64`` seeded with
+Every draw comes from ``numpy.random.SFC64`` seeded with
 ``SeedSequence([seed, workload_id, request, layer, tag])``, so any tensor can
 be regenerated alone and in any order.
 
@@ -26,7 +26,7 @@ from dataclasses import dataclass, field
 import numpy as np
 import torch
 
-GENERATOR_VERSION = 3
+GENERATOR_VERSION = 4
 
 _TAGS = {"h": 1, "wq": 2, "wg": 3, "plant": 4, "keys": 5, "logits": 6,
          "student": 7, "misc": 8}
@@ -35,7 +35,7 @@ _ALL = 0xFFFF  # "not per request / not per layer" slot in the seed tuple
 
 def stream(seed: int, wid: int, b: int, l: int, tag: str) -> np.random.Generator:
     ss = np.random.SeedSequence([seed, wid, b, l, _TAGS[tag]])
-    return np.random.Generator(np.random.PCG64(ss))
+    return np.random.Generator(np.random.SFC64(ss))
 
 
 @dataclass(frozen=True)
@@ -316,6 +316,23 @@ def indexer_inputs(w: Workload, calib: Calibration, threads: int = 8) -> Indexer
     return IndexerInputs(w=w, h=h, Wq=list(Wq), Wg=list(Wg), keys=keys_l,
                          scale=scale_l, bias=np.asarray(calib.bias, np.float32),
                          plant=plant)
+
+
+def to_device(inp: IndexerInputs, device="cuda"):
+    """Copy the inputs into device tensors: bf16 as torch.bfloat16, e4m3 codes
+    as uint8.  Returns a dict of tensors / lists of tensors."""
+    def t(x, dtype=None):
+        if x.dtype == np.uint16:
+            return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(device)
+        return torch.from_numpy(np.ascontiguousarray(x)).to(device)
+    return {
+        "h": t(inp.h),
+        "Wq": [t(w) for w in inp.Wq],
+        "Wg": [t(w) for w in inp.Wg],
+        "keys": [t(k) for k in inp.keys],
+        "scale": None if inp.scale[0] is None else [t(s) for s in inp.scale],
+        "bias": [float(b) for b in inp.bias],
+    }
 
 
 def bias_from_sorted(v: np.ndarray, frac: float) -> float:

@@ -1,0 +1,148 @@
+"""MI355X (gfx950) Lookahead Sparse Attention indexer hot path.
+
+A thin binding of ``liblsa.so``: every function below has the name of the C
+entry point it calls, turns torch tensors into device pointers and sizes, and
+raises ``LSAError`` on a non-OK status.  All computation happens in the HIP
+kernels; torch only provides device memory and streams.  If the library is not
+built, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes as C
+
+from ._abi import (LSA_KEY_BF16, LSA_KEY_FP8_E4M3, LSAError, check, load,
+                   ptr_array)
+
+__all__ = [
+    "LSAError", "LSA_KEY_BF16", "LSA_KEY_FP8_E4M3", "load", "lsa_version",
+    "lsa_trigger_due", "lsa_project_query", "lsa_score",
+    "lsa_select_or_compact_workspace_bytes", "lsa_select_or_compact",
+    "lsa_topk_workspace_bytes", "lsa_topk", "lsa_gather_hot",
+    "lsa_label_vote_workspace_bytes", "lsa_label_vote",
+    "lsa_focal_bce_grad_workspace_bytes", "lsa_focal_bce_grad",
+]
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+def _p(t):
+    return None if t is None else t.data_ptr()
+
+
+def _dev(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("LSA tensors must live on the GPU")
+        if t is not None and not t.is_contiguous():
+            raise ValueError("LSA tensors must be contiguous")
+
+
+def lsa_version() -> str:
+    return load().lsa_version().decode()
+
+
+def lsa_trigger_due(decode_step: int, tau: int = 64) -> bool:
+    return bool(load().lsa_trigger_due(int(decode_step), int(tau)))
+
+
+def lsa_project_query(h, Wq, Wg, q, g, *, h_layer_stride: int = 0, stream=None):
+    """h bf16 [B][D] (or [L][B][D] with h_layer_stride = B*D); Wq/Wg: lists of
+    L bf16 tensors [H*dI][D] / [H][D]; q out bf16 [L][B][H][dI]; g out f32 [L][B][H]."""
+    _dev(h, q, g, *Wq, *Wg)
+    L, B, H, dI = q.shape
+    D = h.shape[-1]
+    wq, _k1 = ptr_array([_p(w) for w in Wq])
+    wg, _k2 = ptr_array([_p(w) for w in Wg])
+    check(load().lsa_project_query(L, B, D, H, dI, _p(h), int(h_layer_stride), wq, wg, _p(q),
+                                   _p(g), _stream(stream)))
+
+
+def lsa_score(keys, key_scale, q, g, bias, z, sel_mask, I=None, *, stream=None):
+    """keys: list of L tensors [B][N][dI] (bf16 bits, or e4m3 codes with
+    key_scale a list of L fp32 [B][N]); bias: L host floats; z out f32
+    [L][B][N]; sel_mask out int32/uint32 [L][B][ceil(N/32)]; I optional out."""
+    fp8 = key_scale is not None
+    _dev(q, g, z, sel_mask, I, *keys, *(key_scale or []))
+    L, B, H, dI = q.shape
+    N = keys[0].shape[1]
+    kp, _k1 = ptr_array([_p(k) for k in keys])
+    if fp8:
+        sp, _k2 = ptr_array([_p(s) for s in key_scale])
+    else:
+        sp = None
+    b = (C.c_float * L)(*[float(x) for x in bias])
+    check(load().lsa_score(L, B, N, H, dI, LSA_KEY_FP8_E4M3 if fp8 else LSA_KEY_BF16, kp, sp,
+                           _p(q), _p(g), b, _p(z), _p(I), _p(sel_mask), _stream(stream)))
+
+
+def lsa_select_or_compact_workspace_bytes(L: int, B: int, N: int) -> int:
+    return int(load().lsa_select_or_compact_workspace_bytes(L, B, N))
+
+
+def lsa_select_or_compact(sel_mask, z, surv_idx, surv_z, surv_count, ws, *, stream=None):
+    """sel_mask [L][B][W], z f32 [L][B][N] -> surv_idx i32 [B][cap], surv_z f32
+    [B][cap], surv_count i32 [B]; ws: uint8 device workspace."""
+    _dev(sel_mask, z, surv_idx, surv_z, surv_count, ws)
+    L, B, N = z.shape
+    cap = surv_idx.shape[1]
+    check(load().lsa_select_or_compact(L, B, N, _p(sel_mask), _p(z), cap, _p(surv_idx),
+                                       _p(surv_z), _p(surv_count), _p(ws),
+                                       0 if ws is None else ws.numel() * ws.element_size(),
+                                       _stream(stream)))
+
+
+def lsa_topk_workspace_bytes(B: int, cap: int, k: int) -> int:
+    return int(load().lsa_topk_workspace_bytes(B, cap, k))
+
+
+def lsa_topk(surv_idx, surv_z, surv_count, topk_idx, topk_count, ws=None, *, stream=None):
+    _dev(surv_idx, surv_z, surv_count, topk_idx, topk_count, ws)
+    B, cap = surv_idx.shape
+    k = topk_idx.shape[1]
+    check(load().lsa_topk(B, cap, k, _p(surv_idx), _p(surv_z), _p(surv_count), _p(topk_idx),
+                          _p(topk_count), _p(ws),
+                          0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def lsa_gather_hot(pool, idx, hot, *, stream=None):
+    """pool [B][N][row] (any dtype), idx i32 [B][k], hot out [B][k][row]."""
+    _dev(pool, idx, hot)
+    B, N = pool.shape[0], pool.shape[1]
+    k = idx.shape[1]
+    row_bytes = pool[0, 0].numel() * pool.element_size() if N > 0 else hot[0, 0].numel() * hot.element_size()
+    check(load().lsa_gather_hot(B, N, k, row_bytes, _p(pool), _p(idx), _p(hot), _stream(stream)))
+
+
+def lsa_label_vote_workspace_bytes(Q: int, L: int, N: int) -> int:
+    return int(load().lsa_label_vote_workspace_bytes(Q, L, N))
+
+
+def lsa_label_vote(logits, top_p, theta, count, label, layer_mask=None, ws=None, *, stream=None):
+    """logits f32 [Q][L][N] -> count u8 [Q][N], label u8 [Q][N], optional
+    layer_mask [Q][L][ceil(N/32)]."""
+    _dev(logits, count, label, layer_mask, ws)
+    Q, L, N = logits.shape
+    check(load().lsa_label_vote(Q, L, N, float(top_p), int(theta), _p(logits), _p(layer_mask),
+                                _p(count), _p(label), _p(ws),
+                                0 if ws is None else ws.numel() * ws.element_size(),
+                                _stream(stream)))
+
+
+def lsa_focal_bce_grad_workspace_bytes(Q: int, N: int, D: int, H: int, dI: int) -> int:
+    return int(load().lsa_focal_bce_grad_workspace_bytes(Q, N, D, H, dI))
+
+
+def lsa_focal_bce_grad(h, Wq, Wg, bias, K, label, gamma, loss, dWq, ws=None, *, H: int,
+                       dI: int, stream=None):
+    _dev(h, Wq, Wg, K, label, loss, dWq, ws)
+    Q, D = h.shape
+    N = K.shape[0]
+    check(load().lsa_focal_bce_grad(Q, N, D, H, dI, float(gamma), _p(h), _p(Wq), _p(Wg),
+                                    float(bias), _p(K), _p(label), _p(loss), _p(dWq), _p(ws),
+                                    0 if ws is None else ws.numel() * ws.element_size(),
+                                    _stream(stream)))

@@ -1,0 +1,230 @@
+// lsa_api.cpp -- C ABI of liblsa.so: host-side argument validation and
+// dispatch to the gfx950 kernels.  Every check runs before any launch, so an
+// invalid call returns an error without touching device memory.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/lsa.h"
+#include "lsa_launch.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+lsa_status fail(lsa_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+lsa_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return LSA_OK;
+  return fail(LSA_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+#define REQUIRE(cond, st, ...)                      \
+  do {                                              \
+    if (!(cond)) return fail((st), __VA_ARGS__);    \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+const char* lsa_last_error(void) { return g_err; }
+
+const char* lsa_version(void) { return "lsa-gfx950 0.1"; }
+
+int lsa_trigger_due(int64_t decode_step, int tau) {
+  if (tau <= 0 || decode_step < 0) return 0;
+  return (decode_step % tau) == 0 ? 1 : 0;
+}
+
+// ---------------------------------------------------------------- projection
+
+lsa_status lsa_project_query(int L, int B, int D, int H, int dI, const uint16_t* h,
+                             int64_t h_layer_stride, const uint16_t* const* Wq,
+                             const uint16_t* const* Wg, uint16_t* q, float* g,
+                             hipStream_t stream) {
+  REQUIRE(L >= 1 && L <= LSA_MAX_LAYERS, LSA_E_SHAPE, "lsa_project_query: L=%d not in [1,%d]", L,
+          LSA_MAX_LAYERS);
+  REQUIRE(B >= 1, LSA_E_SHAPE, "lsa_project_query: B=%d < 1", B);
+  REQUIRE(D >= 256 && D % 256 == 0, LSA_E_SHAPE, "lsa_project_query: D=%d not a positive multiple of 256", D);
+  REQUIRE(H >= 1 && H <= LSA_MAX_HEADS, LSA_E_SHAPE, "lsa_project_query: H=%d not in [1,64]", H);
+  REQUIRE(dI == 64 || dI == 128, LSA_E_SHAPE, "lsa_project_query: dI=%d not 64 or 128", dI);
+  REQUIRE(h_layer_stride >= 0, LSA_E_ARG, "lsa_project_query: negative h_layer_stride");
+  REQUIRE(h && Wq && Wg && q && g, LSA_E_ARG, "lsa_project_query: null pointer argument");
+  REQUIRE(aligned16(h) && aligned16(q) && (h_layer_stride % 8) == 0, LSA_E_ARG,
+          "lsa_project_query: h/q must be 16-byte aligned (stride multiple of 8)");
+  lsa::ProjectArgs a{};
+  for (int l = 0; l < L; ++l) {
+    REQUIRE(Wq[l] && Wg[l], LSA_E_ARG, "lsa_project_query: null weight pointer for layer %d", l);
+    REQUIRE(aligned16(Wq[l]) && aligned16(Wg[l]), LSA_E_ARG,
+            "lsa_project_query: weights of layer %d not 16-byte aligned", l);
+    a.Wq[l] = Wq[l];
+    a.Wg[l] = Wg[l];
+  }
+  a.h = h;
+  a.h_layer_stride = h_layer_stride;
+  a.q = q;
+  a.g = g;
+  a.L = L;
+  a.B = B;
+  a.D = D;
+  a.H = H;
+  a.dI = dI;
+  return hip_status(lsa::launch_project(a, stream), "lsa_project_query launch");
+}
+
+// --------------------------------------------------------------------- score
+
+lsa_status lsa_score(int L, int B, int N, int H, int dI, lsa_key_dtype kdt,
+                     const void* const* keys, const float* const* key_scale, const uint16_t* q,
+                     const float* g, const float* bias, float* z, float* I_opt,
+                     uint32_t* sel_mask, hipStream_t stream) {
+  REQUIRE(kdt == LSA_KEY_BF16 || kdt == LSA_KEY_FP8_E4M3, LSA_E_DTYPE,
+          "lsa_score: unknown key dtype %d", (int)kdt);
+  REQUIRE(L >= 1 && L <= LSA_MAX_LAYERS, LSA_E_SHAPE, "lsa_score: L=%d not in [1,%d]", L,
+          LSA_MAX_LAYERS);
+  REQUIRE(B >= 1, LSA_E_SHAPE, "lsa_score: B=%d < 1", B);
+  REQUIRE(N >= 0, LSA_E_SHAPE, "lsa_score: N=%d < 0", N);
+  REQUIRE(H >= 1 && H <= LSA_MAX_HEADS, LSA_E_SHAPE, "lsa_score: H=%d not in [1,64]", H);
+  REQUIRE(dI == 64 || dI == 128, LSA_E_SHAPE, "lsa_score: dI=%d not 64 or 128", dI);
+  REQUIRE((long long)L * B <= 65535, LSA_E_SHAPE, "lsa_score: L*B=%lld > 65535", (long long)L * B);
+  REQUIRE(bias, LSA_E_ARG, "lsa_score: null bias array");
+  if (N == 0) return LSA_OK;   // nothing to score; outputs are empty
+  REQUIRE(keys && q && g && z && sel_mask, LSA_E_ARG, "lsa_score: null pointer argument");
+  REQUIRE(kdt == LSA_KEY_BF16 || key_scale, LSA_E_ARG, "lsa_score: e4m3 keys need key_scale");
+  REQUIRE(aligned16(q), LSA_E_ARG, "lsa_score: q must be 16-byte aligned");
+  lsa::ScoreArgs a{};
+  for (int l = 0; l < L; ++l) {
+    REQUIRE(keys[l], LSA_E_ARG, "lsa_score: null key pointer for layer %d", l);
+    REQUIRE(aligned16(keys[l]), LSA_E_ARG, "lsa_score: keys of layer %d not 16-byte aligned", l);
+    a.keys[l] = keys[l];
+    if (kdt == LSA_KEY_FP8_E4M3) {
+      REQUIRE(key_scale[l], LSA_E_ARG, "lsa_score: null key_scale pointer for layer %d", l);
+      a.scale[l] = key_scale[l];
+    }
+    a.bias[l] = bias[l];
+  }
+  a.q = q;
+  a.g = g;
+  a.z = z;
+  a.I = I_opt;
+  a.mask = sel_mask;
+  a.B = B;
+  a.N = N;
+  a.H = H;
+  a.W = (N + 31) / 32;
+  a.tiles_per_block = 128;
+  return hip_status(lsa::launch_score(L, dI, kdt, a, stream), "lsa_score launch");
+}
+
+// ----------------------------------------------------------- select/compact
+
+size_t lsa_select_or_compact_workspace_bytes(int L, int B, int N) {
+  (void)L;
+  if (B < 1 || N < 0) return 0;
+  return lsa::select_workspace(B, N);
+}
+
+lsa_status lsa_select_or_compact(int L, int B, int N, const uint32_t* sel_mask, const float* z,
+                                 int cap, int32_t* surv_idx, float* surv_z,
+                                 int32_t* surv_count, void* ws, size_t ws_bytes,
+                                 hipStream_t stream) {
+  REQUIRE(L >= 1 && L <= LSA_MAX_VOTE_LAYERS, LSA_E_SHAPE,
+          "lsa_select_or_compact: L=%d not in [1,%d]", L, LSA_MAX_VOTE_LAYERS);
+  REQUIRE(B >= 1 && B <= 65535, LSA_E_SHAPE, "lsa_select_or_compact: B=%d not in [1,65535]", B);
+  REQUIRE(N >= 0, LSA_E_SHAPE, "lsa_select_or_compact: N=%d < 0", N);
+  REQUIRE(cap >= 0, LSA_E_ARG, "lsa_select_or_compact: cap=%d < 0", cap);
+  REQUIRE(surv_count, LSA_E_ARG, "lsa_select_or_compact: null surv_count");
+  REQUIRE(N == 0 || (sel_mask && z), LSA_E_ARG, "lsa_select_or_compact: null sel_mask or z");
+  REQUIRE(cap == 0 || (surv_idx && surv_z), LSA_E_ARG,
+          "lsa_select_or_compact: null survivor output with cap > 0");
+  const size_t need = lsa::select_workspace(B, N);
+  REQUIRE(N == 0 || (ws && ws_bytes >= need), LSA_E_WORKSPACE,
+          "lsa_select_or_compact: workspace %zu bytes, need %zu", ws_bytes, need);
+  return hip_status(lsa::launch_select(L, B, N, sel_mask, z, cap, surv_idx, surv_z, surv_count,
+                                       ws, stream),
+                    "lsa_select_or_compact launch");
+}
+
+// --------------------------------------------------------------------- top-k
+
+size_t lsa_topk_workspace_bytes(int B, int cap, int k) {
+  (void)B;
+  (void)cap;
+  (void)k;
+  return 0;
+}
+
+lsa_status lsa_topk(int B, int cap, int k, const int32_t* surv_idx, const float* surv_z,
+                    const int32_t* surv_count, int32_t* topk_idx, int32_t* topk_count, void* ws,
+                    size_t ws_bytes, hipStream_t stream) {
+  (void)ws;
+  (void)ws_bytes;
+  REQUIRE(B >= 1 && B <= 65535, LSA_E_SHAPE, "lsa_topk: B=%d not in [1,65535]", B);
+  REQUIRE(cap >= 0 && k >= 0, LSA_E_ARG, "lsa_topk: negative cap or k");
+  REQUIRE(surv_count && topk_count, LSA_E_ARG, "lsa_topk: null count pointer");
+  REQUIRE(cap == 0 || (surv_idx && surv_z), LSA_E_ARG, "lsa_topk: null survivor input");
+  REQUIRE(k == 0 || topk_idx, LSA_E_ARG, "lsa_topk: null topk_idx with k > 0");
+  return hip_status(
+      lsa::launch_topk(B, cap, k, surv_idx, surv_z, surv_count, topk_idx, topk_count, stream),
+      "lsa_topk launch");
+}
+
+// -------------------------------------------------------------------- gather
+
+lsa_status lsa_gather_hot(int B, int N, int k, int row_bytes, const void* pool,
+                          const int32_t* idx, void* hot, hipStream_t stream) {
+  REQUIRE(B >= 1 && N >= 0 && k >= 0, LSA_E_SHAPE, "lsa_gather_hot: bad B/N/k (%d,%d,%d)", B, N, k);
+  REQUIRE(row_bytes > 0 && row_bytes % 16 == 0, LSA_E_ARG,
+          "lsa_gather_hot: row_bytes=%d not a positive multiple of 16", row_bytes);
+  if (k == 0) return LSA_OK;
+  REQUIRE(idx && hot && (N == 0 || pool), LSA_E_ARG, "lsa_gather_hot: null pointer argument");
+  REQUIRE(aligned16(hot) && (N == 0 || aligned16(pool)), LSA_E_ARG,
+          "lsa_gather_hot: pool/hot not 16-byte aligned");
+  return hip_status(lsa::launch_gather(B, N, k, row_bytes, pool, idx, hot, stream),
+                    "lsa_gather_hot launch");
+}
+
+// -------------------------------------------------------- label / loss calls
+
+size_t lsa_label_vote_workspace_bytes(int Q, int L, int N) {
+  (void)Q;
+  (void)L;
+  (void)N;
+  return 0;
+}
+
+lsa_status lsa_label_vote(int Q, int L, int N, float top_p, int theta, const float* logits,
+                          uint32_t* layer_mask_opt, uint8_t* count, uint8_t* label, void* ws,
+                          size_t ws_bytes, hipStream_t stream) {
+  (void)Q; (void)L; (void)N; (void)top_p; (void)theta; (void)logits; (void)layer_mask_opt;
+  (void)count; (void)label; (void)ws; (void)ws_bytes; (void)stream;
+  return fail(LSA_E_ARG, "lsa_label_vote: not built in this library");
+}
+
+size_t lsa_focal_bce_grad_workspace_bytes(int Q, int N, int D, int H, int dI) {
+  (void)Q; (void)N; (void)D; (void)H; (void)dI;
+  return 0;
+}
+
+lsa_status lsa_focal_bce_grad(int Q, int N, int D, int H, int dI, float gamma,
+                              const uint16_t* h, const float* Wq, const float* Wg, float bias,
+                              const uint16_t* K, const uint8_t* label, float* loss, float* dWq,
+                              void* ws, size_t ws_bytes, hipStream_t stream) {
+  (void)Q; (void)N; (void)D; (void)H; (void)dI; (void)gamma; (void)h; (void)Wq; (void)Wg;
+  (void)bias; (void)K; (void)label; (void)loss; (void)dWq; (void)ws; (void)ws_bytes; (void)stream;
+  return fail(LSA_E_ARG, "lsa_focal_bce_grad: not built in this library");
+}
+
+}  // extern "C"

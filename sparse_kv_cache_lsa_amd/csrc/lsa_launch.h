@@ -1,0 +1,55 @@
+// lsa_launch.h -- internal host-side launchers (one per kernel family).  The
+// C ABI in lsa_api.cpp validates arguments and then calls these.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include "../../include/lsa.h"
+
+namespace lsa {
+
+struct ScoreArgs {
+  const void* keys[LSA_MAX_LAYERS];
+  const float* scale[LSA_MAX_LAYERS];
+  float bias[LSA_MAX_LAYERS];
+  const uint16_t* q;
+  const float* g;
+  float* z;
+  float* I;
+  uint32_t* mask;
+  int B, N, H, W;          // W = ceil(N / 32)
+  int tiles_per_block;
+};
+
+hipError_t launch_score(int L, int dI, lsa_key_dtype kdt, const ScoreArgs& a,
+                        hipStream_t s);
+
+struct ProjectArgs {
+  const uint16_t* Wq[LSA_MAX_LAYERS];
+  const uint16_t* Wg[LSA_MAX_LAYERS];
+  const uint16_t* h;
+  int64_t h_layer_stride;
+  uint16_t* q;
+  float* g;
+  int L, B, D, H, dI;
+};
+
+hipError_t launch_project(const ProjectArgs& a, hipStream_t s);
+
+size_t select_workspace(int B, int N);
+hipError_t launch_select(int L, int B, int N, const uint32_t* mask,
+                         const float* z, int cap, int32_t* surv_idx,
+                         float* surv_z, int32_t* surv_count, void* ws,
+                         hipStream_t s);
+
+hipError_t launch_topk(int B, int cap, int k, const int32_t* surv_idx,
+                       const float* surv_z, const int32_t* surv_count,
+                       int32_t* topk_idx, int32_t* topk_count, hipStream_t s);
+
+hipError_t launch_gather(int B, int N, int k, int row_bytes, const void* pool,
+                         const int32_t* idx, void* hot, hipStream_t s);
+
+hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s);
+
+}  // namespace lsa

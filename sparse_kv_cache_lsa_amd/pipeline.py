@@ -1,0 +1,63 @@
+"""Device buffers for one indexer trigger and the call sequence of the hot
+path (project -> score -> select/compact -> top-k -> gather).  Allocation uses
+torch; every step is one C entry point of liblsa.so."""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+from . import (lsa_gather_hot, lsa_project_query, lsa_score, lsa_select_or_compact,
+               lsa_select_or_compact_workspace_bytes, lsa_topk, lsa_topk_workspace_bytes)
+
+
+@dataclass
+class TriggerBuffers:
+    q: object
+    g: object
+    z: object
+    mask: object
+    surv_idx: object
+    surv_z: object
+    surv_count: object
+    ws_select: object
+    ws_topk: object
+    topk_idx: object
+    topk_count: object
+    hot: object
+
+    @classmethod
+    def allocate(cls, L, B, N, H, dI, k, row_elems=512, cap=None, device="cuda"):
+        import torch
+        cap = N if cap is None else cap
+        W = (N + 31) // 32
+        u8 = torch.uint8
+        return cls(
+            q=torch.empty((L, B, H, dI), dtype=torch.bfloat16, device=device),
+            g=torch.empty((L, B, H), dtype=torch.float32, device=device),
+            z=torch.empty((L, B, N), dtype=torch.float32, device=device),
+            mask=torch.empty((L, B, W), dtype=torch.int32, device=device),
+            surv_idx=torch.empty((B, cap), dtype=torch.int32, device=device),
+            surv_z=torch.empty((B, cap), dtype=torch.float32, device=device),
+            surv_count=torch.empty((B,), dtype=torch.int32, device=device),
+            ws_select=torch.empty((max(1, lsa_select_or_compact_workspace_bytes(L, B, N)),),
+                                  dtype=u8, device=device),
+            ws_topk=torch.empty((max(1, lsa_topk_workspace_bytes(B, cap, k)),), dtype=u8,
+                                device=device),
+            topk_idx=torch.empty((B, k), dtype=torch.int32, device=device),
+            topk_count=torch.empty((B,), dtype=torch.int32, device=device),
+            hot=torch.empty((B, k, max(row_elems, 8)), dtype=torch.int16, device=device),
+        )
+
+
+def run_trigger(buf: TriggerBuffers, h, Wq, Wg, keys, key_scale, bias, pool=None, *,
+                stream=None, project=True):
+    """One indexer trigger.  With project=False the query buffers are used as
+    they are (the caller filled buf.q / buf.g)."""
+    if project:
+        lsa_project_query(h, Wq, Wg, buf.q, buf.g, stream=stream)
+    lsa_score(keys, key_scale, buf.q, buf.g, bias, buf.z, buf.mask, stream=stream)
+    lsa_select_or_compact(buf.mask, buf.z, buf.surv_idx, buf.surv_z, buf.surv_count,
+                          buf.ws_select, stream=stream)
+    lsa_topk(buf.surv_idx, buf.surv_z, buf.surv_count, buf.topk_idx, buf.topk_count,
+             buf.ws_topk, stream=stream)
+    if pool is not None:
+        lsa_gather_hot(pool, buf.topk_idx, buf.hot, stream=stream)

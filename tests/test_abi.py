@@ -1,0 +1,102 @@
+"""The C ABI without a GPU: the library loads, exports every entry point the
+header declares, and its host-only logic (trigger cadence, workspace sizes,
+argument validation that returns before any launch) behaves as documented."""
+import ctypes as C
+import math
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lsa.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lsa_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from sparse_kv_cache_lsa_amd import _abi
+    if not os.path.exists(_abi.LIB_PATH):
+        from sparse_kv_cache_lsa_amd import build
+        build.build()
+    return _abi.load()
+
+
+def test_header_symbols_exported(lib):
+    names = _declared()
+    assert len(names) >= 14
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in lsa.h but not exported"
+    from sparse_kv_cache_lsa_amd import _abi
+    assert set(names) == set(_abi.SIGNATURES), "binding signatures out of sync with lsa.h"
+
+
+def test_binding_names_match_entry_points():
+    import sparse_kv_cache_lsa_amd as pkg
+    for n in _declared():
+        if n in ("lsa_last_error",):
+            continue
+        assert hasattr(pkg, n), f"python binding lacks {n}"
+
+
+def test_trigger_cadence(lib):
+    due = [t for t in range(300) if lib.lsa_trigger_due(t, 64)]
+    assert due == [0, 64, 128, 192, 256]
+    for T in (1, 64, 65, 1000):
+        assert sum(lib.lsa_trigger_due(t, 64) for t in range(T)) == math.ceil(T / 64)
+    assert lib.lsa_trigger_due(-64, 64) == 0 and lib.lsa_trigger_due(5, 0) == 0
+
+
+def test_workspace_sizes(lib):
+    assert lib.lsa_select_or_compact_workspace_bytes(3, 32, 262144) >= 32 * 32 * 4
+    assert lib.lsa_select_or_compact_workspace_bytes(3, 1, 1) >= 4
+
+
+def _status(lib, name, *args):
+    return getattr(lib, name)(*args)
+
+
+def test_validation_errors_return_before_launch(lib):
+    from sparse_kv_cache_lsa_amd import _abi
+    P = None
+    fake = C.c_void_p(16)   # never dereferenced: validation fails first
+    arr, _keep = _abi.ptr_array([16])
+    bias = (C.c_float * 1)(0.0)
+    # bad dtype
+    st = lib.lsa_score(1, 1, 64, 8, 64, 7, arr, None, fake, fake, bias, fake, None, fake, None)
+    assert st == _abi.LSA_E_DTYPE and b"dtype" in lib.lsa_last_error()
+    # unsupported head dim
+    st = lib.lsa_score(1, 1, 64, 8, 96, 0, arr, None, fake, fake, bias, fake, None, fake, None)
+    assert st == _abi.LSA_E_SHAPE and b"dI" in lib.lsa_last_error()
+    # too many heads, too many layers
+    assert lib.lsa_score(1, 1, 64, 65, 64, 0, arr, None, fake, fake, bias, fake, None, fake, None) == _abi.LSA_E_SHAPE
+    assert lib.lsa_score(9, 1, 64, 8, 64, 0, arr, None, fake, fake, bias, fake, None, fake, None) == _abi.LSA_E_SHAPE
+    # e4m3 without scales
+    assert lib.lsa_score(1, 1, 64, 8, 64, 1, arr, None, fake, fake, bias, fake, None, fake, None) == _abi.LSA_E_ARG
+    # null output
+    assert lib.lsa_score(1, 1, 64, 8, 64, 0, arr, None, fake, fake, bias, P, None, fake, None) == _abi.LSA_E_ARG
+    # misaligned query
+    assert lib.lsa_score(1, 1, 64, 8, 64, 0, arr, None, C.c_void_p(18), fake, bias, fake, None, fake, None) == _abi.LSA_E_ARG
+    # select: workspace too small
+    st = lib.lsa_select_or_compact(3, 2, 1000, fake, fake, 1000, fake, fake, fake, fake, 1, None)
+    assert st == _abi.LSA_E_WORKSPACE
+    assert lib.lsa_select_or_compact(3, 2, 1000, fake, fake, -1, fake, fake, fake, fake, 1 << 20, None) == _abi.LSA_E_ARG
+    # top-k: negative k
+    assert lib.lsa_topk(1, 10, -1, fake, fake, fake, fake, fake, None, 0, None) == _abi.LSA_E_ARG
+    # gather: row size not a multiple of 16
+    assert lib.lsa_gather_hot(1, 10, 4, 24, fake, fake, fake, None) == _abi.LSA_E_ARG
+    # projection: hidden size not a multiple of 256
+    assert lib.lsa_project_query(1, 1, 100, 8, 64, fake, 0, arr, arr, fake, fake, None) == _abi.LSA_E_SHAPE
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    from sparse_kv_cache_lsa_amd import _abi
+    monkeypatch.setattr(_abi, "_lib", None)
+    monkeypatch.setattr(_abi, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        _abi.load()

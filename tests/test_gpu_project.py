@@ -1,0 +1,68 @@
+"""Parity of lsa_project_query (MFMA query encoder) with the oracle.
+
+q is bf16: bit-exact except where the oracle's fp64 pre-rounding value lies
+within 1e-6 * sum_d |W h| of a bf16 rounding boundary (the GPU accumulates in
+fp32, whose error on these sums is far below that).  g is fp32: relative
+1e-5."""
+import numpy as np
+import pytest
+import torch
+
+import lsa_inputs as gen
+import sparse_kv_cache_lsa_amd as lsa
+from gpu_util import DEV, bf16_dev, bf16_host, dev, host
+from oracle import oracle
+
+pytestmark = pytest.mark.gpu
+
+
+def _bf16_boundary_distance(a):
+    """Distance of each fp64 value to the nearest bf16 rounding midpoint."""
+    a = np.asarray(a, np.float64)
+    m = np.abs(a)
+    e = np.floor(np.log2(np.maximum(m, 1e-300)))
+    ulp = np.exp2(e - 7)
+    frac = m / ulp - np.floor(m / ulp)
+    return np.abs(frac - 0.5) * ulp
+
+
+def _run_and_check(w: gen.Workload, h=None, stride=0):
+    h = gen.hidden(w) if h is None else h
+    Wq, Wg = zip(*[gen.weights(w, l) for l in range(w.L)])
+    q = torch.empty((w.L, w.B, w.H, w.dI), dtype=torch.bfloat16, device=DEV)
+    g = torch.empty((w.L, w.B, w.H), dtype=torch.float32, device=DEV)
+    lsa.lsa_project_query(bf16_dev(h), [bf16_dev(x) for x in Wq], [bf16_dev(x) for x in Wg],
+                          q, g, h_layer_stride=stride)
+    torch.cuda.synchronize()
+    qg, gg = bf16_host(q), host(g)
+    excluded = 0
+    for l in range(w.L):
+        for b in range(w.B):
+            hb = h[l * (stride // w.D) + b] if stride else h[b]
+            qo, go, a = oracle.project(hb, Wq[l], Wg[l], w.H, w.dI, want_a=True)
+            S = np.abs(gen.bf16_bits_to_f32(Wq[l]).astype(np.float64)) @ np.abs(
+                gen.bf16_bits_to_f32(hb).astype(np.float64))
+            band = _bf16_boundary_distance(a.ravel()) <= 1e-6 * S
+            diff = qg[l, b].ravel() != qo.ravel()
+            assert not (diff & ~band).any(), f"layer {l} request {b}: {(diff & ~band).sum()} q mismatches"
+            excluded += int(band.sum())
+            np.testing.assert_allclose(gg[l, b], go, rtol=1e-5, atol=1e-7)
+    return excluded
+
+
+@pytest.mark.parametrize("name", ["tiny", "ctx128k"])
+def test_project_named_workloads(name):
+    print("excluded", _run_and_check(gen.WORKLOADS[name]))
+
+
+@pytest.mark.parametrize("B", [5, 33])
+def test_project_request_groups(B):
+    w = gen.custom("proj", 91, B=B, L=2, H=40, dI=64, D=768, N=64)
+    _run_and_check(w)
+
+
+def test_project_per_layer_hidden_states():
+    w = gen.custom("proj2", 92, B=3, L=2, H=8, dI=128, D=512, N=64)
+    rng = np.random.default_rng(3)
+    h = gen.to_bf16_bits(rng.standard_normal((w.L * w.B, w.D)).astype(np.float32))
+    _run_and_check(w, h=h, stride=w.B * w.D)

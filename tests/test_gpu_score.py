@@ -1,0 +1,123 @@
+"""Parity of lsa_score (MFMA contraction + fused epilogue) with the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import lsa_inputs as gen
+import sparse_kv_cache_lsa_amd as lsa
+import parity
+from gpu_util import DEV, bf16_dev, dev, host
+from oracle import oracle
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(seed, L, B, N, H, dI, e4m3):
+    rng = np.random.default_rng(seed)
+    q = gen.to_bf16_bits(rng.standard_normal((L, B, H, dI)).astype(np.float32))
+    g = rng.uniform(0.1, 1.5, (L, B, H)).astype(np.float32)
+    keys, scales = [], []
+    for l in range(L):
+        x = (rng.standard_normal((B, N, dI)) / np.sqrt(dI)).astype(np.float32)
+        if e4m3:
+            c, s = gen.to_e4m3_rows(x.reshape(-1, dI))
+            keys.append(c.reshape(B, N, dI))
+            scales.append(s.reshape(B, N))
+        else:
+            keys.append(gen.to_bf16_bits(x))
+            scales.append(None)
+    bias = rng.uniform(-1.0, 1.0, L).astype(np.float32)
+    return q, g, keys, scales, bias
+
+
+def _run(q, g, keys, scales, bias, want_I=True):
+    L, B, H, dI = q.shape
+    N = keys[0].shape[1]
+    W = (N + 31) // 32
+    z = torch.full((L, B, N), float("nan"), dtype=torch.float32, device=DEV)
+    I = torch.full((L, B, N), float("nan"), dtype=torch.float32, device=DEV) if want_I else None
+    mask = torch.full((L, B, max(W, 1)), -1, dtype=torch.int32, device=DEV)
+    lsa.lsa_score([dev(k) for k in keys], None if scales[0] is None else [dev(s) for s in scales],
+                  bf16_dev(q), dev(g), bias, z, mask[..., :W] if W else mask, I)
+    torch.cuda.synchronize()
+    return host(z), (host(I) if want_I else None), host(mask)
+
+
+def _check(q, g, keys, scales, bias, z, I, mask):
+    L, B, H, dI = q.shape
+    N = keys[0].shape[1]
+    W = (N + 31) // 32
+    worst = 0.0
+    for l in range(L):
+        for b in range(B):
+            z_or = oracle.score(keys[l][b], None if scales[l] is None else scales[l][b],
+                                q[l, b], g[l, b], float(bias[l]))
+            d = parity.check_scores(z[l, b], z_or, None if I is None else I[l, b])
+            worst = max(worst, d["max_dz"])
+            sel = parity.unpack_mask(mask[l, b, :W], W * 32)
+            parity.check_selection(sel[:N], z_or)
+            assert not sel[N:].any(), "selection bits set past N"
+    return worst
+
+
+CASES = [
+    # (L, B, N, H, dI, e4m3)
+    (1, 1, 4096, 8, 64, False),
+    (1, 1, 1000, 64, 128, False),
+    (1, 1, 1000, 64, 128, True),
+    (1, 1, 4129, 33, 64, True),
+    (1, 1, 31, 1, 128, False),
+    (1, 1, 1, 64, 128, True),
+    (1, 2, 257, 64, 64, False),
+    (3, 2, 5000, 64, 128, False),
+    (3, 2, 5000, 64, 128, True),
+    (2, 3, 8192 + 33, 17, 128, True),
+]
+
+
+@pytest.mark.parametrize("L,B,N,H,dI,e4m3", CASES)
+def test_score_matches_oracle(L, B, N, H, dI, e4m3):
+    q, g, keys, scales, bias = _case(1000 + N + H, L, B, N, H, dI, e4m3)
+    z, I, mask = _run(q, g, keys, scales, bias)
+    worst = _check(q, g, keys, scales, bias, z, I, mask)
+    print(f"max |dz| = {worst:.3g}")
+
+
+def test_score_without_sigmoid_output():
+    q, g, keys, scales, bias = _case(7, 1, 1, 3000, 64, 128, True)
+    z, _, mask = _run(q, g, keys, scales, bias, want_I=False)
+    _check(q, g, keys, scales, bias, z, None, mask)
+
+
+def test_score_n_zero_launches_nothing():
+    q, g, keys, scales, bias = _case(8, 1, 1, 0, 8, 64, False)
+    z = torch.empty((1, 1, 0), device=DEV)
+    mask = torch.empty((1, 1, 0), dtype=torch.int32, device=DEV)
+    lsa.lsa_score([dev(keys[0])], None, bf16_dev(q), dev(g), bias, z, mask)
+
+
+def test_score_deterministic():
+    q, g, keys, scales, bias = _case(9, 2, 2, 20000, 64, 128, True)
+    a = _run(q, g, keys, scales, bias)
+    b = _run(q, g, keys, scales, bias)
+    for x, y in zip(a, b):
+        assert np.array_equal(x.view(np.uint32), y.view(np.uint32))
+
+
+def test_e4m3_widening_is_exact():
+    # every finite e4m3 code, one per key dimension, a one-hot query row:
+    # z must equal the decoded code exactly
+    dI = 128
+    codes = np.arange(256, dtype=np.uint8)
+    codes = codes[(codes & 0x7F) != 0x7F]                       # drop the two NaNs
+    N = codes.size
+    keys = np.zeros((1, N, dI), np.uint8)
+    keys[0, :, 5] = codes
+    scale = np.ones((1, N), np.float32)
+    qv = np.zeros((1, 1, 1, dI), np.float32)
+    qv[..., 5] = 1.0
+    q = gen.to_bf16_bits(qv)
+    g = np.ones((1, 1, 1), np.float32)
+    z, _, _ = _run(q, g, [keys], [scale], np.zeros(1, np.float32))
+    want = oracle.e4m3_to_double(codes)
+    assert np.array_equal(z[0, 0].astype(np.float64), want)

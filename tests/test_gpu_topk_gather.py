@@ -1,0 +1,90 @@
+"""Parity of lsa_topk and lsa_gather_hot with the oracle (bit-exact: both
+rank the same fp32 values, and the gather is a byte copy)."""
+import numpy as np
+import pytest
+import torch
+
+import sparse_kv_cache_lsa_amd as lsa
+from gpu_util import DEV, dev, host
+from oracle import oracle
+
+pytestmark = pytest.mark.gpu
+
+
+def _survivors(rng, B, cap, ns, N=300_000, ties=False):
+    idx = np.full((B, cap), -9, np.int32)
+    z = np.full((B, cap), np.nan, np.float32)
+    for b, n in enumerate(ns):
+        n = min(n, cap)
+        idx[b, :n] = np.sort(rng.choice(N, n, replace=False))
+        v = rng.standard_normal(n) * 20 + 30
+        if ties:
+            v = np.round(v)          # many exact ties
+        z[b, :n] = v.astype(np.float32)
+    return idx, z
+
+
+def _topk(idx, z, counts, k):
+    B, cap = idx.shape
+    out = torch.full((B, max(k, 1)), -5, dtype=torch.int32, device=DEV)
+    oc = torch.full((B,), -5, dtype=torch.int32, device=DEV)
+    o = out[:, :k].contiguous() if k else torch.empty((B, 0), dtype=torch.int32, device=DEV)
+    lsa.lsa_topk(dev(idx), dev(z), dev(np.asarray(counts, np.int32)), o, oc)
+    torch.cuda.synchronize()
+    return host(o), host(oc)
+
+
+@pytest.mark.parametrize("ns,k", [
+    ([0, 1, 5], 4),
+    ([100, 2048, 2049], 2048),
+    ([10000, 63000, 4097], 2048),
+    ([70000, 3, 2], 256),
+    ([500, 600, 700], 1),
+    ([5000, 5000, 5000], 0),
+])
+@pytest.mark.parametrize("ties", [False, True])
+def test_topk_matches_oracle(ns, k, ties):
+    rng = np.random.default_rng(sum(ns) + k + ties)
+    cap = max(max(ns), 1)
+    idx, z = _survivors(rng, len(ns), cap, ns, ties=ties)
+    out, oc = _topk(idx, z, ns, k)
+    for b, n in enumerate(ns):
+        want, cnt = oracle.topk(idx[b, :n], z[b, :n].astype(np.float64), k)
+        assert oc[b] == cnt
+        assert np.array_equal(out[b], want), f"request {b}"
+
+
+def test_topk_count_above_capacity_uses_capacity():
+    rng = np.random.default_rng(5)
+    idx, z = _survivors(rng, 2, 3000, [3000, 3000])
+    out, oc = _topk(idx, z, [9999, 3000], 1000)
+    for b in range(2):
+        want, cnt = oracle.topk(idx[b], z[b].astype(np.float64), 1000)
+        assert np.array_equal(out[b], want) and oc[b] == cnt
+
+
+def test_topk_signed_zero_ties_and_equal_scores():
+    idx = np.arange(10, 30, dtype=np.int32).reshape(1, 20) * 3
+    z = np.zeros((1, 20), np.float32)
+    z[0, ::2] = -0.0
+    out, oc = _topk(idx, z, [20], 7)
+    assert out[0].tolist() == idx[0, :7].tolist()      # all equal: lowest indices
+    z2 = np.full((1, 20), 5.0, np.float32)
+    z2[0, 13] = 6.0
+    out, _ = _topk(idx, z2, [20], 3)
+    assert out[0].tolist() == sorted([idx[0, 13], idx[0, 0], idx[0, 1]])
+
+
+@pytest.mark.parametrize("row_bytes", [1024, 48, 16])
+def test_gather_matches_oracle(row_bytes):
+    rng = np.random.default_rng(row_bytes)
+    B, N, k = 3, 5000, 700
+    pool = rng.integers(0, 256, (B, N, row_bytes), dtype=np.uint8)
+    idx = rng.integers(-3, N + 3, (B, k)).astype(np.int32)
+    idx[:, :5] = [-1, 0, N - 1, N, 2 * N]
+    hot = torch.full((B, k, row_bytes), 0xAB, dtype=torch.uint8, device=DEV)
+    lsa.lsa_gather_hot(dev(pool), dev(idx), hot)
+    torch.cuda.synchronize()
+    got = host(hot)
+    for b in range(B):
+        assert np.array_equal(got[b], oracle.gather(pool[b], idx[b]))

@@ -1,0 +1,209 @@
+#!/usr/bin/env python3
+"""Benchmark of the LSA indexer hot path on one MI355X.
+
+One step = one indexer trigger over one batch: query projection, score +
+threshold, three-layer OR + compaction, top-k, hot-pool gather (all five C
+entry points).  Default workload: 1M-token context (262,144 compressed entries
+per layer), 3 indexer layers, 32 concurrent requests, e4m3 keys with one fp32
+scale per entry, top-k 2048, 1 KiB KV rows.
+
+Prints ONE JSON line.  `value` is (request, layer, entry) triples scored and
+selected per second of whole-step time; the `roofline` object is for the
+dominant kernel, lsa_score, whose per-launch time comes from HIP events
+recorded on the stream the kernels run on, inside the timed region.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak, GB/s
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "lsa_score_ctx1m_traffic.json")
+
+
+def score_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("lsa_score.hip", "lsa_device.h"):
+        with open(os.path.join(ROOT, "sparse_kv_cache_lsa_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="ctx1m")
+    p.add_argument("--skip-cpu", action="store_true", help="do not time the CPU oracle")
+    p.add_argument("--cpu-seconds", type=float, default=12.0,
+                   help="CPU oracle sample budget (whole requests until this much time)")
+    p.add_argument("--copy-probe", type=int, default=0,
+                   help="also run a plain device copy of this many MiB (counter calibration)")
+    p.add_argument("--threads", type=int, default=16)
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    torch.cuda.init()
+    torch.empty(1, device="cuda")
+
+    import lsa_inputs as gen
+    import sparse_kv_cache_lsa_amd as lsa
+    from sparse_kv_cache_lsa_amd.pipeline import TriggerBuffers
+
+    w = gen.WORKLOADS[args.workload]
+    dev = "cuda"
+    t0 = time.time()
+    calib = gen.load_calibration(w)
+    inp = gen.indexer_inputs(w, calib, threads=args.threads)
+    d = gen.to_device(inp, dev)
+    pool = gen.pool_tensor(w, dev)
+    buf = TriggerBuffers.allocate(w.L, w.B, w.N, w.H, w.dI, w.k, w.row_elems, device=dev)
+    torch.cuda.synchronize()
+    print(f"# inputs ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+
+    stream = torch.cuda.current_stream()
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def step(events=None):
+        if events is not None:
+            events[0].record(stream)
+        lsa.lsa_project_query(d["h"], d["Wq"], d["Wg"], buf.q, buf.g, stream=stream)
+        if events is not None:
+            events[1].record(stream)
+        lsa.lsa_score(d["keys"], d["scale"], buf.q, buf.g, d["bias"], buf.z, buf.mask,
+                      stream=stream)
+        if events is not None:
+            events[2].record(stream)
+        lsa.lsa_select_or_compact(buf.mask, buf.z, buf.surv_idx, buf.surv_z, buf.surv_count,
+                                  buf.ws_select, stream=stream)
+        if events is not None:
+            events[3].record(stream)
+        lsa.lsa_topk(buf.surv_idx, buf.surv_z, buf.surv_count, buf.topk_idx, buf.topk_count,
+                     buf.ws_topk, stream=stream)
+        if events is not None:
+            events[4].record(stream)
+        lsa.lsa_gather_hot(pool, buf.topk_idx, buf.hot, stream=stream)
+        if events is not None:
+            events[5].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: K steps between two synchronisations; HIP events on the
+    # kernels' stream bracket every call (recording an event is one stream
+    # command, no host synchronisation)
+    evs = [[ev() for _ in range(6)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for e in evs:
+        step(e)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    ms_per_step = wall * 1e3 / max(args.steps, 1)
+    names = ["project", "score", "select", "topk", "gather"]
+    per = {n: float(np.median([e[i].elapsed_time(e[i + 1]) for e in evs])) for i, n in enumerate(names)}
+    mean_score = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    score_select = float(np.median([e[1].elapsed_time(e[3]) for e in evs]))
+
+    triples = w.triples
+    key_bytes = triples * w.key_bytes_per_entry
+    achieved = key_bytes / (mean_score * 1e-3) / 1e9
+    ss_gbs = key_bytes / (score_select * 1e-3) / 1e9
+
+    traffic = None
+    if os.path.exists(PROFILE_TRAFFIC):
+        with open(PROFILE_TRAFFIC) as f:
+            tr = json.load(f)
+        if tr.get("kernel_source_hash") == score_source_hash() and tr.get("workload") == w.name:
+            traffic = tr.get("traffic_bytes_per_launch")
+
+    counts = buf.surv_count.cpu().numpy()
+    result = {
+        "metric": "compressed entries scored+selected/sec at 1M ctx; % of peak HBM GB/s",
+        "value": triples / (ms_per_step * 1e-3),
+        "unit": "(request, layer, entry) triples/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "requests": w.B, "indexer_layers": w.L,
+                   "entries_per_layer": w.N, "context_tokens": 4 * w.N, "heads": w.H,
+                   "head_dim": w.dI, "hidden": w.D, "key_dtype": w.key_dtype, "top_k": w.k,
+                   "kv_row_bytes": 2 * w.row_elems, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": "lsa_score", "algorithmic_bytes_per_launch": key_bytes,
+                     "mean_launch_ms": mean_score},
+        "score_select": {"ms": score_select, "GB/s": ss_gbs, "frac_of_peak": ss_gbs / HBM_PEAK_GBS,
+                         "triples_per_s": triples / (score_select * 1e-3)},
+        "kernel_ms_median": per,
+        "survivor_fraction": float(counts.mean() / w.N),
+    }
+
+    if args.copy_probe:
+        n = args.copy_probe << 20
+        a = torch.empty(n, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        result["copy_probe_bytes"] = n
+
+    if not args.skip_cpu:
+        result["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(w, inp, budget_s):
+    """The CPU oracle as it stands, on whole requests of the same workload
+    (all layers: projection, score, threshold, OR/compaction, top-k) until
+    the time budget is used; throughput in triples/s."""
+    import numpy as np
+    from oracle import oracle
+    oracle._load()
+    t0 = time.perf_counter()
+    done = 0
+    b = 0
+    while b < w.B and (time.perf_counter() - t0) < budget_s:
+        zs = []
+        for l in range(w.L):
+            q, g = oracle.project(inp.h[b], inp.Wq[l], inp.Wg[l], w.H, w.dI)
+            zs.append(oracle.score(inp.keys[l][b], None if inp.scale[l] is None else inp.scale[l][b],
+                                   q, g, float(inp.bias[l])))
+        z = np.stack(zs)
+        surv, zstar, _ = oracle.merge_compact(oracle.threshold(z), z)
+        oracle.topk(surv, zstar, w.k)
+        done += 1
+        b += 1
+    el = time.perf_counter() - t0
+    return {"value": done * w.L * w.N / el, "unit": "(request, layer, entry) triples/s",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{done} of {w.B} requests x {w.L} layers x {w.N} entries "
+                      f"(project+score+threshold+OR/compact+top-k), {el:.1f}s"}
+
+
+if __name__ == "__main__":
+    main()

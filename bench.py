@@ -165,12 +165,17 @@ def main():
     }
 
     if args.copy_probe:
-        n = args.copy_probe << 20
-        a = torch.empty(n, dtype=torch.uint8, device=dev)
-        b = torch.empty_like(a)
-        b.copy_(a)
+        # plain copy of known size for hardware-counter calibration: the row
+        # gather with the identity index list reads and writes exactly
+        # rows * 1 KiB (plus the 4-byte indices)
+        rows = (args.copy_probe << 20) // 1024
+        src = torch.zeros((1, rows, 512), dtype=torch.int16, device=dev)
+        dst = torch.empty_like(src)
+        ident = torch.arange(rows, dtype=torch.int32, device=dev).reshape(1, rows)
+        lsa.lsa_gather_hot(src, ident, dst, stream=stream)
         torch.cuda.synchronize()
-        result["copy_probe_bytes"] = n
+        result["copy_probe"] = {"kernel": "gather_kernel (identity index list)",
+                                "read_bytes": rows * 1024 + rows * 4, "write_bytes": rows * 1024}
 
     if not args.skip_cpu:
         result["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)

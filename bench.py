@@ -88,12 +88,12 @@ def main():
         lsa.lsa_project_query(d["h"], d["Wq"], d["Wg"], buf.q, buf.g, stream=stream)
         if events is not None:
             events[1].record(stream)
-        lsa.lsa_score(d["keys"], d["scale"], buf.q, buf.g, d["bias"], buf.z, buf.mask,
-                      stream=stream)
+        lsa.lsa_score(d["keys"], d["scale"], buf.q, buf.g, d["bias"], buf.mask, buf.cand_idx,
+                      buf.cand_z, buf.cand_count, stream=stream)
         if events is not None:
             events[2].record(stream)
-        lsa.lsa_select_or_compact(buf.mask, buf.z, buf.surv_idx, buf.surv_z, buf.surv_count,
-                                  buf.ws_select, stream=stream)
+        lsa.lsa_select_or_compact(buf.cand_idx, buf.cand_z, buf.cand_count, w.N, buf.surv_idx,
+                                  buf.surv_z, buf.surv_count, stream=stream)
         if events is not None:
             events[3].record(stream)
         lsa.lsa_topk(buf.surv_idx, buf.surv_z, buf.surv_count, buf.topk_idx, buf.topk_count,

@@ -54,6 +54,7 @@ typedef enum {
 } lsa_key_dtype;
 
 #define LSA_MAX_LAYERS 8      /* indexer layers per lsa_score call */
+#define LSA_CAND_CHUNK 4096   /* entries per candidate chunk (see lsa_score) */
 #define LSA_MAX_HEADS 64      /* indexer heads */
 #define LSA_MAX_VOTE_LAYERS 32
 
@@ -103,43 +104,61 @@ lsa_status lsa_project_query(int L, int B, int D, int H, int dI,
  *   I = sigmoid(z);  selected  <=>  I >= 0.5  <=>  z >= 0 (NaN: not selected)
  * with sigma = key_scale[l][b][s] for e4m3 keys and 1 for bf16 keys.
  *
- *   keys      HOST array of L device pointers, each [B][N][dI] (bf16 or e4m3)
- *   key_scale HOST array of L device pointers, each fp32 [B][N]; required for
- *             LSA_KEY_FP8_E4M3, ignored (may be NULL) for bf16
- *   q, g      as written by lsa_project_query
- *   bias      HOST array of L fp32 values
- *   z         out fp32 [L][B][N]
- *   I_opt     out fp32 [L][B][N] or NULL
- *   sel_mask  out uint32 [L][B][ceil(N/32)]: bit (s % 32) of word s / 32;
- *             bits past N are zero
- * Limits: 1 <= L <= LSA_MAX_LAYERS, B >= 1, N >= 0 (N = 0 launches nothing),
- * 1 <= H <= 64, dI in {64, 128}, L * B <= 65535.
+ * All layers of a request are scored in one call, and the three-layer OR
+ * merge ([SUMMARY] 2.4: layer predictions united in OR mode; [REVIEW] section
+ * 2: an entry is fetched when any layer asks for it) is done here, chunk by
+ * chunk: the entries are cut into chunks of LSA_CAND_CHUNK, and for request b
+ * and chunk c the call writes the candidate list
+ *   cand_idx[b][c][0..n)  the entries of the chunk selected by at least one
+ *                         layer, ascending, n = cand_count[b][c]
+ *   cand_z[b][c][i]       their merged logit: the maximum of z over the layers
+ *                         that select the entry (for a selected entry this is
+ *                         the maximum over all layers, since every selecting
+ *                         layer has z >= 0 and every other layer z < 0)
+ * lsa_select_or_compact turns the chunk lists into one survivor list.
+ *
+ *   keys       HOST array of L device pointers, each [B][N][dI] (bf16 or e4m3)
+ *   key_scale  HOST array of L device pointers, each fp32 [B][N]; required for
+ *              LSA_KEY_FP8_E4M3, ignored (may be NULL) for bf16
+ *   q, g       as written by lsa_project_query
+ *   bias       HOST array of L fp32 values
+ *   sel_mask   out uint32 [L][B][ceil(N/32)]: bit (s % 32) of word s / 32;
+ *              bits past N are zero
+ *   cand_idx   out int32 [B][nchunks][LSA_CAND_CHUNK], nchunks = ceil(N / LSA_CAND_CHUNK)
+ *   cand_z     out fp32  [B][nchunks][LSA_CAND_CHUNK]
+ *   cand_count out int32 [B][nchunks]
+ *              (list slots past a chunk's count are left unwritten)
+ *   z_opt      out fp32 [L][B][N] or NULL: every layer's z.  Costs extra
+ *              writes; the hot path passes NULL
+ *   I_opt      out fp32 [L][B][N] or NULL: sigmoid(z)
+ * Limits: 1 <= L <= LSA_MAX_LAYERS, 1 <= B <= 65535, 0 <= N <= 2^24 (N = 0
+ * launches nothing), 1 <= H <= 64, dI in {64, 128}.
  */
 lsa_status lsa_score(int L, int B, int N, int H, int dI, lsa_key_dtype kdt,
                      const void* const* keys, const float* const* key_scale,
                      const uint16_t* q, const float* g, const float* bias,
-                     float* z, float* I_opt, uint32_t* sel_mask,
+                     uint32_t* sel_mask, int32_t* cand_idx, float* cand_z,
+                     int32_t* cand_count, float* z_opt, float* I_opt,
                      hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
- * Three-layer OR merge and survivor compaction ([SUMMARY] 2.4: the
- * predictions of the indexer layers are combined by union; [REVIEW] section
- * 2: an entry is fetched when any layer asks for it).  For every request b:
- *   surv_idx[b]   = the entries s selected by at least one layer, ascending
- *   surv_z[b][i]  = max over layers of z[l][b][s]  (NaN ignored)
+ * Survivor compaction of the OR-merged selection ([SUMMARY] 2.1 dynamic-fetch
+ * bullet: every entry some indexer layer selects is fetched).  Concatenates
+ * the chunk candidate lists of lsa_score, in chunk order, so for every
+ * request b:
+ *   surv_idx[b]   = the entries selected by at least one layer, ascending
+ *   surv_z[b][i]  = their merged logit
  *   surv_count[b] = the TRUE number of survivors, even when it exceeds cap;
  *                   only the first cap are written
  *
- *   sel_mask  uint32 [L][B][ceil(N/32)]     z  fp32 [L][B][N]
+ *   cand_idx, cand_z, cand_count   as written by lsa_score
  *   surv_idx  out int32 [B][cap]  surv_z out fp32 [B][cap]  surv_count out int32 [B]
- *   ws        device workspace of lsa_select_or_compact_workspace_bytes()
- * Limits: 1 <= L <= LSA_MAX_VOTE_LAYERS, B >= 1, N >= 0, cap >= 0.
+ * Limits: 1 <= B <= 65535, N >= 0, cap >= 0.
  */
-size_t lsa_select_or_compact_workspace_bytes(int L, int B, int N);
-lsa_status lsa_select_or_compact(int L, int B, int N, const uint32_t* sel_mask,
-                                 const float* z, int cap, int32_t* surv_idx,
-                                 float* surv_z, int32_t* surv_count, void* ws,
-                                 size_t ws_bytes, hipStream_t stream);
+lsa_status lsa_select_or_compact(int B, int N, const int32_t* cand_idx,
+                                 const float* cand_z, const int32_t* cand_count,
+                                 int cap, int32_t* surv_idx, float* surv_z,
+                                 int32_t* surv_count, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
  * Top-k inside the fetched set ([SUMMARY] 2.1 hierarchical-selection bullet:

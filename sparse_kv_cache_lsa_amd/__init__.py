@@ -10,13 +10,12 @@ from __future__ import annotations
 
 import ctypes as C
 
-from ._abi import (LSA_KEY_BF16, LSA_KEY_FP8_E4M3, LSAError, check, load,
+from ._abi import (LSA_CAND_CHUNK, LSA_KEY_BF16, LSA_KEY_FP8_E4M3, LSAError, check, load,
                    ptr_array)
 
 __all__ = [
-    "LSAError", "LSA_KEY_BF16", "LSA_KEY_FP8_E4M3", "load", "lsa_version",
-    "lsa_trigger_due", "lsa_project_query", "lsa_score",
-    "lsa_select_or_compact_workspace_bytes", "lsa_select_or_compact",
+    "LSAError", "LSA_KEY_BF16", "LSA_KEY_FP8_E4M3", "LSA_CAND_CHUNK", "load", "lsa_version",
+    "lsa_trigger_due", "lsa_project_query", "lsa_score", "lsa_select_or_compact",
     "lsa_topk_workspace_bytes", "lsa_topk", "lsa_gather_hot",
     "lsa_label_vote_workspace_bytes", "lsa_label_vote",
     "lsa_focal_bce_grad_workspace_bytes", "lsa_focal_bce_grad",
@@ -62,12 +61,15 @@ def lsa_project_query(h, Wq, Wg, q, g, *, h_layer_stride: int = 0, stream=None):
                                    _p(g), _stream(stream)))
 
 
-def lsa_score(keys, key_scale, q, g, bias, z, sel_mask, I=None, *, stream=None):
+def lsa_score(keys, key_scale, q, g, bias, sel_mask, cand_idx, cand_z, cand_count, z=None,
+              I=None, *, stream=None):
     """keys: list of L tensors [B][N][dI] (bf16 bits, or e4m3 codes with
-    key_scale a list of L fp32 [B][N]); bias: L host floats; z out f32
-    [L][B][N]; sel_mask out int32/uint32 [L][B][ceil(N/32)]; I optional out."""
+    key_scale a list of L fp32 [B][N]); bias: L host floats.  Outputs:
+    sel_mask int32 [L][B][ceil(N/32)]; chunk candidate lists cand_idx int32 /
+    cand_z f32 [B][nchunks][LSA_CAND_CHUNK], cand_count int32 [B][nchunks];
+    optional per-layer z and I, f32 [L][B][N]."""
     fp8 = key_scale is not None
-    _dev(q, g, z, sel_mask, I, *keys, *(key_scale or []))
+    _dev(q, g, sel_mask, cand_idx, cand_z, cand_count, z, I, *keys, *(key_scale or []))
     L, B, H, dI = q.shape
     N = keys[0].shape[1]
     kp, _k1 = ptr_array([_p(k) for k in keys])
@@ -77,22 +79,18 @@ def lsa_score(keys, key_scale, q, g, bias, z, sel_mask, I=None, *, stream=None):
         sp = None
     b = (C.c_float * L)(*[float(x) for x in bias])
     check(load().lsa_score(L, B, N, H, dI, LSA_KEY_FP8_E4M3 if fp8 else LSA_KEY_BF16, kp, sp,
-                           _p(q), _p(g), b, _p(z), _p(I), _p(sel_mask), _stream(stream)))
+                           _p(q), _p(g), b, _p(sel_mask), _p(cand_idx), _p(cand_z),
+                           _p(cand_count), _p(z), _p(I), _stream(stream)))
 
 
-def lsa_select_or_compact_workspace_bytes(L: int, B: int, N: int) -> int:
-    return int(load().lsa_select_or_compact_workspace_bytes(L, B, N))
-
-
-def lsa_select_or_compact(sel_mask, z, surv_idx, surv_z, surv_count, ws, *, stream=None):
-    """sel_mask [L][B][W], z f32 [L][B][N] -> surv_idx i32 [B][cap], surv_z f32
-    [B][cap], surv_count i32 [B]; ws: uint8 device workspace."""
-    _dev(sel_mask, z, surv_idx, surv_z, surv_count, ws)
-    L, B, N = z.shape
-    cap = surv_idx.shape[1]
-    check(load().lsa_select_or_compact(L, B, N, _p(sel_mask), _p(z), cap, _p(surv_idx),
-                                       _p(surv_z), _p(surv_count), _p(ws),
-                                       0 if ws is None else ws.numel() * ws.element_size(),
+def lsa_select_or_compact(cand_idx, cand_z, cand_count, N, surv_idx, surv_z, surv_count, *,
+                          stream=None):
+    """Chunk candidate lists of lsa_score (N entries per request) ->
+    surv_idx i32 [B][cap], surv_z f32 [B][cap], surv_count i32 [B]."""
+    _dev(cand_idx, cand_z, cand_count, surv_idx, surv_z, surv_count)
+    B, cap = surv_idx.shape
+    check(load().lsa_select_or_compact(B, int(N), _p(cand_idx), _p(cand_z), _p(cand_count), cap,
+                                       _p(surv_idx), _p(surv_z), _p(surv_count),
                                        _stream(stream)))
 
 

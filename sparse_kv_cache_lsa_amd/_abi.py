@@ -11,6 +11,7 @@ LIB_PATH = os.path.join(PKG, "liblsa.so")
 
 LSA_OK, LSA_E_ARG, LSA_E_SHAPE, LSA_E_DTYPE, LSA_E_HIP, LSA_E_WORKSPACE = range(6)
 LSA_KEY_BF16, LSA_KEY_FP8_E4M3 = 0, 1
+LSA_CAND_CHUNK = 4096
 STATUS_NAMES = {0: "LSA_OK", 1: "LSA_E_ARG", 2: "LSA_E_SHAPE", 3: "LSA_E_DTYPE",
                 4: "LSA_E_HIP", 5: "LSA_E_WORKSPACE"}
 
@@ -27,9 +28,8 @@ SIGNATURES = {
     "lsa_version": (C.c_char_p, []),
     "lsa_trigger_due": (I32, [I64, I32]),
     "lsa_project_query": (I32, [I32, I32, I32, I32, I32, P, I64, PP, PP, P, P, P]),
-    "lsa_score": (I32, [I32, I32, I32, I32, I32, I32, PP, PP, P, P, PF, P, P, P, P]),
-    "lsa_select_or_compact_workspace_bytes": (SZ, [I32, I32, I32]),
-    "lsa_select_or_compact": (I32, [I32, I32, I32, P, P, I32, P, P, P, P, SZ, P]),
+    "lsa_score": (I32, [I32, I32, I32, I32, I32, I32, PP, PP, P, P, PF, P, P, P, P, P, P, P]),
+    "lsa_select_or_compact": (I32, [I32, I32, P, P, P, I32, P, P, P, P]),
     "lsa_topk_workspace_bytes": (SZ, [I32, I32, I32]),
     "lsa_topk": (I32, [I32, I32, I32, P, P, P, P, P, P, SZ, P]),
     "lsa_gather_hot": (I32, [I32, I32, I32, I32, P, P, P, P]),

@@ -19,10 +19,13 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 SOURCES = ["lsa_api.cpp", "lsa_score.hip", "lsa_select.hip", "lsa_topk.hip",
            "lsa_gather.hip", "lsa_project.hip", "lsa_labels.hip", "lsa_focal.hip"]
 
-# Packed fp32 VALU ops are switched off for every HIP translation unit.
+# Packed fp32 VALU ops are switched off for every HIP translation unit.  MFMA
+# results are kept in ordinary VGPRs (not AGPRs), so fused epilogues read the
+# accumulators without v_accvgpr_read copies.
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-Wno-unused-command-line-argument",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-mllvm", "-amdgpu-mfma-vgpr-form",
          "-I", os.path.join(ROOT, "include")]
 
 

@@ -88,20 +88,21 @@ lsa_status lsa_project_query(int L, int B, int D, int H, int dI, const uint16_t*
 
 lsa_status lsa_score(int L, int B, int N, int H, int dI, lsa_key_dtype kdt,
                      const void* const* keys, const float* const* key_scale, const uint16_t* q,
-                     const float* g, const float* bias, float* z, float* I_opt,
-                     uint32_t* sel_mask, hipStream_t stream) {
+                     const float* g, const float* bias, uint32_t* sel_mask, int32_t* cand_idx,
+                     float* cand_z, int32_t* cand_count, float* z_opt, float* I_opt,
+                     hipStream_t stream) {
   REQUIRE(kdt == LSA_KEY_BF16 || kdt == LSA_KEY_FP8_E4M3, LSA_E_DTYPE,
           "lsa_score: unknown key dtype %d", (int)kdt);
   REQUIRE(L >= 1 && L <= LSA_MAX_LAYERS, LSA_E_SHAPE, "lsa_score: L=%d not in [1,%d]", L,
           LSA_MAX_LAYERS);
-  REQUIRE(B >= 1, LSA_E_SHAPE, "lsa_score: B=%d < 1", B);
-  REQUIRE(N >= 0, LSA_E_SHAPE, "lsa_score: N=%d < 0", N);
+  REQUIRE(B >= 1 && B <= 65535, LSA_E_SHAPE, "lsa_score: B=%d not in [1,65535]", B);
+  REQUIRE(N >= 0 && N <= (1 << 24), LSA_E_SHAPE, "lsa_score: N=%d not in [0,2^24]", N);
   REQUIRE(H >= 1 && H <= LSA_MAX_HEADS, LSA_E_SHAPE, "lsa_score: H=%d not in [1,64]", H);
   REQUIRE(dI == 64 || dI == 128, LSA_E_SHAPE, "lsa_score: dI=%d not 64 or 128", dI);
-  REQUIRE((long long)L * B <= 65535, LSA_E_SHAPE, "lsa_score: L*B=%lld > 65535", (long long)L * B);
   REQUIRE(bias, LSA_E_ARG, "lsa_score: null bias array");
   if (N == 0) return LSA_OK;   // nothing to score; outputs are empty
-  REQUIRE(keys && q && g && z && sel_mask, LSA_E_ARG, "lsa_score: null pointer argument");
+  REQUIRE(keys && q && g && sel_mask && cand_idx && cand_z && cand_count, LSA_E_ARG,
+          "lsa_score: null pointer argument");
   REQUIRE(kdt == LSA_KEY_BF16 || key_scale, LSA_E_ARG, "lsa_score: e4m3 keys need key_scale");
   REQUIRE(aligned16(q), LSA_E_ARG, "lsa_score: q must be 16-byte aligned");
   lsa::ScoreArgs a{};
@@ -117,43 +118,37 @@ lsa_status lsa_score(int L, int B, int N, int H, int dI, lsa_key_dtype kdt,
   }
   a.q = q;
   a.g = g;
-  a.z = z;
-  a.I = I_opt;
   a.mask = sel_mask;
+  a.cand_idx = cand_idx;
+  a.cand_z = cand_z;
+  a.cand_count = cand_count;
+  a.z = z_opt;
+  a.I = I_opt;
+  a.L = L;
   a.B = B;
   a.N = N;
   a.H = H;
   a.W = (N + 31) / 32;
-  a.tiles_per_block = 128;
-  return hip_status(lsa::launch_score(L, dI, kdt, a, stream), "lsa_score launch");
+  a.nchunks = (N + LSA_CAND_CHUNK - 1) / LSA_CAND_CHUNK;
+  return hip_status(lsa::launch_score(dI, kdt, a, stream), "lsa_score launch");
 }
 
 // ----------------------------------------------------------- select/compact
 
-size_t lsa_select_or_compact_workspace_bytes(int L, int B, int N) {
-  (void)L;
-  if (B < 1 || N < 0) return 0;
-  return lsa::select_workspace(B, N);
-}
-
-lsa_status lsa_select_or_compact(int L, int B, int N, const uint32_t* sel_mask, const float* z,
-                                 int cap, int32_t* surv_idx, float* surv_z,
-                                 int32_t* surv_count, void* ws, size_t ws_bytes,
-                                 hipStream_t stream) {
-  REQUIRE(L >= 1 && L <= LSA_MAX_VOTE_LAYERS, LSA_E_SHAPE,
-          "lsa_select_or_compact: L=%d not in [1,%d]", L, LSA_MAX_VOTE_LAYERS);
+lsa_status lsa_select_or_compact(int B, int N, const int32_t* cand_idx, const float* cand_z,
+                                 const int32_t* cand_count, int cap, int32_t* surv_idx,
+                                 float* surv_z, int32_t* surv_count, hipStream_t stream) {
   REQUIRE(B >= 1 && B <= 65535, LSA_E_SHAPE, "lsa_select_or_compact: B=%d not in [1,65535]", B);
-  REQUIRE(N >= 0, LSA_E_SHAPE, "lsa_select_or_compact: N=%d < 0", N);
+  REQUIRE(N >= 0 && N <= (1 << 24), LSA_E_SHAPE, "lsa_select_or_compact: N=%d not in [0,2^24]", N);
   REQUIRE(cap >= 0, LSA_E_ARG, "lsa_select_or_compact: cap=%d < 0", cap);
   REQUIRE(surv_count, LSA_E_ARG, "lsa_select_or_compact: null surv_count");
-  REQUIRE(N == 0 || (sel_mask && z), LSA_E_ARG, "lsa_select_or_compact: null sel_mask or z");
+  REQUIRE(N == 0 || (cand_idx && cand_z && cand_count), LSA_E_ARG,
+          "lsa_select_or_compact: null candidate list");
   REQUIRE(cap == 0 || (surv_idx && surv_z), LSA_E_ARG,
           "lsa_select_or_compact: null survivor output with cap > 0");
-  const size_t need = lsa::select_workspace(B, N);
-  REQUIRE(N == 0 || (ws && ws_bytes >= need), LSA_E_WORKSPACE,
-          "lsa_select_or_compact: workspace %zu bytes, need %zu", ws_bytes, need);
-  return hip_status(lsa::launch_select(L, B, N, sel_mask, z, cap, surv_idx, surv_z, surv_count,
-                                       ws, stream),
+  const int nchunks = (N + LSA_CAND_CHUNK - 1) / LSA_CAND_CHUNK;
+  return hip_status(lsa::launch_select(B, nchunks, cand_idx, cand_z, cand_count, cap, surv_idx,
+                                       surv_z, surv_count, stream),
                     "lsa_select_or_compact launch");
 }
 

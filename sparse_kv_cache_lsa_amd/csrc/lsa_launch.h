@@ -15,15 +15,17 @@ struct ScoreArgs {
   float bias[LSA_MAX_LAYERS];
   const uint16_t* q;
   const float* g;
-  float* z;
-  float* I;
-  uint32_t* mask;
-  int B, N, H, W;          // W = ceil(N / 32)
-  int tiles_per_block;
+  uint32_t* mask;          // [L][B][W]
+  int32_t* cand_idx;       // [B][nchunks][LSA_CAND_CHUNK]
+  float* cand_z;           // [B][nchunks][LSA_CAND_CHUNK]
+  int32_t* cand_count;     // [B][nchunks]
+  float* z;                // [L][B][N] or null
+  float* I;                // [L][B][N] or null
+  int L, B, N, H, W;       // W = ceil(N / 32)
+  int nchunks;             // ceil(N / LSA_CAND_CHUNK)
 };
 
-hipError_t launch_score(int L, int dI, lsa_key_dtype kdt, const ScoreArgs& a,
-                        hipStream_t s);
+hipError_t launch_score(int dI, lsa_key_dtype kdt, const ScoreArgs& a, hipStream_t s);
 
 struct ProjectArgs {
   const uint16_t* Wq[LSA_MAX_LAYERS];
@@ -37,11 +39,9 @@ struct ProjectArgs {
 
 hipError_t launch_project(const ProjectArgs& a, hipStream_t s);
 
-size_t select_workspace(int B, int N);
-hipError_t launch_select(int L, int B, int N, const uint32_t* mask,
-                         const float* z, int cap, int32_t* surv_idx,
-                         float* surv_z, int32_t* surv_count, void* ws,
-                         hipStream_t s);
+hipError_t launch_select(int B, int nchunks, const int32_t* cand_idx, const float* cand_z,
+                         const int32_t* cand_count, int cap, int32_t* surv_idx,
+                         float* surv_z, int32_t* surv_count, hipStream_t s);
 
 hipError_t launch_topk(int B, int cap, int k, const int32_t* surv_idx,
                        const float* surv_z, const int32_t* surv_count,

@@ -5,20 +5,22 @@ from __future__ import annotations
 
 from dataclasses import dataclass
 
-from . import (lsa_gather_hot, lsa_project_query, lsa_score, lsa_select_or_compact,
-               lsa_select_or_compact_workspace_bytes, lsa_topk, lsa_topk_workspace_bytes)
+from . import (LSA_CAND_CHUNK, lsa_gather_hot, lsa_project_query, lsa_score,
+               lsa_select_or_compact, lsa_topk, lsa_topk_workspace_bytes)
 
 
 @dataclass
 class TriggerBuffers:
+    N: int
     q: object
     g: object
-    z: object
     mask: object
+    cand_idx: object
+    cand_z: object
+    cand_count: object
     surv_idx: object
     surv_z: object
     surv_count: object
-    ws_select: object
     ws_topk: object
     topk_idx: object
     topk_count: object
@@ -29,17 +31,19 @@ class TriggerBuffers:
         import torch
         cap = N if cap is None else cap
         W = (N + 31) // 32
+        nch = (N + LSA_CAND_CHUNK - 1) // LSA_CAND_CHUNK
         u8 = torch.uint8
         return cls(
+            N=N,
             q=torch.empty((L, B, H, dI), dtype=torch.bfloat16, device=device),
             g=torch.empty((L, B, H), dtype=torch.float32, device=device),
-            z=torch.empty((L, B, N), dtype=torch.float32, device=device),
             mask=torch.empty((L, B, W), dtype=torch.int32, device=device),
+            cand_idx=torch.empty((B, nch, LSA_CAND_CHUNK), dtype=torch.int32, device=device),
+            cand_z=torch.empty((B, nch, LSA_CAND_CHUNK), dtype=torch.float32, device=device),
+            cand_count=torch.empty((B, nch), dtype=torch.int32, device=device),
             surv_idx=torch.empty((B, cap), dtype=torch.int32, device=device),
             surv_z=torch.empty((B, cap), dtype=torch.float32, device=device),
             surv_count=torch.empty((B,), dtype=torch.int32, device=device),
-            ws_select=torch.empty((max(1, lsa_select_or_compact_workspace_bytes(L, B, N)),),
-                                  dtype=u8, device=device),
             ws_topk=torch.empty((max(1, lsa_topk_workspace_bytes(B, cap, k)),), dtype=u8,
                                 device=device),
             topk_idx=torch.empty((B, k), dtype=torch.int32, device=device),
@@ -49,14 +53,16 @@ class TriggerBuffers:
 
 
 def run_trigger(buf: TriggerBuffers, h, Wq, Wg, keys, key_scale, bias, pool=None, *,
-                stream=None, project=True):
+                stream=None, project=True, z_layers=None):
     """One indexer trigger.  With project=False the query buffers are used as
-    they are (the caller filled buf.q / buf.g)."""
+    they are (the caller filled buf.q / buf.g).  z_layers: optional f32
+    [L][B][N] that receives every layer's logit (extra write traffic)."""
     if project:
         lsa_project_query(h, Wq, Wg, buf.q, buf.g, stream=stream)
-    lsa_score(keys, key_scale, buf.q, buf.g, bias, buf.z, buf.mask, stream=stream)
-    lsa_select_or_compact(buf.mask, buf.z, buf.surv_idx, buf.surv_z, buf.surv_count,
-                          buf.ws_select, stream=stream)
+    lsa_score(keys, key_scale, buf.q, buf.g, bias, buf.mask, buf.cand_idx, buf.cand_z,
+              buf.cand_count, z_layers, stream=stream)
+    lsa_select_or_compact(buf.cand_idx, buf.cand_z, buf.cand_count, buf.N, buf.surv_idx,
+                          buf.surv_z, buf.surv_count, stream=stream)
     lsa_topk(buf.surv_idx, buf.surv_z, buf.surv_count, buf.topk_idx, buf.topk_count,
              buf.ws_topk, stream=stream)
     if pool is not None:

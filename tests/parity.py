@@ -63,6 +63,29 @@ def check_selection(sel_gpu, z_or):
     return int(band.sum())
 
 
+def flatten_candidates(cand_idx, cand_z, cand_count):
+    """Chunk candidate lists of one request -> (entries, merged logits)."""
+    cnt = np.asarray(cand_count)
+    idx = np.concatenate([np.asarray(cand_idx)[c, :cnt[c]] for c in range(cnt.size)]) if cnt.size else np.zeros(0, np.int32)
+    z = np.concatenate([np.asarray(cand_z)[c, :cnt[c]] for c in range(cnt.size)]) if cnt.size else np.zeros(0, np.float32)
+    return idx, z
+
+
+def check_merged_scores(idx_gpu, z_gpu, z_or_layers):
+    """Merged logit of each listed entry: the max over the layers selecting
+    it, compared where every layer's selection is outside the band."""
+    z = np.asarray(z_or_layers, np.float64)
+    idx = np.asarray(idx_gpu, np.int64)
+    zg = np.asarray(z_gpu, np.float64)
+    sel = z >= 0
+    want = np.where(sel, z, -np.inf).max(axis=0)[idx]
+    certain = (np.abs(z) > Z_BAND).all(axis=0)[idx]
+    assert np.isfinite(zg).all(), "non-finite merged logit in a survivor list"
+    d = np.abs(zg[certain] - want[certain])
+    assert d.max(initial=0) <= Z_TOL, f"merged logit max |dz| = {d.max():.3g}"
+    return float(d.max(initial=0))
+
+
 def check_survivors(idx_gpu, count_gpu, z_or_layers, cap=None):
     """z_or_layers: fp64 [L][N].  idx_gpu: the GPU survivor list (first
     min(count, cap) entries)."""

@@ -29,7 +29,7 @@ def lib():
 
 def test_header_symbols_exported(lib):
     names = _declared()
-    assert len(names) >= 14
+    assert len(names) >= 13
     for n in names:
         assert hasattr(lib, n), f"{n} declared in lsa.h but not exported"
     from sparse_kv_cache_lsa_amd import _abi
@@ -52,11 +52,6 @@ def test_trigger_cadence(lib):
     assert lib.lsa_trigger_due(-64, 64) == 0 and lib.lsa_trigger_due(5, 0) == 0
 
 
-def test_workspace_sizes(lib):
-    assert lib.lsa_select_or_compact_workspace_bytes(3, 32, 262144) >= 32 * 32 * 4
-    assert lib.lsa_select_or_compact_workspace_bytes(3, 1, 1) >= 4
-
-
 def _status(lib, name, *args):
     return getattr(lib, name)(*args)
 
@@ -68,24 +63,23 @@ def test_validation_errors_return_before_launch(lib):
     arr, _keep = _abi.ptr_array([16])
     bias = (C.c_float * 1)(0.0)
     # bad dtype
-    st = lib.lsa_score(1, 1, 64, 8, 64, 7, arr, None, fake, fake, bias, fake, None, fake, None)
+    st = lib.lsa_score(1, 1, 64, 8, 64, 7, arr, None, fake, fake, bias, fake, fake, fake, fake, None, None, None)
     assert st == _abi.LSA_E_DTYPE and b"dtype" in lib.lsa_last_error()
     # unsupported head dim
-    st = lib.lsa_score(1, 1, 64, 8, 96, 0, arr, None, fake, fake, bias, fake, None, fake, None)
+    st = lib.lsa_score(1, 1, 64, 8, 96, 0, arr, None, fake, fake, bias, fake, fake, fake, fake, None, None, None)
     assert st == _abi.LSA_E_SHAPE and b"dI" in lib.lsa_last_error()
     # too many heads, too many layers
-    assert lib.lsa_score(1, 1, 64, 65, 64, 0, arr, None, fake, fake, bias, fake, None, fake, None) == _abi.LSA_E_SHAPE
-    assert lib.lsa_score(9, 1, 64, 8, 64, 0, arr, None, fake, fake, bias, fake, None, fake, None) == _abi.LSA_E_SHAPE
+    assert lib.lsa_score(1, 1, 64, 65, 64, 0, arr, None, fake, fake, bias, fake, fake, fake, fake, None, None, None) == _abi.LSA_E_SHAPE
+    assert lib.lsa_score(9, 1, 64, 8, 64, 0, arr, None, fake, fake, bias, fake, fake, fake, fake, None, None, None) == _abi.LSA_E_SHAPE
     # e4m3 without scales
-    assert lib.lsa_score(1, 1, 64, 8, 64, 1, arr, None, fake, fake, bias, fake, None, fake, None) == _abi.LSA_E_ARG
+    assert lib.lsa_score(1, 1, 64, 8, 64, 1, arr, None, fake, fake, bias, fake, fake, fake, fake, None, None, None) == _abi.LSA_E_ARG
     # null output
-    assert lib.lsa_score(1, 1, 64, 8, 64, 0, arr, None, fake, fake, bias, P, None, fake, None) == _abi.LSA_E_ARG
+    assert lib.lsa_score(1, 1, 64, 8, 64, 0, arr, None, fake, fake, bias, fake, P, fake, fake, None, None, None) == _abi.LSA_E_ARG
     # misaligned query
-    assert lib.lsa_score(1, 1, 64, 8, 64, 0, arr, None, C.c_void_p(18), fake, bias, fake, None, fake, None) == _abi.LSA_E_ARG
-    # select: workspace too small
-    st = lib.lsa_select_or_compact(3, 2, 1000, fake, fake, 1000, fake, fake, fake, fake, 1, None)
-    assert st == _abi.LSA_E_WORKSPACE
-    assert lib.lsa_select_or_compact(3, 2, 1000, fake, fake, -1, fake, fake, fake, fake, 1 << 20, None) == _abi.LSA_E_ARG
+    assert lib.lsa_score(1, 1, 64, 8, 64, 0, arr, None, C.c_void_p(18), fake, bias, fake, fake, fake, fake, None, None, None) == _abi.LSA_E_ARG
+    # select: negative capacity, missing candidate lists
+    assert lib.lsa_select_or_compact(2, 1000, fake, fake, fake, -1, fake, fake, fake, None) == _abi.LSA_E_ARG
+    assert lib.lsa_select_or_compact(2, 1000, None, fake, fake, 10, fake, fake, fake, None) == _abi.LSA_E_ARG
     # top-k: negative k
     assert lib.lsa_topk(1, 10, -1, fake, fake, fake, fake, fake, None, 0, None) == _abi.LSA_E_ARG
     # gather: row size not a multiple of 16

@@ -19,24 +19,30 @@ from sparse_kv_cache_lsa_amd.pipeline import TriggerBuffers, run_trigger
 pytestmark = pytest.mark.gpu
 
 
-def _run(inp, pool):
+def _run(inp, pool, with_layers=False, d=None):
+    """One trigger in the benchmark's configuration (masks + merged logits
+    only); with_layers additionally returns every layer's logit."""
     w = inp.w
-    d = gen.to_device(inp, DEV)
+    d = gen.to_device(inp, DEV) if d is None else d
     buf = TriggerBuffers.allocate(w.L, w.B, w.N, w.H, w.dI, w.k, w.row_elems, device=DEV)
-    run_trigger(buf, d["h"], d["Wq"], d["Wg"], d["keys"], d["scale"], d["bias"], pool)
+    zl = torch.empty((w.L, w.B, w.N), dtype=torch.float32, device=DEV) if with_layers else None
+    run_trigger(buf, d["h"], d["Wq"], d["Wg"], d["keys"], d["scale"], d["bias"], pool, z_layers=zl)
     torch.cuda.synchronize()
-    return buf
+    return buf, zl
 
 
-def _check_request(inp, q_or, g_or, buf, b, pool):
+def _check_request(inp, q_or, g_or, buf, b, pool, zl=None):
     w = inp.w
     z_or, surv, zstar, count, topk, kcount = oracle_request(inp, q_or, g_or, b, w.k)
-    zg = host(buf.z[:, b])
+    if zl is not None:
+        zg = host(zl[:, b])
+        for l in range(w.L):
+            parity.check_scores(zg[l], z_or[l])
     for l in range(w.L):
-        parity.check_scores(zg[l], z_or[l])
         parity.check_selection(parity.unpack_mask(host(buf.mask[l, b]), w.N), z_or[l])
     cnt = int(host(buf.surv_count)[b])
     unc = parity.check_survivors(host(buf.surv_idx[b, :cnt]), cnt, z_or)
+    parity.check_merged_scores(host(buf.surv_idx[b, :cnt]), host(buf.surv_z[b, :cnt]), z_or)
     uncertain = ~(z_or >= parity.Z_BAND).any(0) & ~(z_or < -parity.Z_BAND).all(0)
     kc = int(host(buf.topk_count)[b])
     nb = parity.check_topk(host(buf.topk_idx[b]), kc, surv, zstar, w.k, uncertain=uncertain)
@@ -57,16 +63,25 @@ def test_chain_small_workloads(name):
     w = gen.WORKLOADS[name]
     inp, q_or, g_or = fx.build(w)
     pool = gen.pool_tensor(w, DEV)
-    buf = _run(inp, pool)
+    buf, _ = _run(inp, pool)
     # the GPU query encoder must agree with the oracle's (bf16 bits)
     qg = bf16_host(buf.q)
     assert (qg != q_or).mean() < 1e-3
     for b in range(w.B):
         print(name, b, _check_request(inp, q_or, g_or, buf, b, pool))
-    # a second trigger on the same inputs is bit-identical
-    buf2 = _run(inp, pool)
-    for a, c in [(buf.z, buf2.z), (buf.surv_idx, buf2.surv_idx), (buf.topk_idx, buf2.topk_idx)]:
+    # with per-layer logits requested: the same selection, plus every z
+    buf2, zl = _run(inp, pool, with_layers=True)
+    for b in range(w.B):
+        _check_request(inp, q_or, g_or, buf2, b, pool, zl)
+    # and the same inputs give bit-identical results
+    assert torch.equal(buf.surv_count, buf2.surv_count)
+    for a, c in [(buf.mask, buf2.mask), (buf.cand_count, buf2.cand_count),
+                 (buf.topk_idx, buf2.topk_idx)]:
         assert torch.equal(a, c)
+    for b in range(w.B):
+        n = int(buf.surv_count[b])      # entries past the count are never written
+        assert torch.equal(buf.surv_idx[b, :n], buf2.surv_idx[b, :n])
+        assert torch.equal(buf.surv_z[b, :n], buf2.surv_z[b, :n])
 
 
 @pytest.mark.parametrize("name", ["ctx512k", "ctx1m"])
@@ -76,7 +91,8 @@ def test_chain_full_size(name):
     inp = gen.indexer_inputs(w, calib, threads=16)
     print(f"{name}: inputs generated", flush=True)
     pool = gen.pool_tensor(w, DEV)
-    buf = _run(inp, pool)
+    d = gen.to_device(inp, DEV)
+    buf, _ = _run(inp, pool, d=d)
     print(f"{name}: GPU trigger done", flush=True)
     counts = host(buf.surv_count)
     tcounts = host(buf.topk_count)
@@ -94,3 +110,7 @@ def test_chain_full_size(name):
         for l in range(w.L):
             q_or[l, b], g_or[l, b] = fx.oracle.project(inp.h[b], inp.Wq[l], inp.Wg[l], w.H, w.dI)
         print(name, b, _check_request(inp, q_or, g_or, buf, b, pool), flush=True)
+    # per-layer logits of the same launch shape, checked on the first request
+    buf2, zl = _run(inp, pool, with_layers=True, d=d)
+    assert torch.equal(buf2.surv_count, buf.surv_count) and torch.equal(buf2.mask, buf.mask)
+    _check_request(inp, q_or, g_or, buf2, 0, pool, zl)

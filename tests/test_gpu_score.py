@@ -30,33 +30,51 @@ def _case(seed, L, B, N, H, dI, e4m3):
     return q, g, keys, scales, bias
 
 
-def _run(q, g, keys, scales, bias, want_I=True):
+CH = lsa.LSA_CAND_CHUNK
+
+
+def _run(q, g, keys, scales, bias, want_I=True, want_z=True):
     L, B, H, dI = q.shape
     N = keys[0].shape[1]
     W = (N + 31) // 32
-    z = torch.full((L, B, N), float("nan"), dtype=torch.float32, device=DEV)
+    nch = (N + CH - 1) // CH
+    z = torch.full((L, B, N), float("nan"), dtype=torch.float32, device=DEV) if want_z else None
     I = torch.full((L, B, N), float("nan"), dtype=torch.float32, device=DEV) if want_I else None
     mask = torch.full((L, B, max(W, 1)), -1, dtype=torch.int32, device=DEV)
+    ci = torch.full((B, max(nch, 1), CH), -3, dtype=torch.int32, device=DEV)
+    cz = torch.full((B, max(nch, 1), CH), float("nan"), dtype=torch.float32, device=DEV)
+    cc = torch.full((B, max(nch, 1)), -3, dtype=torch.int32, device=DEV)
     lsa.lsa_score([dev(k) for k in keys], None if scales[0] is None else [dev(s) for s in scales],
-                  bf16_dev(q), dev(g), bias, z, mask[..., :W] if W else mask, I)
+                  bf16_dev(q), dev(g), bias, mask[..., :W] if W else mask, ci, cz, cc, z, I)
     torch.cuda.synchronize()
-    return host(z), (host(I) if want_I else None), host(mask)
+    return ((host(z) if want_z else None), (host(I) if want_I else None), host(mask),
+            (host(ci), host(cz), host(cc)))
 
 
-def _check(q, g, keys, scales, bias, z, I, mask):
+def _check(q, g, keys, scales, bias, z, I, mask, cand):
     L, B, H, dI = q.shape
     N = keys[0].shape[1]
     W = (N + 31) // 32
     worst = 0.0
-    for l in range(L):
-        for b in range(B):
-            z_or = oracle.score(keys[l][b], None if scales[l] is None else scales[l][b],
-                                q[l, b], g[l, b], float(bias[l]))
-            d = parity.check_scores(z[l, b], z_or, None if I is None else I[l, b])
-            worst = max(worst, d["max_dz"])
+    ci, cz, cc = cand
+    for b in range(B):
+        z_or = np.stack([oracle.score(keys[l][b], None if scales[l] is None else scales[l][b],
+                                      q[l, b], g[l, b], float(bias[l])) for l in range(L)])
+        for l in range(L):
+            if z is not None:
+                d = parity.check_scores(z[l, b], z_or[l], None if I is None else I[l, b])
+                worst = max(worst, d["max_dz"])
             sel = parity.unpack_mask(mask[l, b, :W], W * 32)
-            parity.check_selection(sel[:N], z_or)
+            parity.check_selection(sel[:N], z_or[l])
             assert not sel[N:].any(), "selection bits set past N"
+        # the chunk lists: each chunk ascending, inside its chunk, OR of the
+        # layers' selections, merged logit = max over selecting layers
+        for c in range((N + CH - 1) // CH):
+            lst = ci[b, c, :cc[b, c]]
+            assert ((lst >= c * CH) & (lst < min(N, (c + 1) * CH))).all()
+        idx, zs = parity.flatten_candidates(ci[b], cz[b], cc[b])
+        parity.check_survivors(idx, idx.size, z_or)
+        worst = max(worst, parity.check_merged_scores(idx, zs, z_or))
     return worst
 
 
@@ -78,30 +96,37 @@ CASES = [
 @pytest.mark.parametrize("L,B,N,H,dI,e4m3", CASES)
 def test_score_matches_oracle(L, B, N, H, dI, e4m3):
     q, g, keys, scales, bias = _case(1000 + N + H, L, B, N, H, dI, e4m3)
-    z, I, mask = _run(q, g, keys, scales, bias)
-    worst = _check(q, g, keys, scales, bias, z, I, mask)
+    z, I, mask, cand = _run(q, g, keys, scales, bias)
+    worst = _check(q, g, keys, scales, bias, z, I, mask, cand)
     print(f"max |dz| = {worst:.3g}")
 
 
-def test_score_without_sigmoid_output():
-    q, g, keys, scales, bias = _case(7, 1, 1, 3000, 64, 128, True)
-    z, _, mask = _run(q, g, keys, scales, bias, want_I=False)
-    _check(q, g, keys, scales, bias, z, None, mask)
+@pytest.mark.parametrize("want_z,want_I", [(False, False), (False, True), (True, False)])
+def test_score_optional_outputs(want_z, want_I):
+    # the hot path writes only masks + merged logits; optional per-layer
+    # outputs must not change them
+    q, g, keys, scales, bias = _case(7, 3, 2, 3000, 64, 128, True)
+    z, I, mask, cand = _run(q, g, keys, scales, bias, want_I=want_I, want_z=want_z)
+    _check(q, g, keys, scales, bias, z, I, mask, cand)
 
 
 def test_score_n_zero_launches_nothing():
     q, g, keys, scales, bias = _case(8, 1, 1, 0, 8, 64, False)
-    z = torch.empty((1, 1, 0), device=DEV)
-    mask = torch.empty((1, 1, 0), dtype=torch.int32, device=DEV)
-    lsa.lsa_score([dev(keys[0])], None, bf16_dev(q), dev(g), bias, z, mask)
+    e = lambda *sh: torch.empty(sh, dtype=torch.int32, device=DEV)
+    lsa.lsa_score([dev(keys[0])], None, bf16_dev(q), dev(g), bias, e(1, 1, 0), e(1, 0, CH),
+                  torch.empty((1, 0, CH), device=DEV), e(1, 0))
 
 
 def test_score_deterministic():
     q, g, keys, scales, bias = _case(9, 2, 2, 20000, 64, 128, True)
     a = _run(q, g, keys, scales, bias)
     b = _run(q, g, keys, scales, bias)
-    for x, y in zip(a, b):
-        assert np.array_equal(x.view(np.uint32), y.view(np.uint32))
+    for x, y in zip(a[:3], b[:3]):
+        assert np.array_equal(np.asarray(x).view(np.uint32), np.asarray(y).view(np.uint32))
+    for bb in range(2):
+        ia, za = parity.flatten_candidates(a[3][0][bb], a[3][1][bb], a[3][2][bb])
+        ib, zb = parity.flatten_candidates(b[3][0][bb], b[3][1][bb], b[3][2][bb])
+        assert np.array_equal(ia, ib) and np.array_equal(za.view(np.uint32), zb.view(np.uint32))
 
 
 def test_e4m3_widening_is_exact():
@@ -118,6 +143,6 @@ def test_e4m3_widening_is_exact():
     qv[..., 5] = 1.0
     q = gen.to_bf16_bits(qv)
     g = np.ones((1, 1, 1), np.float32)
-    z, _, _ = _run(q, g, [keys], [scale], np.zeros(1, np.float32))
+    z, _, _, _ = _run(q, g, [keys], [scale], np.zeros(1, np.float32))
     want = oracle.e4m3_to_double(codes)
     assert np.array_equal(z[0, 0].astype(np.float64), want)

@@ -201,12 +201,21 @@ lsa_status lsa_gather_hot(int B, int N, int k, int row_bytes, const void* pool,
  *   top_p is kept);
  * then count[t][s] = number of layers keeping s, label[t][s] = count >= theta.
  *
- *   logits          fp32 [Q][L][N] (finite values)
- *   layer_mask_opt  out uint32 [Q][L][ceil(N/32)] or NULL
- *   count           out uint8 [Q][N]        label  out uint8 [Q][N]
+ *   logits          fp32 [Q][L][N] (finite values), 16-byte aligned
+ *   layer_mask_opt  out uint32 [Q][L][ceil(N/32)]: bit j of word w is
+ *                   entry 32w+j kept by that layer; or NULL
+ *   count           out uint8 [Q][N]        label  out uint8 [Q][N] (0/1),
+ *                   both 16-byte aligned
  *   ws              device workspace of lsa_label_vote_workspace_bytes()
+ *                   bytes (holds the per-layer masks); needed only when
+ *                   layer_mask_opt is NULL, else may be NULL
+ * The kept mass is computed in 64-bit fixed point (exp(x - max) in units of
+ * 2^-40), so the result is deterministic; it differs from exact arithmetic
+ * only for entries whose mass ahead lies within ~1e-6 of top_p.
  * Limits: Q >= 1, 1 <= L <= LSA_MAX_VOTE_LAYERS, 1 <= N <= 65536,
- * 0 < top_p <= 1, theta >= 0.
+ * 0 < top_p <= 1, theta >= 0.  Errors: LSA_E_SHAPE / LSA_E_ARG for the
+ * limits, null or misaligned pointers; LSA_E_WORKSPACE for a missing or
+ * short workspace; LSA_E_HIP for a launch failure.
  */
 size_t lsa_label_vote_workspace_bytes(int Q, int L, int N);
 lsa_status lsa_label_vote(int Q, int L, int N, float top_p, int theta,

@@ -194,18 +194,34 @@ lsa_status lsa_gather_hot(int B, int N, int k, int row_bytes, const void* pool,
 // -------------------------------------------------------- label / loss calls
 
 size_t lsa_label_vote_workspace_bytes(int Q, int L, int N) {
-  (void)Q;
-  (void)L;
-  (void)N;
-  return 0;
+  if (Q < 1 || L < 1 || N < 1) return 0;
+  return (size_t)Q * (size_t)L * (size_t)((N + 31) / 32) * sizeof(uint32_t);
 }
 
 lsa_status lsa_label_vote(int Q, int L, int N, float top_p, int theta, const float* logits,
                           uint32_t* layer_mask_opt, uint8_t* count, uint8_t* label, void* ws,
                           size_t ws_bytes, hipStream_t stream) {
-  (void)Q; (void)L; (void)N; (void)top_p; (void)theta; (void)logits; (void)layer_mask_opt;
-  (void)count; (void)label; (void)ws; (void)ws_bytes; (void)stream;
-  return fail(LSA_E_ARG, "lsa_label_vote: not built in this library");
+  REQUIRE(Q >= 1, LSA_E_SHAPE, "lsa_label_vote: Q=%d < 1", Q);
+  REQUIRE(L >= 1 && L <= LSA_MAX_VOTE_LAYERS, LSA_E_SHAPE, "lsa_label_vote: L=%d not in [1,%d]", L,
+          LSA_MAX_VOTE_LAYERS);
+  REQUIRE(N >= 1 && N <= 65536, LSA_E_SHAPE, "lsa_label_vote: N=%d not in [1,65536]", N);
+  REQUIRE(top_p > 0.f && top_p <= 1.f, LSA_E_ARG, "lsa_label_vote: top_p=%g not in (0,1]",
+          (double)top_p);
+  REQUIRE(theta >= 0, LSA_E_ARG, "lsa_label_vote: theta=%d < 0", theta);
+  REQUIRE(logits && count && label, LSA_E_ARG, "lsa_label_vote: null logits/count/label");
+  REQUIRE(aligned16(logits) && aligned16(count) && aligned16(label), LSA_E_ARG,
+          "lsa_label_vote: logits, count and label must be 16-byte aligned");
+  uint32_t* mask = layer_mask_opt;
+  if (!mask) {
+    const size_t need = lsa_label_vote_workspace_bytes(Q, L, N);
+    REQUIRE(ws && ws_bytes >= need, LSA_E_WORKSPACE,
+            "lsa_label_vote: workspace of %zu bytes needed without layer_mask_opt (got %zu)", need,
+            ws ? ws_bytes : (size_t)0);
+    mask = (uint32_t*)ws;
+  }
+  return hip_status(lsa::launch_label_vote(Q, L, N, top_p, theta, logits, mask, count, label,
+                                           stream),
+                    "lsa_label_vote");
 }
 
 size_t lsa_focal_bce_grad_workspace_bytes(int Q, int N, int D, int H, int dI) {

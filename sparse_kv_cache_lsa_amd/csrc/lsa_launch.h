@@ -50,6 +50,9 @@ hipError_t launch_topk(int B, int cap, int k, const int32_t* surv_idx,
 hipError_t launch_gather(int B, int N, int k, int row_bytes, const void* pool,
                          const int32_t* idx, void* hot, hipStream_t s);
 
+hipError_t launch_label_vote(int Q, int L, int N, float top_p, int theta, const float* logits,
+                             uint32_t* mask, uint8_t* count, uint8_t* label, hipStream_t s);
+
 hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s);
 
 }  // namespace lsa

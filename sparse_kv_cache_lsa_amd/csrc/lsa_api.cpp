@@ -225,17 +225,36 @@ lsa_status lsa_label_vote(int Q, int L, int N, float top_p, int theta, const flo
 }
 
 size_t lsa_focal_bce_grad_workspace_bytes(int Q, int N, int D, int H, int dI) {
-  (void)Q; (void)N; (void)D; (void)H; (void)dI;
-  return 0;
+  if (Q < 1 || Q > 64 || N < 1 || D < 64 || D % 64 || H < 1 || H > 64 || (dI != 64 && dI != 128))
+    return 0;
+  return lsa::focal_workspace_bytes(Q, N, D, H, dI);
 }
 
 lsa_status lsa_focal_bce_grad(int Q, int N, int D, int H, int dI, float gamma,
                               const uint16_t* h, const float* Wq, const float* Wg, float bias,
                               const uint16_t* K, const uint8_t* label, float* loss, float* dWq,
                               void* ws, size_t ws_bytes, hipStream_t stream) {
-  (void)Q; (void)N; (void)D; (void)H; (void)dI; (void)gamma; (void)h; (void)Wq; (void)Wg;
-  (void)bias; (void)K; (void)label; (void)loss; (void)dWq; (void)ws; (void)ws_bytes; (void)stream;
-  return fail(LSA_E_ARG, "lsa_focal_bce_grad: not built in this library");
+  REQUIRE(Q >= 1 && Q <= 64, LSA_E_SHAPE, "lsa_focal_bce_grad: Q=%d not in [1,64]", Q);
+  REQUIRE(N >= 1, LSA_E_SHAPE, "lsa_focal_bce_grad: N=%d < 1", N);
+  REQUIRE(D >= 64 && D % 64 == 0, LSA_E_SHAPE, "lsa_focal_bce_grad: D=%d not a positive multiple of 64", D);
+  REQUIRE(H >= 1 && H <= 64, LSA_E_SHAPE, "lsa_focal_bce_grad: H=%d not in [1,64]", H);
+  REQUIRE(dI == 64 || dI == 128, LSA_E_SHAPE, "lsa_focal_bce_grad: dI=%d not 64 or 128", dI);
+  REQUIRE(gamma >= 0.f && gamma <= 16.f, LSA_E_ARG, "lsa_focal_bce_grad: gamma=%g not in [0,16]",
+          (double)gamma);
+  REQUIRE(bias == bias && bias - bias == 0.f, LSA_E_ARG, "lsa_focal_bce_grad: bias not finite");
+  REQUIRE(h && Wq && Wg && K && label && loss && dWq, LSA_E_ARG,
+          "lsa_focal_bce_grad: null input or output pointer");
+  REQUIRE(aligned16(Wq) && aligned16(Wg) && aligned16(dWq), LSA_E_ARG,
+          "lsa_focal_bce_grad: Wq, Wg and dWq must be 16-byte aligned");
+  REQUIRE(((uintptr_t)h & 7u) == 0 && ((uintptr_t)K & 7u) == 0, LSA_E_ARG,
+          "lsa_focal_bce_grad: h and K must be 8-byte aligned");
+  const size_t need = lsa::focal_workspace_bytes(Q, N, D, H, dI);
+  REQUIRE(ws && ws_bytes >= need && ((uintptr_t)ws & 255u) == 0, LSA_E_WORKSPACE,
+          "lsa_focal_bce_grad: workspace of %zu bytes, 256-byte aligned, needed (got %zu)", need,
+          ws ? ws_bytes : (size_t)0);
+  return hip_status(lsa::launch_focal(Q, N, D, H, dI, gamma, h, Wq, Wg, bias, K, label, loss, dWq,
+                                      ws, stream),
+                    "lsa_focal_bce_grad");
 }
 
 }  // extern "C"

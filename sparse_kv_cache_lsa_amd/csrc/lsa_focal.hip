@@ -1,0 +1,404 @@
+// lsa_focal.hip -- student loss and gradient of the indexer's query
+// projection, for gfx950, in fp32.
+//
+// The keys K_IComp are frozen and only the query encoder's projection W_q is
+// trained, with binary cross-entropy plus a focal term that down-weights easy
+// negatives (gist.science technical summary, section 2.3 "backbone-free
+// decoupled training"; paper.oopus.info review, section 2, loss function).
+//   q_t = W_q h_t, g_t = softplus(W_g h_t), z_ts = sum_h g_th (q_th . k_s) + b
+//   u = (2y - 1) z, BCE = softplus(-u), FL = sigmoid(-u)^gamma softplus(-u)
+//   loss = mean_ts BCE + mean_ts FL,   dW_q = d loss / d W_q
+//
+// The gated head sum is linear in the key, so the forward pass contracts the
+// keys with one collapsed query per row, qe_t = sum_h g_th q_th (dI wide),
+// and the backward pass goes through G_t = sum_s delta_ts k_s:
+//   d loss / d q_thi = g_th G_ti,   dW_q[(h,i)][d] = sum_t g_th G_ti h_td.
+// Every product runs on v_mfma_f32_32x32x2_f32 (fp32 in, fp32 accumulate).
+// The operands of each product are stored with the contraction axis
+// contiguous, so a lane loads four consecutive k values of its row of A and
+// of its row of B with one vector load and feeds four MFMAs; the k order is
+// permuted identically in A and B (lane half 0 supplies k0..k0+3, half 1
+// k0+4..k0+7), which leaves every dot product unchanged.
+//
+// Kernels (one stream, in order):
+//   1 project   qa[t][r] = ([W_q; W_g] h_t)_r            (W read once, 4 waves split D)
+//   2 collapse  g = softplus(gate rows), qe_t, gT[h][t]
+//   3 transpose K -> KT [dI][Np], h -> hT [D][64] (contraction axes contiguous)
+//   4 logits    z = K qe^T + b; loss terms; delta = dloss/dz -> [Q][Np]
+//   5 grad      partial G over 256-entry chunks
+//   6 reduce    GT[i][t] = sum of partials (fixed order); loss = sum / (Q N)
+//   7 dW        dW_q = (gT * GT) hT^T, written once (nontemporal)
+#include "lsa_device.h"
+#include "lsa_launch.h"
+
+namespace lsa {
+namespace {
+
+constexpr int kQP = 64;      // padded query count (rows of the small operands)
+constexpr int kChunk = 256;  // entries per partial-gradient block
+
+__device__ __forceinline__ f32x4 bf16x4_to_f32(uint2 raw) {
+  f32x4 r;
+  r[0] = __uint_as_float(raw.x << 16);
+  r[1] = __uint_as_float(raw.x & 0xFFFF0000u);
+  r[2] = __uint_as_float(raw.y << 16);
+  r[3] = __uint_as_float(raw.y & 0xFFFF0000u);
+  return r;
+}
+
+__device__ __forceinline__ f32x4 load_bf16x4(const uint16_t* p) {
+  return bf16x4_to_f32(*(const uint2*)p);
+}
+
+__device__ __forceinline__ f32x16 mfma4(f32x4 a, f32x4 b, f32x16 c) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) c = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i], b[i], c, 0, 0, 0);
+  return c;
+}
+
+// accumulator element rr of lane l: row (rr&3) + 4*(l/32) + 8*(rr/4), col l%32
+__device__ __forceinline__ int acc_row(int rr, int half) { return (rr & 3) + 4 * half + 8 * (rr >> 2); }
+
+__device__ __forceinline__ float sigmoid_f(float x) { return 1.f / (1.f + __expf(-x)); }
+__device__ __forceinline__ float softplus_f(float x) { return fmaxf(x, 0.f) + log1pf(__expf(-fabsf(x))); }
+
+// ---------------------------------------------------------------- 1 project
+// grid: ceil(R/32) row tiles, R = H*dI + H; 4 waves split D; each wave keeps
+// a 32-row x 64-query tile.
+__global__ __launch_bounds__(256) void fproj_kernel(int Q, int D, int HdI, int H,
+                                                    const float* __restrict__ Wq,
+                                                    const float* __restrict__ Wg,
+                                                    const uint16_t* __restrict__ h,
+                                                    float* __restrict__ qa) {
+  __shared__ float red[4][2][16][64];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int n = lane & 31, half = lane >> 5;
+  const int R = HdI + H;
+  const int r = blockIdx.x * 32 + n;
+  const float* arow = nullptr;
+  if (r < HdI) arow = Wq + (size_t)r * D;
+  else if (r < R) arow = Wg + (size_t)(r - HdI) * D;
+  const uint16_t* b0 = n < Q ? h + (size_t)n * D : nullptr;
+  const uint16_t* b1 = n + 32 < Q ? h + (size_t)(n + 32) * D : nullptr;
+  const int kq = D / 4;
+  const int kbeg = wave * kq, kend = kbeg + kq;
+  f32x16 acc0 = {}, acc1 = {};
+#pragma unroll 4
+  for (int k = kbeg; k < kend; k += 8) {
+    const int kk = k + 4 * half;
+    const f32x4 a = arow ? *(const f32x4*)(arow + kk) : f32x4{0.f, 0.f, 0.f, 0.f};
+    const f32x4 x0 = b0 ? load_bf16x4(b0 + kk) : f32x4{0.f, 0.f, 0.f, 0.f};
+    const f32x4 x1 = b1 ? load_bf16x4(b1 + kk) : f32x4{0.f, 0.f, 0.f, 0.f};
+    acc0 = mfma4(a, x0, acc0);
+    acc1 = mfma4(a, x1, acc1);
+  }
+#pragma unroll
+  for (int rr = 0; rr < 16; ++rr) {
+    red[wave][0][rr][lane] = acc0[rr];
+    red[wave][1][rr][lane] = acc1[rr];
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < 2 * 16 * 64; e += 256) {
+    const int j = e >> 10, rr = (e >> 6) & 15, l = e & 63;
+    const float v = red[0][j][rr][l] + red[1][j][rr][l] + red[2][j][rr][l] + red[3][j][rr][l];
+    const int t = 32 * j + (l & 31);
+    const int row = blockIdx.x * 32 + acc_row(rr, l >> 5);
+    if (t < Q && row < R) qa[(size_t)t * R + row] = v;
+  }
+}
+
+// ---------------------------------------------------------------- 2 collapse
+// grid: kQP queries; block: 128 threads.  Rows t >= Q get zeros.
+__global__ __launch_bounds__(128) void fcollapse_kernel(int Q, int H, int dI,
+                                                        const float* __restrict__ qa,
+                                                        float* __restrict__ gT,
+                                                        float* __restrict__ qe) {
+  __shared__ float gs[64];
+  const int t = blockIdx.x;
+  const int R = H * dI + H;
+  const bool live = t < Q;
+  if (threadIdx.x < 64) {
+    float g = 0.f;
+    if (live && threadIdx.x < H) g = softplus_f(qa[(size_t)t * R + H * dI + threadIdx.x]);
+    gs[threadIdx.x] = g;
+    if (threadIdx.x < H) gT[threadIdx.x * kQP + t] = g;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < dI; i += 128) {
+    float acc = 0.f;
+    if (live)
+      for (int hh = 0; hh < H; ++hh) acc = fmaf(gs[hh], qa[(size_t)t * R + hh * dI + i], acc);
+    qe[t * dI + i] = acc;
+  }
+}
+
+// ---------------------------------------------------------------- 3 transpose
+// out[c][r] = in[r][c] for r < rows, 0 for rows <= r < out_ld (bf16 bits).
+__global__ __launch_bounds__(256) void ftranspose_kernel(const uint16_t* __restrict__ in, int rows,
+                                                         int cols, uint16_t* __restrict__ out,
+                                                         int out_ld) {
+  __shared__ uint16_t tile[64][65];
+  const int r0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
+  for (int e = threadIdx.x; e < 64 * 64; e += 256) {
+    const int rr = e >> 6, cc = e & 63;
+    const int r = r0 + rr, c = c0 + cc;
+    tile[rr][cc] = (r < rows && c < cols) ? in[(size_t)r * cols + c] : (uint16_t)0;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < 64 * 64; e += 256) {
+    const int cc = e >> 6, rr = e & 63;
+    const int r = r0 + rr, c = c0 + cc;
+    if (c < cols && r < out_ld) out[(size_t)c * out_ld + r] = tile[rr][cc];
+  }
+}
+
+// ---------------------------------------------------------------- 4 logits + delta
+// grid: ceil(N/128); 4 waves x 32 entries; each wave a 32-entry x 64-query tile.
+template <int DI>
+__global__ __launch_bounds__(256) void flogits_kernel(int Q, int N, int Np, float gamma,
+                                                      float bias, float inv_qn,
+                                                      const uint16_t* __restrict__ K,
+                                                      const float* __restrict__ qe,
+                                                      const uint8_t* __restrict__ label,
+                                                      float* __restrict__ delta,
+                                                      double* __restrict__ loss_part) {
+  __shared__ double wsum[4];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int n = lane & 31, half = lane >> 5;
+  const int s0 = (blockIdx.x * 4 + wave) * 32;
+  const int s = s0 + n;
+  const uint16_t* arow = s < N ? K + (size_t)s * DI : nullptr;
+  f32x16 acc0 = {}, acc1 = {};
+#pragma unroll
+  for (int k = 0; k < DI; k += 8) {
+    const int kk = k + 4 * half;
+    const f32x4 a = arow ? load_bf16x4(arow + kk) : f32x4{0.f, 0.f, 0.f, 0.f};
+    const f32x4 x0 = *(const f32x4*)(qe + n * DI + kk);
+    const f32x4 x1 = *(const f32x4*)(qe + (n + 32) * DI + kk);
+    acc0 = mfma4(a, x0, acc0);
+    acc1 = mfma4(a, x1, acc1);
+  }
+  double lsum = 0.0;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int t = 32 * j + n;
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) {
+      const int se = s0 + acc_row(rr, half);
+      if (t >= Q || se >= Np) continue;
+      float d = 0.f;
+      if (se < N) {
+        const float z = (j == 0 ? acc0[rr] : acc1[rr]) + bias;
+        const int y = label[(size_t)t * N + se] ? 1 : 0;
+        const float u = y ? z : -z;
+        const float nll = softplus_f(-u);          // -log sigmoid(u)
+        const float pu = sigmoid_f(u);
+        const float qu = sigmoid_f(-u);
+        const float mod = gamma == 0.f ? 1.f : powf(qu, gamma);
+        lsum += (double)nll + (double)(mod * nll);
+        const float dbce = sigmoid_f(z) - (float)y;
+        const float dfl_du = mod * (-gamma * pu * nll - qu);
+        d = (dbce + (y ? dfl_du : -dfl_du)) * inv_qn;
+      }
+      delta[(size_t)t * Np + se] = d;
+    }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) lsum += __shfl_xor(lsum, off, 64);
+  if (lane == 0) wsum[wave] = lsum;
+  __syncthreads();
+  if (threadIdx.x == 0) loss_part[blockIdx.x] = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
+}
+
+// ---------------------------------------------------------------- 5 partial G
+// grid: ceil(Np/kChunk) chunks; wave w: queries 32*(w&1).., dims half (w>>1).
+template <int DI>
+__global__ __launch_bounds__(256) void fgrad_kernel(int Q, int Np, const float* __restrict__ delta,
+                                                    const uint16_t* __restrict__ KT,
+                                                    float* __restrict__ Gp) {
+  constexpr int NTI = DI / 64;   // 32-dim tiles per wave
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int n = lane & 31, half = lane >> 5;
+  const int t = 32 * (wave & 1) + n;
+  const int i0 = (wave >> 1) * (DI / 2);
+  const float* arow = t < Q ? delta + (size_t)t * Np : nullptr;
+  const int kbeg = blockIdx.x * kChunk, kend = min(Np, kbeg + kChunk);
+  f32x16 acc[NTI];
+#pragma unroll
+  for (int j = 0; j < NTI; ++j) acc[j] = f32x16{};
+#pragma unroll 2
+  for (int k = kbeg; k < kend; k += 8) {
+    const int kk = k + 4 * half;
+    const f32x4 a = arow ? *(const f32x4*)(arow + kk) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < NTI; ++j) {
+      const f32x4 b = load_bf16x4(KT + (size_t)(i0 + 32 * j + n) * Np + kk);
+      acc[j] = mfma4(a, b, acc[j]);
+    }
+  }
+  float* out = Gp + (size_t)blockIdx.x * kQP * DI;
+#pragma unroll
+  for (int j = 0; j < NTI; ++j)
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) {
+      const int tt = 32 * (wave & 1) + acc_row(rr, half);
+      out[tt * DI + i0 + 32 * j + n] = acc[j][rr];
+    }
+}
+
+// ---------------------------------------------------------------- 6 reduce
+__global__ __launch_bounds__(256) void freduce_kernel(int Q, int DI, int nchunks, int nloss,
+                                                      double inv_qn, const float* __restrict__ Gp,
+                                                      float* __restrict__ GT,
+                                                      const double* __restrict__ loss_part,
+                                                      float* __restrict__ loss) {
+  const int e = blockIdx.x * 256 + threadIdx.x;   // e = i * kQP + t
+  if (e < DI * kQP) {
+    const int i = e / kQP, t = e % kQP;
+    float acc = 0.f;
+    if (t < Q)
+      for (int c = 0; c < nchunks; ++c) acc += Gp[((size_t)c * kQP + t) * DI + i];
+    GT[e] = acc;
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    double s = 0.0;
+    for (int b = 0; b < nloss; ++b) s += loss_part[b];
+    loss[0] = (float)(s * inv_qn);
+  }
+}
+
+// ---------------------------------------------------------------- 7 dW
+// grid: (ceil(D/256), HdI/32); wave w takes 64 columns; contraction over the
+// kQP padded queries: A[(h,i)][t] = gT[h][t] GT[i][t], B[d][t] = hT[d][t].
+template <int DI>
+__global__ __launch_bounds__(256) void fdw_kernel(int D, const float* __restrict__ gT,
+                                                  const float* __restrict__ GT,
+                                                  const uint16_t* __restrict__ hT,
+                                                  float* __restrict__ dW) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int n = lane & 31, half = lane >> 5;
+  const int row = blockIdx.y * 32 + n;             // (h, i) = (row / DI, row % DI)
+  const int c0 = blockIdx.x * 256 + wave * 64;
+  if (c0 >= D) return;
+  const float* ga = gT + (row / DI) * kQP;
+  const float* Ga = GT + (row % DI) * kQP;
+  const uint16_t* b0 = hT + (size_t)(c0 + n) * kQP;
+  const uint16_t* b1 = hT + (size_t)(c0 + 32 + n) * kQP;
+  f32x16 acc0 = {}, acc1 = {};
+#pragma unroll
+  for (int k = 0; k < kQP; k += 8) {
+    const int kk = k + 4 * half;
+    const f32x4 a = *(const f32x4*)(ga + kk) * *(const f32x4*)(Ga + kk);
+    acc0 = mfma4(a, load_bf16x4(b0 + kk), acc0);
+    acc1 = mfma4(a, load_bf16x4(b1 + kk), acc1);
+  }
+#pragma unroll
+  for (int rr = 0; rr < 16; ++rr) {
+    const size_t r = (size_t)blockIdx.y * 32 + acc_row(rr, half);
+    __builtin_nontemporal_store(acc0[rr], dW + r * D + c0 + n);
+    __builtin_nontemporal_store(acc1[rr], dW + r * D + c0 + 32 + n);
+  }
+}
+
+struct FocalWs {
+  float* qa;
+  float* gT;
+  float* qe;
+  uint16_t* KT;
+  uint16_t* hT;
+  float* delta;
+  float* Gp;
+  float* GT;
+  double* loss_part;
+  size_t bytes;
+};
+
+size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+FocalWs carve(void* base, int Q, int N, int D, int H, int dI) {
+  (void)Q;
+  const int Np = (N + 7) & ~7;
+  const size_t R = (size_t)H * dI + H;
+  const int nchunks = (Np + kChunk - 1) / kChunk;
+  const int nloss = (N + 127) / 128;
+  size_t off = 0;
+  FocalWs w;
+  auto take = [&](size_t bytes) {
+    char* p = (char*)base + off;
+    off += up256(bytes);
+    return (void*)p;
+  };
+  w.qa = (float*)take((size_t)kQP * R * 4);
+  w.gT = (float*)take((size_t)64 * kQP * 4);
+  w.qe = (float*)take((size_t)kQP * dI * 4);
+  w.KT = (uint16_t*)take((size_t)dI * Np * 2);
+  w.hT = (uint16_t*)take((size_t)D * kQP * 2);
+  w.delta = (float*)take((size_t)kQP * Np * 4);
+  w.Gp = (float*)take((size_t)nchunks * kQP * dI * 4);
+  w.GT = (float*)take((size_t)dI * kQP * 4);
+  w.loss_part = (double*)take((size_t)nloss * 8);
+  w.bytes = off;
+  return w;
+}
+
+}  // namespace
+
+size_t focal_workspace_bytes(int Q, int N, int D, int H, int dI) {
+  return carve(nullptr, Q, N, D, H, dI).bytes;
+}
+
+hipError_t launch_focal(int Q, int N, int D, int H, int dI, float gamma, const uint16_t* h,
+                        const float* Wq, const float* Wg, float bias, const uint16_t* K,
+                        const uint8_t* label, float* loss, float* dWq, void* ws, hipStream_t s) {
+  const FocalWs w = carve(ws, Q, N, D, H, dI);
+  const int Np = (N + 7) & ~7;
+  const int HdI = H * dI;
+  const int R = HdI + H;
+  const int nchunks = (Np + kChunk - 1) / kChunk;
+  const int nloss = (N + 127) / 128;
+  const double inv_qn = 1.0 / ((double)Q * (double)N);
+  hipError_t e;
+#define FOCAL_CHECK()                        \
+  do {                                       \
+    e = hipGetLastError();                   \
+    if (e != hipSuccess) return e;           \
+  } while (0)
+  hipLaunchKernelGGL(fproj_kernel, dim3((R + 31) / 32), dim3(256), 0, s, Q, D, HdI, H, Wq, Wg, h,
+                     w.qa);
+  FOCAL_CHECK();
+  hipLaunchKernelGGL(fcollapse_kernel, dim3(kQP), dim3(128), 0, s, Q, H, dI, w.qa, w.gT, w.qe);
+  FOCAL_CHECK();
+  hipLaunchKernelGGL(ftranspose_kernel, dim3((Np + 63) / 64, (dI + 63) / 64), dim3(256), 0, s, K,
+                     N, dI, w.KT, Np);
+  FOCAL_CHECK();
+  hipLaunchKernelGGL(ftranspose_kernel, dim3(1, (D + 63) / 64), dim3(256), 0, s, h, Q, D, w.hT,
+                     kQP);
+  FOCAL_CHECK();
+  if (dI == 64)
+    hipLaunchKernelGGL((flogits_kernel<64>), dim3(nloss), dim3(256), 0, s, Q, N, Np, gamma, bias,
+                       (float)inv_qn, K, w.qe, label, w.delta, w.loss_part);
+  else
+    hipLaunchKernelGGL((flogits_kernel<128>), dim3(nloss), dim3(256), 0, s, Q, N, Np, gamma, bias,
+                       (float)inv_qn, K, w.qe, label, w.delta, w.loss_part);
+  FOCAL_CHECK();
+  if (dI == 64)
+    hipLaunchKernelGGL((fgrad_kernel<64>), dim3(nchunks), dim3(256), 0, s, Q, Np, w.delta, w.KT,
+                       w.Gp);
+  else
+    hipLaunchKernelGGL((fgrad_kernel<128>), dim3(nchunks), dim3(256), 0, s, Q, Np, w.delta, w.KT,
+                       w.Gp);
+  FOCAL_CHECK();
+  hipLaunchKernelGGL(freduce_kernel, dim3((dI * kQP + 255) / 256), dim3(256), 0, s, Q, dI, nchunks,
+                     nloss, inv_qn, w.Gp, w.GT, w.loss_part, loss);
+  FOCAL_CHECK();
+  const dim3 gdw((D + 255) / 256, HdI / 32);
+  if (dI == 64)
+    hipLaunchKernelGGL((fdw_kernel<64>), gdw, dim3(256), 0, s, D, w.gT, w.GT, w.hT, dWq);
+  else
+    hipLaunchKernelGGL((fdw_kernel<128>), gdw, dim3(256), 0, s, D, w.gT, w.GT, w.hT, dWq);
+  FOCAL_CHECK();
+#undef FOCAL_CHECK
+  return hipSuccess;
+}
+
+}  // namespace lsa

@@ -53,6 +53,12 @@ hipError_t launch_gather(int B, int N, int k, int row_bytes, const void* pool,
 hipError_t launch_label_vote(int Q, int L, int N, float top_p, int theta, const float* logits,
                              uint32_t* mask, uint8_t* count, uint8_t* label, hipStream_t s);
 
+size_t focal_workspace_bytes(int Q, int N, int D, int H, int dI);
+
+hipError_t launch_focal(int Q, int N, int D, int H, int dI, float gamma, const uint16_t* h,
+                        const float* Wq, const float* Wg, float bias, const uint16_t* K,
+                        const uint8_t* label, float* loss, float* dWq, void* ws, hipStream_t s);
+
 hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s);
 
 }  // namespace lsa

@@ -86,6 +86,31 @@ def test_validation_errors_return_before_launch(lib):
     assert lib.lsa_gather_hot(1, 10, 4, 24, fake, fake, fake, None) == _abi.LSA_E_ARG
     # projection: hidden size not a multiple of 256
     assert lib.lsa_project_query(1, 1, 100, 8, 64, fake, 0, arr, arr, fake, fake, None) == _abi.LSA_E_SHAPE
+    # label vote: too many layers, top_p out of range, no mask and no workspace
+    assert lib.lsa_label_vote(1, 33, 100, 0.6, 3, fake, fake, fake, fake, None, 0, None) == _abi.LSA_E_SHAPE
+    assert lib.lsa_label_vote(1, 3, 65537, 0.6, 3, fake, fake, fake, fake, None, 0, None) == _abi.LSA_E_SHAPE
+    assert lib.lsa_label_vote(1, 3, 100, 0.0, 3, fake, fake, fake, fake, None, 0, None) == _abi.LSA_E_ARG
+    assert lib.lsa_label_vote(1, 3, 100, 1.5, 3, fake, fake, fake, fake, None, 0, None) == _abi.LSA_E_ARG
+    assert lib.lsa_label_vote(1, 3, 100, 0.6, 3, fake, None, fake, fake, None, 0, None) == _abi.LSA_E_WORKSPACE
+    assert lib.lsa_label_vote(1, 3, 100, 0.6, 3, C.c_void_p(20), fake, fake, fake, None, 0, None) == _abi.LSA_E_ARG
+    # focal: Q above 64, D not a multiple of 64, unsupported dI, short workspace
+    F = lambda Q, N, D, H, dI, g=2.0, ws=fake, nws=1 << 30: lib.lsa_focal_bce_grad(
+        Q, N, D, H, dI, g, fake, fake, fake, 0.0, fake, fake, fake, fake, ws, nws, None)
+    assert F(65, 10, 64, 1, 64) == _abi.LSA_E_SHAPE
+    assert F(4, 10, 96, 1, 64) == _abi.LSA_E_SHAPE
+    assert F(4, 10, 64, 1, 96) == _abi.LSA_E_SHAPE
+    assert F(4, 10, 64, 1, 64, g=-1.0) == _abi.LSA_E_ARG
+    assert F(4, 10, 64, 1, 64, ws=C.c_void_p(256), nws=16) == _abi.LSA_E_WORKSPACE
+    assert F(4, 10, 64, 1, 64, ws=C.c_void_p(16 + 256)) == _abi.LSA_E_WORKSPACE   # misaligned
+
+
+def test_workspace_sizes(lib):
+    W = (32768 + 31) // 32
+    assert lib.lsa_label_vote_workspace_bytes(64, 20, 32768) == 64 * 20 * W * 4
+    big = lib.lsa_focal_bce_grad_workspace_bytes(64, 32768, 4096, 64, 128)
+    # at least dloss/dz [64][N] fp32 and the transposed keys [dI][N] bf16
+    assert big >= 64 * 32768 * 4 + 128 * 32768 * 2
+    assert lib.lsa_focal_bce_grad_workspace_bytes(65, 10, 64, 1, 64) == 0
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

@@ -64,6 +64,9 @@ def main():
     torch.cuda.init()
     torch.empty(1, device="cuda")
 
+    if args.workload == "labels128k":
+        return bench_labels(args)
+
     import lsa_inputs as gen
     import sparse_kv_cache_lsa_amd as lsa
     from sparse_kv_cache_lsa_amd.pipeline import TriggerBuffers
@@ -121,6 +124,8 @@ def main():
     ms_per_step = wall * 1e3 / max(args.steps, 1)
     names = ["project", "score", "select", "topk", "gather"]
     per = {n: float(np.median([e[i].elapsed_time(e[i + 1]) for e in evs])) for i, n in enumerate(names)}
+    pct = {n: [float(np.percentile([e[i].elapsed_time(e[i + 1]) for e in evs], q)) for q in (10, 90)]
+           for i, n in enumerate(names)}
     mean_score = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
     score_select = float(np.median([e[1].elapsed_time(e[3]) for e in evs]))
 
@@ -161,6 +166,7 @@ def main():
         "score_select": {"ms": score_select, "GB/s": ss_gbs, "frac_of_peak": ss_gbs / HBM_PEAK_GBS,
                          "triples_per_s": triples / (score_select * 1e-3)},
         "kernel_ms_median": per,
+        "kernel_ms_p10_p90": pct,
         "survivor_fraction": float(counts.mean() / w.N),
     }
 
@@ -180,6 +186,117 @@ def main():
     if not args.skip_cpu:
         result["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def bench_labels(args):
+    """Offline label workload: one step = golden labels by majority vote over
+    the teacher layers (lsa_label_vote) followed by the student loss and its
+    W_q gradient on those labels (lsa_focal_bce_grad)."""
+    import numpy as np
+    import torch
+
+    import lsa_inputs as gen
+    import sparse_kv_cache_lsa_amd as lsa
+
+    w = gen.LABELS
+    dev = "cuda"
+    t0 = time.time()
+    x = np.stack([gen.teacher_logits(w, q) for q in range(w.Q)])
+    h, Wq, Wg, K, bias = gen.student(w)
+    xd = torch.from_numpy(x).to(dev)
+    hd = torch.from_numpy(h.view(np.int16)).view(torch.bfloat16).to(dev)
+    Kd = torch.from_numpy(K.view(np.int16)).view(torch.bfloat16).to(dev)
+    Wqd, Wgd = torch.from_numpy(Wq).to(dev), torch.from_numpy(Wg).to(dev)
+    W = (w.N + 31) // 32
+    mask = torch.empty((w.Q, w.L, W), dtype=torch.int32, device=dev)
+    count = torch.empty((w.Q, w.N), dtype=torch.uint8, device=dev)
+    label = torch.empty((w.Q, w.N), dtype=torch.uint8, device=dev)
+    loss = torch.empty(1, dtype=torch.float32, device=dev)
+    dW = torch.empty((w.H * w.dI, w.D), dtype=torch.float32, device=dev)
+    ws = torch.empty(lsa.lsa_focal_bce_grad_workspace_bytes(w.Q, w.N, w.D, w.H, w.dI),
+                     dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    print(f"# inputs ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    stream = torch.cuda.current_stream()
+
+    def step(e=None):
+        if e is not None:
+            e[0].record(stream)
+        lsa.lsa_label_vote(xd, w.top_p, w.theta, count, label, layer_mask=mask, stream=stream)
+        if e is not None:
+            e[1].record(stream)
+        lsa.lsa_focal_bce_grad(hd, Wqd, Wgd, bias, Kd, label, w.gamma, loss, dW, ws, H=w.H,
+                               dI=w.dI, stream=stream)
+        if e is not None:
+            e[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for e in evs:
+        step(e)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    ms_per_step = wall * 1e3 / max(args.steps, 1)
+    vote_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    focal_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    logits = w.Q * w.L * w.N
+    # algorithmic bytes: logits read once, masks + counts + labels written
+    vote_bytes = logits * 4 + w.Q * w.L * W * 4 + 2 * w.Q * w.N
+    # algorithmic flops of the student step: projection (q and gates), logits,
+    # key gradient, dW_q -- each 2 flops per multiply-add
+    HdI = w.H * w.dI
+    focal_flops = 2.0 * w.Q * w.D * (HdI + w.H) + 2 * 2.0 * w.Q * w.N * w.dI + 2.0 * HdI * w.D * w.Q
+    vote_mean = float(np.mean(vote_ms))
+    focal_mean = float(np.mean(focal_ms))
+    vote_gbs = vote_bytes / (vote_mean * 1e-3) / 1e9
+    focal_tfs = focal_flops / (focal_mean * 1e-3) / 1e12
+    result = {
+        "metric": "teacher logits labelled per second (label vote + student loss/grad)",
+        "value": logits / (ms_per_step * 1e-3),
+        "unit": "(query, layer, entry) logits/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "queries": w.Q, "teacher_layers": w.L, "entries": w.N,
+                   "top_p": w.top_p, "theta": w.theta, "gamma": w.gamma, "heads": w.H,
+                   "head_dim": w.dI, "hidden": w.D, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": vote_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": vote_gbs / HBM_PEAK_GBS, "traffic": None, "kernel": "lsa_label_vote",
+                     "algorithmic_bytes_per_launch": vote_bytes, "mean_launch_ms": vote_mean},
+        "focal": {"bound": "mfma", "achieved": focal_tfs, "peak": 157.3, "unit": "TFLOP/s",
+                  "frac": focal_tfs / 157.3, "kernel": "lsa_focal_bce_grad (fp32)",
+                  "algorithmic_flops_per_launch": focal_flops, "mean_launch_ms": focal_mean},
+        "kernel_ms_median": {"label_vote": float(np.median(vote_ms)),
+                             "focal_bce_grad": float(np.median(focal_ms))},
+        "loss": float(loss.item()),
+        "positive_label_fraction": float(label.float().mean().item()),
+    }
+    if not args.skip_cpu:
+        result["cpu_baseline"] = cpu_baseline_labels(w, x, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline_labels(w, x, budget_s):
+    """The CPU oracle's nucleus + vote on whole queries until the budget is
+    used; throughput in teacher logits per second."""
+    from oracle import oracle
+    oracle._load()
+    import numpy as np
+    t0 = time.perf_counter()
+    done = 0
+    while done < w.Q and (time.perf_counter() - t0) < budget_s:
+        sel = np.stack([oracle.nucleus(x[done, l], w.top_p)[0] for l in range(w.L)])
+        oracle.vote(sel, w.theta)
+        done += 1
+    el = time.perf_counter() - t0
+    return {"value": done * w.L * w.N / el, "unit": "(query, layer, entry) logits/s",
+            "cores": 1, "kind": "oracle",
+            "sample": f"{done} of {w.Q} queries x {w.L} layers x {w.N} entries "
+                      f"(softmax + nucleus + vote, no student step), {el:.1f}s"}
 
 
 def cpu_baseline(w, inp, budget_s):

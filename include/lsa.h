@@ -209,9 +209,10 @@ lsa_status lsa_gather_hot(int B, int N, int k, int row_bytes, const void* pool,
  *   ws              device workspace of lsa_label_vote_workspace_bytes()
  *                   bytes (holds the per-layer masks); needed only when
  *                   layer_mask_opt is NULL, else may be NULL
- * The kept mass is computed in 64-bit fixed point (exp(x - max) in units of
- * 2^-40), so the result is deterministic; it differs from exact arithmetic
- * only for entries whose mass ahead lies within ~1e-6 of top_p.
+ * Each entry's mass exp(x - max) is truncated to units of 2^-31 and summed
+ * exactly in 64-bit integers, so the result is deterministic; it differs
+ * from exact arithmetic only for entries whose mass ahead lies within
+ * N * 2^-31 (relative) of top_p.
  * Limits: Q >= 1, 1 <= L <= LSA_MAX_VOTE_LAYERS, 1 <= N <= 65536,
  * 0 < top_p <= 1, theta >= 0.  Errors: LSA_E_SHAPE / LSA_E_ARG for the
  * limits, null or misaligned pointers; LSA_E_WORKSPACE for a missing or
@@ -240,8 +241,8 @@ lsa_status lsa_label_vote(int Q, int L, int N, float top_p, int theta,
  *         queries, transposed K and h, dloss/dz, partial key gradients)
  * Every product is an fp32 contraction with fp32 accumulation; the loss sum
  * is accumulated in fp64 in a fixed order, so results are deterministic.
- * Limits: 1 <= Q <= 64, N >= 1, D % 64 == 0, 1 <= H <= 64, dI in {64, 128},
- * 0 <= gamma <= 16, finite bias.  Errors: LSA_E_SHAPE / LSA_E_ARG for the
+ * Limits: 1 <= Q <= 64, 1 <= N <= 4,000,000, D % 64 == 0 and D <= 16384,
+ * 1 <= H <= 64, dI in {64, 128}, 0 <= gamma <= 16, finite bias.  Errors: LSA_E_SHAPE / LSA_E_ARG for the
  * limits, null or misaligned pointers; LSA_E_WORKSPACE for a missing, short
  * or misaligned workspace; LSA_E_HIP for a launch failure.
  */

@@ -225,7 +225,8 @@ lsa_status lsa_label_vote(int Q, int L, int N, float top_p, int theta, const flo
 }
 
 size_t lsa_focal_bce_grad_workspace_bytes(int Q, int N, int D, int H, int dI) {
-  if (Q < 1 || Q > 64 || N < 1 || D < 64 || D % 64 || H < 1 || H > 64 || (dI != 64 && dI != 128))
+  if (Q < 1 || Q > 64 || N < 1 || N > 4000000 || D < 64 || D > 16384 || D % 64 || H < 1 ||
+      H > 64 || (dI != 64 && dI != 128))
     return 0;
   return lsa::focal_workspace_bytes(Q, N, D, H, dI);
 }
@@ -235,8 +236,9 @@ lsa_status lsa_focal_bce_grad(int Q, int N, int D, int H, int dI, float gamma,
                               const uint16_t* K, const uint8_t* label, float* loss, float* dWq,
                               void* ws, size_t ws_bytes, hipStream_t stream) {
   REQUIRE(Q >= 1 && Q <= 64, LSA_E_SHAPE, "lsa_focal_bce_grad: Q=%d not in [1,64]", Q);
-  REQUIRE(N >= 1, LSA_E_SHAPE, "lsa_focal_bce_grad: N=%d < 1", N);
-  REQUIRE(D >= 64 && D % 64 == 0, LSA_E_SHAPE, "lsa_focal_bce_grad: D=%d not a positive multiple of 64", D);
+  REQUIRE(N >= 1 && N <= 4000000, LSA_E_SHAPE, "lsa_focal_bce_grad: N=%d not in [1,4000000]", N);
+  REQUIRE(D >= 64 && D <= 16384 && D % 64 == 0, LSA_E_SHAPE,
+          "lsa_focal_bce_grad: D=%d not a multiple of 64 in [64,16384]", D);
   REQUIRE(H >= 1 && H <= 64, LSA_E_SHAPE, "lsa_focal_bce_grad: H=%d not in [1,64]", H);
   REQUIRE(dI == 64 || dI == 128, LSA_E_SHAPE, "lsa_focal_bce_grad: dI=%d not 64 or 128", dI);
   REQUIRE(gamma >= 0.f && gamma <= 16.f, LSA_E_ARG, "lsa_focal_bce_grad: gamma=%g not in [0,16]",

@@ -21,12 +21,12 @@
 // k0+4..k0+7), which leaves every dot product unchanged.
 //
 // Kernels (one stream, in order):
-//   1 project   qa[t][r] = ([W_q; W_g] h_t)_r            (W read once, 4 waves split D)
+//   1 project   qa[t][r] = ([W_q; W_g] h_t)_r            (W read once, D split over blocks)
 //   2 collapse  g = softplus(gate rows), qe_t, gT[h][t]
 //   3 transpose K -> KT [dI][Np], h -> hT [D][64] (contraction axes contiguous)
 //   4 logits    z = K qe^T + b; loss terms; delta = dloss/dz -> [Q][Np]
-//   5 grad      partial G over 256-entry chunks
-//   6 reduce    GT[i][t] = sum of partials (fixed order); loss = sum / (Q N)
+//   5 grad      partial G over 128-entry chunks
+//   6 reduce    GT[i][t] = sum of partials, loss = sum / (Q N) (fixed orders)
 //   7 dW        dW_q = (gT * GT) hT^T, written once (nontemporal)
 #include "lsa_device.h"
 #include "lsa_launch.h"
@@ -35,7 +35,7 @@ namespace lsa {
 namespace {
 
 constexpr int kQP = 64;      // padded query count (rows of the small operands)
-constexpr int kChunk = 256;  // entries per partial-gradient block
+constexpr int kChunk = 128;  // entries per partial-gradient block
 
 __device__ __forceinline__ f32x4 bf16x4_to_f32(uint2 raw) {
   f32x4 r;
@@ -50,6 +50,26 @@ __device__ __forceinline__ f32x4 load_bf16x4(const uint16_t* p) {
   return bf16x4_to_f32(*(const uint2*)p);
 }
 
+// Buffer resources: loads past `bytes` return 0, so rows beyond the operand
+// (padding queries, the tail of the last tile) need no branch -- a branch
+// around a load makes the compiler wait for every load in flight.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, size_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
+                                           (int)(bytes < 0x7FFFFFFFu ? bytes : 0x7FFFFFFFu),
+                                           0x00020000);
+}
+
+__device__ __forceinline__ f32x4 buf_f32x4(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
+}
+
+__device__ __forceinline__ f32x4 buf_bf16x4(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  const u32x2 v = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, byte_off, 0, 0));
+  return bf16x4_to_f32(uint2{v[0], v[1]});
+}
+
+constexpr uint32_t kFar = 0x7FFFFFF0u;   // an offset past every range used here
+
 __device__ __forceinline__ f32x16 mfma4(f32x4 a, f32x4 b, f32x16 c) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) c = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i], b[i], c, 0, 0, 0);
@@ -63,34 +83,54 @@ __device__ __forceinline__ float sigmoid_f(float x) { return 1.f / (1.f + __expf
 __device__ __forceinline__ float softplus_f(float x) { return fmaxf(x, 0.f) + log1pf(__expf(-fabsf(x))); }
 
 // ---------------------------------------------------------------- 1 project
-// grid: ceil(R/32) row tiles, R = H*dI + H; 4 waves split D; each wave keeps
-// a 32-row x 64-query tile.
+// grid: (ceil(R/32) row tiles, KS slices of D), R = H*dI + H; the 4 waves of
+// a block split the block's slice again; each wave keeps a 32-row x 64-query
+// tile.  Block (tile, ks) writes its partial sums to qp[ks][t][r]; splitting D
+// over KS blocks keeps enough loads in flight to stream W at full rate.
 __global__ __launch_bounds__(256) void fproj_kernel(int Q, int D, int HdI, int H,
                                                     const float* __restrict__ Wq,
                                                     const float* __restrict__ Wg,
                                                     const uint16_t* __restrict__ h,
-                                                    float* __restrict__ qa) {
+                                                    float* __restrict__ qp) {
   __shared__ float red[4][2][16][64];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n = lane & 31, half = lane >> 5;
   const int R = HdI + H;
-  const int r = blockIdx.x * 32 + n;
-  const float* arow = nullptr;
-  if (r < HdI) arow = Wq + (size_t)r * D;
-  else if (r < R) arow = Wg + (size_t)(r - HdI) * D;
-  const uint16_t* b0 = n < Q ? h + (size_t)n * D : nullptr;
-  const uint16_t* b1 = n + 32 < Q ? h + (size_t)(n + 32) * D : nullptr;
-  const int kq = D / 4;
-  const int kbeg = wave * kq, kend = kbeg + kq;
+  const int KS = gridDim.y;
+  // a 32-row tile lies wholly in W_q or wholly in W_g (H*dI is a multiple of
+  // 32); rows past the gate rows read 0 through the buffer range check
+  const bool gate_tile = blockIdx.x * 32 >= HdI;
+  const __amdgpu_buffer_rsrc_t ra = gate_tile ? rsrc(Wg, (size_t)H * D * 4)
+                                              : rsrc(Wq, (size_t)HdI * D * 4);
+  const int rl = blockIdx.x * 32 + n - (gate_tile ? HdI : 0);
+  const __amdgpu_buffer_rsrc_t rb = rsrc(h, (size_t)Q * D * 2);
+  const int kq = D / (4 * KS);
+  const int kbeg = (blockIdx.y * 4 + wave) * kq, kend = kbeg + kq;
+  const uint32_t aoff = (uint32_t)rl * D * 4, b0off = (uint32_t)n * D * 2,
+                 b1off = (uint32_t)(n + 32) * D * 2;
   f32x16 acc0 = {}, acc1 = {};
-#pragma unroll 4
-  for (int k = kbeg; k < kend; k += 8) {
+  int k = kbeg;
+  // batches of four k-steps: twelve loads in flight before the first MFMA
+  for (; k + 32 <= kend; k += 32) {
+    f32x4 a[4], x0[4], x1[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int kk = k + 8 * j + 4 * half;
+      a[j] = buf_f32x4(ra, aoff + kk * 4);
+      x0[j] = buf_bf16x4(rb, b0off + kk * 2);
+      x1[j] = buf_bf16x4(rb, b1off + kk * 2);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      acc0 = mfma4(a[j], x0[j], acc0);
+      acc1 = mfma4(a[j], x1[j], acc1);
+    }
+  }
+  for (; k < kend; k += 8) {
     const int kk = k + 4 * half;
-    const f32x4 a = arow ? *(const f32x4*)(arow + kk) : f32x4{0.f, 0.f, 0.f, 0.f};
-    const f32x4 x0 = b0 ? load_bf16x4(b0 + kk) : f32x4{0.f, 0.f, 0.f, 0.f};
-    const f32x4 x1 = b1 ? load_bf16x4(b1 + kk) : f32x4{0.f, 0.f, 0.f, 0.f};
-    acc0 = mfma4(a, x0, acc0);
-    acc1 = mfma4(a, x1, acc1);
+    const f32x4 a = buf_f32x4(ra, aoff + kk * 4);
+    acc0 = mfma4(a, buf_bf16x4(rb, b0off + kk * 2), acc0);
+    acc1 = mfma4(a, buf_bf16x4(rb, b1off + kk * 2), acc1);
   }
 #pragma unroll
   for (int rr = 0; rr < 16; ++rr) {
@@ -98,13 +138,25 @@ __global__ __launch_bounds__(256) void fproj_kernel(int Q, int D, int HdI, int H
     red[wave][1][rr][lane] = acc1[rr];
   }
   __syncthreads();
+  float* out = qp + (size_t)blockIdx.y * kQP * R;
   for (int e = threadIdx.x; e < 2 * 16 * 64; e += 256) {
     const int j = e >> 10, rr = (e >> 6) & 15, l = e & 63;
     const float v = red[0][j][rr][l] + red[1][j][rr][l] + red[2][j][rr][l] + red[3][j][rr][l];
     const int t = 32 * j + (l & 31);
     const int row = blockIdx.x * 32 + acc_row(rr, l >> 5);
-    if (t < Q && row < R) qa[(size_t)t * R + row] = v;
+    if (t < Q && row < R) out[(size_t)t * R + row] = v;
   }
+}
+
+// qa[t][r] = sum over the KS slices in order (one thread per element)
+__global__ __launch_bounds__(256) void fproj_sum_kernel(int n, int KS, size_t slice,
+                                                        const float* __restrict__ qp,
+                                                        float* __restrict__ qa) {
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  if (e >= n) return;
+  float acc = qp[e];
+  for (int ks = 1; ks < KS; ++ks) acc += qp[ks * slice + e];
+  qa[e] = acc;
 }
 
 // ---------------------------------------------------------------- 2 collapse
@@ -153,7 +205,11 @@ __global__ __launch_bounds__(256) void ftranspose_kernel(const uint16_t* __restr
 }
 
 // ---------------------------------------------------------------- 4 logits + delta
-// grid: ceil(N/128); 4 waves x 32 entries; each wave a 32-entry x 64-query tile.
+// grid: ceil(N/64); wave w takes entries 32*(2*blockIdx.x + w/2) .. +31 and
+// queries 32*(w%2) .. +31 (A = collapsed queries, B = keys), so the 32 lanes
+// of a half-wave hold consecutive entries of one query: label loads and delta
+// stores coalesce.  The epilogue (loss terms, dloss/dz) is VALU work; small
+// tiles give enough waves to hide its latency.
 template <int DI>
 __global__ __launch_bounds__(256) void flogits_kernel(int Q, int N, int Np, float gamma,
                                                       float bias, float inv_qn,
@@ -165,43 +221,48 @@ __global__ __launch_bounds__(256) void flogits_kernel(int Q, int N, int Np, floa
   __shared__ double wsum[4];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n = lane & 31, half = lane >> 5;
-  const int s0 = (blockIdx.x * 4 + wave) * 32;
+  const int s0 = (blockIdx.x * 2 + (wave >> 1)) * 32;
+  const int t0 = 32 * (wave & 1);
   const int s = s0 + n;
-  const uint16_t* arow = s < N ? K + (size_t)s * DI : nullptr;
-  f32x16 acc0 = {}, acc1 = {};
+  const __amdgpu_buffer_rsrc_t rk = rsrc(K, (size_t)N * DI * 2);
+  const uint32_t boff = s < N ? (uint32_t)s * DI * 2 : kFar;
+  f32x16 acc = {};
 #pragma unroll
   for (int k = 0; k < DI; k += 8) {
     const int kk = k + 4 * half;
-    const f32x4 a = arow ? load_bf16x4(arow + kk) : f32x4{0.f, 0.f, 0.f, 0.f};
-    const f32x4 x0 = *(const f32x4*)(qe + n * DI + kk);
-    const f32x4 x1 = *(const f32x4*)(qe + (n + 32) * DI + kk);
-    acc0 = mfma4(a, x0, acc0);
-    acc1 = mfma4(a, x1, acc1);
+    const f32x4 b = buf_bf16x4(rk, boff + kk * 2);
+    const f32x4 a = *(const f32x4*)(qe + (t0 + n) * DI + kk);
+    acc = mfma4(a, b, acc);
+  }
+  // labels of the lane's 16 (query, entry) pairs, all loads issued first;
+  // pairs outside [0,Q) x [0,N) read 0 and are masked below
+  const __amdgpu_buffer_rsrc_t rl = rsrc(label, (size_t)Q * N);
+  const __amdgpu_buffer_rsrc_t rdl = rsrc(delta, (size_t)Q * Np * 4);
+  uint32_t yv[16];
+#pragma unroll
+  for (int rr = 0; rr < 16; ++rr) {
+    const int t = t0 + acc_row(rr, half);
+    yv[rr] = __builtin_amdgcn_raw_buffer_load_b8(rl, s < N ? (uint32_t)t * N + s : kFar, 0, 0);
   }
   double lsum = 0.0;
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int t = 32 * j + n;
-#pragma unroll
-    for (int rr = 0; rr < 16; ++rr) {
-      const int se = s0 + acc_row(rr, half);
-      if (t >= Q || se >= Np) continue;
-      float d = 0.f;
-      if (se < N) {
-        const float z = (j == 0 ? acc0[rr] : acc1[rr]) + bias;
-        const int y = label[(size_t)t * N + se] ? 1 : 0;
-        const float u = y ? z : -z;
-        const float nll = softplus_f(-u);          // -log sigmoid(u)
-        const float pu = sigmoid_f(u);
-        const float qu = sigmoid_f(-u);
-        const float mod = gamma == 0.f ? 1.f : powf(qu, gamma);
-        lsum += (double)nll + (double)(mod * nll);
-        const float dbce = sigmoid_f(z) - (float)y;
-        const float dfl_du = mod * (-gamma * pu * nll - qu);
-        d = (dbce + (y ? dfl_du : -dfl_du)) * inv_qn;
-      }
-      delta[(size_t)t * Np + se] = d;
-    }
+  for (int rr = 0; rr < 16; ++rr) {
+    const int t = t0 + acc_row(rr, half);
+    const bool valid = t < Q && s < N;
+    const float z = acc[rr] + bias;
+    const int y = yv[rr] ? 1 : 0;
+    const float u = y ? z : -z;
+    const float nll = softplus_f(-u);          // -log sigmoid(u)
+    const float pu = sigmoid_f(u);
+    const float qu = sigmoid_f(-u);
+    const float mod = gamma == 0.f ? 1.f : powf(qu, gamma);
+    if (valid) lsum += (double)nll + (double)(mod * nll);
+    const float dbce = sigmoid_f(z) - (float)y;
+    const float dfl_du = mod * (-gamma * pu * nll - qu);
+    const float d = valid ? (dbce + (y ? dfl_du : -dfl_du)) * inv_qn : 0.f;
+    // entries in [N, Np) get 0; rows t >= Q and entries >= Np are dropped
+    const uint32_t off = s < Np ? ((uint32_t)t * Np + s) * 4 : kFar;
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, d), rdl, off, 0, 0);
   }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) lsum += __shfl_xor(lsum, off, 64);
@@ -221,20 +282,36 @@ __global__ __launch_bounds__(256) void fgrad_kernel(int Q, int Np, const float* 
   const int n = lane & 31, half = lane >> 5;
   const int t = 32 * (wave & 1) + n;
   const int i0 = (wave >> 1) * (DI / 2);
-  const float* arow = t < Q ? delta + (size_t)t * Np : nullptr;
+  const __amdgpu_buffer_rsrc_t rd = rsrc(delta, (size_t)Q * Np * 4);
+  const uint32_t aoff = (uint32_t)t * Np * 4;   // rows t >= Q lie past the range
   const int kbeg = blockIdx.x * kChunk, kend = min(Np, kbeg + kChunk);
   f32x16 acc[NTI];
 #pragma unroll
   for (int j = 0; j < NTI; ++j) acc[j] = f32x16{};
-#pragma unroll 2
-  for (int k = kbeg; k < kend; k += 8) {
-    const int kk = k + 4 * half;
-    const f32x4 a = arow ? *(const f32x4*)(arow + kk) : f32x4{0.f, 0.f, 0.f, 0.f};
+  const __amdgpu_buffer_rsrc_t rkt = rsrc(KT, (size_t)DI * Np * 2);
+  uint32_t boff[NTI];
 #pragma unroll
-    for (int j = 0; j < NTI; ++j) {
-      const f32x4 b = load_bf16x4(KT + (size_t)(i0 + 32 * j + n) * Np + kk);
-      acc[j] = mfma4(a, b, acc[j]);
+  for (int j = 0; j < NTI; ++j) boff[j] = (uint32_t)(i0 + 32 * j + n) * Np * 2;
+  int k = kbeg;
+  for (; k + 32 <= kend; k += 32) {
+    f32x4 a[4], b[4][NTI];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int kk = k + 8 * u + 4 * half;
+      a[u] = buf_f32x4(rd, aoff + kk * 4);
+#pragma unroll
+      for (int j = 0; j < NTI; ++j) b[u][j] = buf_bf16x4(rkt, boff[j] + kk * 2);
     }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int j = 0; j < NTI; ++j) acc[j] = mfma4(a[u], b[u][j], acc[j]);
+  }
+  for (; k < kend; k += 8) {
+    const int kk = k + 4 * half;
+    const f32x4 a = buf_f32x4(rd, aoff + kk * 4);
+#pragma unroll
+    for (int j = 0; j < NTI; ++j) acc[j] = mfma4(a, buf_bf16x4(rkt, boff[j] + kk * 2), acc[j]);
   }
   float* out = Gp + (size_t)blockIdx.x * kQP * DI;
 #pragma unroll
@@ -247,24 +324,49 @@ __global__ __launch_bounds__(256) void fgrad_kernel(int Q, int Np, const float* 
 }
 
 // ---------------------------------------------------------------- 6 reduce
-__global__ __launch_bounds__(256) void freduce_kernel(int Q, int DI, int nchunks, int nloss,
-                                                      double inv_qn, const float* __restrict__ Gp,
-                                                      float* __restrict__ GT,
-                                                      const double* __restrict__ loss_part,
-                                                      float* __restrict__ loss) {
-  const int e = blockIdx.x * 256 + threadIdx.x;   // e = i * kQP + t
-  if (e < DI * kQP) {
-    const int i = e / kQP, t = e % kQP;
-    float acc = 0.f;
-    if (t < Q)
-      for (int c = 0; c < nchunks; ++c) acc += Gp[((size_t)c * kQP + t) * DI + i];
-    GT[e] = acc;
+// GT[i][t] = sum over chunks of Gp[c][t][i]: a block owns 64 consecutive
+// (t, i) elements; four thread slices sum every fourth chunk, then the slices
+// are added in a fixed order.
+__global__ __launch_bounds__(256) void freduce_kernel(int Q, int DI, int nchunks,
+                                                      const float* __restrict__ Gp,
+                                                      float* __restrict__ GT) {
+  __shared__ float part[4][64];
+  const int slice = threadIdx.x >> 6, j = threadIdx.x & 63;
+  const int e = blockIdx.x * 64 + j;          // e = t * DI + i
+  const size_t stride = (size_t)kQP * DI;
+  float acc = 0.f;
+  int c = slice;
+  for (; c + 28 < nchunks; c += 32) {   // eight loads in flight, summed in chunk order
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = Gp[(size_t)(c + 4 * u) * stride + e];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc += v[u];
   }
-  if (blockIdx.x == 0 && threadIdx.x == 0) {
-    double s = 0.0;
-    for (int b = 0; b < nloss; ++b) s += loss_part[b];
-    loss[0] = (float)(s * inv_qn);
+  for (; c < nchunks; c += 4) acc += Gp[(size_t)c * stride + e];
+  part[slice][j] = acc;
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    const float v = (part[0][j] + part[1][j]) + (part[2][j] + part[3][j]);
+    const int t = e / DI, i = e % DI;
+    GT[i * kQP + t] = t < Q ? v : 0.f;
   }
+}
+
+// loss = (sum of the block partials) / (Q N), summed in a fixed tree order
+__global__ __launch_bounds__(256) void floss_kernel(int nloss, double inv_qn,
+                                                    const double* __restrict__ loss_part,
+                                                    float* __restrict__ loss) {
+  __shared__ double red[256];
+  double acc = 0.0;
+  for (int b = threadIdx.x; b < nloss; b += 256) acc += loss_part[b];
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) loss[0] = (float)(red[0] * inv_qn);
 }
 
 // ---------------------------------------------------------------- 7 dW
@@ -301,6 +403,7 @@ __global__ __launch_bounds__(256) void fdw_kernel(int D, const float* __restrict
 }
 
 struct FocalWs {
+  float* qp;
   float* qa;
   float* gT;
   float* qe;
@@ -315,12 +418,16 @@ struct FocalWs {
 
 size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// slices of D for the projection: each wave of a slice takes D / (4 KS)
+// columns, a multiple of 8
+int proj_slices(int D) { return D % 512 == 0 ? 8 : (D % 256 == 0 ? 4 : 2); }
+
 FocalWs carve(void* base, int Q, int N, int D, int H, int dI) {
   (void)Q;
   const int Np = (N + 7) & ~7;
   const size_t R = (size_t)H * dI + H;
   const int nchunks = (Np + kChunk - 1) / kChunk;
-  const int nloss = (N + 127) / 128;
+  const int nloss = (N + 63) / 64;
   size_t off = 0;
   FocalWs w;
   auto take = [&](size_t bytes) {
@@ -328,6 +435,7 @@ FocalWs carve(void* base, int Q, int N, int D, int H, int dI) {
     off += up256(bytes);
     return (void*)p;
   };
+  w.qp = (float*)take((size_t)proj_slices(D) * kQP * R * 4);
   w.qa = (float*)take((size_t)kQP * R * 4);
   w.gT = (float*)take((size_t)64 * kQP * 4);
   w.qe = (float*)take((size_t)kQP * dI * 4);
@@ -355,7 +463,7 @@ hipError_t launch_focal(int Q, int N, int D, int H, int dI, float gamma, const u
   const int HdI = H * dI;
   const int R = HdI + H;
   const int nchunks = (Np + kChunk - 1) / kChunk;
-  const int nloss = (N + 127) / 128;
+  const int nloss = (N + 63) / 64;
   const double inv_qn = 1.0 / ((double)Q * (double)N);
   hipError_t e;
 #define FOCAL_CHECK()                        \
@@ -363,8 +471,12 @@ hipError_t launch_focal(int Q, int N, int D, int H, int dI, float gamma, const u
     e = hipGetLastError();                   \
     if (e != hipSuccess) return e;           \
   } while (0)
-  hipLaunchKernelGGL(fproj_kernel, dim3((R + 31) / 32), dim3(256), 0, s, Q, D, HdI, H, Wq, Wg, h,
-                     w.qa);
+  const int KS = proj_slices(D);
+  hipLaunchKernelGGL(fproj_kernel, dim3((R + 31) / 32, KS), dim3(256), 0, s, Q, D, HdI, H, Wq, Wg,
+                     h, w.qp);
+  FOCAL_CHECK();
+  hipLaunchKernelGGL(fproj_sum_kernel, dim3((Q * R + 255) / 256), dim3(256), 0, s, Q * R, KS,
+                     (size_t)kQP * R, w.qp, w.qa);
   FOCAL_CHECK();
   hipLaunchKernelGGL(fcollapse_kernel, dim3(kQP), dim3(128), 0, s, Q, H, dI, w.qa, w.gT, w.qe);
   FOCAL_CHECK();
@@ -388,8 +500,10 @@ hipError_t launch_focal(int Q, int N, int D, int H, int dI, float gamma, const u
     hipLaunchKernelGGL((fgrad_kernel<128>), dim3(nchunks), dim3(256), 0, s, Q, Np, w.delta, w.KT,
                        w.Gp);
   FOCAL_CHECK();
-  hipLaunchKernelGGL(freduce_kernel, dim3((dI * kQP + 255) / 256), dim3(256), 0, s, Q, dI, nchunks,
-                     nloss, inv_qn, w.Gp, w.GT, w.loss_part, loss);
+  hipLaunchKernelGGL(freduce_kernel, dim3(kQP * dI / 64), dim3(256), 0, s, Q, dI, nchunks, w.Gp,
+                     w.GT);
+  FOCAL_CHECK();
+  hipLaunchKernelGGL(floss_kernel, dim3(1), dim3(256), 0, s, nloss, inv_qn, w.loss_part, loss);
   FOCAL_CHECK();
   const dim3 gdw((D + 255) / 256, HdI / 32);
   if (dI == 64)

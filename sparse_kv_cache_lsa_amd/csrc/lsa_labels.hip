@@ -13,10 +13,11 @@
 // EPT consecutive entries [i*EPT, i*EPT + EPT) in registers, so one thread
 // owns EPT/32 whole selection words and index order is (thread, register)
 // order.  No sort:
-//  * mass in fixed point: w_s = trunc(exp(x_s - max) * 2^40) as a 64-bit
-//    integer, so every partial sum is exact and independent of summation
+//  * mass in fixed point: w_s = trunc(exp(x_s - max) * 2^31), summed in 64-bit
+//    integers, so every partial sum is exact and independent of summation
 //    order -- the result is deterministic and the same as a sequential walk
-//    over the same weights;
+//    over the same weights (truncation changes a mass ratio by at most
+//    N * 2^-31 of the largest entry's mass);
 //  * a histogram of mass over 2048 value bins (linear in max - x, so the
 //    bins follow the logit order and hold few entries each) finds the bin in
 //    which the running mass crosses top_p * S;
@@ -38,7 +39,7 @@ namespace {
 constexpr int kNT = 1024;              // threads per row block
 constexpr int kNWv = kNT / kWave;      // wavefronts per row block
 constexpr int kBins = 2048;            // histogram bins per pass
-constexpr float kFix = 1099511627776.f;   // 2^40: fixed-point unit of exp(x - max)
+constexpr float kFix = 2147483648.f;   // 2^31: fixed-point unit of exp(x - max)
 
 // order key: smaller key = larger logit; -0 and +0 share a key
 __device__ __forceinline__ uint32_t desc_key(float x) {
@@ -82,15 +83,25 @@ __device__ __forceinline__ uint64_t block_exclusive_scan_u64(uint64_t v, uint64_
   return res;
 }
 
-__device__ __forceinline__ float block_max(float v, float* scratch) {
+// block-wide max of a and of b (one pass); scratch: 2 * kNWv floats
+__device__ __forceinline__ void block_max2(float& a, float& b, float* scratch) {
 #pragma unroll
-  for (int off = kWave / 2; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
-  if (lane_id() == 0) scratch[threadIdx.x / kWave] = v;
+  for (int off = kWave / 2; off > 0; off >>= 1) {
+    a = fmaxf(a, __shfl_xor(a, off, kWave));
+    b = fmaxf(b, __shfl_xor(b, off, kWave));
+  }
+  if (lane_id() == 0) {
+    scratch[threadIdx.x / kWave] = a;
+    scratch[kNWv + threadIdx.x / kWave] = b;
+  }
   __syncthreads();
-  float r = scratch[0];
-  for (int w = 1; w < kNWv; ++w) r = fmaxf(r, scratch[w]);
+  a = scratch[0];
+  b = scratch[kNWv];
+  for (int w = 1; w < kNWv; ++w) {
+    a = fmaxf(a, scratch[w]);
+    b = fmaxf(b, scratch[kNWv + w]);
+  }
   __syncthreads();
-  return r;
 }
 
 // Given a mass histogram over kBins bins (in order) and the mass M already
@@ -129,7 +140,7 @@ __global__ __launch_bounds__(kNT) void nucleus_kernel(int N, int W, float top_p,
   static_assert(EPT % 32 == 0, "a thread owns whole selection words");
   __shared__ uint64_t hist[kBins];
   __shared__ uint64_t scan_scratch[kNWv + 1];
-  __shared__ float red[kNWv];
+  __shared__ float red[2 * kNWv];
   __shared__ int s_bin;
   __shared__ uint64_t s_before;
 
@@ -149,43 +160,43 @@ __global__ __launch_bounds__(kNT) void nucleus_kernel(int N, int W, float top_p,
     for (int i = 0; i < EPT; ++i) v[i] = (e0 + i < N) ? x[e0 + i] : -__builtin_inff();
   }
 
-  // softmax normaliser in fixed point
-  float lmax = -__builtin_inff(), lmin = __builtin_inff();
+  // max and min of the row
+  float m = -__builtin_inff(), nmin = -__builtin_inff();
 #pragma unroll
   for (int i = 0; i < EPT; ++i) {
-    lmax = fmaxf(lmax, v[i]);
-    if (e0 + i < N) lmin = fminf(lmin, v[i]);
+    m = fmaxf(m, v[i]);
+    if (e0 + i < N) nmin = fmaxf(nmin, -v[i]);
   }
-  const float m = block_max(lmax, red);
-  const float xmin = -block_max(-lmin, red);
-  auto weight = [&](int i) -> uint64_t {
-    return (e0 + i < N) ? (uint64_t)(__expf(v[i] - m) * kFix) : 0ull;
+  block_max2(m, nmin, red);
+  const float xmin = -nmin;
+  auto weight = [&](int i) -> uint32_t {
+    return (e0 + i < N) ? (uint32_t)(__expf(v[i] - m) * kFix) : 0u;
   };
-  uint64_t lsum = 0;
-#pragma unroll
-  for (int i = 0; i < EPT; ++i) lsum += weight(i);
-  uint64_t S;
-  (void)block_exclusive_scan_u64(lsum, scan_scratch, &S);
-  // keep s iff (mass ahead of s) < top_p * S, i.e. < R for integer masses
-  const double rd = (double)top_p * (double)S;
-  uint64_t R = (uint64_t)rd;
-  if ((double)R < rd) ++R;
-
-  // pass 0: value bins, bin(x) = floor((max - x) * kBins / (max - min))
+  // value bins, bin(x) = floor((max - x) * kBins / (max - min)): monotone in x
   const float range = m - xmin;
   const float inv = range > 0.f ? (float)kBins / range : 0.f;
   auto vbin = [&](int i) -> int {
     const float t = (m - v[i]) * inv;
     return t < (float)(kBins - 1) ? (int)t : kBins - 1;
   };
+
+  // pass 0: softmax normaliser and the mass histogram over value bins, with
+  // one exponential per entry
   for (int j = threadIdx.x; j < kBins; j += kNT) hist[j] = 0;
   __syncthreads();
+  uint64_t lsum = 0;
 #pragma unroll
   for (int i = 0; i < EPT; ++i) {
-    const uint64_t w = weight(i);
+    const uint32_t w = weight(i);
+    lsum += w;
     if (w) atomicAdd((unsigned long long*)&hist[vbin(i)], (unsigned long long)w);
   }
-  __syncthreads();
+  uint64_t S;
+  (void)block_exclusive_scan_u64(lsum, scan_scratch, &S);
+  // keep s iff (mass ahead of s) < top_p * S, i.e. < R for integer masses
+  const double rd = (double)top_p * (double)S;
+  uint64_t R = (uint64_t)rd;
+  if ((double)R < rd) ++R;
   find_crossing(hist, 0, R, scan_scratch, &s_bin, &s_before);
   const int cbin = s_bin;
   uint64_t M = s_before;
@@ -205,10 +216,11 @@ __global__ __launch_bounds__(kNT) void nucleus_kernel(int N, int W, float top_p,
       const int hi = sh + kBits[p];
 #pragma unroll
       for (int i = 0; i < EPT; ++i) {
-        const uint64_t w = weight(i);
+        if (e0 + i >= N || vbin(i) != cbin) continue;
         const uint32_t k = desc_key(v[i]);
-        const bool match = w && vbin(i) == cbin && (hi >= 32 || (k >> hi) == prefix);
-        if (match)
+        if (hi < 32 && (k >> hi) != prefix) continue;
+        const uint32_t w = weight(i);
+        if (w)
           atomicAdd((unsigned long long*)&hist[(k >> sh) & ((1u << kBits[p]) - 1u)],
                     (unsigned long long)w);
       }

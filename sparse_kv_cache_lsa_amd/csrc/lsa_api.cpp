@@ -57,7 +57,10 @@ lsa_status lsa_project_query(int L, int B, int D, int H, int dI, const uint16_t*
   REQUIRE(L >= 1 && L <= LSA_MAX_LAYERS, LSA_E_SHAPE, "lsa_project_query: L=%d not in [1,%d]", L,
           LSA_MAX_LAYERS);
   REQUIRE(B >= 1, LSA_E_SHAPE, "lsa_project_query: B=%d < 1", B);
-  REQUIRE(D >= 256 && D % 256 == 0, LSA_E_SHAPE, "lsa_project_query: D=%d not a positive multiple of 256", D);
+  REQUIRE(D >= 256 && D <= 65536 && D % 256 == 0, LSA_E_SHAPE,
+          "lsa_project_query: D=%d not a multiple of 256 in [256,65536]", D);
+  REQUIRE((int64_t)B * D * 2 < ((int64_t)1 << 31), LSA_E_SHAPE,
+          "lsa_project_query: B*D*2 must stay below 2^31 bytes");
   REQUIRE(H >= 1 && H <= LSA_MAX_HEADS, LSA_E_SHAPE, "lsa_project_query: H=%d not in [1,64]", H);
   REQUIRE(dI == 64 || dI == 128, LSA_E_SHAPE, "lsa_project_query: dI=%d not 64 or 128", dI);
   REQUIRE(h_layer_stride >= 0, LSA_E_ARG, "lsa_project_query: negative h_layer_stride");

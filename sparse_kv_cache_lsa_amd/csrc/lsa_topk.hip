@@ -14,6 +14,10 @@
 //  * One ordered sweep then keeps every key > T and the first ones equal to T
 //    (the survivor list is ascending, so array order is index order), with
 //    block prefix sums giving each kept entry its output slot.
+// Lists of up to kThreads * kReg survivors (80K) are read from memory once:
+// thread i keeps the keys of positions [i*kReg, (i+1)*kReg) in registers for
+// every pass, and the sweep needs only two block prefix sums.  Longer lists
+// stream from memory in every pass.
 #include "lsa_device.h"
 #include "lsa_launch.h"
 
@@ -21,6 +25,7 @@ namespace lsa {
 namespace {
 
 constexpr int kThreads = 1024;
+constexpr int kReg = 80;   // keys per thread held in registers
 
 __device__ __forceinline__ uint32_t order_key(float z) {
   if (z != z) return 0u;            // NaN ranks last
@@ -83,7 +88,73 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(int cap, int k,
     return;
   }
 
-  // ---- radix select of the k-th largest key
+  if (n <= kThreads * kReg) {
+    // ---- register-resident path
+    const int base = t * kReg;
+    uint32_t key[kReg];
+    if ((cap & 3) == 0 && ((uintptr_t)sz & 15) == 0 && base + kReg <= n) {
+#pragma unroll
+      for (int j = 0; j < kReg; j += 4) {
+        const f32x4 v = *(const f32x4*)(sz + base + j);
+        key[j] = order_key(v[0]);
+        key[j + 1] = order_key(v[1]);
+        key[j + 2] = order_key(v[2]);
+        key[j + 3] = order_key(v[3]);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < kReg; ++j) key[j] = base + j < n ? order_key(sz[base + j]) : 0u;
+    }
+    const int nv = min(kReg, max(0, n - base));   // valid keys of this thread
+    uint32_t prefix = 0;
+    int krem = k;
+#pragma unroll
+    for (int pass = 0; pass < 3; ++pass) {
+      const int shift = pass == 0 ? 20 : (pass == 1 ? 10 : 0);
+      const int NB = pass == 0 ? 4096 : 1024;
+      const int hi = pass == 0 ? 32 : shift + 10;
+      for (int i = t; i < NB; i += kThreads) hist[i] = 0;
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < kReg; ++j)
+        if (j < nv && (hi >= 32 || (key[j] >> hi) == (prefix >> hi)))
+          atomicAdd(&hist[(key[j] >> shift) & (NB - 1)], 1);
+      __syncthreads();
+      if (pass == 0)
+        find_crossing<4096>(hist, krem, scratch, &s_digit, &s_above);
+      else
+        find_crossing<1024>(hist, krem, scratch, &s_digit, &s_above);
+      prefix |= (uint32_t)s_digit << shift;
+      krem -= s_above;
+      __syncthreads();
+    }
+    const uint32_t T = prefix;
+    int ties = 0, above = 0;
+#pragma unroll
+    for (int j = 0; j < kReg; ++j) {
+      ties += (j < nv && key[j] == T) ? 1 : 0;
+      above += (j < nv && key[j] > T) ? 1 : 0;
+    }
+    int tie_total;
+    const int tie_rank0 = block_exclusive_scan<kThreads>(ties, scratch, &tie_total);
+    const int take_ties = min(ties, max(0, krem - tie_rank0));
+    int kept_total;
+    int pos = block_exclusive_scan<kThreads>(above + take_ties, scratch, &kept_total);
+    int tie_rank = tie_rank0;
+#pragma unroll
+    for (int j = 0; j < kReg; ++j) {
+      bool keep = false;
+      if (j < nv) {
+        if (key[j] > T) keep = true;
+        else if (key[j] == T) keep = tie_rank++ < krem;
+      }
+      if (keep && pos < k) o[pos++] = si[base + j];
+    }
+    if (t == 0) out_count[b] = k;
+    return;
+  }
+
+  // ---- radix select of the k-th largest key (long lists, streamed)
   uint32_t prefix = 0, pmask = 0;
   int krem = k;
   const int shifts[3] = {20, 10, 0};

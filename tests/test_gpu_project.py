@@ -55,9 +55,9 @@ def test_project_named_workloads(name):
     print("excluded", _run_and_check(gen.WORKLOADS[name]))
 
 
-@pytest.mark.parametrize("B", [5, 33])
-def test_project_request_groups(B):
-    w = gen.custom("proj", 91, B=B, L=2, H=40, dI=64, D=768, N=64)
+@pytest.mark.parametrize("B,D,H", [(5, 768, 40), (33, 768, 40), (3, 256, 3)])
+def test_project_request_groups(B, D, H):
+    w = gen.custom("proj", 91, B=B, L=2, H=H, dI=64, D=D, N=64)
     _run_and_check(w)
 
 

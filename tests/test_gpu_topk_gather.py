@@ -39,6 +39,8 @@ def _topk(idx, z, counts, k):
     ([100, 2048, 2049], 2048),
     ([10000, 63000, 4097], 2048),
     ([70000, 3, 2], 256),
+    ([81920, 81921, 40001], 2048),
+    ([100000, 5, 9], 512),
     ([500, 600, 700], 1),
     ([5000, 5000, 5000], 0),
 ])

@@ -158,25 +158,25 @@ lsa_status lsa_select_or_compact(int B, int N, const int32_t* cand_idx, const fl
 // --------------------------------------------------------------------- top-k
 
 size_t lsa_topk_workspace_bytes(int B, int cap, int k) {
-  (void)B;
-  (void)cap;
-  (void)k;
-  return 0;
+  if (B < 1 || cap < 0 || k < 0) return 0;
+  return lsa::topk_workspace_bytes(B, cap, k);
 }
 
 lsa_status lsa_topk(int B, int cap, int k, const int32_t* surv_idx, const float* surv_z,
                     const int32_t* surv_count, int32_t* topk_idx, int32_t* topk_count, void* ws,
                     size_t ws_bytes, hipStream_t stream) {
-  (void)ws;
-  (void)ws_bytes;
   REQUIRE(B >= 1 && B <= 65535, LSA_E_SHAPE, "lsa_topk: B=%d not in [1,65535]", B);
   REQUIRE(cap >= 0 && k >= 0, LSA_E_ARG, "lsa_topk: negative cap or k");
   REQUIRE(surv_count && topk_count, LSA_E_ARG, "lsa_topk: null count pointer");
   REQUIRE(cap == 0 || (surv_idx && surv_z), LSA_E_ARG, "lsa_topk: null survivor input");
   REQUIRE(k == 0 || topk_idx, LSA_E_ARG, "lsa_topk: null topk_idx with k > 0");
-  return hip_status(
-      lsa::launch_topk(B, cap, k, surv_idx, surv_z, surv_count, topk_idx, topk_count, stream),
-      "lsa_topk launch");
+  const size_t need = lsa::topk_workspace_bytes(B, cap, k);
+  REQUIRE(need == 0 || (ws && ws_bytes >= need && ((uintptr_t)ws & 15) == 0), LSA_E_WORKSPACE,
+          "lsa_topk: workspace of %zu bytes (16-byte aligned) needed, got %zu", need,
+          ws ? ws_bytes : (size_t)0);
+  return hip_status(lsa::launch_topk(B, cap, k, surv_idx, surv_z, surv_count, topk_idx,
+                                     topk_count, ws, stream),
+                    "lsa_topk launch");
 }
 
 // -------------------------------------------------------------------- gather

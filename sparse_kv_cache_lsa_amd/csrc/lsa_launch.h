@@ -43,9 +43,11 @@ hipError_t launch_select(int B, int nchunks, const int32_t* cand_idx, const floa
                          const int32_t* cand_count, int cap, int32_t* surv_idx,
                          float* surv_z, int32_t* surv_count, hipStream_t s);
 
+size_t topk_workspace_bytes(int B, int cap, int k);
+
 hipError_t launch_topk(int B, int cap, int k, const int32_t* surv_idx,
                        const float* surv_z, const int32_t* surv_count,
-                       int32_t* topk_idx, int32_t* topk_count, hipStream_t s);
+                       int32_t* topk_idx, int32_t* topk_count, void* ws, hipStream_t s);
 
 hipError_t launch_gather(int B, int N, int k, int row_bytes, const void* pool,
                          const int32_t* idx, void* hot, hipStream_t s);

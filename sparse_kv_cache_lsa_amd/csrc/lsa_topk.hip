@@ -26,6 +26,8 @@ namespace {
 
 constexpr int kThreads = 1024;
 constexpr int kReg = 80;   // keys per thread held in registers
+constexpr int kMBMinCap = 16384;   // longer lists are first cut down slice by slice
+constexpr int kStage = 8192;       // output slots staged in LDS
 
 __device__ __forceinline__ uint32_t order_key(float z) {
   if (z != z) return 0u;            // NaN ranks last
@@ -34,18 +36,75 @@ __device__ __forceinline__ uint32_t order_key(float z) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Exclusive prefix sum over a block of NT threads (thread order), total in
+// *total.  The per-wave totals are scanned by one wavefront with shuffles
+// (no serial loop).  scratch: NT/64 + 1 ints.  All threads call.
+template <int NT>
+__device__ __forceinline__ int scan_block(int v, int* scratch, int* total) {
+  constexpr int NW = NT / kWave;
+  const int lane = lane_id();
+  const int wave = threadIdx.x / kWave;
+  const int inc = wave_inclusive_scan(v);
+  if (lane == kWave - 1) scratch[wave] = inc;
+  __syncthreads();
+  if (wave == 0) {
+    const int w = lane < NW ? scratch[lane] : 0;
+    const int wi = wave_inclusive_scan(w);
+    if (lane < NW) scratch[lane] = wi - w;
+    if (lane == NW - 1) scratch[NW] = wi;
+  }
+  __syncthreads();
+  const int res = scratch[wave] + inc - v;
+  *total = scratch[NW];
+  __syncthreads();
+  return res;
+}
+
+// block-wide min of a and max of b; scratch: 2 * (NT / 64) + 2 ints.  All threads call.
+template <int NT>
+__device__ __forceinline__ void block_minmax_t(uint32_t& a, uint32_t& b, int* scratch) {
+  constexpr int NW = NT / kWave;
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) {
+    a = min(a, (uint32_t)__shfl_xor((int)a, off, kWave));
+    b = max(b, (uint32_t)__shfl_xor((int)b, off, kWave));
+  }
+  if (lane_id() == 0) {
+    scratch[threadIdx.x / kWave] = (int)a;
+    scratch[NW + threadIdx.x / kWave] = (int)b;
+  }
+  __syncthreads();
+  if (threadIdx.x < kWave) {
+    uint32_t x = threadIdx.x < NW ? (uint32_t)scratch[threadIdx.x] : 0xFFFFFFFFu;
+    uint32_t y = threadIdx.x < NW ? (uint32_t)scratch[NW + threadIdx.x] : 0u;
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) {
+      x = min(x, (uint32_t)__shfl_xor((int)x, off, kWave));
+      y = max(y, (uint32_t)__shfl_xor((int)y, off, kWave));
+    }
+    if (threadIdx.x == 0) {
+      scratch[2 * NW] = (int)x;
+      scratch[2 * NW + 1] = (int)y;
+    }
+  }
+  __syncthreads();
+  a = (uint32_t)scratch[2 * NW];
+  b = (uint32_t)scratch[2 * NW + 1];
+  __syncthreads();
+}
+
 // Finds, scanning bins from the highest digit down, the bin holding the
 // krem-th key; returns the digit and the number of keys in higher bins.
-template <int NB>
+template <int NB, int NT = kThreads>
 __device__ __forceinline__ void find_crossing(const int* hist, int krem, int* scratch,
                                               int* out_digit, int* out_above) {
-  constexpr int PER = NB / kThreads;   // 4 or 1 bins per thread
+  constexpr int PER = NB / NT;   // bins per thread
   const int t = threadIdx.x;
   int sum = 0;
 #pragma unroll
   for (int i = 0; i < PER; ++i) sum += hist[NB - 1 - (t * PER + i)];
   int total;
-  const int before = block_exclusive_scan<kThreads>(sum, scratch, &total);
+  const int before = scan_block<NT>(sum, scratch, &total);
   if (before < krem && krem <= before + sum) {
     int cum = before;
 #pragma unroll
@@ -62,6 +121,139 @@ __device__ __forceinline__ void find_crossing(const int* hist, int krem, int* sc
   __syncthreads();
 }
 
+__device__ __forceinline__ float key_to_float(uint32_t key) {
+  return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
+}
+
+// Top-k of the n (> k > 0) scores sz[0..n) of one list by one block of NT
+// threads: thread t holds positions [t*chunk, (t+1)*chunk) (chunk <= KREG,
+// chunk * NT >= n) in registers for every pass, so array order (= entry
+// order) is (thread, register) order.  Radix select over 12/10/10-bit digits
+// (LDS histograms, block scans) finds the k-th key T and how many keys equal
+// to T belong to the top-k; two block prefix sums then give every kept
+// position its output slot.  Writes out_idx[0..k) = si[kept positions], in
+// position order, and out_z (if not null) the scores.  stage: LDS for
+// kStage ints (used when k <= kStage); scratch: 2 * NT/64 + 2 ints.  All
+// threads call.
+template <int NT, int KREG>
+__device__ __forceinline__ void block_select(int n, int k, int chunk, const float* sz,
+                                             const int32_t* si, int* hist, int* scratch,
+                                             int* s_digit, int* s_above, int* stage,
+                                             int32_t* out_idx, float* out_z) {
+  const int t = threadIdx.x;
+  const int base = t * chunk;
+  // buffer loads over the n valid scores: positions past n read 0 and are
+  // masked below, so the loads need no branches and are all in flight at once
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(sz), (short)0, n * 4, 0x00020000);
+  uint32_t key[KREG];
+  if ((chunk & 3) == 0 && ((uintptr_t)sz & 15) == 0) {
+#pragma unroll
+    for (int j = 0; j < KREG; j += 4)
+      if (j < chunk) {
+        const f32x4 v = __builtin_bit_cast(
+            f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (uint32_t)(base + j) * 4, 0, 0));
+        key[j] = order_key(v[0]);
+        key[j + 1] = order_key(v[1]);
+        key[j + 2] = order_key(v[2]);
+        key[j + 3] = order_key(v[3]);
+      }
+  } else {
+#pragma unroll
+    for (int j = 0; j < KREG; ++j)
+      if (j < chunk)
+        key[j] = order_key(__builtin_bit_cast(
+            float, __builtin_amdgcn_raw_buffer_load_b32(r, (uint32_t)(base + j) * 4, 0, 0)));
+  }
+  const int nv = min(chunk, max(0, n - base));   // valid keys of this thread
+  // Digits are taken from key - kmin, the first one from the top bits of the
+  // list's actual key span: a narrow list (the candidates of the slices are
+  // all near the top) then spreads over the first histogram instead of piling
+  // into a few bins, whose LDS atomics would serialise, and needs fewer passes.
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+#pragma unroll
+  for (int j = 0; j < KREG; ++j)
+    if (j < chunk && j < nv) {
+      kmin = min(kmin, key[j]);
+      kmax = max(kmax, key[j]);
+    }
+  block_minmax_t<NT>(kmin, kmax, scratch);
+  const uint32_t span = kmax - kmin;
+  // from here on the registers hold key - kmin (order-preserving for valid keys)
+#pragma unroll
+  for (int j = 0; j < KREG; ++j)
+    if (j < chunk) key[j] -= kmin;
+  const int bits = span ? 32 - __builtin_clz(span) : 0;
+  uint32_t prefix = 0;   // the digits fixed so far, as a value of the top bits of key - kmin
+  int krem = k;
+  int hi = bits;         // key - kmin bits above hi are fixed
+  while (hi > 0) {       // uniform: at most three passes (12 + 10 + 10 bits)
+    const int width = hi == bits ? 12 : 10;
+    const int shift = max(0, hi - width);
+    const int NB = 1 << (hi - shift);
+    const int FB = NB > 1024 ? 4096 : 1024;   // bins the crossing search reads
+    for (int i = t; i < FB; i += NT) hist[i] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < KREG; ++j)
+      if (j < chunk && j < nv && (hi >= 32 || (key[j] >> hi) == prefix))
+        atomicAdd(&hist[(key[j] >> shift) & (NB - 1)], 1);
+    __syncthreads();
+    if (NB > 1024)
+      find_crossing<4096, NT>(hist, krem, scratch, s_digit, s_above);
+    else
+      find_crossing<1024, NT>(hist, krem, scratch, s_digit, s_above);
+    prefix = (prefix << (hi - shift)) | (uint32_t)*s_digit;
+    krem -= *s_above;
+    hi = shift;
+    __syncthreads();
+  }
+  const uint32_t T = prefix;   // k-th key - kmin: all bits fixed (span 0: every key is kmin)
+  int ties = 0, above = 0;
+#pragma unroll
+  for (int j = 0; j < KREG; ++j)
+    if (j < chunk) {
+      ties += (j < nv && key[j] == T) ? 1 : 0;
+      above += (j < nv && key[j] > T) ? 1 : 0;
+    }
+  int tie_total;
+  const int tie_rank0 = scan_block<NT>(ties, scratch, &tie_total);
+  const int take_ties = min(ties, max(0, krem - tie_rank0));
+  int kept_total;
+  int pos = scan_block<NT>(above + take_ties, scratch, &kept_total);
+  int tie_rank = tie_rank0;
+  // Kept positions go to LDS at their output slot first; the gather of the
+  // entry indices (and scores) then runs as one round of independent loads
+  // instead of a chain of dependent ones per thread.
+  const bool staged = k <= kStage;
+#pragma unroll
+  for (int j = 0; j < KREG; ++j)
+    if (j < chunk) {
+      bool keep = false;
+      if (j < nv) {
+        if (key[j] > T) keep = true;
+        else if (key[j] == T) keep = tie_rank++ < krem;
+      }
+      if (keep && pos < k) {
+        if (staged) {
+          stage[pos] = base + j;
+        } else {
+          out_idx[pos] = si[base + j];
+          if (out_z) out_z[pos] = key_to_float(key[j] + kmin);
+        }
+        ++pos;
+      }
+    }
+  if (staged) {
+    __syncthreads();
+    for (int i = t; i < k; i += NT) {
+      const int q = stage[i];
+      out_idx[i] = si[q];
+      if (out_z) out_z[i] = sz[q];
+    }
+  }
+}
+
 __global__ __launch_bounds__(kThreads) void topk_kernel(int cap, int k,
                                                         const int32_t* __restrict__ surv_idx,
                                                         const float* __restrict__ surv_z,
@@ -69,7 +261,8 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(int cap, int k,
                                                         int32_t* __restrict__ out,
                                                         int32_t* __restrict__ out_count) {
   __shared__ int hist[4096];
-  __shared__ int scratch[kThreads / kWave + 1];
+  __shared__ int scratch[2 * (kThreads / kWave) + 2];
+  __shared__ int stage[kStage];
   __shared__ int s_digit, s_above;
   const int b = blockIdx.x;
   const int t = threadIdx.x;
@@ -89,67 +282,10 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(int cap, int k,
   }
 
   if (n <= kThreads * kReg) {
-    // ---- register-resident path
-    const int base = t * kReg;
-    uint32_t key[kReg];
-    if ((cap & 3) == 0 && ((uintptr_t)sz & 15) == 0 && base + kReg <= n) {
-#pragma unroll
-      for (int j = 0; j < kReg; j += 4) {
-        const f32x4 v = *(const f32x4*)(sz + base + j);
-        key[j] = order_key(v[0]);
-        key[j + 1] = order_key(v[1]);
-        key[j + 2] = order_key(v[2]);
-        key[j + 3] = order_key(v[3]);
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < kReg; ++j) key[j] = base + j < n ? order_key(sz[base + j]) : 0u;
-    }
-    const int nv = min(kReg, max(0, n - base));   // valid keys of this thread
-    uint32_t prefix = 0;
-    int krem = k;
-#pragma unroll
-    for (int pass = 0; pass < 3; ++pass) {
-      const int shift = pass == 0 ? 20 : (pass == 1 ? 10 : 0);
-      const int NB = pass == 0 ? 4096 : 1024;
-      const int hi = pass == 0 ? 32 : shift + 10;
-      for (int i = t; i < NB; i += kThreads) hist[i] = 0;
-      __syncthreads();
-#pragma unroll
-      for (int j = 0; j < kReg; ++j)
-        if (j < nv && (hi >= 32 || (key[j] >> hi) == (prefix >> hi)))
-          atomicAdd(&hist[(key[j] >> shift) & (NB - 1)], 1);
-      __syncthreads();
-      if (pass == 0)
-        find_crossing<4096>(hist, krem, scratch, &s_digit, &s_above);
-      else
-        find_crossing<1024>(hist, krem, scratch, &s_digit, &s_above);
-      prefix |= (uint32_t)s_digit << shift;
-      krem -= s_above;
-      __syncthreads();
-    }
-    const uint32_t T = prefix;
-    int ties = 0, above = 0;
-#pragma unroll
-    for (int j = 0; j < kReg; ++j) {
-      ties += (j < nv && key[j] == T) ? 1 : 0;
-      above += (j < nv && key[j] > T) ? 1 : 0;
-    }
-    int tie_total;
-    const int tie_rank0 = block_exclusive_scan<kThreads>(ties, scratch, &tie_total);
-    const int take_ties = min(ties, max(0, krem - tie_rank0));
-    int kept_total;
-    int pos = block_exclusive_scan<kThreads>(above + take_ties, scratch, &kept_total);
-    int tie_rank = tie_rank0;
-#pragma unroll
-    for (int j = 0; j < kReg; ++j) {
-      bool keep = false;
-      if (j < nv) {
-        if (key[j] > T) keep = true;
-        else if (key[j] == T) keep = tie_rank++ < krem;
-      }
-      if (keep && pos < k) o[pos++] = si[base + j];
-    }
+    // ---- register-resident path: thread t holds positions [t*chunk, (t+1)*chunk)
+    const int chunk = (n + kThreads - 1) / kThreads;
+    block_select<kThreads, kReg>(n, k, chunk, sz, si, hist, scratch, &s_digit, &s_above, stage,
+                                 o, nullptr);
     if (t == 0) out_count[b] = k;
     return;
   }
@@ -219,13 +355,88 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(int cap, int k,
   if (t == 0) out_count[b] = k;
 }
 
+// ----------------------------------------------------------------------------
+// Long lists (more than kMBMinCap survivors of capacity): two stages.
+//  1. slice_kernel, several blocks per request: block p takes positions
+//     [p*kSlice, (p+1)*kSlice) and writes the top min(k, kSlice) of its slice
+//     (same ranking, in position order) to a candidate list in the workspace,
+//     at offset p * min(k, kSlice) -- every earlier slice is full, so the
+//     offset needs no communication.  The global top-k is contained in the
+//     union of the slices' top-k (fewer than k entries of a member's slice
+//     precede it), and the candidate list stays in position order.
+//  2. topk_kernel over the candidate list (a few thousand to tens of
+//     thousands of entries instead of the whole survivor list).
+constexpr int kMT = 256;               // threads per slice block
+constexpr int kMK = 32;                // scores per thread
+constexpr int kSlice = kMT * kMK;      // survivors per slice
+
+__global__ __launch_bounds__(kMT) void slice_kernel(int cap, int k, int cap_c,
+                                                    const int32_t* __restrict__ surv_idx,
+                                                    const float* __restrict__ surv_z,
+                                                    const int32_t* __restrict__ surv_count,
+                                                    int32_t* __restrict__ cand_idx,
+                                                    float* __restrict__ cand_z,
+                                                    int32_t* __restrict__ cand_count) {
+  __shared__ int hist[4096];
+  __shared__ int scratch[2 * (kMT / kWave) + 2];
+  __shared__ int stage[kStage];
+  __shared__ int s_digit, s_above;
+  const int b = blockIdx.y, p = blockIdx.x;
+  const int n = min(max(surv_count[b], 0), cap);
+  const int kc = min(k, kSlice);
+  if (p == 0 && threadIdx.x == 0)
+    cand_count[b] = k == 0 ? 0 : (n / kSlice) * kc + min(kc, n % kSlice);
+  const int np = min(kSlice, n - p * kSlice);
+  if (k == 0 || np <= 0) return;
+  const int32_t* si = surv_idx + (size_t)b * cap + (size_t)p * kSlice;
+  const float* sz = surv_z + (size_t)b * cap + (size_t)p * kSlice;
+  int32_t* ci = cand_idx + (size_t)b * cap_c + (size_t)p * kc;
+  float* cz = cand_z + (size_t)b * cap_c + (size_t)p * kc;
+  if (np <= kc) {
+    for (int i = threadIdx.x; i < np; i += kMT) {
+      ci[i] = si[i];
+      cz[i] = sz[i];
+    }
+    return;
+  }
+  block_select<kMT, kMK>(np, kc, kMK, sz, si, hist, scratch, &s_digit, &s_above, stage, ci, cz);
+}
+
 }  // namespace
+
+static size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+static int cand_capacity(int cap, int k) {
+  const int P = (cap + kSlice - 1) / kSlice;
+  return P * min(k, kSlice);
+}
+
+size_t topk_workspace_bytes(int B, int cap, int k) {
+  if (cap <= kMBMinCap || k == 0) return 0;
+  const size_t cc = (size_t)B * cand_capacity(cap, k);
+  return up256(cc * 4) * 2 + up256((size_t)B * 4);
+}
 
 hipError_t launch_topk(int B, int cap, int k, const int32_t* surv_idx, const float* surv_z,
                        const int32_t* surv_count, int32_t* topk_idx, int32_t* topk_count,
-                       hipStream_t s) {
-  hipLaunchKernelGGL(topk_kernel, dim3(B), dim3(kThreads), 0, s, cap, k, surv_idx, surv_z,
-                     surv_count, topk_idx, topk_count);
+                       void* ws, hipStream_t s) {
+  if (cap <= kMBMinCap || k == 0) {
+    hipLaunchKernelGGL(topk_kernel, dim3(B), dim3(kThreads), 0, s, cap, k, surv_idx, surv_z,
+                       surv_count, topk_idx, topk_count);
+    return hipGetLastError();
+  }
+  const int P = (cap + kSlice - 1) / kSlice;
+  const int cap_c = cand_capacity(cap, k);
+  const size_t cc = (size_t)B * cap_c;
+  int32_t* cand_idx = (int32_t*)ws;
+  float* cand_z = (float*)((char*)ws + up256(cc * 4));
+  int32_t* cand_count = (int32_t*)((char*)ws + 2 * up256(cc * 4));
+  hipLaunchKernelGGL(slice_kernel, dim3(P, B), dim3(kMT), 0, s, cap, k, cap_c, surv_idx, surv_z,
+                     surv_count, cand_idx, cand_z, cand_count);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(topk_kernel, dim3(B), dim3(kThreads), 0, s, cap_c, k, cand_idx, cand_z,
+                     cand_count, topk_idx, topk_count);
   return hipGetLastError();
 }
 

@@ -80,8 +80,10 @@ def test_validation_errors_return_before_launch(lib):
     # select: negative capacity, missing candidate lists
     assert lib.lsa_select_or_compact(2, 1000, fake, fake, fake, -1, fake, fake, fake, None) == _abi.LSA_E_ARG
     assert lib.lsa_select_or_compact(2, 1000, None, fake, fake, 10, fake, fake, fake, None) == _abi.LSA_E_ARG
-    # top-k: negative k
+    # top-k: negative k; long lists need the workspace
     assert lib.lsa_topk(1, 10, -1, fake, fake, fake, fake, fake, None, 0, None) == _abi.LSA_E_ARG
+    assert lib.lsa_topk_workspace_bytes(2, 100000, 2048) > 0
+    assert lib.lsa_topk(2, 100000, 2048, fake, fake, fake, fake, fake, None, 0, None) == _abi.LSA_E_WORKSPACE
     # gather: row size not a multiple of 16
     assert lib.lsa_gather_hot(1, 10, 4, 24, fake, fake, fake, None) == _abi.LSA_E_ARG
     # projection: hidden size not a multiple of 256

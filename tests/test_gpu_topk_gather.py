@@ -11,7 +11,8 @@ from oracle import oracle
 pytestmark = pytest.mark.gpu
 
 
-def _survivors(rng, B, cap, ns, N=300_000, ties=False):
+def _survivors(rng, B, cap, ns, N=None, ties=False):
+    N = max(300_000, 2 * cap) if N is None else N
     idx = np.full((B, cap), -9, np.int32)
     z = np.full((B, cap), np.nan, np.float32)
     for b, n in enumerate(ns):
@@ -29,7 +30,10 @@ def _topk(idx, z, counts, k):
     out = torch.full((B, max(k, 1)), -5, dtype=torch.int32, device=DEV)
     oc = torch.full((B,), -5, dtype=torch.int32, device=DEV)
     o = out[:, :k].contiguous() if k else torch.empty((B, 0), dtype=torch.int32, device=DEV)
-    lsa.lsa_topk(dev(idx), dev(z), dev(np.asarray(counts, np.int32)), o, oc)
+    nws = lsa.lsa_topk_workspace_bytes(B, cap, k)
+    # stale workspace contents must not matter: fill it with garbage first
+    ws = torch.full((max(nws, 1),), 0x5A, dtype=torch.uint8, device=DEV) if nws else None
+    lsa.lsa_topk(dev(idx), dev(z), dev(np.asarray(counts, np.int32)), o, oc, ws)
     torch.cuda.synchronize()
     return host(o), host(oc)
 
@@ -41,6 +45,9 @@ def _topk(idx, z, counts, k):
     ([70000, 3, 2], 256),
     ([81920, 81921, 40001], 2048),
     ([100000, 5, 9], 512),
+    ([17000, 3], 20000),
+    ([16384, 16385, 16383], 1000),
+    ([530000, 10], 2048),
     ([500, 600, 700], 1),
     ([5000, 5000, 5000], 0),
 ])
@@ -56,10 +63,11 @@ def test_topk_matches_oracle(ns, k, ties):
         assert np.array_equal(out[b], want), f"request {b}"
 
 
-def test_topk_count_above_capacity_uses_capacity():
+@pytest.mark.parametrize("cap", [3000, 30000])
+def test_topk_count_above_capacity_uses_capacity(cap):
     rng = np.random.default_rng(5)
-    idx, z = _survivors(rng, 2, 3000, [3000, 3000])
-    out, oc = _topk(idx, z, [9999, 3000], 1000)
+    idx, z = _survivors(rng, 2, cap, [cap, cap])
+    out, oc = _topk(idx, z, [99999, cap], 1000)
     for b in range(2):
         want, cnt = oracle.topk(idx[b], z[b].astype(np.float64), 1000)
         assert np.array_equal(out[b], want) and oc[b] == cnt

@@ -21,13 +21,15 @@
 //  * a histogram of mass over 2048 value bins (linear in max - x, so the
 //    bins follow the logit order and hold few entries each) finds the bin in
 //    which the running mass crosses top_p * S;
-//  * inside that bin, three radix passes over the order key of the logit
-//    (11 + 11 + 10 bits) find the exact logit value of the crossing entry and
-//    the mass strictly ahead of that value;
-//  * among entries with exactly that logit, a block prefix sum in index
-//    order gives each one its mass ahead, and it is kept iff that is below
-//    top_p * S.
-// Every other entry is kept iff its logit is larger than the crossing value.
+//  * the entries of that bin (usually a handful) are compared pairwise in
+//    LDS: each gets its exact mass ahead in the walk order, so it is kept iff
+//    the mass ahead of the bin plus that is below top_p * S;
+//  * a bin with more than kCand entries (heavy ties, near-constant rows)
+//    instead takes three radix passes over the order key of the logit
+//    (11 + 11 + 10 bits) to find the crossing logit and the mass ahead of
+//    it, and a block prefix sum in index order over the entries with exactly
+//    that logit.
+// Every other entry is kept iff its bin is ahead of the crossing bin.
 // A second kernel adds the layers' selection words per query into the vote
 // counts and labels.
 #include "lsa_device.h"
@@ -40,6 +42,7 @@ constexpr int kNT = 1024;              // threads per row block
 constexpr int kNWv = kNT / kWave;      // wavefronts per row block
 constexpr int kBins = 2048;            // histogram bins per pass
 constexpr float kFix = 2147483648.f;   // 2^31: fixed-point unit of exp(x - max)
+constexpr int kCand = 1024;            // crossing-bin entries handled by direct comparison
 
 // order key: smaller key = larger logit; -0 and +0 share a key
 __device__ __forceinline__ uint32_t desc_key(float x) {
@@ -67,14 +70,11 @@ __device__ __forceinline__ uint64_t block_exclusive_scan_u64(uint64_t v, uint64_
   const uint64_t inc = wave_inclusive_scan_u64(v);
   if (lane == kWave - 1) scratch[wave] = inc;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    uint64_t run = 0;
-    for (int w = 0; w < kNWv; ++w) {
-      const uint64_t t = scratch[w];
-      scratch[w] = run;
-      run += t;
-    }
-    scratch[kNWv] = run;
+  if (wave == 0) {   // one wavefront scans the per-wave totals
+    const uint64_t w = lane < kNWv ? scratch[lane] : 0ull;
+    const uint64_t wi = wave_inclusive_scan_u64(w);
+    if (lane < kNWv) scratch[lane] = wi - w;
+    if (lane == kNWv - 1) scratch[kNWv] = wi;
   }
   __syncthreads();
   const uint64_t res = scratch[wave] + inc - v;
@@ -143,8 +143,15 @@ __global__ __launch_bounds__(kNT) void nucleus_kernel(int N, int W, float top_p,
   __shared__ float red[2 * kNWv];
   __shared__ int s_bin;
   __shared__ uint64_t s_before;
+  __shared__ uint32_t c_key[kCand];
+  __shared__ int c_idx[kCand];
+  __shared__ uint32_t c_w[kCand];
+  __shared__ int s_ncand;
+  __shared__ uint32_t keepbits[65536 / 32];
 
   const size_t row = blockIdx.x;
+  if (threadIdx.x == 0) s_ncand = 0;
+  for (int j = threadIdx.x; j < W; j += kNT) keepbits[j] = 0;   // ordered by the barriers below
   const float* x = logits + row * (size_t)N;
   const int e0 = threadIdx.x * EPT;
 
@@ -201,9 +208,45 @@ __global__ __launch_bounds__(kNT) void nucleus_kernel(int N, int W, float top_p,
   const int cbin = s_bin;
   uint64_t M = s_before;
 
-  uint32_t ckey = 0xFFFFFFFFu;   // order key of the crossing logit
+  uint32_t ckey = 0xFFFFFFFFu;   // order key of the crossing logit (radix path)
   bool found = cbin >= 0;
+  // Candidate path: the crossing value bin usually holds a handful of
+  // entries.  They are collected (order key, index, mass) in LDS, and each
+  // gets its exact mass ahead inside the bin by comparing with every other
+  // candidate in the walk order (logit descending, index ascending); its
+  // keep bit goes to an LDS bitmap.  More than kCand candidates (heavy ties,
+  // near-constant rows) take the radix path below.
+  bool cand_path = false;
   if (found) {
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+      if (e0 + i < N && vbin(i) == cbin) {
+        const int slot = atomicAdd(&s_ncand, 1);
+        if (slot < kCand) {
+          c_key[slot] = desc_key(v[i]);
+          c_idx[slot] = e0 + i;
+          c_w[slot] = weight(i);
+        }
+      }
+    }
+    __syncthreads();
+    const int nc = s_ncand;
+    cand_path = nc <= kCand;   // uniform
+    if (cand_path) {
+      for (int sl = threadIdx.x; sl < nc; sl += kNT) {
+        const uint32_t ks = c_key[sl];
+        const int is = c_idx[sl];
+        uint64_t ahead = 0;
+        for (int j = 0; j < nc; ++j) {
+          const uint32_t kj = c_key[j];
+          if (kj < ks || (kj == ks && c_idx[j] < is)) ahead += c_w[j];
+        }
+        if (M + ahead < R) atomicOr(&keepbits[is >> 5], 1u << (is & 31));
+      }
+      __syncthreads();
+    }
+  }
+  if (found && !cand_path) {
     // passes 1-3: radix over the order key, inside the crossing value bin
     uint32_t prefix = 0;
     constexpr int kShift[3] = {21, 10, 0};
@@ -231,6 +274,25 @@ __global__ __launch_bounds__(kNT) void nucleus_kernel(int N, int W, float top_p,
       M = s_before;
     }
     ckey = prefix;
+  }
+
+  if (cand_path) {
+#pragma unroll
+    for (int wd = 0; wd < EPT / 32; ++wd) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int j = 0; j < 32; ++j) {
+        const int i = wd * 32 + j;
+        if (e0 + i < N) {
+          const int vb = vbin(i);
+          const bool keep = vb < cbin || (vb == cbin && ((keepbits[(e0 + i) >> 5] >> ((e0 + i) & 31)) & 1u));
+          word |= (keep ? 1u : 0u) << j;
+        }
+      }
+      const int widx = threadIdx.x * (EPT / 32) + wd;
+      if (widx < W) mask[row * (size_t)W + widx] = word;
+    }
+    return;
   }
 
   // entries with the crossing logit: mass ahead in index order

@@ -232,7 +232,7 @@ lsa_status lsa_label_vote(int Q, int L, int N, float top_p, int theta,
  *   loss = mean_ts BCE(z_ts, y_ts) + mean_ts (1 - p_t)^gamma BCE(z_ts, y_ts)
  *   dWq  = d loss / d Wq
  *
- *   h     bf16 [Q][D] (8-byte aligned)   Wq fp32 [H*dI][D], row = head*dI + i
+ *   h     bf16 [Q][D] (16-byte aligned)  Wq fp32 [H*dI][D], row = head*dI + i
  *   Wg    fp32 [H][D]   (Wq, Wg 16-byte aligned)   bias: host scalar
  *   K     bf16 [N][dI] (8-byte aligned)   label uint8 [Q][N] (nonzero = 1)
  *   loss  out fp32 [1]  dWq out fp32 [H*dI][D] (16-byte aligned)
@@ -241,7 +241,7 @@ lsa_status lsa_label_vote(int Q, int L, int N, float top_p, int theta,
  *         queries, transposed K and h, dloss/dz, partial key gradients)
  * Every product is an fp32 contraction with fp32 accumulation; the loss sum
  * is accumulated in fp64 in a fixed order, so results are deterministic.
- * Limits: 1 <= Q <= 64, 1 <= N <= 4,000,000, D % 64 == 0 and D <= 16384,
+ * Limits: 1 <= Q <= 64, 1 <= N <= 4,000,000, D % 128 == 0 and D <= 16384,
  * 1 <= H <= 64, dI in {64, 128}, 0 <= gamma <= 16, finite bias.  Errors: LSA_E_SHAPE / LSA_E_ARG for the
  * limits, null or misaligned pointers; LSA_E_WORKSPACE for a missing, short
  * or misaligned workspace; LSA_E_HIP for a launch failure.

@@ -228,7 +228,7 @@ lsa_status lsa_label_vote(int Q, int L, int N, float top_p, int theta, const flo
 }
 
 size_t lsa_focal_bce_grad_workspace_bytes(int Q, int N, int D, int H, int dI) {
-  if (Q < 1 || Q > 64 || N < 1 || N > 4000000 || D < 64 || D > 16384 || D % 64 || H < 1 ||
+  if (Q < 1 || Q > 64 || N < 1 || N > 4000000 || D < 128 || D > 16384 || D % 128 || H < 1 ||
       H > 64 || (dI != 64 && dI != 128))
     return 0;
   return lsa::focal_workspace_bytes(Q, N, D, H, dI);
@@ -240,8 +240,8 @@ lsa_status lsa_focal_bce_grad(int Q, int N, int D, int H, int dI, float gamma,
                               void* ws, size_t ws_bytes, hipStream_t stream) {
   REQUIRE(Q >= 1 && Q <= 64, LSA_E_SHAPE, "lsa_focal_bce_grad: Q=%d not in [1,64]", Q);
   REQUIRE(N >= 1 && N <= 4000000, LSA_E_SHAPE, "lsa_focal_bce_grad: N=%d not in [1,4000000]", N);
-  REQUIRE(D >= 64 && D <= 16384 && D % 64 == 0, LSA_E_SHAPE,
-          "lsa_focal_bce_grad: D=%d not a multiple of 64 in [64,16384]", D);
+  REQUIRE(D >= 128 && D <= 16384 && D % 128 == 0, LSA_E_SHAPE,
+          "lsa_focal_bce_grad: D=%d not a multiple of 128 in [128,16384]", D);
   REQUIRE(H >= 1 && H <= 64, LSA_E_SHAPE, "lsa_focal_bce_grad: H=%d not in [1,64]", H);
   REQUIRE(dI == 64 || dI == 128, LSA_E_SHAPE, "lsa_focal_bce_grad: dI=%d not 64 or 128", dI);
   REQUIRE(gamma >= 0.f && gamma <= 16.f, LSA_E_ARG, "lsa_focal_bce_grad: gamma=%g not in [0,16]",
@@ -251,8 +251,8 @@ lsa_status lsa_focal_bce_grad(int Q, int N, int D, int H, int dI, float gamma,
           "lsa_focal_bce_grad: null input or output pointer");
   REQUIRE(aligned16(Wq) && aligned16(Wg) && aligned16(dWq), LSA_E_ARG,
           "lsa_focal_bce_grad: Wq, Wg and dWq must be 16-byte aligned");
-  REQUIRE(((uintptr_t)h & 7u) == 0 && ((uintptr_t)K & 7u) == 0, LSA_E_ARG,
-          "lsa_focal_bce_grad: h and K must be 8-byte aligned");
+  REQUIRE(aligned16(h) && ((uintptr_t)K & 7u) == 0, LSA_E_ARG,
+          "lsa_focal_bce_grad: h must be 16-byte and K 8-byte aligned");
   const size_t need = lsa::focal_workspace_bytes(Q, N, D, H, dI);
   REQUIRE(ws && ws_bytes >= need && ((uintptr_t)ws & 255u) == 0, LSA_E_WORKSPACE,
           "lsa_focal_bce_grad: workspace of %zu bytes, 256-byte aligned, needed (got %zu)", need,

@@ -13,7 +13,9 @@
 // keys with one collapsed query per row, qe_t = sum_h g_th q_th (dI wide),
 // and the backward pass goes through G_t = sum_s delta_ts k_s:
 //   d loss / d q_thi = g_th G_ti,   dW_q[(h,i)][d] = sum_t g_th G_ti h_td.
-// Every product runs on v_mfma_f32_32x32x2_f32 (fp32 in, fp32 accumulate).
+// The two large products (projection, dW_q) split their fp32 operand three
+// ways into bf16 and run on v_mfma_f32_32x32x16_bf16 against the exactly-bf16
+// hidden states; the others run on v_mfma_f32_32x32x2_f32.
 // The operands of each product are stored with the contraction axis
 // contiguous, so a lane loads four consecutive k values of its row of A and
 // of its row of B with one vector load and feeds four MFMAs; the k order is
@@ -76,6 +78,37 @@ __device__ __forceinline__ f32x16 mfma4(f32x4 a, f32x4 b, f32x16 c) {
   return c;
 }
 
+// Three-way bf16 split of eight fp32 values: x = hi + mid + lo exactly (each
+// residual is exact in fp32 and 3 x 8 significant bits cover fp32's 24), so
+// three bf16 MFMAs against an exactly-bf16 operand reproduce the fp32 product
+// terms exactly; only the fp32 accumulation rounds, as in an fp32 MFMA.  Ten
+// times cheaper than v_mfma_f32_32x32x2_f32 per multiply-add.
+struct Split3 {
+  bf16x8 hi, mid, lo;
+};
+
+__device__ __forceinline__ Split3 split3(f32x4 a, f32x4 b) {
+  Split3 r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float x = i < 4 ? a[i] : b[i - 4];
+    const __bf16 h = (__bf16)x;
+    const float r1 = x - (float)h;
+    const __bf16 m = (__bf16)r1;
+    const float r2 = r1 - (float)m;
+    r.hi[i] = h;
+    r.mid[i] = m;
+    r.lo[i] = (__bf16)r2;
+  }
+  return r;
+}
+
+__device__ __forceinline__ f32x16 mfma_split(const Split3& a, bf16x8 b, f32x16 c) {
+  c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.hi, b, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.mid, b, c, 0, 0, 0);
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.lo, b, c, 0, 0, 0);
+}
+
 // accumulator element rr of lane l: row (rr&3) + 4*(l/32) + 8*(rr/4), col l%32
 __device__ __forceinline__ int acc_row(int rr, int half) { return (rr & 3) + 4 * half + 8 * (rr >> 2); }
 
@@ -108,29 +141,37 @@ __global__ __launch_bounds__(256) void fproj_kernel(int Q, int D, int HdI, int H
   const int kbeg = (blockIdx.y * 4 + wave) * kq, kend = kbeg + kq;
   const uint32_t aoff = (uint32_t)rl * D * 4, b0off = (uint32_t)n * D * 2,
                  b1off = (uint32_t)(n + 32) * D * 2;
+  // v_mfma_f32_32x32x16_bf16, two steps per 32 k: lane (m, half) holds
+  // k = k0 + 16 half + 8 s .. +7 of row m in step s, so each lane reads 64
+  // contiguous weight bytes (the two halves of a row fill a 128-byte line)
+  // and 32 bytes of each hidden state.  The next 32 k are loaded before the
+  // current ones are split and multiplied.
+  struct Stage {
+    f32x4 w[4];
+    bf16x8 x0[2], x1[2];
+  };
+  auto load_stage = [&](int k, Stage& st) {
+    const int kk = k + 16 * half;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) st.w[j] = buf_f32x4(ra, aoff + (kk + 4 * j) * 4);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      st.x0[j] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rb, b0off + (kk + 8 * j) * 2, 0, 0));
+      st.x1[j] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rb, b1off + (kk + 8 * j) * 2, 0, 0));
+    }
+  };
   f32x16 acc0 = {}, acc1 = {};
-  int k = kbeg;
-  // batches of four k-steps: twelve loads in flight before the first MFMA
-  for (; k + 32 <= kend; k += 32) {
-    f32x4 a[4], x0[4], x1[4];
+  Stage cur, nxt;
+  load_stage(kbeg, cur);
+  for (int k = kbeg; k < kend; k += 32) {
+    load_stage(min(k + 32, kend - 32), nxt);   // the last pass re-reads its own k (cached)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int kk = k + 8 * j + 4 * half;
-      a[j] = buf_f32x4(ra, aoff + kk * 4);
-      x0[j] = buf_bf16x4(rb, b0off + kk * 2);
-      x1[j] = buf_bf16x4(rb, b1off + kk * 2);
+    for (int st = 0; st < 2; ++st) {
+      const Split3 a = split3(cur.w[2 * st], cur.w[2 * st + 1]);
+      acc0 = mfma_split(a, cur.x0[st], acc0);
+      acc1 = mfma_split(a, cur.x1[st], acc1);
     }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      acc0 = mfma4(a[j], x0[j], acc0);
-      acc1 = mfma4(a[j], x1[j], acc1);
-    }
-  }
-  for (; k < kend; k += 8) {
-    const int kk = k + 4 * half;
-    const f32x4 a = buf_f32x4(ra, aoff + kk * 4);
-    acc0 = mfma4(a, buf_bf16x4(rb, b0off + kk * 2), acc0);
-    acc1 = mfma4(a, buf_bf16x4(rb, b1off + kk * 2), acc1);
+    cur = nxt;
   }
 #pragma unroll
   for (int rr = 0; rr < 16; ++rr) {
@@ -388,11 +429,12 @@ __global__ __launch_bounds__(256) void fdw_kernel(int D, const float* __restrict
   const uint16_t* b1 = hT + (size_t)(c0 + 32 + n) * kQP;
   f32x16 acc0 = {}, acc1 = {};
 #pragma unroll
-  for (int k = 0; k < kQP; k += 8) {
-    const int kk = k + 4 * half;
-    const f32x4 a = *(const f32x4*)(ga + kk) * *(const f32x4*)(Ga + kk);
-    acc0 = mfma4(a, load_bf16x4(b0 + kk), acc0);
-    acc1 = mfma4(a, load_bf16x4(b1 + kk), acc1);
+  for (int k = 0; k < kQP; k += 16) {
+    const int kk = k + 8 * half;
+    const Split3 a = split3(*(const f32x4*)(ga + kk) * *(const f32x4*)(Ga + kk),
+                            *(const f32x4*)(ga + kk + 4) * *(const f32x4*)(Ga + kk + 4));
+    acc0 = mfma_split(a, *(const bf16x8*)(b0 + kk), acc0);
+    acc1 = mfma_split(a, *(const bf16x8*)(b1 + kk), acc1);
   }
 #pragma unroll
   for (int rr = 0; rr < 16; ++rr) {
@@ -419,8 +461,8 @@ struct FocalWs {
 size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // slices of D for the projection: each wave of a slice takes D / (4 KS)
-// columns, a multiple of 8
-int proj_slices(int D) { return D % 512 == 0 ? 8 : (D % 256 == 0 ? 4 : 2); }
+// columns, a multiple of 32 (two bf16 MFMA steps; D % 128 == 0)
+int proj_slices(int D) { return D % 1024 == 0 ? 8 : (D % 512 == 0 ? 4 : (D % 256 == 0 ? 2 : 1)); }
 
 FocalWs carve(void* base, int Q, int N, int D, int H, int dI) {
   (void)Q;

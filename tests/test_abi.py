@@ -98,12 +98,12 @@ def test_validation_errors_return_before_launch(lib):
     # focal: Q above 64, D not a multiple of 64, unsupported dI, short workspace
     F = lambda Q, N, D, H, dI, g=2.0, ws=fake, nws=1 << 30: lib.lsa_focal_bce_grad(
         Q, N, D, H, dI, g, fake, fake, fake, 0.0, fake, fake, fake, fake, ws, nws, None)
-    assert F(65, 10, 64, 1, 64) == _abi.LSA_E_SHAPE
-    assert F(4, 10, 96, 1, 64) == _abi.LSA_E_SHAPE
-    assert F(4, 10, 64, 1, 96) == _abi.LSA_E_SHAPE
-    assert F(4, 10, 64, 1, 64, g=-1.0) == _abi.LSA_E_ARG
-    assert F(4, 10, 64, 1, 64, ws=C.c_void_p(256), nws=16) == _abi.LSA_E_WORKSPACE
-    assert F(4, 10, 64, 1, 64, ws=C.c_void_p(16 + 256)) == _abi.LSA_E_WORKSPACE   # misaligned
+    assert F(65, 10, 128, 1, 64) == _abi.LSA_E_SHAPE
+    assert F(4, 10, 192, 1, 64) == _abi.LSA_E_SHAPE
+    assert F(4, 10, 128, 1, 96) == _abi.LSA_E_SHAPE
+    assert F(4, 10, 128, 1, 64, g=-1.0) == _abi.LSA_E_ARG
+    assert F(4, 10, 128, 1, 64, ws=C.c_void_p(256), nws=16) == _abi.LSA_E_WORKSPACE
+    assert F(4, 10, 128, 1, 64, ws=C.c_void_p(16 + 256)) == _abi.LSA_E_WORKSPACE   # misaligned
 
 
 def test_workspace_sizes(lib):
@@ -112,7 +112,7 @@ def test_workspace_sizes(lib):
     big = lib.lsa_focal_bce_grad_workspace_bytes(64, 32768, 4096, 64, 128)
     # at least dloss/dz [64][N] fp32 and the transposed keys [dI][N] bf16
     assert big >= 64 * 32768 * 4 + 128 * 32768 * 2
-    assert lib.lsa_focal_bce_grad_workspace_bytes(65, 10, 64, 1, 64) == 0
+    assert lib.lsa_focal_bce_grad_workspace_bytes(65, 10, 128, 1, 64) == 0
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

@@ -62,8 +62,9 @@ def test_focal_full_label_workload():
     print(f"loss gpu {lg:.7f} oracle {lo:.7f}; dW rel fro err {fro:.2e}")
 
 
-@pytest.mark.parametrize("Q,N,D,H,dI", [(1, 1, 64, 1, 64), (3, 100, 64, 3, 64), (5, 1000, 256, 8, 128),
-                                         (64, 4097, 128, 64, 64), (17, 333, 192, 5, 128)])
+@pytest.mark.parametrize("Q,N,D,H,dI", [(1, 1, 128, 1, 64), (3, 100, 128, 3, 64), (5, 1000, 256, 8, 128),
+                                         (64, 4097, 128, 64, 64), (17, 333, 384, 5, 128),
+                                         (2, 50, 640, 2, 64)])
 def test_focal_ragged_shapes(Q, N, D, H, dI):
     rng = np.random.default_rng(Q * 1000 + N)
     h, Wq, Wg, K, y = _random_student(rng, Q, N, D, H, dI)
@@ -80,7 +81,7 @@ def test_focal_gamma_values(gamma):
 def test_focal_gamma_zero_is_twice_bce():
     # with gamma = 0 the focal term equals the BCE term: loss = 2 * mean BCE
     rng = np.random.default_rng(9)
-    h, Wq, Wg, K, y = _random_student(rng, 4, 500, 64, 2, 64)
+    h, Wq, Wg, K, y = _random_student(rng, 4, 500, 128, 2, 64)
     lg, _ = _gpu(h, Wq, Wg, 0.0, K, y, 0.0, 2, 64)
     _, _, z = oracle.focal_bce_grad(h, Wq, Wg, 0.0, K, y, 0.0, 2, 64, want_grad=False, want_z=True)
     bce = np.mean(np.logaddexp(0.0, z) - y * z)

@@ -17,15 +17,21 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "lsa_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liblsa_oracle.so")
+# A test may point the wrapper at another build of the oracle source (the
+# mutation tests build copies with one planted mistake each).
+_ALT_LIB = os.environ.get("LSA_ORACLE_LIB")
 _lib = None
+
+
+GCC_FLAGS = ["-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-fno-fast-math",
+             "-ffp-contract=off"]
 
 
 def build(force: bool = True) -> str:
     """Compile the oracle with gcc (-O2, OpenMP, IEEE semantics kept)."""
     if force or not os.path.exists(_LIB_PATH):
         tmp = _LIB_PATH + ".tmp"
-        cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared",
-               "-fno-fast-math", "-ffp-contract=off", _SRC, "-o", tmp, "-lm"]
+        cmd = ["gcc", *GCC_FLAGS, "-I", _HERE, _SRC, "-o", tmp, "-lm"]
         subprocess.run(cmd, check=True)
         os.replace(tmp, _LIB_PATH)
     return _LIB_PATH
@@ -35,9 +41,12 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB_PATH):
-        build()
-    lib = C.CDLL(_LIB_PATH)
+    if _ALT_LIB:
+        lib = C.CDLL(_ALT_LIB)
+    else:
+        if not os.path.exists(_LIB_PATH):
+            build()
+        lib = C.CDLL(_LIB_PATH)
     P = C.c_void_p
     i32, i64, f64 = C.c_int, C.c_int64, C.c_double
     sig = {

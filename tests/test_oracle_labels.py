@@ -61,6 +61,13 @@ def test_nucleus_is_minimum_cardinality_set(oracle, seed):
     assert pi[sel.astype(bool)].sum() >= p - 1e-12
 
 
+def test_nucleus_exact_boundary(oracle):
+    # equal logits, N = 8, p = 0.5: four entries carry exactly 0.5, so the
+    # smallest set reaching p has four entries; the fifth has mass ahead = p
+    sel, n = oracle.nucleus(np.full(8, -1.5, np.float32), 0.5)
+    assert n == 4 and sel.tolist() == [1, 1, 1, 1, 0, 0, 0, 0]
+
+
 def test_nucleus_crossing_entry_included(oracle):
     # masses 0.5, 0.3, 0.2: the second entry crosses 0.6 and is included
     x = np.log(np.array([0.5, 0.3, 0.2])).astype(np.float32)

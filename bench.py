@@ -48,6 +48,9 @@ def parse():
     p.add_argument("--copy-probe", type=int, default=0,
                    help="also run a plain device copy of this many MiB (counter calibration)")
     p.add_argument("--threads", type=int, default=16)
+    p.add_argument("--graph", action="store_true",
+                   help="time the steps as replays of one captured HIP graph (per-kernel "
+                        "times still come from an evented eager pass)")
     return p.parse_args()
 
 
@@ -122,6 +125,32 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     ms_per_step = wall * 1e3 / max(args.steps, 1)
+    launch = "eager"
+    if args.graph:
+        # the same step captured once and replayed K times
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(graph, stream=side):
+                lsa.lsa_project_query(d["h"], d["Wq"], d["Wg"], buf.q, buf.g)
+                lsa.lsa_score(d["keys"], d["scale"], buf.q, buf.g, d["bias"], buf.mask,
+                              buf.cand_idx, buf.cand_z, buf.cand_count)
+                lsa.lsa_select_or_compact(buf.cand_idx, buf.cand_z, buf.cand_count, w.N,
+                                          buf.surv_idx, buf.surv_z, buf.surv_count)
+                lsa.lsa_topk(buf.surv_idx, buf.surv_z, buf.surv_count, buf.topk_idx,
+                             buf.topk_count, buf.ws_topk)
+                lsa.lsa_gather_hot(pool, buf.topk_idx, buf.hot)
+        stream.wait_stream(side)
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        t_start = time.perf_counter()
+        for _ in range(args.steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        ms_per_step = (time.perf_counter() - t_start) * 1e3 / max(args.steps, 1)
+        launch = "hip_graph"
     names = ["project", "score", "select", "topk", "gather"]
     per = {n: float(np.median([e[i].elapsed_time(e[i + 1]) for e in evs])) for i, n in enumerate(names)}
     pct = {n: [float(np.percentile([e[i].elapsed_time(e[i + 1]) for e in evs], q)) for q in (10, 90)]
@@ -168,6 +197,7 @@ def main():
         "kernel_ms_median": per,
         "kernel_ms_p10_p90": pct,
         "survivor_fraction": float(counts.mean() / w.N),
+        "launch": launch,
     }
 
     if args.copy_probe:

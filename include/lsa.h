@@ -86,7 +86,7 @@ int lsa_trigger_due(int64_t decode_step, int tau);
  *            (row index = head * dI + i)
  *   Wg       HOST array of L device pointers, each bf16 [H][D]
  *   q        out bf16 [L][B][H][dI]        g   out fp32 [L][B][H]
- * Limits: 1 <= L <= LSA_MAX_LAYERS, B >= 1, D % 256 == 0 and D <= 65536,
+ * Limits: 1 <= L <= LSA_MAX_LAYERS, B >= 1, D % 64 == 0 and 64 <= D <= 65536,
  * B * D * 2 < 2^31, 1 <= H <= 64, dI in {64, 128}.
  */
 lsa_status lsa_project_query(int L, int B, int D, int H, int dI,

@@ -57,8 +57,8 @@ lsa_status lsa_project_query(int L, int B, int D, int H, int dI, const uint16_t*
   REQUIRE(L >= 1 && L <= LSA_MAX_LAYERS, LSA_E_SHAPE, "lsa_project_query: L=%d not in [1,%d]", L,
           LSA_MAX_LAYERS);
   REQUIRE(B >= 1, LSA_E_SHAPE, "lsa_project_query: B=%d < 1", B);
-  REQUIRE(D >= 256 && D <= 65536 && D % 256 == 0, LSA_E_SHAPE,
-          "lsa_project_query: D=%d not a multiple of 256 in [256,65536]", D);
+  REQUIRE(D >= 64 && D <= 65536 && D % 64 == 0, LSA_E_SHAPE,
+          "lsa_project_query: D=%d not a multiple of 64 in [64,65536]", D);
   REQUIRE((int64_t)B * D * 2 < ((int64_t)1 << 31), LSA_E_SHAPE,
           "lsa_project_query: B*D*2 must stay below 2^31 bytes");
   REQUIRE(H >= 1 && H <= LSA_MAX_HEADS, LSA_E_SHAPE, "lsa_project_query: H=%d not in [1,64]", H);

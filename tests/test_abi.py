@@ -86,7 +86,7 @@ def test_validation_errors_return_before_launch(lib):
     assert lib.lsa_topk(2, 100000, 2048, fake, fake, fake, fake, fake, None, 0, None) == _abi.LSA_E_WORKSPACE
     # gather: row size not a multiple of 16
     assert lib.lsa_gather_hot(1, 10, 4, 24, fake, fake, fake, None) == _abi.LSA_E_ARG
-    # projection: hidden size not a multiple of 256
+    # projection: hidden size not a multiple of 64
     assert lib.lsa_project_query(1, 1, 100, 8, 64, fake, 0, arr, arr, fake, fake, None) == _abi.LSA_E_SHAPE
     # label vote: too many layers, top_p out of range, no mask and no workspace
     assert lib.lsa_label_vote(1, 33, 100, 0.6, 3, fake, fake, fake, fake, None, 0, None) == _abi.LSA_E_SHAPE

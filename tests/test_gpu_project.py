@@ -55,9 +55,20 @@ def test_project_named_workloads(name):
     print("excluded", _run_and_check(gen.WORKLOADS[name]))
 
 
-@pytest.mark.parametrize("B,D,H", [(5, 768, 40), (33, 768, 40), (3, 256, 3)])
+@pytest.mark.parametrize("B,D,H", [(5, 768, 40), (33, 768, 40), (3, 256, 3), (2, 64, 4), (7, 320, 5)])
 def test_project_request_groups(B, D, H):
     w = gen.custom("proj", 91, B=B, L=2, H=H, dI=64, D=D, N=64)
+    _run_and_check(w)
+
+
+# Launch regimes of the tile split (R = H*dI + H rows in 16-row tiles, about
+# one block per compute unit per (layer, request group), at most 8 tiles a
+# block): one tile per block; 3-4 tiles per block; more tiles than
+# 8 x blocks, so extra blocks; ten request groups.
+@pytest.mark.parametrize("B,L,D,H,dI", [(65, 1, 512, 7, 64), (40, 2, 1024, 24, 128),
+                                        (32, 4, 768, 64, 128), (300, 3, 256, 64, 128)])
+def test_project_tile_split(B, L, D, H, dI):
+    w = gen.custom("proj3", 93, B=B, L=L, H=H, dI=dI, D=D, N=64)
     _run_and_check(w)
 
 

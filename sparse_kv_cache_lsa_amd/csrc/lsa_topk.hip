@@ -283,9 +283,17 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(int cap, int k,
 
   if (n <= kThreads * kReg) {
     // ---- register-resident path: thread t holds positions [t*chunk, (t+1)*chunk)
+    // the register array is sized to the list (every pass walks all its slots)
     const int chunk = (n + kThreads - 1) / kThreads;
-    block_select<kThreads, kReg>(n, k, chunk, sz, si, hist, scratch, &s_digit, &s_above, stage,
-                                 o, nullptr);
+    if (chunk <= 16)
+      block_select<kThreads, 16>(n, k, chunk, sz, si, hist, scratch, &s_digit, &s_above, stage, o,
+                                 nullptr);
+    else if (chunk <= 32)
+      block_select<kThreads, 32>(n, k, chunk, sz, si, hist, scratch, &s_digit, &s_above, stage, o,
+                                 nullptr);
+    else
+      block_select<kThreads, kReg>(n, k, chunk, sz, si, hist, scratch, &s_digit, &s_above, stage,
+                                   o, nullptr);
     if (t == 0) out_count[b] = k;
     return;
   }
@@ -381,7 +389,9 @@ __global__ __launch_bounds__(kMT) void slice_kernel(int cap, int k, int cap_c,
   __shared__ int scratch[2 * (kMT / kWave) + 2];
   __shared__ int stage[kStage];
   __shared__ int s_digit, s_above;
-  const int b = blockIdx.y, p = blockIdx.x;
+  // request index fastest: the blocks of the first slices of every request
+  // are dispatched first (most later slices are empty and exit at once)
+  const int b = blockIdx.x, p = blockIdx.y;
   const int n = min(max(surv_count[b], 0), cap);
   const int kc = min(k, kSlice);
   if (p == 0 && threadIdx.x == 0)
@@ -431,7 +441,7 @@ hipError_t launch_topk(int B, int cap, int k, const int32_t* surv_idx, const flo
   int32_t* cand_idx = (int32_t*)ws;
   float* cand_z = (float*)((char*)ws + up256(cc * 4));
   int32_t* cand_count = (int32_t*)((char*)ws + 2 * up256(cc * 4));
-  hipLaunchKernelGGL(slice_kernel, dim3(P, B), dim3(kMT), 0, s, cap, k, cap_c, surv_idx, surv_z,
+  hipLaunchKernelGGL(slice_kernel, dim3(B, P), dim3(kMT), 0, s, cap, k, cap_c, surv_idx, surv_z,
                      surv_count, cand_idx, cand_z, cand_count);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

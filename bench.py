@@ -182,7 +182,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": w.name, "requests": w.B, "indexer_layers": w.L,
                    "entries_per_layer": w.N, "context_tokens": 4 * w.N, "heads": w.H,

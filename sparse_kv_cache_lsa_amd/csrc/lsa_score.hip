@@ -6,10 +6,14 @@
 // summary, section 2.1 "scoring mechanism", with I >= 0.5 written as z >= 0
 // as in its "dynamic fetch" bullet).
 //
-// Design (memory-bound key stream, MFMA for the dense H x dI x entries part):
-//  * grid.y = (layer, request) pair, grid.x = chunk of 32-entry tiles; the NW
-//    wavefronts of a block take every NW-th tile of the chunk, so a block
-//    streams one contiguous key range (the pattern HBM serves best).
+// Design (memory-bound key stream):
+//  * The head sum is linear in the keys: sum_h g_h (q_h . k) = qt . k with
+//    qt = sum_h g_h q_h.  Each block forms qt (fp32) for its request and
+//    every layer once, from the bf16 queries and fp32 gates, so scoring an
+//    entry is one dI-long dot product, not H of them.
+//  * grid.y = request, grid.x = chunk of 32-entry tiles; the NW wavefronts of
+//    a block take every NW-th tile of the chunk, so a block streams one
+//    contiguous key range (the pattern HBM serves best).
 //  * Keys are read through a buffer resource per (layer, request): each load
 //    instruction covers 1 KiB of contiguous keys (16 B per lane, nontemporal),
 //    the lane offset is a 32-bit VGPR, and the hardware range check returns 0
@@ -17,18 +21,12 @@
 //    the loop.  Stores use the same mechanism: a lane with nothing to store
 //    gets an out-of-range offset and the store is dropped.
 //  * A register ring keeps RING-1 tiles in flight while one is scored.
-//  * A tile (32 entries x dI) is staged in the wave's private LDS slice with
-//    the 16-byte chunks of each entry row XOR-swizzled by the entry index, so
-//    the MFMA-layout reads spread over LDS banks.
-//  * The contraction runs on v_mfma_f32_32x32x16_bf16: query as A (32 heads x
-//    16 dims, in registers for the whole block), keys as B (16 dims x 32
-//    entries).  e4m3 keys are widened to bf16 exactly in registers (every e4m3
-//    value is a bf16 value); the per-entry fp32 scale is applied in the
-//    epilogue.  The key dimension is permuted identically in A and B (lane
-//    half 0 takes dims [0, dI/2), half 1 takes [dI/2, dI)), which leaves every
-//    dot product unchanged.
-//  * Epilogue in registers: gate-weighted head sum over the 16 accumulator
-//    rows a lane holds, one cross-half sum, scale, bias, optional sigmoid,
+//  * The tile stays in the registers it was loaded into: lane l holds 16
+//    bytes of one entry row (16 e4m3 or 8 bf16 key elements, widened exactly
+//    to fp32), multiplies them by its slice of qt, and the lanes sharing a row
+//    add their partial sums with DPP; one lane-to-lane gather then gives lane
+//    n the score of entry n (the layout the epilogue uses).
+//  * Epilogue in registers: per-entry fp32 scale, bias, optional sigmoid,
 //    threshold by wavefront ballot -> one 32-bit selection word per tile.
 #include "lsa_device.h"
 #include "lsa_launch.h"
@@ -51,9 +49,9 @@ struct Geo {
   static constexpr int RB = DI * ESZ;           // bytes per entry row
   static constexpr int TB = 32 * RB;            // bytes per 32-entry tile
   static constexpr int LOADS = TB / 1024;       // 16-byte loads per lane per tile
-  static constexpr int NCH = RB / 16;           // 16-byte chunks per row
-  static constexpr int KSTEPS = DI / 16;        // MFMA steps (K = 16)
-  static constexpr int HALF = DI / 2;           // key dims per lane half
+  static constexpr int LPR = RB / 16;           // lanes holding one entry row (per load)
+  static constexpr int EPC = 16 / ESZ;          // key elements per lane and load
+  static constexpr int EPL = 64 / LPR;          // entry rows per load
 };
 
 // One tile in flight: its key bytes (LOADS x 16 B per lane) and, for e4m3
@@ -79,57 +77,80 @@ __device__ __forceinline__ void load_tile(__amdgpu_buffer_rsrc_t kr, __amdgpu_bu
     r.sc = 1.f;
 }
 
-// Scores one staged tile: returns z of entry column (lane & 31) in every lane
-// (both lane halves hold the same value).
-template <int KT, int DI, int HT>
-__device__ __forceinline__ float score_tile(const TileRegs<KT, DI>& r, unsigned char* lds,
-                                            int lane, const bf16x8 (&af)[HT][Geo<KT, DI>::KSTEPS],
-                                            const float* gs, float bias) {
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// One halving step of the row reduction: lanes whose bit (the one the DPP
+// partner differs in) is clear keep values [0, C/2) and hand over [C/2, C);
+// lanes with it set keep the upper half.  Each kept value adds the partner's.
+template <int C, int CTRL, int N>
+__device__ __forceinline__ void halve(float (&v)[N], bool upper) {
+#pragma unroll
+  for (int i = 0; i < C / 2; ++i) {
+    const float keep = upper ? v[C / 2 + i] : v[i];
+    const float give = upper ? v[i] : v[C / 2 + i];
+    v[i] = keep + dpp<CTRL>(give);
+  }
+}
+
+// v[j] (j < NL) is a lane's partial dot product for the entry row it holds in
+// load j; the LPR = 2 NL lanes of an aligned group hold the same rows.
+// Halving steps over the lane bits (partners: row_mirror for bit 3,
+// row_half_mirror for bit 2, quad_perm ^2 for bit 1) leave lane li of the
+// group with row (li >> 1)'s sum over half of the group; quad_perm ^1 adds
+// the other half.  Result: lanes 2j and 2j + 1 of a group hold the full dot
+// product of load j's row (same bits in both).
+template <int LPR, int NL>
+__device__ __forceinline__ float reduce_rows(float (&v)[NL], int lane) {
+  static_assert(2 * NL == LPR && (NL == 2 || NL == 4 || NL == 8), "row geometry");
+  const int li = lane & (LPR - 1);
+  if constexpr (NL == 8) halve<8, 0x140>(v, li & 8);   // row_mirror: i <-> 15 - i
+  if constexpr (NL >= 4) halve<4, 0x141>(v, li & 4);   // row_half_mirror: i <-> 7 - i
+  halve<2, 0x4E>(v, li & 2);                           // quad_perm [2,3,0,1]: lane ^ 2
+  return v[0] + dpp<0xB1>(v[0]);                       // quad_perm [1,0,3,2]: lane ^ 1
+}
+
+// Partial dot product of one 16-byte key chunk with the lane's qt slice.
+template <int KT>
+__device__ __forceinline__ float chunk_dot(u32x4 k, const float* qv) {
+  float acc0 = 0.f, acc1 = 0.f;
+  if constexpr (KT == 1) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const auto lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(k[w], 1.0f, false);
+      const auto hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(k[w], 1.0f, true);
+      acc0 = fmaf(lo[0], qv[4 * w], acc0);
+      acc1 = fmaf(lo[1], qv[4 * w + 1], acc1);
+      acc0 = fmaf(hi[0], qv[4 * w + 2], acc0);
+      acc1 = fmaf(hi[1], qv[4 * w + 3], acc1);
+    }
+  } else {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      acc0 = fmaf(__uint_as_float(k[w] << 16), qv[2 * w], acc0);
+      acc1 = fmaf(__uint_as_float(k[w] & 0xFFFF0000u), qv[2 * w + 1], acc1);
+    }
+  }
+  return acc0 + acc1;
+}
+
+// Scores one tile held in registers: returns z of entry (lane & 31) in every
+// lane (both lane halves hold the same value).  qv: the lane's EPC elements
+// of qt, dims [EPC * (lane % LPR), EPC * (lane % LPR + 1)).
+template <int KT, int DI>
+__device__ __forceinline__ float score_tile(const TileRegs<KT, DI>& r, int lane, const float* qv,
+                                            float bias) {
   using G = Geo<KT, DI>;
   const int n = lane & 31;
-  const int half = lane >> 5;
-
-  // stage: coalesced chunk o of the tile -> row e, swizzled chunk position
+  float d[G::LOADS];
 #pragma unroll
-  for (int j = 0; j < G::LOADS; ++j) {
-    const int o = 1024 * j + 16 * lane;
-    const int e = o / G::RB;
-    const int c = (o % G::RB) >> 4;
-    *(u32x4*)(lds + e * G::RB + ((c ^ (e & (G::NCH - 1))) << 4)) = r.k[j];
-  }
-  wave_lds_sync();
-
-  f32x16 acc[HT];
-#pragma unroll
-  for (int ht = 0; ht < HT; ++ht) acc[ht] = f32x16{};
-#pragma unroll
-  for (int s = 0; s < G::KSTEPS; ++s) {
-    const int byte0 = (half * G::HALF + 8 * s) * G::ESZ;
-    const int c = byte0 >> 4;
-    const unsigned char* src = lds + n * G::RB + ((c ^ (n & (G::NCH - 1))) << 4) + (byte0 & 15);
-    bf16x8 bfrag;
-    if constexpr (KT == 0) {
-      bfrag = __builtin_bit_cast(bf16x8, *(const u32x4*)src);
-    } else {
-      bfrag = e4m3x8_to_bf16x8(*(const u32x2*)src);
-    }
-#pragma unroll
-    for (int ht = 0; ht < HT; ++ht)
-      acc[ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ht][s], bfrag, acc[ht], 0, 0, 0);
-  }
-  wave_lds_sync();
-
-  // accumulator register r of lane l holds head row (r&3) + 4*(l/32) + 8*(r/4)
-  // of entry column l%32; the gates come from the block's LDS copy (every
-  // lane of a half reads the same address: a broadcast)
-  float part = 0.f;
-#pragma unroll
-  for (int ht = 0; ht < HT; ++ht)
-#pragma unroll
-    for (int rr = 0; rr < 16; ++rr)
-      part = fmaf(gs[ht * 32 + (rr & 3) + 4 * half + 8 * (rr >> 2)], acc[ht][rr], part);
-  part = add_halves(part);
-  return fmaf(part, r.sc, bias);
+  for (int j = 0; j < G::LOADS; ++j) d[j] = chunk_dot<KT>(r.k[j], qv);
+  const float sum = reduce_rows<G::LPR, G::LOADS>(d, lane);
+  // entry n = load (n / EPL), row group (n % EPL): held by lane LPR (n % EPL) + 2 (n / EPL)
+  const float zv = __shfl(sum, G::LPR * (n % G::EPL) + 2 * (n / G::EPL), kWave);
+  return fmaf(zv, r.sc, bias);
 }
 
 // One block = one request b and one chunk of kChunkTiles 32-entry tiles
@@ -149,13 +170,12 @@ constexpr int kNW = 4;
 constexpr int kTPW = LSA_CAND_CHUNK / 32 / kNW;    // tiles per wave and layer
 static_assert(kTPW * 32 * kNW == LSA_CAND_CHUNK, "chunk must split evenly");
 
-template <int KT, int DI, int HT, int RING, bool WZ, bool WI, int WPE>
+template <int KT, int DI, int RING, bool WZ, bool WI, int WPE>
 __global__ __launch_bounds__(64 * kNW) __attribute__((amdgpu_waves_per_eu(WPE)))
 void score_kernel(ScoreArgs a) {
   using G = Geo<KT, DI>;
   constexpr int NW = kNW;
-  __shared__ __attribute__((aligned(16))) unsigned char lds_all[NW][G::TB];
-  __shared__ __attribute__((aligned(16))) float gs[LSA_MAX_LAYERS][64];
+  __shared__ __attribute__((aligned(16))) float qt[LSA_MAX_LAYERS][DI];
   __shared__ __attribute__((aligned(16))) float zacc[NW][kTPW][32];
   __shared__ uint32_t mwords[LSA_MAX_LAYERS][NW * kTPW];
   __shared__ int s_wave[NW];
@@ -163,16 +183,72 @@ void score_kernel(ScoreArgs a) {
   const int lane = threadIdx.x & 63;
   const int n = lane & 31;
   const int half = lane >> 5;
-  unsigned char* lds = lds_all[wave];
   const int b = blockIdx.y;
   const int c = blockIdx.x;
   const int L = a.L;
 
-  for (int i = threadIdx.x; i < L * 64; i += 64 * NW) {
-    const int l = i >> 6, h = i & 63;
-    gs[l][h] = h < a.H ? a.g[((size_t)l * a.B + b) * a.H + h] : 0.f;
+  // qt[l] = sum_h g_h q_h of (layer l, request b), fp32, in one round of
+  // loads (a chain of dependent loads here would queue behind the key streams
+  // of the other blocks on this compute unit).  Thread t takes dims
+  // [8 (t % TPR), +8) of heads t / TPR + NG i; the sums run over a thread's
+  // heads, then over the lanes of its wave with the same dims, then over the
+  // waves in order (through the zacc area, free until the first tile).
+  {
+    constexpr int TPR = DI / 8;              // threads per 16-byte-wide head row
+    constexpr int NG = 64 * NW / TPR;        // head groups
+    constexpr int HPG = (64 + NG - 1) / NG;  // heads per group (H <= 64)
+    const int dg = threadIdx.x % TPR, hg = threadIdx.x / TPR;
+    float* red = &zacc[0][0][0];             // [L][NW][DI] partial sums
+    static_assert(LSA_MAX_LAYERS * NW * DI <= NW * kTPW * 32, "zacc holds the partial sums");
+    for (int l0 = 0; l0 < L; l0 += 4) {      // up to four layers per round of loads
+      u32x4 qv4[4][HPG];
+      float gv[4][HPG];
+#pragma unroll
+      for (int lb = 0; lb < 4; ++lb) {
+        const size_t p = (size_t)min(l0 + lb, L - 1) * a.B + b;
+        const __amdgpu_buffer_rsrc_t qr = buffer(a.q + p * a.H * DI, (uint32_t)a.H * DI * 2);
+        const __amdgpu_buffer_rsrc_t gr = buffer(a.g + p * a.H, (uint32_t)a.H * 4);
+#pragma unroll
+        for (int i = 0; i < HPG; ++i) {
+          const uint32_t h = (uint32_t)(hg + NG * i);   // past H: the range check reads 0
+          qv4[lb][i] = __builtin_bit_cast(
+              u32x4, __builtin_amdgcn_raw_buffer_load_b128(qr, (h * DI + 8 * dg) * 2, 0, 0));
+          gv[lb][i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(gr, h * 4, 0, 0));
+        }
+      }
+#pragma unroll
+      for (int lb = 0; lb < 4; ++lb) {
+        if (l0 + lb >= L) break;
+        float acc[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+#pragma unroll
+        for (int i = 0; i < HPG; ++i)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const uint32_t w = qv4[lb][i][e >> 1];
+            const float qe = __uint_as_float((e & 1) ? (w & 0xFFFF0000u) : (w << 16));
+            acc[e] = fmaf(gv[lb][i], qe, acc[e]);
+          }
+#pragma unroll
+        for (int off = TPR; off < 64; off <<= 1)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[e] += __shfl_xor(acc[e], off, kWave);
+        if (lane < TPR)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) red[((l0 + lb) * NW + wave) * DI + 8 * dg + e] = acc[e];
+      }
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < L * DI; i += 64 * NW) {
+      const int l = i / DI, d = i - l * DI;
+      float acc = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) acc += red[(l * NW + w) * DI + d];
+      qt[l][d] = acc;
+    }
+    __syncthreads();
   }
-  __syncthreads();
 
   const uint32_t N = (uint32_t)a.N;
   const int ntiles = (a.N + 31) >> 5;
@@ -184,19 +260,10 @@ void score_kernel(ScoreArgs a) {
 
   for (int l = 0; l < L && n_my > 0; ++l) {
     const int p = l * a.B + b;
-    // A operand: query rows of (layer l, request b), one head per lane row
-    const uint16_t* qp = a.q + (size_t)p * a.H * DI;
-    bf16x8 af[HT][G::KSTEPS];
+    // this lane's slice of qt: dims [EPC * (lane % LPR), EPC * (lane % LPR + 1))
+    float qv[G::EPC];
 #pragma unroll
-    for (int ht = 0; ht < HT; ++ht) {
-      const int head = ht * 32 + n;
-#pragma unroll
-      for (int s = 0; s < G::KSTEPS; ++s) {
-        u32x4 v = u32x4{0u, 0u, 0u, 0u};
-        if (head < a.H) v = *(const u32x4*)(qp + head * DI + half * G::HALF + 8 * s);
-        af[ht][s] = __builtin_bit_cast(bf16x8, v);
-      }
-    }
+    for (int i = 0; i < G::EPC; ++i) qv[i] = qt[l][G::EPC * (lane % G::LPR) + i];
     const __amdgpu_buffer_rsrc_t kr =
         buffer((const unsigned char*)a.keys[l] + (size_t)b * N * G::RB, N * G::RB);
     const __amdgpu_buffer_rsrc_t sr =
@@ -220,7 +287,7 @@ void score_kernel(ScoreArgs a) {
         const int t = min(t0 + NW * ii, t_last);
         load_tile<KT, DI>(kr, sr, min(t0 + NW * (ii + RING - 1), t_last), lane,
                           ring[(r + RING - 1) % RING]);
-        const float zv = score_tile<KT, DI, HT>(ring[r], lds, lane, af, gs[l], bias);
+        const float zv = score_tile<KT, DI>(ring[r], lane, qv, bias);
         const bool live = ii < n_my;
         const int s_idx = t * 32 + n;
         const bool sel = live && s_idx < a.N && zv >= 0.f;
@@ -283,31 +350,26 @@ void score_kernel(ScoreArgs a) {
   if (threadIdx.x == 0) a.cand_count[(size_t)b * a.nchunks + c] = base;
 }
 
-template <int KT, int DI, int HT, int RING = 2, int WPE = 2>
+template <int KT, int DI, int RING = 2, int WPE = 2>
 hipError_t launch_t(const ScoreArgs& a, hipStream_t s) {
   dim3 grid(a.nchunks, a.B);
   const bool wz = a.z != nullptr, wi = a.I != nullptr;
   if (!wz && !wi)
-    hipLaunchKernelGGL((score_kernel<KT, DI, HT, RING, false, false, WPE>), grid, dim3(64 * kNW), 0, s, a);
+    hipLaunchKernelGGL((score_kernel<KT, DI, RING, false, false, WPE>), grid, dim3(64 * kNW), 0, s, a);
   else if (wz && !wi)
-    hipLaunchKernelGGL((score_kernel<KT, DI, HT, RING, true, false, WPE>), grid, dim3(64 * kNW), 0, s, a);
+    hipLaunchKernelGGL((score_kernel<KT, DI, RING, true, false, WPE>), grid, dim3(64 * kNW), 0, s, a);
   else if (!wz && wi)
-    hipLaunchKernelGGL((score_kernel<KT, DI, HT, RING, false, true, WPE>), grid, dim3(64 * kNW), 0, s, a);
+    hipLaunchKernelGGL((score_kernel<KT, DI, RING, false, true, WPE>), grid, dim3(64 * kNW), 0, s, a);
   else
-    hipLaunchKernelGGL((score_kernel<KT, DI, HT, RING, true, true, WPE>), grid, dim3(64 * kNW), 0, s, a);
+    hipLaunchKernelGGL((score_kernel<KT, DI, RING, true, true, WPE>), grid, dim3(64 * kNW), 0, s, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_score(int dI, lsa_key_dtype kdt, const ScoreArgs& a, hipStream_t s) {
-  const bool two = a.H > 32;
-  if (kdt == LSA_KEY_BF16) {
-    if (dI == 64) return two ? launch_t<0, 64, 2>(a, s) : launch_t<0, 64, 1>(a, s);
-    return two ? launch_t<0, 128, 2>(a, s) : launch_t<0, 128, 1>(a, s);
-  }
-  if (dI == 64) return two ? launch_t<1, 64, 2>(a, s) : launch_t<1, 64, 1>(a, s);
-  return two ? launch_t<1, 128, 2>(a, s) : launch_t<1, 128, 1>(a, s);
+  if (kdt == LSA_KEY_BF16) return dI == 64 ? launch_t<0, 64>(a, s) : launch_t<0, 128>(a, s);
+  return dI == 64 ? launch_t<1, 64>(a, s) : launch_t<1, 128>(a, s);
 }
 
 }  // namespace lsa

@@ -1,4 +1,4 @@
-"""Parity of lsa_score (MFMA contraction + fused epilogue) with the oracle."""
+"""Parity of lsa_score (collapsed-head dot products + fused epilogue) with the oracle."""
 import numpy as np
 import pytest
 import torch
@@ -129,19 +129,20 @@ def test_score_deterministic():
         assert np.array_equal(ia, ib) and np.array_equal(za.view(np.uint32), zb.view(np.uint32))
 
 
-def test_e4m3_widening_is_exact():
-    # every finite e4m3 code, one per key dimension, a one-hot query row:
-    # z must equal the decoded code exactly
-    dI = 128
+@pytest.mark.parametrize("dI", [64, 128])
+def test_e4m3_widening_is_exact(dI):
+    # every finite e4m3 code, each in its own entry at key dimension
+    # (entry % dI) -- so every lane position of a key row is used -- with all
+    # query elements 1 and one head of gate 1: z must equal the decoded code
+    # exactly (the other dimensions are zero)
     codes = np.arange(256, dtype=np.uint8)
     codes = codes[(codes & 0x7F) != 0x7F]                       # drop the two NaNs
+    codes = np.concatenate([codes, codes[::-1]])                # each code at two dimensions
     N = codes.size
     keys = np.zeros((1, N, dI), np.uint8)
-    keys[0, :, 5] = codes
+    keys[0, np.arange(N), np.arange(N) % dI] = codes
     scale = np.ones((1, N), np.float32)
-    qv = np.zeros((1, 1, 1, dI), np.float32)
-    qv[..., 5] = 1.0
-    q = gen.to_bf16_bits(qv)
+    q = gen.to_bf16_bits(np.ones((1, 1, 1, dI), np.float32))
     g = np.ones((1, 1, 1), np.float32)
     z, _, _, _ = _run(q, g, [keys], [scale], np.zeros(1, np.float32))
     want = oracle.e4m3_to_double(codes)

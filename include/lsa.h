@@ -132,7 +132,11 @@ lsa_status lsa_project_query(int L, int B, int D, int H, int dI,
  *              writes; the hot path passes NULL
  *   I_opt      out fp32 [L][B][N] or NULL: sigmoid(z)
  * Limits: 1 <= L <= LSA_MAX_LAYERS, 1 <= B <= 65535, 0 <= N <= 2^24 (N = 0
- * launches nothing), 1 <= H <= 64, dI in {64, 128}.
+ * launches nothing), 1 <= H <= 64, dI in {64, 128}, and the keys of one
+ * (layer, request), N * dI * (2 for bf16, 1 for e4m3) bytes, below 2^31.
+ * The sum over heads is evaluated as one dot product with
+ * sum_h g[l][b][h] q[l][b][h] (fp32), which equals the per-head form up to
+ * rounding.
  */
 lsa_status lsa_score(int L, int B, int N, int H, int dI, lsa_key_dtype kdt,
                      const void* const* keys, const float* const* key_scale,

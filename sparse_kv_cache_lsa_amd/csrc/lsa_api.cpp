@@ -102,6 +102,9 @@ lsa_status lsa_score(int L, int B, int N, int H, int dI, lsa_key_dtype kdt,
   REQUIRE(N >= 0 && N <= (1 << 24), LSA_E_SHAPE, "lsa_score: N=%d not in [0,2^24]", N);
   REQUIRE(H >= 1 && H <= LSA_MAX_HEADS, LSA_E_SHAPE, "lsa_score: H=%d not in [1,64]", H);
   REQUIRE(dI == 64 || dI == 128, LSA_E_SHAPE, "lsa_score: dI=%d not 64 or 128", dI);
+  REQUIRE((int64_t)N * dI * (kdt == LSA_KEY_BF16 ? 2 : 1) < ((int64_t)1 << 31), LSA_E_SHAPE,
+          "lsa_score: keys of one (layer, request) must stay below 2^31 bytes (N=%d, dI=%d)", N,
+          dI);
   REQUIRE(bias, LSA_E_ARG, "lsa_score: null bias array");
   if (N == 0) return LSA_OK;   // nothing to score; outputs are empty
   REQUIRE(keys && q && g && sel_mask && cand_idx && cand_z && cand_count, LSA_E_ARG,

@@ -39,6 +39,9 @@ struct ProjectArgs {
 
 hipError_t launch_project(const ProjectArgs& a, hipStream_t s);
 
+// Compute units of the current device (queried once per device).
+int device_cu_count();
+
 hipError_t launch_select(int B, int nchunks, const int32_t* cand_idx, const float* cand_z,
                          const int32_t* cand_count, int cap, int32_t* surv_idx,
                          float* surv_z, int32_t* surv_count, hipStream_t s);

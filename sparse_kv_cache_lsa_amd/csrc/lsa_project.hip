@@ -172,8 +172,15 @@ __global__ __launch_bounds__(64 * kPW) void project_kernel(ProjectArgs a, int nb
   }
 }
 
+template <int TM>
+void launch_tm(const ProjectArgs& a, int nbs, int BG, hipStream_t s) {
+  hipLaunchKernelGGL((project_kernel<TM>), dim3(nbs, a.L, BG), dim3(64 * kPW), 0, s, a, nbs);
+}
+
+}  // namespace
+
 // Compute units of the current device (queried once per device).
-int cu_count() {
+int device_cu_count() {
   static std::atomic<int> cache[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
@@ -186,13 +193,6 @@ int cu_count() {
   return n;
 }
 
-template <int TM>
-void launch_tm(const ProjectArgs& a, int nbs, int BG, hipStream_t s) {
-  hipLaunchKernelGGL((project_kernel<TM>), dim3(nbs, a.L, BG), dim3(64 * kPW), 0, s, a, nbs);
-}
-
-}  // namespace
-
 hipError_t launch_project(const ProjectArgs& a, hipStream_t s) {
   const int R = a.H * a.dI + a.H;
   const int T = (R + 15) / 16;
@@ -200,7 +200,7 @@ hipError_t launch_project(const ProjectArgs& a, hipStream_t s) {
   // one block per compute unit when the tiles allow it (at most kMaxTiles
   // tiles per block; more blocks otherwise), the tiles split evenly
   const int segs = a.L * BG;
-  int nbs = std::max(1, cu_count() / segs);
+  int nbs = std::max(1, device_cu_count() / segs);
   nbs = std::min(nbs, T);
   nbs = std::max(nbs, (T + kMaxTiles - 1) / kMaxTiles);
   const int tm = (T + nbs - 1) / nbs;

@@ -71,6 +71,8 @@ def test_validation_errors_return_before_launch(lib):
     # too many heads, too many layers
     assert lib.lsa_score(1, 1, 64, 65, 64, 0, arr, None, fake, fake, bias, fake, fake, fake, fake, None, None, None) == _abi.LSA_E_SHAPE
     assert lib.lsa_score(9, 1, 64, 8, 64, 0, arr, None, fake, fake, bias, fake, fake, fake, fake, None, None, None) == _abi.LSA_E_SHAPE
+    # bf16 keys of one (layer, request) at 2^31 bytes: N = 2^23, dI = 128
+    assert lib.lsa_score(1, 1, 1 << 23, 8, 128, 0, arr, None, fake, fake, bias, fake, fake, fake, fake, None, None, None) == _abi.LSA_E_SHAPE
     # e4m3 without scales
     assert lib.lsa_score(1, 1, 64, 8, 64, 1, arr, None, fake, fake, bias, fake, fake, fake, fake, None, None, None) == _abi.LSA_E_ARG
     # null output

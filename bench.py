@@ -48,6 +48,12 @@ def parse():
     p.add_argument("--copy-probe", type=int, default=0,
                    help="also run a plain device copy of this many MiB (counter calibration)")
     p.add_argument("--threads", type=int, default=16)
+    p.add_argument("--rotate", type=int, default=1,
+                   help="cycle the steps over this many copies of every input (keys, scales, "
+                        "weights, hidden states, pool), so that small workloads stream from "
+                        "HBM instead of the 256 MB Infinity Cache")
+    p.add_argument("--no-stream-probe", action="store_true",
+                   help="skip the plain streaming-read reference measurement")
     p.add_argument("--graph", action="store_true",
                    help="time the steps as replays of one captured HIP graph (per-kernel "
                         "times still come from an evented eager pass)")
@@ -88,7 +94,23 @@ def main():
     stream = torch.cuda.current_stream()
     ev = lambda: torch.cuda.Event(enable_timing=True)
 
+    # input copies the steps cycle over (one unless --rotate)
+    def clone(v):
+        if v is None:
+            return None
+        if isinstance(v, (list, tuple)):
+            return [clone(x) for x in v]
+        return v.clone() if isinstance(v, torch.Tensor) else v
+    copies = [(d, pool)] + [(clone(d), pool.clone()) for _ in range(max(1, args.rotate) - 1)]
+    rot_bytes = sum(t.numel() * t.element_size() for t in
+                    [d["h"], pool] + list(d["Wq"]) + list(d["Wg"]) + list(d["keys"]) +
+                    [x for x in (d["scale"] or []) if x is not None]) * len(copies)
+    torch.cuda.synchronize()
+    it = [0]
+
     def step(events=None):
+        d, pool = copies[it[0] % len(copies)]
+        it[0] += 1
         if events is not None:
             events[0].record(stream)
         lsa.lsa_project_query(d["h"], d["Wq"], d["Wg"], buf.q, buf.g, stream=stream)
@@ -198,7 +220,31 @@ def main():
         "kernel_ms_p10_p90": pct,
         "survivor_fraction": float(counts.mean() / w.N),
         "launch": launch,
+        "input_copies": {"count": len(copies), "bytes": rot_bytes},
     }
+
+    if not args.no_stream_probe:
+        # reference: a plain streaming read of the same byte count on this GPU
+        # (row-wise max over an fp32 buffer, torch's own reduction kernel)
+        nrow = max(1, key_bytes // 4096)
+        x = torch.ones((nrow, 1024), dtype=torch.float32, device=dev)
+        for _ in range(2):
+            x.amax(dim=1)
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(10):
+            e0, e1 = ev(), ev()
+            e0.record(stream)
+            x.amax(dim=1)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        pms = float(np.median(ts))
+        pgbs = x.numel() * 4 / (pms * 1e-3) / 1e9
+        result["stream_probe"] = {"kernel": "torch amax over rows (plain streaming read)",
+                                  "bytes": x.numel() * 4, "ms": pms, "GB/s": pgbs,
+                                  "score_frac_of_probe": achieved / pgbs}
+        del x
 
     if args.copy_probe:
         # plain copy of known size for hardware-counter calibration: the row
@@ -351,10 +397,60 @@ def cpu_baseline(w, inp, budget_s):
         done += 1
         b += 1
     el = time.perf_counter() - t0
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")),
+                         "unknown")
+    except OSError:
+        pass
     return {"value": done * w.L * w.N / el, "unit": "(request, layer, entry) triples/s",
             "cores": oracle.num_threads(), "kind": "oracle",
             "sample": f"{done} of {w.B} requests x {w.L} layers x {w.N} entries "
-                      f"(project+score+threshold+OR/compact+top-k), {el:.1f}s"}
+                      f"(project+score+threshold+OR/compact+top-k), {el:.1f}s",
+            "cpu_model": model, "nproc": os.cpu_count(),
+            "single_thread_tiny": oracle_tiny_single_thread()}
+
+
+_TINY_ORACLE = r"""
+import json, sys, time
+sys.path.insert(0, sys.argv[1]); sys.path.insert(0, sys.argv[1] + "/tests")
+import lsa_inputs as gen
+from oracle import oracle
+w = gen.WORKLOADS["tiny"]
+inp = gen.indexer_inputs(w, gen.load_calibration(w), threads=1)
+oracle._load()
+oracle.set_num_threads(1)
+t0 = time.perf_counter(); reps = 0
+while reps < 3 or time.perf_counter() - t0 < 1.0:
+    for b in range(w.B):
+        zs = []
+        for l in range(w.L):
+            q, g = oracle.project(inp.h[b], inp.Wq[l], inp.Wg[l], w.H, w.dI)
+            zs.append(oracle.score(inp.keys[l][b], None if inp.scale[l] is None else inp.scale[l][b],
+                                   q, g, float(inp.bias[l])))
+        z = __import__("numpy").stack(zs)
+        surv, zstar, _ = oracle.merge_compact(oracle.threshold(z), z)
+        oracle.topk(surv, zstar, w.k)
+    reps += 1
+el = time.perf_counter() - t0
+print(json.dumps({"value": reps * w.B * w.L * w.N / el, "unit": "(request, layer, entry) triples/s",
+                  "threads": oracle.num_threads(), "repeats": reps, "seconds": el}))
+"""
+
+
+def oracle_tiny_single_thread():
+    """The oracle on the tiny workload (1 request, 1 layer, 4096 entries) with
+    one OpenMP thread, in a child process (the thread count is fixed when the
+    OpenMP runtime starts)."""
+    import subprocess
+    env = dict(os.environ, OMP_NUM_THREADS="1")
+    try:
+        r = subprocess.run([sys.executable, "-c", _TINY_ORACLE, os.path.dirname(os.path.abspath(__file__))],
+                           env=env, capture_output=True, text=True, timeout=120)
+        return json.loads(r.stdout.strip().splitlines()[-1])
+    except Exception as e:   # reported, never fatal for the GPU figures
+        return {"error": str(e)[:200]}
 
 
 if __name__ == "__main__":

@@ -21,6 +21,15 @@ int lsa_or_num_threads(void) {
 #endif
 }
 
+/* Thread count of the parallel loops (timing the oracle on one core). */
+void lsa_or_set_num_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
 int lsa_or_trigger_due(int64_t t, int tau) {
   if (t < 0 || tau <= 0) return 0;
   return (t % tau) == 0;

@@ -123,6 +123,7 @@ double lsa_or_focal_bce_loss64(int Q, int64_t N, int D, int H, int dI,
 int lsa_or_trigger_due(int64_t t, int tau);
 
 int lsa_or_num_threads(void);
+void lsa_or_set_num_threads(int n);
 
 #ifdef __cplusplus
 }

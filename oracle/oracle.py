@@ -67,6 +67,7 @@ def _load():
         "lsa_or_focal_bce_grad": (f64, [i32, i64, i32, i32, i32, f64, P, P, P, f64, P, P, P, P]),
         "lsa_or_focal_bce_loss64": (f64, [i32, i64, i32, i32, i32, f64, P, P, P, f64, P, P]),
         "lsa_or_num_threads": (i32, []),
+        "lsa_or_set_num_threads": (None, [i32]),
         "lsa_or_trigger_due": (i32, [i64, i32]),
     }
     for name, (res, args) in sig.items():
@@ -120,6 +121,11 @@ def trigger_due(t: int, tau: int) -> bool:
 
 def num_threads() -> int:
     return _load().lsa_or_num_threads()
+
+
+def set_num_threads(n: int) -> None:
+    """Threads of the oracle's parallel loops (for timing on one core)."""
+    _load().lsa_or_set_num_threads(int(n))
 
 
 # ---- O1 projection ----------------------------------------------------------

@@ -166,15 +166,17 @@ __device__ __forceinline__ float score_tile(const TileRegs<KT, DI>& r, int lane,
 // So the kernel writes a few contiguous runs per block instead of one line per
 // tile; writes interleaved with the key stream cost far more HBM time than
 // their bytes.  RING: register-ring depth (RING-1 tiles in flight per wave).
-constexpr int kNW = 4;
-constexpr int kTPW = LSA_CAND_CHUNK / 32 / kNW;    // tiles per wave and layer
-static_assert(kTPW * 32 * kNW == LSA_CAND_CHUNK, "chunk must split evenly");
+// NW = 4 wavefronts per block; 16 when the grid has fewer blocks than twice
+// the compute units (few requests, short lists), so that a short list still
+// spreads over many wavefronts.
+constexpr int kSetupW = 4;   // wavefronts that form q~ (their layout below)
 
-template <int KT, int DI, int RING, bool WZ, bool WI, int WPE>
-__global__ __launch_bounds__(64 * kNW) __attribute__((amdgpu_waves_per_eu(WPE)))
+template <int KT, int DI, int RING, bool WZ, bool WI, int WPE, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE)))
 void score_kernel(ScoreArgs a) {
   using G = Geo<KT, DI>;
-  constexpr int NW = kNW;
+  constexpr int kTPW = LSA_CAND_CHUNK / 32 / NW;   // tiles per wave and layer
+  static_assert(kTPW * 32 * NW == LSA_CAND_CHUNK, "chunk must split evenly");
   __shared__ __attribute__((aligned(16))) float qt[LSA_MAX_LAYERS][DI];
   __shared__ __attribute__((aligned(16))) float zacc[NW][kTPW][32];
   __shared__ uint32_t mwords[LSA_MAX_LAYERS][NW * kTPW];
@@ -192,15 +194,16 @@ void score_kernel(ScoreArgs a) {
   // of the other blocks on this compute unit).  Thread t takes dims
   // [8 (t % TPR), +8) of heads t / TPR + NG i; the sums run over a thread's
   // heads, then over the lanes of its wave with the same dims, then over the
-  // waves in order (through the zacc area, free until the first tile).
+  // first kSetupW waves in order (through the zacc area, free until the
+  // first tile).
   {
     constexpr int TPR = DI / 8;              // threads per 16-byte-wide head row
-    constexpr int NG = 64 * NW / TPR;        // head groups
+    constexpr int NG = 64 * kSetupW / TPR;   // head groups
     constexpr int HPG = (64 + NG - 1) / NG;  // heads per group (H <= 64)
     const int dg = threadIdx.x % TPR, hg = threadIdx.x / TPR;
-    float* red = &zacc[0][0][0];             // [L][NW][DI] partial sums
-    static_assert(LSA_MAX_LAYERS * NW * DI <= NW * kTPW * 32, "zacc holds the partial sums");
-    for (int l0 = 0; l0 < L; l0 += 4) {      // up to four layers per round of loads
+    float* red = &zacc[0][0][0];             // [L][kSetupW][DI] partial sums
+    static_assert(LSA_MAX_LAYERS * kSetupW * DI <= NW * kTPW * 32, "zacc holds the partial sums");
+    for (int l0 = 0; l0 < L && wave < kSetupW; l0 += 4) {   // up to four layers per round of loads
       u32x4 qv4[4][HPG];
       float gv[4][HPG];
 #pragma unroll
@@ -236,7 +239,7 @@ void score_kernel(ScoreArgs a) {
           for (int e = 0; e < 8; ++e) acc[e] += __shfl_xor(acc[e], off, kWave);
         if (lane < TPR)
 #pragma unroll
-          for (int e = 0; e < 8; ++e) red[((l0 + lb) * NW + wave) * DI + 8 * dg + e] = acc[e];
+          for (int e = 0; e < 8; ++e) red[((l0 + lb) * kSetupW + wave) * DI + 8 * dg + e] = acc[e];
       }
     }
     __syncthreads();
@@ -244,7 +247,7 @@ void score_kernel(ScoreArgs a) {
       const int l = i / DI, d = i - l * DI;
       float acc = 0.f;
 #pragma unroll
-      for (int w = 0; w < NW; ++w) acc += red[(l * NW + w) * DI + d];
+      for (int w = 0; w < kSetupW; ++w) acc += red[(l * kSetupW + w) * DI + d];
       qt[l][d] = acc;
     }
     __syncthreads();
@@ -350,19 +353,25 @@ void score_kernel(ScoreArgs a) {
   if (threadIdx.x == 0) a.cand_count[(size_t)b * a.nchunks + c] = base;
 }
 
-template <int KT, int DI, int RING = 2, int WPE = 2>
-hipError_t launch_t(const ScoreArgs& a, hipStream_t s) {
+template <int KT, int DI, int RING, int WPE, int NW>
+hipError_t launch_nw(const ScoreArgs& a, hipStream_t s) {
   dim3 grid(a.nchunks, a.B);
   const bool wz = a.z != nullptr, wi = a.I != nullptr;
   if (!wz && !wi)
-    hipLaunchKernelGGL((score_kernel<KT, DI, RING, false, false, WPE>), grid, dim3(64 * kNW), 0, s, a);
+    hipLaunchKernelGGL((score_kernel<KT, DI, RING, false, false, WPE, NW>), grid, dim3(64 * NW), 0, s, a);
   else if (wz && !wi)
-    hipLaunchKernelGGL((score_kernel<KT, DI, RING, true, false, WPE>), grid, dim3(64 * kNW), 0, s, a);
+    hipLaunchKernelGGL((score_kernel<KT, DI, RING, true, false, WPE, NW>), grid, dim3(64 * NW), 0, s, a);
   else if (!wz && wi)
-    hipLaunchKernelGGL((score_kernel<KT, DI, RING, false, true, WPE>), grid, dim3(64 * kNW), 0, s, a);
+    hipLaunchKernelGGL((score_kernel<KT, DI, RING, false, true, WPE, NW>), grid, dim3(64 * NW), 0, s, a);
   else
-    hipLaunchKernelGGL((score_kernel<KT, DI, RING, true, true, WPE>), grid, dim3(64 * kNW), 0, s, a);
+    hipLaunchKernelGGL((score_kernel<KT, DI, RING, true, true, WPE, NW>), grid, dim3(64 * NW), 0, s, a);
   return hipGetLastError();
+}
+
+template <int KT, int DI, int RING = 2, int WPE = 2>
+hipError_t launch_t(const ScoreArgs& a, hipStream_t s) {
+  if ((int64_t)a.nchunks * a.B < 2 * device_cu_count()) return launch_nw<KT, DI, RING, 1, 16>(a, s);
+  return launch_nw<KT, DI, RING, WPE, 4>(a, s);
 }
 
 }  // namespace

@@ -90,6 +90,8 @@ CASES = [
     (3, 2, 5000, 64, 128, False),
     (3, 2, 5000, 64, 128, True),
     (2, 3, 8192 + 33, 17, 128, True),
+    # enough (chunk, request) blocks for the 4-wavefront launch, ragged last chunk
+    (1, 128, 4 * 4096 + 1, 8, 64, True),
 ]
 
 

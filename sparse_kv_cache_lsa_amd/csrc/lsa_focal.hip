@@ -23,9 +23,9 @@
 // k0+4..k0+7), which leaves every dot product unchanged.
 //
 // Kernels (one stream, in order):
-//   1 project   qa[t][r] = ([W_q; W_g] h_t)_r            (W read once, D split over blocks)
-//   2 collapse  g = softplus(gate rows), qe_t, gT[h][t]
-//   3 transpose K -> KT [dI][Np], h -> hT [D][64] (contraction axes contiguous)
+//   1 project   partials of ([W_q; W_g] h_t)_r per slice of D (W read once)
+//   2 collapse  slice sums in order; g = softplus(gate rows), qe_t, gT[h][t]
+//   3 transpose K -> KT [dI][Np], h -> hT [D][64] in one launch (contraction axes contiguous)
 //   4 logits    z = K qe^T + b; loss terms; delta = dloss/dz -> [Q][Np]
 //   5 grad      partial G over 128-entry chunks
 //   6 reduce    GT[i][t] = sum of partials, loss = sum / (Q N) (fixed orders)
@@ -38,6 +38,7 @@ namespace {
 
 constexpr int kQP = 64;      // padded query count (rows of the small operands)
 constexpr int kChunk = 128;  // entries per partial-gradient block
+constexpr int kProjTR = 2;   // 32-row weight tiles per projection wave
 
 __device__ __forceinline__ f32x4 bf16x4_to_f32(uint2 raw) {
   f32x4 r;
@@ -113,6 +114,18 @@ __device__ __forceinline__ f32x16 mfma_split(const Split3& a, bf16x8 b, f32x16 c
 __device__ __forceinline__ int acc_row(int rr, int half) { return (rr & 3) + 4 * half + 8 * (rr >> 2); }
 
 __device__ __forceinline__ float sigmoid_f(float x) { return 1.f / (1.f + __expf(-x)); }
+
+// sigmoid(-u)^gamma: repeated products for whole gamma in [1, 8] (a few ulps,
+// where powf costs a logarithm and an exponential per element), powf else.
+__device__ __forceinline__ float focal_mod(float qu, float gamma, int igamma) {
+  if (gamma == 0.f) return 1.f;
+  if (igamma > 0) {
+    float r = qu;
+    for (int i = 1; i < igamma; ++i) r *= qu;
+    return r;
+  }
+  return powf(qu, gamma);
+}
 __device__ __forceinline__ float softplus_f(float x) { return fmaxf(x, 0.f) + log1pf(__expf(-fabsf(x))); }
 
 // ---------------------------------------------------------------- 1 project
@@ -120,128 +133,171 @@ __device__ __forceinline__ float softplus_f(float x) { return fmaxf(x, 0.f) + lo
 // a block split the block's slice again; each wave keeps a 32-row x 64-query
 // tile.  Block (tile, ks) writes its partial sums to qp[ks][t][r]; splitting D
 // over KS blocks keeps enough loads in flight to stream W at full rate.
+template <int TR>   // 32-row tiles per wave (they share the hidden-state loads)
 __global__ __launch_bounds__(256) void fproj_kernel(int Q, int D, int HdI, int H,
                                                     const float* __restrict__ Wq,
                                                     const float* __restrict__ Wg,
                                                     const uint16_t* __restrict__ h,
                                                     float* __restrict__ qp) {
-  __shared__ float red[4][2][16][64];
+  __shared__ float red[4][2 * TR][16][64];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n = lane & 31, half = lane >> 5;
   const int R = HdI + H;
-  const int KS = gridDim.y;
   // a 32-row tile lies wholly in W_q or wholly in W_g (H*dI is a multiple of
   // 32); rows past the gate rows read 0 through the buffer range check
-  const bool gate_tile = blockIdx.x * 32 >= HdI;
-  const __amdgpu_buffer_rsrc_t ra = gate_tile ? rsrc(Wg, (size_t)H * D * 4)
-                                              : rsrc(Wq, (size_t)HdI * D * 4);
-  const int rl = blockIdx.x * 32 + n - (gate_tile ? HdI : 0);
+  __amdgpu_buffer_rsrc_t ra[TR];
+  uint32_t aoff[TR];
+#pragma unroll
+  for (int i = 0; i < TR; ++i) {
+    const int r0 = (blockIdx.x * TR + i) * 32;
+    const bool gate_tile = r0 >= HdI;
+    ra[i] = gate_tile ? rsrc(Wg, (size_t)H * D * 4) : rsrc(Wq, (size_t)HdI * D * 4);
+    aoff[i] = (uint32_t)(r0 + n - (gate_tile ? HdI : 0)) * D * 4;
+  }
   const __amdgpu_buffer_rsrc_t rb = rsrc(h, (size_t)Q * D * 2);
+  const int KS = gridDim.y;
   const int kq = D / (4 * KS);
   const int kbeg = (blockIdx.y * 4 + wave) * kq, kend = kbeg + kq;
-  const uint32_t aoff = (uint32_t)rl * D * 4, b0off = (uint32_t)n * D * 2,
-                 b1off = (uint32_t)(n + 32) * D * 2;
+  const uint32_t b0off = (uint32_t)n * D * 2, b1off = (uint32_t)(n + 32) * D * 2;
   // v_mfma_f32_32x32x16_bf16, two steps per 32 k: lane (m, half) holds
   // k = k0 + 16 half + 8 s .. +7 of row m in step s, so each lane reads 64
   // contiguous weight bytes (the two halves of a row fill a 128-byte line)
   // and 32 bytes of each hidden state.  The next 32 k are loaded before the
   // current ones are split and multiplied.
   struct Stage {
-    f32x4 w[4];
+    f32x4 w[TR][4];
     bf16x8 x0[2], x1[2];
   };
   auto load_stage = [&](int k, Stage& st) {
     const int kk = k + 16 * half;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) st.w[j] = buf_f32x4(ra, aoff + (kk + 4 * j) * 4);
+    for (int i = 0; i < TR; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) st.w[i][j] = buf_f32x4(ra[i], aoff[i] + (kk + 4 * j) * 4);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       st.x0[j] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rb, b0off + (kk + 8 * j) * 2, 0, 0));
       st.x1[j] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rb, b1off + (kk + 8 * j) * 2, 0, 0));
     }
   };
-  f32x16 acc0 = {}, acc1 = {};
+  f32x16 acc[TR][2] = {};
   Stage cur, nxt;
   load_stage(kbeg, cur);
   for (int k = kbeg; k < kend; k += 32) {
     load_stage(min(k + 32, kend - 32), nxt);   // the last pass re-reads its own k (cached)
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      const Split3 a = split3(cur.w[2 * st], cur.w[2 * st + 1]);
-      acc0 = mfma_split(a, cur.x0[st], acc0);
-      acc1 = mfma_split(a, cur.x1[st], acc1);
-    }
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int i = 0; i < TR; ++i) {
+        const Split3 a = split3(cur.w[i][2 * st], cur.w[i][2 * st + 1]);
+        acc[i][0] = mfma_split(a, cur.x0[st], acc[i][0]);
+        acc[i][1] = mfma_split(a, cur.x1[st], acc[i][1]);
+      }
     cur = nxt;
   }
 #pragma unroll
-  for (int rr = 0; rr < 16; ++rr) {
-    red[wave][0][rr][lane] = acc0[rr];
-    red[wave][1][rr][lane] = acc1[rr];
-  }
+  for (int i = 0; i < TR; ++i)
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) {
+      red[wave][2 * i][rr][lane] = acc[i][0][rr];
+      red[wave][2 * i + 1][rr][lane] = acc[i][1][rr];
+    }
   __syncthreads();
   float* out = qp + (size_t)blockIdx.y * kQP * R;
-  for (int e = threadIdx.x; e < 2 * 16 * 64; e += 256) {
-    const int j = e >> 10, rr = (e >> 6) & 15, l = e & 63;
-    const float v = red[0][j][rr][l] + red[1][j][rr][l] + red[2][j][rr][l] + red[3][j][rr][l];
+  for (int e = threadIdx.x; e < 2 * TR * 16 * 64; e += 256) {
+    const int ij = e >> 10, rr = (e >> 6) & 15, l = e & 63;
+    const int i = ij >> 1, j = ij & 1;
+    const float v = red[0][ij][rr][l] + red[1][ij][rr][l] + red[2][ij][rr][l] + red[3][ij][rr][l];
     const int t = 32 * j + (l & 31);
-    const int row = blockIdx.x * 32 + acc_row(rr, l >> 5);
+    const int row = (blockIdx.x * TR + i) * 32 + acc_row(rr, l >> 5);
     if (t < Q && row < R) out[(size_t)t * R + row] = v;
   }
 }
 
-// qa[t][r] = sum over the KS slices in order (one thread per element)
-__global__ __launch_bounds__(256) void fproj_sum_kernel(int n, int KS, size_t slice,
-                                                        const float* __restrict__ qp,
-                                                        float* __restrict__ qa) {
-  const int e = blockIdx.x * 256 + threadIdx.x;
-  if (e >= n) return;
-  float acc = qp[e];
-  for (int ks = 1; ks < KS; ++ks) acc += qp[ks * slice + e];
-  qa[e] = acc;
-}
-
 // ---------------------------------------------------------------- 2 collapse
-// grid: kQP queries; block: 128 threads.  Rows t >= Q get zeros.
-__global__ __launch_bounds__(128) void fcollapse_kernel(int Q, int H, int dI,
-                                                        const float* __restrict__ qa,
+// qa[t][r] = sum of the KS slice partials in slice order, formed where needed.
+// grid: (kQP queries, dI/32 dim groups); block: 256 threads.  Each thread sums
+// the partials of 8 (head, dim) pairs of the group with all loads in flight
+// (into LDS), then one thread per dim runs the gate-weighted sum over heads in
+// head order.  Rows t >= Q get zeros; the gates are formed by every block and
+// written by group 0.
+__global__ __launch_bounds__(256) void fcollapse_kernel(int Q, int H, int dI, int KS,
+                                                        const float* __restrict__ qp,
                                                         float* __restrict__ gT,
                                                         float* __restrict__ qe) {
   __shared__ float gs[64];
+  __shared__ float qs[64][33];
   const int t = blockIdx.x;
   const int R = H * dI + H;
+  const size_t slice = (size_t)kQP * R;
+  const size_t rowb = (size_t)t * R;
   const bool live = t < Q;
+  const int i0 = blockIdx.y * 32;
+  // (head, dim) pairs p = threadIdx.x + 256 u, u < 8: head p / 32, dim i0 + p % 32;
+  // threads 0..63 also take the gate row of head threadIdx.x
+  float acc[9];
+#pragma unroll
+  for (int u = 0; u < 9; ++u) acc[u] = 0.f;
+  if (live) {
+    for (int ks = 0; ks < KS; ++ks) {
+      const float* base = qp + ks * slice + rowb;
+      float v[9];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int pr = threadIdx.x + 256 * u, hh = pr >> 5, i = i0 + (pr & 31);
+        v[u] = (hh < H && i < dI) ? base[hh * dI + i] : 0.f;
+      }
+      v[8] = threadIdx.x < H ? base[H * dI + threadIdx.x] : 0.f;
+#pragma unroll
+      for (int u = 0; u < 9; ++u) acc[u] = ks == 0 ? v[u] : acc[u] + v[u];
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int pr = threadIdx.x + 256 * u;
+    qs[pr >> 5][pr & 31] = acc[u];
+  }
   if (threadIdx.x < 64) {
-    float g = 0.f;
-    if (live && threadIdx.x < H) g = softplus_f(qa[(size_t)t * R + H * dI + threadIdx.x]);
+    const float g = (live && threadIdx.x < H) ? softplus_f(acc[8]) : 0.f;
     gs[threadIdx.x] = g;
-    if (threadIdx.x < H) gT[threadIdx.x * kQP + t] = g;
+    if (blockIdx.y == 0 && threadIdx.x < H) gT[threadIdx.x * kQP + t] = g;
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < dI; i += 128) {
-    float acc = 0.f;
+  const int i = i0 + threadIdx.x;
+  if (threadIdx.x < 32 && i < dI) {
+    float a = 0.f;
     if (live)
-      for (int hh = 0; hh < H; ++hh) acc = fmaf(gs[hh], qa[(size_t)t * R + hh * dI + i], acc);
-    qe[t * dI + i] = acc;
+      for (int hh = 0; hh < H; ++hh) a = fmaf(gs[hh], qs[hh][threadIdx.x], a);
+    qe[t * dI + i] = a;
   }
 }
 
 // ---------------------------------------------------------------- 3 transpose
-// out[c][r] = in[r][c] for r < rows, 0 for rows <= r < out_ld (bf16 bits).
-__global__ __launch_bounds__(256) void ftranspose_kernel(const uint16_t* __restrict__ in, int rows,
-                                                         int cols, uint16_t* __restrict__ out,
-                                                         int out_ld) {
+// Two jobs in one launch (blocks [0, nb0) job 0, the rest job 1); per job
+// out[c][r] = in[r][c] for r < rows, 0 for rows <= r < out_ld (bf16 bits),
+// in 64 x 64 tiles, ntx tiles along r.
+struct TransposeJob {
+  const uint16_t* in;
+  uint16_t* out;
+  int rows, cols, out_ld, ntx;
+};
+
+__global__ __launch_bounds__(256) void ftranspose_kernel(TransposeJob j0, TransposeJob j1, int nb0) {
   __shared__ uint16_t tile[64][65];
-  const int r0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
+  const bool second = (int)blockIdx.x >= nb0;
+  const TransposeJob jb = second ? j1 : j0;
+  const int b = second ? (int)blockIdx.x - nb0 : (int)blockIdx.x;
+  const int r0 = (b % jb.ntx) * 64, c0 = (b / jb.ntx) * 64;
   for (int e = threadIdx.x; e < 64 * 64; e += 256) {
     const int rr = e >> 6, cc = e & 63;
     const int r = r0 + rr, c = c0 + cc;
-    tile[rr][cc] = (r < rows && c < cols) ? in[(size_t)r * cols + c] : (uint16_t)0;
+    tile[rr][cc] = (r < jb.rows && c < jb.cols) ? jb.in[(size_t)r * jb.cols + c] : (uint16_t)0;
   }
   __syncthreads();
   for (int e = threadIdx.x; e < 64 * 64; e += 256) {
     const int cc = e >> 6, rr = e & 63;
     const int r = r0 + rr, c = c0 + cc;
-    if (c < cols && r < out_ld) out[(size_t)c * out_ld + r] = tile[rr][cc];
+    if (c < jb.cols && r < jb.out_ld) jb.out[(size_t)c * jb.out_ld + r] = tile[rr][cc];
   }
 }
 
@@ -285,6 +341,8 @@ __global__ __launch_bounds__(256) void flogits_kernel(int Q, int N, int Np, floa
     const int t = t0 + acc_row(rr, half);
     yv[rr] = __builtin_amdgcn_raw_buffer_load_b8(rl, s < N ? (uint32_t)t * N + s : kFar, 0, 0);
   }
+  // gamma as a whole number in [1, 8], else 0 (uniform)
+  const int igamma = (gamma >= 1.f && gamma <= 8.f && gamma == floorf(gamma)) ? (int)gamma : 0;
   double lsum = 0.0;
 #pragma unroll
   for (int rr = 0; rr < 16; ++rr) {
@@ -296,7 +354,7 @@ __global__ __launch_bounds__(256) void flogits_kernel(int Q, int N, int Np, floa
     const float nll = softplus_f(-u);          // -log sigmoid(u)
     const float pu = sigmoid_f(u);
     const float qu = sigmoid_f(-u);
-    const float mod = gamma == 0.f ? 1.f : powf(qu, gamma);
+    const float mod = focal_mod(qu, gamma, igamma);
     if (valid) lsum += (double)nll + (double)(mod * nll);
     const float dbce = sigmoid_f(z) - (float)y;
     const float dfl_du = mod * (-gamma * pu * nll - qu);
@@ -370,8 +428,12 @@ __global__ __launch_bounds__(256) void fgrad_kernel(int Q, int Np, const float* 
 // are added in a fixed order.
 __global__ __launch_bounds__(256) void freduce_kernel(int Q, int DI, int nchunks,
                                                       const float* __restrict__ Gp,
-                                                      float* __restrict__ GT) {
+                                                      float* __restrict__ GT, int nloss,
+                                                      double inv_qn,
+                                                      const double* __restrict__ loss_part,
+                                                      float* __restrict__ loss) {
   __shared__ float part[4][64];
+  __shared__ double lred[256];
   const int slice = threadIdx.x >> 6, j = threadIdx.x & 63;
   const int e = blockIdx.x * 64 + j;          // e = t * DI + i
   const size_t stride = (size_t)kQP * DI;
@@ -392,26 +454,22 @@ __global__ __launch_bounds__(256) void freduce_kernel(int Q, int DI, int nchunks
     const int t = e / DI, i = e % DI;
     GT[i * kQP + t] = t < Q ? v : 0.f;
   }
-}
-
-// loss = (sum of the block partials) / (Q N), summed in a fixed tree order
-__global__ __launch_bounds__(256) void floss_kernel(int nloss, double inv_qn,
-                                                    const double* __restrict__ loss_part,
-                                                    float* __restrict__ loss) {
-  __shared__ double red[256];
-  double acc = 0.0;
-  for (int b = threadIdx.x; b < nloss; b += 256) acc += loss_part[b];
-  red[threadIdx.x] = acc;
-  __syncthreads();
-  for (int w = 128; w > 0; w >>= 1) {
-    if (threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+  // loss = (sum of the logits blocks' partials) / (Q N), in a fixed tree order
+  if (blockIdx.x == 0) {
+    double acc = 0.0;
+    for (int b = threadIdx.x; b < nloss; b += 256) acc += loss_part[b];
+    lred[threadIdx.x] = acc;
     __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+      if (threadIdx.x < w) lred[threadIdx.x] += lred[threadIdx.x + w];
+      __syncthreads();
+    }
+    if (threadIdx.x == 0) loss[0] = (float)(lred[0] * inv_qn);
   }
-  if (threadIdx.x == 0) loss[0] = (float)(red[0] * inv_qn);
 }
 
 // ---------------------------------------------------------------- 7 dW
-// grid: (ceil(D/256), HdI/32); wave w takes 64 columns; contraction over the
+// grid: (ceil(D/512), HdI/32); wave w takes 128 columns; contraction over the
 // kQP padded queries: A[(h,i)][t] = gT[h][t] GT[i][t], B[d][t] = hT[d][t].
 template <int DI>
 __global__ __launch_bounds__(256) void fdw_kernel(int D, const float* __restrict__ gT,
@@ -421,32 +479,31 @@ __global__ __launch_bounds__(256) void fdw_kernel(int D, const float* __restrict
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n = lane & 31, half = lane >> 5;
   const int row = blockIdx.y * 32 + n;             // (h, i) = (row / DI, row % DI)
-  const int c0 = blockIdx.x * 256 + wave * 64;
+  const int c0 = blockIdx.x * 512 + wave * 128;
   if (c0 >= D) return;
   const float* ga = gT + (row / DI) * kQP;
   const float* Ga = GT + (row % DI) * kQP;
-  const uint16_t* b0 = hT + (size_t)(c0 + n) * kQP;
-  const uint16_t* b1 = hT + (size_t)(c0 + 32 + n) * kQP;
-  f32x16 acc0 = {}, acc1 = {};
+  f32x16 acc[4] = {};
 #pragma unroll
   for (int k = 0; k < kQP; k += 16) {
     const int kk = k + 8 * half;
     const Split3 a = split3(*(const f32x4*)(ga + kk) * *(const f32x4*)(Ga + kk),
                             *(const f32x4*)(ga + kk + 4) * *(const f32x4*)(Ga + kk + 4));
-    acc0 = mfma_split(a, *(const bf16x8*)(b0 + kk), acc0);
-    acc1 = mfma_split(a, *(const bf16x8*)(b1 + kk), acc1);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      acc[j] = mfma_split(a, *(const bf16x8*)(hT + (size_t)(c0 + 32 * j + n) * kQP + kk), acc[j]);
   }
 #pragma unroll
   for (int rr = 0; rr < 16; ++rr) {
     const size_t r = (size_t)blockIdx.y * 32 + acc_row(rr, half);
-    __builtin_nontemporal_store(acc0[rr], dW + r * D + c0 + n);
-    __builtin_nontemporal_store(acc1[rr], dW + r * D + c0 + 32 + n);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (c0 + 32 * j < D) __builtin_nontemporal_store(acc[j][rr], dW + r * D + c0 + 32 * j + n);
   }
 }
 
 struct FocalWs {
   float* qp;
-  float* qa;
   float* gT;
   float* qe;
   uint16_t* KT;
@@ -478,7 +535,6 @@ FocalWs carve(void* base, int Q, int N, int D, int H, int dI) {
     return (void*)p;
   };
   w.qp = (float*)take((size_t)proj_slices(D) * kQP * R * 4);
-  w.qa = (float*)take((size_t)kQP * R * 4);
   w.gT = (float*)take((size_t)64 * kQP * 4);
   w.qe = (float*)take((size_t)kQP * dI * 4);
   w.KT = (uint16_t*)take((size_t)dI * Np * 2);
@@ -514,19 +570,18 @@ hipError_t launch_focal(int Q, int N, int D, int H, int dI, float gamma, const u
     if (e != hipSuccess) return e;           \
   } while (0)
   const int KS = proj_slices(D);
-  hipLaunchKernelGGL(fproj_kernel, dim3((R + 31) / 32, KS), dim3(256), 0, s, Q, D, HdI, H, Wq, Wg,
-                     h, w.qp);
+  hipLaunchKernelGGL((fproj_kernel<kProjTR>), dim3((R + 32 * kProjTR - 1) / (32 * kProjTR), KS),
+                     dim3(256), 0, s, Q, D, HdI, H, Wq, Wg, h, w.qp);
   FOCAL_CHECK();
-  hipLaunchKernelGGL(fproj_sum_kernel, dim3((Q * R + 255) / 256), dim3(256), 0, s, Q * R, KS,
-                     (size_t)kQP * R, w.qp, w.qa);
+  hipLaunchKernelGGL(fcollapse_kernel, dim3(kQP, (dI + 31) / 32), dim3(256), 0, s, Q, H, dI, KS,
+                     w.qp, w.gT, w.qe);
   FOCAL_CHECK();
-  hipLaunchKernelGGL(fcollapse_kernel, dim3(kQP), dim3(128), 0, s, Q, H, dI, w.qa, w.gT, w.qe);
-  FOCAL_CHECK();
-  hipLaunchKernelGGL(ftranspose_kernel, dim3((Np + 63) / 64, (dI + 63) / 64), dim3(256), 0, s, K,
-                     N, dI, w.KT, Np);
-  FOCAL_CHECK();
-  hipLaunchKernelGGL(ftranspose_kernel, dim3(1, (D + 63) / 64), dim3(256), 0, s, h, Q, D, w.hT,
-                     kQP);
+  {
+    const TransposeJob jk{K, w.KT, N, dI, Np, (Np + 63) / 64};
+    const TransposeJob jh{h, w.hT, Q, D, kQP, 1};
+    const int nbk = jk.ntx * ((dI + 63) / 64), nbh = (D + 63) / 64;
+    hipLaunchKernelGGL(ftranspose_kernel, dim3(nbk + nbh), dim3(256), 0, s, jk, jh, nbk);
+  }
   FOCAL_CHECK();
   if (dI == 64)
     hipLaunchKernelGGL((flogits_kernel<64>), dim3(nloss), dim3(256), 0, s, Q, N, Np, gamma, bias,
@@ -543,11 +598,9 @@ hipError_t launch_focal(int Q, int N, int D, int H, int dI, float gamma, const u
                        w.Gp);
   FOCAL_CHECK();
   hipLaunchKernelGGL(freduce_kernel, dim3(kQP * dI / 64), dim3(256), 0, s, Q, dI, nchunks, w.Gp,
-                     w.GT);
+                     w.GT, nloss, inv_qn, w.loss_part, loss);
   FOCAL_CHECK();
-  hipLaunchKernelGGL(floss_kernel, dim3(1), dim3(256), 0, s, nloss, inv_qn, w.loss_part, loss);
-  FOCAL_CHECK();
-  const dim3 gdw((D + 255) / 256, HdI / 32);
+  const dim3 gdw((D + 511) / 512, HdI / 32);
   if (dI == 64)
     hipLaunchKernelGGL((fdw_kernel<64>), gdw, dim3(256), 0, s, D, w.gT, w.GT, w.hT, dWq);
   else

@@ -71,7 +71,7 @@ def test_focal_ragged_shapes(Q, N, D, H, dI):
     _check(h, Wq, Wg, 0.37, K, y, 2.0, H, dI)
 
 
-@pytest.mark.parametrize("gamma", [0.0, 0.5, 2.0, 5.0])
+@pytest.mark.parametrize("gamma", [0.0, 0.5, 1.0, 2.0, 5.0, 8.0, 9.0])
 def test_focal_gamma_values(gamma):
     rng = np.random.default_rng(5)
     h, Wq, Wg, K, y = _random_student(rng, 8, 2000, 128, 4, 64, pos=0.3)

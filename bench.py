@@ -108,45 +108,53 @@ def main():
     torch.cuda.synchronize()
     it = [0]
 
-    def step(events=None):
+    def step(marks=None):
+        """One trigger; marks: {position: event} recorded on the stream before
+        call 0..4 (position 5: after the last call)."""
         d, pool = copies[it[0] % len(copies)]
         it[0] += 1
-        if events is not None:
-            events[0].record(stream)
+
+        def mark(i):
+            if marks is not None and i in marks:
+                marks[i].record(stream)
+        mark(0)
         lsa.lsa_project_query(d["h"], d["Wq"], d["Wg"], buf.q, buf.g, stream=stream)
-        if events is not None:
-            events[1].record(stream)
+        mark(1)
         lsa.lsa_score(d["keys"], d["scale"], buf.q, buf.g, d["bias"], buf.mask, buf.cand_idx,
                       buf.cand_z, buf.cand_count, stream=stream)
-        if events is not None:
-            events[2].record(stream)
+        mark(2)
         lsa.lsa_select_or_compact(buf.cand_idx, buf.cand_z, buf.cand_count, w.N, buf.surv_idx,
                                   buf.surv_z, buf.surv_count, stream=stream)
-        if events is not None:
-            events[3].record(stream)
+        mark(3)
         lsa.lsa_topk(buf.surv_idx, buf.surv_z, buf.surv_count, buf.topk_idx, buf.topk_count,
                      buf.ws_topk, stream=stream)
-        if events is not None:
-            events[4].record(stream)
+        mark(4)
         lsa.lsa_gather_hot(pool, buf.topk_idx, buf.hot, stream=stream)
-        if events is not None:
-            events[5].record(stream)
+        mark(5)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    # timed region: K steps between two synchronisations; HIP events on the
-    # kernels' stream bracket every call (recording an event is one stream
-    # command, no host synchronisation)
-    evs = [[ev() for _ in range(6)] for _ in range(args.steps)]
+    # timed region: K steps between two synchronisations.  Two HIP events on
+    # the kernels' stream bracket every score launch (the roofline kernel).
+    # Each recorded event costs the stream a few microseconds between two
+    # kernels, so the per-call breakdown comes from a separate pass below.
+    evs = [(ev(), ev()) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for e in evs:
-        step(e)
+        step({1: e[0], 2: e[1]})
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     ms_per_step = wall * 1e3 / max(args.steps, 1)
+    mean_score = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+
+    # per-call breakdown: K more steps (untimed) with an event between calls
+    bd = [[ev() for _ in range(6)] for _ in range(args.steps)]
+    for e in bd:
+        step(dict(enumerate(e)))
+    torch.cuda.synchronize()
     launch = "eager"
     if args.graph:
         # the same step captured once and replayed K times
@@ -174,11 +182,10 @@ def main():
         ms_per_step = (time.perf_counter() - t_start) * 1e3 / max(args.steps, 1)
         launch = "hip_graph"
     names = ["project", "score", "select", "topk", "gather"]
-    per = {n: float(np.median([e[i].elapsed_time(e[i + 1]) for e in evs])) for i, n in enumerate(names)}
-    pct = {n: [float(np.percentile([e[i].elapsed_time(e[i + 1]) for e in evs], q)) for q in (10, 90)]
+    per = {n: float(np.median([e[i].elapsed_time(e[i + 1]) for e in bd])) for i, n in enumerate(names)}
+    pct = {n: [float(np.percentile([e[i].elapsed_time(e[i + 1]) for e in bd], q)) for q in (10, 90)]
            for i, n in enumerate(names)}
-    mean_score = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
-    score_select = float(np.median([e[1].elapsed_time(e[3]) for e in evs]))
+    score_select = float(np.median([e[1].elapsed_time(e[3]) for e in bd]))
 
     triples = w.triples
     key_bytes = triples * w.key_bytes_per_entry
@@ -295,30 +302,39 @@ def bench_labels(args):
     print(f"# inputs ready in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
     stream = torch.cuda.current_stream()
 
-    def step(e=None):
-        if e is not None:
+    def step(e=None, n=3):
+        """One step; e: events recorded before the vote, between the calls and
+        after the loss/gradient (the first n of them)."""
+        if e is not None and n > 0:
             e[0].record(stream)
         lsa.lsa_label_vote(xd, w.top_p, w.theta, count, label, layer_mask=mask, stream=stream)
-        if e is not None:
+        if e is not None and n > 1:
             e[1].record(stream)
         lsa.lsa_focal_bce_grad(hd, Wqd, Wgd, bias, Kd, label, w.gamma, loss, dW, ws, H=w.H,
                                dI=w.dI, stream=stream)
-        if e is not None:
+        if e is not None and n > 2:
             e[2].record(stream)
 
+    ev = lambda: torch.cuda.Event(enable_timing=True)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    # timed region: two events bracket every vote launch (the roofline
+    # kernel); the loss/gradient time comes from a separate pass
+    evs = [[ev(), ev()] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for e in evs:
-        step(e)
+        step(e, 2)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     ms_per_step = wall * 1e3 / max(args.steps, 1)
     vote_ms = [e[0].elapsed_time(e[1]) for e in evs]
-    focal_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    bd = [[ev() for _ in range(3)] for _ in range(args.steps)]
+    for e in bd:
+        step(e)
+    torch.cuda.synchronize()
+    focal_ms = [e[1].elapsed_time(e[2]) for e in bd]
     logits = w.Q * w.L * w.N
     # algorithmic bytes: logits read once, masks + counts + labels written
     vote_bytes = logits * 4 + w.Q * w.L * W * 4 + 2 * w.Q * w.N

@@ -153,30 +153,35 @@ __device__ __forceinline__ float score_tile(const TileRegs<KT, DI>& r, int lane,
   return fmaf(zv, r.sc, bias);
 }
 
-// One block = one request b and one chunk of kChunkTiles 32-entry tiles
-// (LSA_CAND_CHUNK entries), for every indexer layer in turn (outer loop).
+// One block = one request b and CPB consecutive chunks of LSA_CAND_CHUNK
+// entries (32-entry tiles), for every indexer layer in turn (outer loop).
 // Wave w scores chunk tiles w, w + NW, ...  Per tile and layer the selection
 // word goes to LDS; per entry the maximum z over the layers that select it
 // stays in the wave's LDS slice across layers (-inf while none has).  After the
 // last layer the whole block
 //   * writes its selection words, one contiguous run per layer, and
-//   * compacts the chunk: every entry with a finite merged logit, in
-//     ascending order (ballot + mbcnt inside a wave, a 4-wave prefix in LDS),
-//     into the chunk's candidate list (entry index, merged logit) plus count.
+//   * compacts each of its chunks: every entry with a finite merged logit,
+//     in ascending order (ballot + mbcnt inside a wave, a prefix over the
+//     waves in LDS), into the chunk's candidate list (entry index, merged
+//     logit) plus count.
 // So the kernel writes a few contiguous runs per block instead of one line per
 // tile; writes interleaved with the key stream cost far more HBM time than
 // their bytes.  RING: register-ring depth (RING-1 tiles in flight per wave).
 // NW = 4 wavefronts per block; 16 when the grid has fewer blocks than twice
 // the compute units (few requests, short lists), so that a short list still
-// spreads over many wavefronts.
+// spreads over many wavefronts.  CPB = 2 chunks per block when that still
+// leaves three blocks per compute unit: every block pays a fixed start and
+// end (q~ set-up, ring fill, compaction), and halving the block count was
+// 2% faster at 1M context.
 constexpr int kSetupW = 4;   // wavefronts that form q~ (their layout below)
 
-template <int KT, int DI, int RING, bool WZ, bool WI, int WPE, int NW>
+template <int KT, int DI, int RING, bool WZ, bool WI, int WPE, int NW, int CPB>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WPE)))
 void score_kernel(ScoreArgs a) {
   using G = Geo<KT, DI>;
-  constexpr int kTPW = LSA_CAND_CHUNK / 32 / NW;   // tiles per wave and layer
-  static_assert(kTPW * 32 * NW == LSA_CAND_CHUNK, "chunk must split evenly");
+  constexpr int kTPW = CPB * LSA_CAND_CHUNK / 32 / NW;   // tiles per wave and layer
+  static_assert(kTPW * 32 * NW == CPB * LSA_CAND_CHUNK, "chunk must split evenly");
+  static_assert(LSA_CAND_CHUNK % (64 * NW) == 0, "a compaction round stays in one chunk");
   __shared__ __attribute__((aligned(16))) float qt[LSA_MAX_LAYERS][DI];
   __shared__ __attribute__((aligned(16))) float zacc[NW][kTPW][32];
   __shared__ uint32_t mwords[LSA_MAX_LAYERS][NW * kTPW];
@@ -186,7 +191,7 @@ void score_kernel(ScoreArgs a) {
   const int n = lane & 31;
   const int half = lane >> 5;
   const int b = blockIdx.y;
-  const int c = blockIdx.x;
+  const int c = blockIdx.x;   // this block's chunks: CPB c, ..., CPB c + CPB - 1
   const int L = a.L;
 
   // qt[l] = sum_h g_h q_h of (layer l, request b), fp32, in one round of
@@ -255,8 +260,8 @@ void score_kernel(ScoreArgs a) {
 
   const uint32_t N = (uint32_t)a.N;
   const int ntiles = (a.N + 31) >> 5;
-  const int c_tile0 = c * NW * kTPW;                       // first tile of the chunk
-  const int c_tiles = min(NW * kTPW, ntiles - c_tile0);    // tiles in this chunk
+  const int c_tile0 = c * NW * kTPW;                       // first tile of the block
+  const int c_tiles = min(NW * kTPW, ntiles - c_tile0);    // tiles in this block
   const int n_my = wave < c_tiles ? (c_tiles - wave + NW - 1) / NW : 0;
   const int t0 = c_tile0 + wave;
   const int t_last = t0 + NW * (n_my - 1);
@@ -320,58 +325,68 @@ void score_kernel(ScoreArgs a) {
     const int l = i / c_tiles, tc = i - l * c_tiles;
     a.mask[((size_t)l * a.B + b) * a.W + c_tile0 + tc] = mwords[l][tc];
   }
-  // chunk compaction, ascending: thread j of round r takes chunk entry
-  // e = 256 r + j, held by wave (e/32) % NW at local tile (e/32) / NW
-  int* cidx = a.cand_idx + ((size_t)b * a.nchunks + c) * LSA_CAND_CHUNK;
-  float* cz = a.cand_z + ((size_t)b * a.nchunks + c) * LSA_CAND_CHUNK;
-  int base = 0;
-  const int c_entries = min(LSA_CAND_CHUNK, a.N - c_tile0 * 32);
-  for (int e0 = 0; e0 < c_entries; e0 += 64 * NW) {
-    const int e = e0 + threadIdx.x;
-    const int tc = e >> 5;
-    float zm = -__builtin_inff();
-    if (e < c_entries) zm = zacc[tc % NW][tc / NW][e & 31];
-    const bool f = zm > -__builtin_inff();
-    const uint64_t bal = __ballot(f);
-    if (lane == 0) s_wave[wave] = __popcll(bal);
-    __syncthreads();
-    int before = 0, total = 0;
+  // chunk compaction, ascending: thread j of round r takes block entry
+  // e = 64 NW r + j, held by wave (e/32) % NW at local tile (e/32) / NW; the
+  // rounds of chunk cc cover block entries [cc, cc + 1) * LSA_CAND_CHUNK
+  const int b_entries = min(CPB * LSA_CAND_CHUNK, a.N - c_tile0 * 32);
 #pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const int cnt = s_wave[w];
-      before += (w < wave) ? cnt : 0;
-      total += cnt;
+  for (int cc = 0; cc < CPB; ++cc) {
+    const int e_beg = cc * LSA_CAND_CHUNK;
+    if (e_beg >= b_entries) break;
+    const int e_end = min(e_beg + LSA_CAND_CHUNK, b_entries);
+    const size_t list = (size_t)b * a.nchunks + (size_t)c * CPB + cc;
+    int* cidx = a.cand_idx + list * LSA_CAND_CHUNK;
+    float* cz = a.cand_z + list * LSA_CAND_CHUNK;
+    int base = 0;
+    for (int e0 = e_beg; e0 < e_end; e0 += 64 * NW) {
+      const int e = e0 + threadIdx.x;
+      const int tc = e >> 5;
+      float zm = -__builtin_inff();
+      if (e < e_end) zm = zacc[tc % NW][tc / NW][e & 31];
+      const bool f = zm > -__builtin_inff();
+      const uint64_t bal = __ballot(f);
+      if (lane == 0) s_wave[wave] = __popcll(bal);
+      __syncthreads();
+      int before = 0, total = 0;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const int cnt = s_wave[w];
+        before += (w < wave) ? cnt : 0;
+        total += cnt;
+      }
+      if (f) {
+        const int pos = base + before + lanes_below(bal);
+        cidx[pos] = c_tile0 * 32 + e;
+        cz[pos] = zm;
+      }
+      base += total;
+      __syncthreads();
     }
-    if (f) {
-      const int pos = base + before + lanes_below(bal);
-      cidx[pos] = c_tile0 * 32 + e;
-      cz[pos] = zm;
-    }
-    base += total;
-    __syncthreads();
+    if (threadIdx.x == 0) a.cand_count[list] = base;
   }
-  if (threadIdx.x == 0) a.cand_count[(size_t)b * a.nchunks + c] = base;
 }
 
-template <int KT, int DI, int RING, int WPE, int NW>
+template <int KT, int DI, int RING, int WPE, int NW, int CPB>
 hipError_t launch_nw(const ScoreArgs& a, hipStream_t s) {
-  dim3 grid(a.nchunks, a.B);
+  dim3 grid((a.nchunks + CPB - 1) / CPB, a.B);
   const bool wz = a.z != nullptr, wi = a.I != nullptr;
   if (!wz && !wi)
-    hipLaunchKernelGGL((score_kernel<KT, DI, RING, false, false, WPE, NW>), grid, dim3(64 * NW), 0, s, a);
+    hipLaunchKernelGGL((score_kernel<KT, DI, RING, false, false, WPE, NW, CPB>), grid, dim3(64 * NW), 0, s, a);
   else if (wz && !wi)
-    hipLaunchKernelGGL((score_kernel<KT, DI, RING, true, false, WPE, NW>), grid, dim3(64 * NW), 0, s, a);
+    hipLaunchKernelGGL((score_kernel<KT, DI, RING, true, false, WPE, NW, CPB>), grid, dim3(64 * NW), 0, s, a);
   else if (!wz && wi)
-    hipLaunchKernelGGL((score_kernel<KT, DI, RING, false, true, WPE, NW>), grid, dim3(64 * NW), 0, s, a);
+    hipLaunchKernelGGL((score_kernel<KT, DI, RING, false, true, WPE, NW, CPB>), grid, dim3(64 * NW), 0, s, a);
   else
-    hipLaunchKernelGGL((score_kernel<KT, DI, RING, true, true, WPE, NW>), grid, dim3(64 * NW), 0, s, a);
+    hipLaunchKernelGGL((score_kernel<KT, DI, RING, true, true, WPE, NW, CPB>), grid, dim3(64 * NW), 0, s, a);
   return hipGetLastError();
 }
 
 template <int KT, int DI, int RING = 2, int WPE = 2>
 hipError_t launch_t(const ScoreArgs& a, hipStream_t s) {
-  if ((int64_t)a.nchunks * a.B < 2 * device_cu_count()) return launch_nw<KT, DI, RING, 1, 16>(a, s);
-  return launch_nw<KT, DI, RING, WPE, 4>(a, s);
+  const int64_t cus = device_cu_count();
+  if ((int64_t)a.nchunks * a.B < 2 * cus) return launch_nw<KT, DI, RING, 1, 16, 1>(a, s);
+  if ((int64_t)((a.nchunks + 1) / 2) * a.B >= 3 * cus) return launch_nw<KT, DI, RING, WPE, 4, 2>(a, s);
+  return launch_nw<KT, DI, RING, WPE, 4, 1>(a, s);
 }
 
 }  // namespace

@@ -92,6 +92,10 @@ CASES = [
     (2, 3, 8192 + 33, 17, 128, True),
     # enough (chunk, request) blocks for the 4-wavefront launch, ragged last chunk
     (1, 128, 4 * 4096 + 1, 8, 64, True),
+    # two chunks a block (enough requests for three such blocks per compute
+    # unit): a full chunk and a ragged one; a single short chunk
+    (1, 768, 4096 + 33, 8, 64, True),
+    (2, 768, 300, 8, 64, False),
 ]
 
 

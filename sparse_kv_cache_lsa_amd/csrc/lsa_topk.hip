@@ -133,13 +133,15 @@ __device__ __forceinline__ float key_to_float(uint32_t key) {
 // to T belong to the top-k; two block prefix sums then give every kept
 // position its output slot.  Writes out_idx[0..k) = si[kept positions], in
 // position order, and out_z (if not null) the scores.  stage: LDS for
-// kStage ints (used when k <= kStage); scratch: 2 * NT/64 + 2 ints.  All
-// threads call.
+// kStage ints (used when k <= kStage); scratch: 2 * NT/64 + 2 ints.  With
+// seg_kept (LDS, zeroed) every kept position p also counts into
+// seg_kept[p / seg].  All threads call.
 template <int NT, int KREG>
 __device__ __forceinline__ void block_select(int n, int k, int chunk, const float* sz,
                                              const int32_t* si, int* hist, int* scratch,
                                              int* s_digit, int* s_above, int* stage,
-                                             int32_t* out_idx, float* out_z) {
+                                             int32_t* out_idx, float* out_z,
+                                             int* seg_kept = nullptr, int seg = 1) {
   const int t = threadIdx.x;
   const int base = t * chunk;
   // buffer loads over the n valid scores: positions past n read 0 and are
@@ -235,6 +237,7 @@ __device__ __forceinline__ void block_select(int n, int k, int chunk, const floa
         else if (key[j] == T) keep = tie_rank++ < krem;
       }
       if (keep && pos < k) {
+        if (seg_kept) atomicAdd(&seg_kept[(base + j) / seg], 1);
         if (staged) {
           stage[pos] = base + j;
         } else {
@@ -254,30 +257,29 @@ __device__ __forceinline__ void block_select(int n, int k, int chunk, const floa
   }
 }
 
-__global__ __launch_bounds__(kThreads) void topk_kernel(int cap, int k,
-                                                        const int32_t* __restrict__ surv_idx,
-                                                        const float* __restrict__ surv_z,
-                                                        const int32_t* __restrict__ surv_count,
-                                                        int32_t* __restrict__ out,
-                                                        int32_t* __restrict__ out_count) {
-  __shared__ int hist[4096];
-  __shared__ int scratch[2 * (kThreads / kWave) + 2];
-  __shared__ int stage[kStage];
-  __shared__ int s_digit, s_above;
-  const int b = blockIdx.x;
-  const int t = threadIdx.x;
-  const int n = min(max(surv_count[b], 0), cap);
-  const int32_t* si = surv_idx + (size_t)b * cap;
-  const float* sz = surv_z + (size_t)b * cap;
-  int32_t* o = out + (size_t)b * k;
+struct SelectLDS {
+  int hist[4096];
+  int scratch[2 * (kThreads / kWave) + 2];
+  int stage[kStage];
+  int digit, above;
+};
 
+// Top-k of one list of n scores (entry indices si, scores sz) by the whole
+// block into o[0..k) (ascending positions, -1 padding) and *count.
+__device__ __forceinline__ void select_list(int n, int k, const int32_t* __restrict__ si,
+                            const float* __restrict__ sz, int32_t* __restrict__ o,
+                            int32_t* count, SelectLDS& S) {
+  int* hist = S.hist;
+  int* scratch = S.scratch;
+  int* stage = S.stage;
+  const int t = threadIdx.x;
   if (k == 0) {
-    if (t == 0) out_count[b] = 0;
+    if (t == 0) *count = 0;
     return;
   }
   if (n <= k) {
     for (int i = t; i < k; i += kThreads) o[i] = i < n ? si[i] : -1;
-    if (t == 0) out_count[b] = n;
+    if (t == 0) *count = n;
     return;
   }
 
@@ -286,15 +288,15 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(int cap, int k,
     // the register array is sized to the list (every pass walks all its slots)
     const int chunk = (n + kThreads - 1) / kThreads;
     if (chunk <= 16)
-      block_select<kThreads, 16>(n, k, chunk, sz, si, hist, scratch, &s_digit, &s_above, stage, o,
+      block_select<kThreads, 16>(n, k, chunk, sz, si, hist, scratch, &S.digit, &S.above, stage, o,
                                  nullptr);
     else if (chunk <= 32)
-      block_select<kThreads, 32>(n, k, chunk, sz, si, hist, scratch, &s_digit, &s_above, stage, o,
+      block_select<kThreads, 32>(n, k, chunk, sz, si, hist, scratch, &S.digit, &S.above, stage, o,
                                  nullptr);
     else
-      block_select<kThreads, kReg>(n, k, chunk, sz, si, hist, scratch, &s_digit, &s_above, stage,
+      block_select<kThreads, kReg>(n, k, chunk, sz, si, hist, scratch, &S.digit, &S.above, stage,
                                    o, nullptr);
-    if (t == 0) out_count[b] = k;
+    if (t == 0) *count = k;
     return;
   }
 
@@ -315,12 +317,12 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(int cap, int k,
     }
     __syncthreads();
     if (pass == 0)
-      find_crossing<4096>(hist, krem, scratch, &s_digit, &s_above);
+      find_crossing<4096>(hist, krem, scratch, &S.digit, &S.above);
     else
-      find_crossing<1024>(hist, krem, scratch, &s_digit, &s_above);
-    prefix |= (uint32_t)s_digit << shift;
+      find_crossing<1024>(hist, krem, scratch, &S.digit, &S.above);
+    prefix |= (uint32_t)S.digit << shift;
     pmask |= (uint32_t)(NB - 1) << shift;
-    krem -= s_above;
+    krem -= S.above;
     __syncthreads();
   }
   const uint32_t T = prefix;
@@ -360,25 +362,50 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(int cap, int k,
     tie_base += tie_total;
     out_base += kept_total;
   }
-  if (t == 0) out_count[b] = k;
+  if (t == 0) *count = k;
+}
+
+__global__ __launch_bounds__(kThreads) void topk_kernel(int cap, int k,
+                                                        const int32_t* __restrict__ surv_idx,
+                                                        const float* __restrict__ surv_z,
+                                                        const int32_t* __restrict__ surv_count,
+                                                        int32_t* __restrict__ out,
+                                                        int32_t* __restrict__ out_count) {
+  __shared__ SelectLDS S;
+  const int b = blockIdx.x;
+  const int n = min(max(surv_count[b], 0), cap);
+  select_list(n, k, surv_idx + (size_t)b * cap, surv_z + (size_t)b * cap, out + (size_t)b * k,
+              out_count + b, S);
 }
 
 // ----------------------------------------------------------------------------
 // Long lists (more than kMBMinCap survivors of capacity): two stages.
 //  1. slice_kernel, several blocks per request: block p takes positions
-//     [p*kSlice, (p+1)*kSlice) and writes the top min(k, kSlice) of its slice
-//     (same ranking, in position order) to a candidate list in the workspace,
-//     at offset p * min(k, kSlice) -- every earlier slice is full, so the
-//     offset needs no communication.  The global top-k is contained in the
-//     union of the slices' top-k (fewer than k entries of a member's slice
-//     precede it), and the candidate list stays in position order.
-//  2. topk_kernel over the candidate list (a few thousand to tens of
-//     thousands of entries instead of the whole survivor list).
+//     [p*kSlice, (p+1)*kSlice) and writes the top kc of its slice (same
+//     ranking, in position order) to a candidate list in the workspace, at
+//     offset p * kc -- every earlier slice is full, so the offset needs no
+//     communication.  The candidate list stays in position order.
+//  2. final_kernel: the top-k of the candidate list.
+// With kc = min(k, kSlice) the global top-k lies inside the candidates
+// (fewer than k entries of a member's slice precede it).  With kc < k a
+// slice keeps only its best kc: each of the slice's dropped entries ranks
+// below all kc kept ones, so the candidates' top-k is the exact top-k unless
+// a truncated slice (more than kc entries) has all its kc kept entries in
+// it.  The final stage counts the entries of each slice it keeps and, in
+// that case, selects over the request's whole survivor list instead.  About
+// k * kSlice / n of a slice's entries belong to the top-k (n survivors; at
+// 1M context 2048 * 4096 / 63K = 133, standard deviation about 11), so with
+// kc = 256 the fallback stays rare unless the best entries cluster in a few
+// slices.  (Kept per slice: 512 timed 32 us, 256 timed 29.5 us at 1M
+// context; slices of 2048 or 8192 survivors were slower.)
 constexpr int kMT = 256;               // threads per slice block
-constexpr int kMK = 32;                // scores per thread
+constexpr int kMK = 16;                // scores per thread
 constexpr int kSlice = kMT * kMK;      // survivors per slice
+constexpr int kKeep = 256;             // candidates a truncating slice keeps
+constexpr int kMaxSeg = 320;           // slices the final stage can check (kMaxSeg * kKeep <= 80K)
+static_assert(kMaxSeg * kKeep <= kThreads * kReg, "the final stage holds every candidate in registers");
 
-__global__ __launch_bounds__(kMT) void slice_kernel(int cap, int k, int cap_c,
+__global__ __launch_bounds__(kMT) void slice_kernel(int cap, int k, int kc, int cap_c,
                                                     const int32_t* __restrict__ surv_idx,
                                                     const float* __restrict__ surv_z,
                                                     const int32_t* __restrict__ surv_count,
@@ -393,7 +420,6 @@ __global__ __launch_bounds__(kMT) void slice_kernel(int cap, int k, int cap_c,
   // are dispatched first (most later slices are empty and exit at once)
   const int b = blockIdx.x, p = blockIdx.y;
   const int n = min(max(surv_count[b], 0), cap);
-  const int kc = min(k, kSlice);
   if (p == 0 && threadIdx.x == 0)
     cand_count[b] = k == 0 ? 0 : (n / kSlice) * kc + min(kc, n % kSlice);
   const int np = min(kSlice, n - p * kSlice);
@@ -412,13 +438,72 @@ __global__ __launch_bounds__(kMT) void slice_kernel(int cap, int k, int cap_c,
   block_select<kMT, kMK>(np, kc, kMK, sz, si, hist, scratch, &s_digit, &s_above, stage, ci, cz);
 }
 
+__global__ __launch_bounds__(kThreads) void final_kernel(int cap_c, int k, int kc, int cap,
+                                                         const int32_t* __restrict__ cand_idx,
+                                                         const float* __restrict__ cand_z,
+                                                         const int32_t* __restrict__ cand_count,
+                                                         const int32_t* __restrict__ surv_idx,
+                                                         const float* __restrict__ surv_z,
+                                                         const int32_t* __restrict__ surv_count,
+                                                         int32_t* __restrict__ out,
+                                                         int32_t* __restrict__ out_count) {
+  __shared__ SelectLDS S;
+  __shared__ int seg_kept[kMaxSeg];
+  __shared__ int s_full;
+  const int b = blockIdx.x, t = threadIdx.x;
+  const int n = min(max(surv_count[b], 0), cap);
+  const int nc = min(max(cand_count[b], 0), cap_c);
+  const int32_t* ci = cand_idx + (size_t)b * cap_c;
+  const float* cz = cand_z + (size_t)b * cap_c;
+  int32_t* o = out + (size_t)b * k;
+  if (kc >= k || n <= k) {   // nothing dropped that could belong
+    select_list(n <= k ? n : nc, k, n <= k ? surv_idx + (size_t)b * cap : ci,
+                n <= k ? surv_z + (size_t)b * cap : cz, o, out_count + b, S);
+    return;
+  }
+  const int P = (n + kSlice - 1) / kSlice;   // <= kMaxSeg (host check)
+  for (int i = t; i < kMaxSeg; i += kThreads) seg_kept[i] = 0;
+  if (t == 0) s_full = nc <= k;   // every candidate kept while entries were dropped
+  __syncthreads();
+  if (nc > k) {
+    // nc <= P * kc <= kMaxSeg * kKeep = kThreads * kReg: register-resident
+    const int chunk = (nc + kThreads - 1) / kThreads;
+    if (chunk <= 16)
+      block_select<kThreads, 16>(nc, k, chunk, cz, ci, S.hist, S.scratch, &S.digit, &S.above,
+                                 S.stage, o, nullptr, seg_kept, kc);
+    else if (chunk <= 32)
+      block_select<kThreads, 32>(nc, k, chunk, cz, ci, S.hist, S.scratch, &S.digit, &S.above,
+                                 S.stage, o, nullptr, seg_kept, kc);
+    else
+      block_select<kThreads, kReg>(nc, k, chunk, cz, ci, S.hist, S.scratch, &S.digit, &S.above,
+                                   S.stage, o, nullptr, seg_kept, kc);
+    __syncthreads();
+    for (int p = t; p < P; p += kThreads)
+      if (min(kSlice, n - p * kSlice) > kc && seg_kept[p] >= kc) s_full = 1;
+    __syncthreads();
+    if (!s_full) {
+      if (t == 0) out_count[b] = k;
+      return;
+    }
+  }
+  // a truncated slice may hold more of the top-k: select over the whole list
+  select_list(n, k, surv_idx + (size_t)b * cap, surv_z + (size_t)b * cap, o, out_count + b, S);
+}
+
 }  // namespace
 
 static size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// candidates a slice keeps: kKeep when k is larger and the final stage can
+// check every slice, else min(k, kSlice) (exact without a check)
+static int slice_keep(int cap, int k) {
+  const int P = (cap + kSlice - 1) / kSlice;
+  return (k > kKeep && P <= kMaxSeg) ? kKeep : min(k, kSlice);
+}
+
 static int cand_capacity(int cap, int k) {
   const int P = (cap + kSlice - 1) / kSlice;
-  return P * min(k, kSlice);
+  return P * slice_keep(cap, k);
 }
 
 size_t topk_workspace_bytes(int B, int cap, int k) {
@@ -436,17 +521,23 @@ hipError_t launch_topk(int B, int cap, int k, const int32_t* surv_idx, const flo
     return hipGetLastError();
   }
   const int P = (cap + kSlice - 1) / kSlice;
+  const int kc = slice_keep(cap, k);
   const int cap_c = cand_capacity(cap, k);
   const size_t cc = (size_t)B * cap_c;
   int32_t* cand_idx = (int32_t*)ws;
   float* cand_z = (float*)((char*)ws + up256(cc * 4));
   int32_t* cand_count = (int32_t*)((char*)ws + 2 * up256(cc * 4));
-  hipLaunchKernelGGL(slice_kernel, dim3(B, P), dim3(kMT), 0, s, cap, k, cap_c, surv_idx, surv_z,
-                     surv_count, cand_idx, cand_z, cand_count);
+  hipLaunchKernelGGL(slice_kernel, dim3(B, P), dim3(kMT), 0, s, cap, k, kc, cap_c, surv_idx,
+                     surv_z, surv_count, cand_idx, cand_z, cand_count);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(topk_kernel, dim3(B), dim3(kThreads), 0, s, cap_c, k, cand_idx, cand_z,
-                     cand_count, topk_idx, topk_count);
+  if (kc >= k) {
+    hipLaunchKernelGGL(topk_kernel, dim3(B), dim3(kThreads), 0, s, cap_c, k, cand_idx, cand_z,
+                       cand_count, topk_idx, topk_count);
+  } else {
+    hipLaunchKernelGGL(final_kernel, dim3(B), dim3(kThreads), 0, s, cap_c, k, kc, cap, cand_idx,
+                       cand_z, cand_count, surv_idx, surv_z, surv_count, topk_idx, topk_count);
+  }
   return hipGetLastError();
 }
 

@@ -85,6 +85,37 @@ def test_topk_signed_zero_ties_and_equal_scores():
     assert out[0].tolist() == sorted([idx[0, 13], idx[0, 0], idx[0, 1]])
 
 
+# Long lists are cut into slices of 4096 survivors that keep their best 256
+# when k is larger; the final stage must notice when a slice may have lost
+# members of the top-k (all its kept entries made the top-k) and redo the
+# select over the whole list.  Each case makes that happen for some request.
+@pytest.mark.parametrize("pattern", ["clustered", "equal", "exact256", "dense512", "short"])
+def test_topk_truncated_slices_stay_exact(pattern):
+    rng = np.random.default_rng(77)
+    B, cap, k = 3, 63000, 2048
+    ns = [63000, 40000, 20001]
+    idx, z = _survivors(rng, B, cap, ns)
+    for b, n in enumerate(ns):
+        if pattern == "clustered":      # the best entries all in one slice
+            lo = 4096 * b
+            z[b, lo:lo + 3000] = (1000.0 - np.arange(3000)).astype(np.float32)
+        elif pattern == "equal":        # one score everywhere: the first k positions win
+            z[b, :n] = 7.0
+        elif pattern in ("exact256", "dense512"):   # slice 1 holds 256 / 512 of the top-k
+            m = 256 if pattern == "exact256" else 512
+            z[b, :n] = rng.uniform(0, 1, n).astype(np.float32)
+            top = np.concatenate([4096 + rng.choice(4096, m, replace=False),
+                                  rng.choice(np.arange(8192, n), k - m, replace=False)])
+            z[b, top] = (10.0 + rng.uniform(0, 1, k)).astype(np.float32)
+        else:                           # the slices keep fewer than k entries in total
+            ns[b] = [5000, 4097, 9000][b]
+    out, oc = _topk(idx, z, ns, k)
+    for b, n in enumerate(ns):
+        want, cnt = oracle.topk(idx[b, :n], z[b, :n].astype(np.float64), k)
+        assert oc[b] == cnt
+        assert np.array_equal(out[b], want), f"{pattern}: request {b}"
+
+
 @pytest.mark.parametrize("row_bytes", [1024, 48, 16])
 def test_gather_matches_oracle(row_bytes):
     rng = np.random.default_rng(row_bytes)

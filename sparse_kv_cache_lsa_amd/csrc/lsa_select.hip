@@ -13,15 +13,19 @@
 namespace lsa {
 namespace {
 
-__global__ __launch_bounds__(256) void select_concat_kernel(
+constexpr int kSelThreads = 256;
+
+__global__ __launch_bounds__(kSelThreads) void select_concat_kernel(
     int nchunks, const int32_t* __restrict__ cand_idx, const float* __restrict__ cand_z,
     const int32_t* __restrict__ cand_count, int cap, int32_t* __restrict__ surv_idx,
     float* __restrict__ surv_z, int32_t* __restrict__ surv_count) {
   __shared__ int s_base;
   const int c = blockIdx.x;
   const int b = blockIdx.y;
+  const int t = threadIdx.x;
   const int32_t* cnt = cand_count + (size_t)b * nchunks;
-  if (threadIdx.x < kWave) {
+  const int n = cnt[c];   // in flight together with the earlier chunks' counts
+  if (t < kWave) {
     int acc = 0;
     for (int i = lane_id(); i < c; i += kWave) acc += cnt[i];
     acc = wave_sum(acc);
@@ -29,15 +33,33 @@ __global__ __launch_bounds__(256) void select_concat_kernel(
   }
   __syncthreads();
   const int base = s_base;
-  const int n = cnt[c];
-  const int32_t* ci = cand_idx + ((size_t)b * nchunks + c) * LSA_CAND_CHUNK;
-  const float* cz = cand_z + ((size_t)b * nchunks + c) * LSA_CAND_CHUNK;
-  const int lim = min(n, cap - base);
-  for (int i = threadIdx.x; i < lim; i += blockDim.x) {
-    surv_idx[(size_t)b * cap + base + i] = ci[i];
-    surv_z[(size_t)b * cap + base + i] = cz[i];
+  const int lim = max(0, min(n, cap - base));
+  // the whole list in one round of loads: thread t takes entries t + 256 r;
+  // the buffer range check reads 0 past lim, the stores are predicated
+  const size_t list = (size_t)b * nchunks + c;
+  const __amdgpu_buffer_rsrc_t ri = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<int32_t*>(cand_idx + list * LSA_CAND_CHUNK), (short)0, lim * 4, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rz = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(cand_z + list * LSA_CAND_CHUNK), (short)0, lim * 4, 0x00020000);
+  constexpr int R = LSA_CAND_CHUNK / kSelThreads;
+  int vi[R], vz[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const uint32_t off = (uint32_t)(r * kSelThreads + t) * 4;
+    vi[r] = __builtin_amdgcn_raw_buffer_load_b32(ri, off, 0, 0);
+    vz[r] = __builtin_amdgcn_raw_buffer_load_b32(rz, off, 0, 0);
   }
-  if (c == nchunks - 1 && threadIdx.x == 0) surv_count[b] = base + n;
+  int32_t* oi = surv_idx + (size_t)b * cap + base;
+  int32_t* oz = (int32_t*)(surv_z + (size_t)b * cap + base);
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int e = r * kSelThreads + t;
+    if (e < lim) {
+      oi[e] = vi[r];
+      oz[e] = vz[r];
+    }
+  }
+  if (c == nchunks - 1 && t == 0) surv_count[b] = base + n;
 }
 
 __global__ void fill_i32_kernel(int32_t* p, int64_t n, int32_t v) {
@@ -57,7 +79,7 @@ hipError_t launch_select(int B, int nchunks, const int32_t* cand_idx, const floa
                          const int32_t* cand_count, int cap, int32_t* surv_idx, float* surv_z,
                          int32_t* surv_count, hipStream_t s) {
   if (nchunks == 0) return launch_fill_i32(surv_count, B, 0, s);
-  hipLaunchKernelGGL(select_concat_kernel, dim3(nchunks, B), dim3(256), 0, s, nchunks, cand_idx,
+  hipLaunchKernelGGL(select_concat_kernel, dim3(nchunks, B), dim3(kSelThreads), 0, s, nchunks, cand_idx,
                      cand_z, cand_count, cap, surv_idx, surv_z, surv_count);
   return hipGetLastError();
 }

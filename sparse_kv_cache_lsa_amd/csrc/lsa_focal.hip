@@ -345,7 +345,10 @@ __global__ __launch_bounds__(256) void ftranspose_kernel(TransposeJob j0, Transp
 // queries 32*(w%2) .. +31 (A = collapsed queries, B = keys), so the 32 lanes
 // of a half-wave hold consecutive entries of one query: label loads and delta
 // stores coalesce.  The epilogue (loss terms, dloss/dz) is VALU work; small
-// tiles give enough waves to hide its latency.
+// tiles give enough waves to hide its latency.  The collapsed queries (64 x
+// DI fp32) are first copied into LDS with contiguous loads: every wave needs
+// 32 of their rows, and fragment loads straight from memory touch 32 rows
+// per instruction.
 template <int DI>
 __global__ __launch_bounds__(256) void flogits_kernel(int Q, int N, int Np, float gamma,
                                                       float bias, float inv_qn,
@@ -355,6 +358,13 @@ __global__ __launch_bounds__(256) void flogits_kernel(int Q, int N, int Np, floa
                                                       float* __restrict__ delta,
                                                       double* __restrict__ loss_part) {
   __shared__ double wsum[4];
+  __shared__ __attribute__((aligned(16))) float qs[kQP][DI + 4];   // rows 16 B apart in the banks
+#pragma unroll
+  for (int i = 0; i < kQP * DI / 4 / 256; ++i) {
+    const int c = threadIdx.x + 256 * i, r = c / (DI / 4), col = 4 * (c - r * (DI / 4));
+    *(f32x4*)&qs[r][col] = *(const f32x4*)(qe + r * DI + col);
+  }
+  __syncthreads();
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n = lane & 31, half = lane >> 5;
   const int s0 = (blockIdx.x * 2 + (wave >> 1)) * 32;
@@ -367,7 +377,7 @@ __global__ __launch_bounds__(256) void flogits_kernel(int Q, int N, int Np, floa
   for (int k = 0; k < DI; k += 8) {
     const int kk = k + 4 * half;
     const f32x4 b = buf_bf16x4(rk, boff + kk * 2);
-    const f32x4 a = *(const f32x4*)(qe + (t0 + n) * DI + kk);
+    const f32x4 a = *(const f32x4*)&qs[t0 + n][kk];
     acc = mfma4(a, b, acc);
   }
   // labels of the lane's 16 (query, entry) pairs, all loads issued first;

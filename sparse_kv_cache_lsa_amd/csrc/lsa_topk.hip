@@ -95,7 +95,7 @@ __device__ __forceinline__ void block_minmax_t(uint32_t& a, uint32_t& b, int* sc
 
 // Finds, scanning bins from the highest digit down, the bin holding the
 // krem-th key; returns the digit and the number of keys in higher bins.
-template <int NB, int NT = kThreads>
+template <int NB, int NT>
 __device__ __forceinline__ void find_crossing(const int* hist, int krem, int* scratch,
                                               int* out_digit, int* out_above) {
   constexpr int PER = NB / NT;   // bins per thread
@@ -257,18 +257,20 @@ __device__ __forceinline__ void block_select(int n, int k, int chunk, const floa
   }
 }
 
+template <int NT>
 struct SelectLDS {
   int hist[4096];
-  int scratch[2 * (kThreads / kWave) + 2];
+  int scratch[2 * (NT / kWave) + 2];
   int stage[kStage];
   int digit, above;
 };
 
 // Top-k of one list of n scores (entry indices si, scores sz) by the whole
 // block into o[0..k) (ascending positions, -1 padding) and *count.
+template <int NT>
 __device__ __forceinline__ void select_list(int n, int k, const int32_t* __restrict__ si,
                             const float* __restrict__ sz, int32_t* __restrict__ o,
-                            int32_t* count, SelectLDS& S) {
+                            int32_t* count, SelectLDS<NT>& S) {
   int* hist = S.hist;
   int* scratch = S.scratch;
   int* stage = S.stage;
@@ -278,23 +280,23 @@ __device__ __forceinline__ void select_list(int n, int k, const int32_t* __restr
     return;
   }
   if (n <= k) {
-    for (int i = t; i < k; i += kThreads) o[i] = i < n ? si[i] : -1;
+    for (int i = t; i < k; i += NT) o[i] = i < n ? si[i] : -1;
     if (t == 0) *count = n;
     return;
   }
 
-  if (n <= kThreads * kReg) {
+  if (n <= NT * kReg) {
     // ---- register-resident path: thread t holds positions [t*chunk, (t+1)*chunk)
     // the register array is sized to the list (every pass walks all its slots)
-    const int chunk = (n + kThreads - 1) / kThreads;
+    const int chunk = (n + NT - 1) / NT;
     if (chunk <= 16)
-      block_select<kThreads, 16>(n, k, chunk, sz, si, hist, scratch, &S.digit, &S.above, stage, o,
+      block_select<NT, 16>(n, k, chunk, sz, si, hist, scratch, &S.digit, &S.above, stage, o,
                                  nullptr);
     else if (chunk <= 32)
-      block_select<kThreads, 32>(n, k, chunk, sz, si, hist, scratch, &S.digit, &S.above, stage, o,
+      block_select<NT, 32>(n, k, chunk, sz, si, hist, scratch, &S.digit, &S.above, stage, o,
                                  nullptr);
     else
-      block_select<kThreads, kReg>(n, k, chunk, sz, si, hist, scratch, &S.digit, &S.above, stage,
+      block_select<NT, kReg>(n, k, chunk, sz, si, hist, scratch, &S.digit, &S.above, stage,
                                    o, nullptr);
     if (t == 0) *count = k;
     return;
@@ -309,17 +311,17 @@ __device__ __forceinline__ void select_list(int n, int k, const int32_t* __restr
   for (int pass = 0; pass < 3; ++pass) {
     const int shift = shifts[pass];
     const int NB = nbins[pass];
-    for (int i = t; i < NB; i += kThreads) hist[i] = 0;
+    for (int i = t; i < NB; i += NT) hist[i] = 0;
     __syncthreads();
-    for (int i = t; i < n; i += kThreads) {
+    for (int i = t; i < n; i += NT) {
       const uint32_t key = order_key(sz[i]);
       if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & (NB - 1)], 1);
     }
     __syncthreads();
     if (pass == 0)
-      find_crossing<4096>(hist, krem, scratch, &S.digit, &S.above);
+      find_crossing<4096, NT>(hist, krem, scratch, &S.digit, &S.above);
     else
-      find_crossing<1024>(hist, krem, scratch, &S.digit, &S.above);
+      find_crossing<1024, NT>(hist, krem, scratch, &S.digit, &S.above);
     prefix |= (uint32_t)S.digit << shift;
     pmask |= (uint32_t)(NB - 1) << shift;
     krem -= S.above;
@@ -329,7 +331,7 @@ __device__ __forceinline__ void select_list(int n, int k, const int32_t* __restr
 
   // ---- ordered sweep: keys > T, then the first krem keys == T
   int tie_base = 0, out_base = 0;
-  for (int seg = 0; seg < n; seg += 4 * kThreads) {
+  for (int seg = 0; seg < n; seg += 4 * NT) {
     const int i0 = seg + 4 * t;
     uint32_t key[4];
     bool ok[4];
@@ -341,7 +343,7 @@ __device__ __forceinline__ void select_list(int n, int k, const int32_t* __restr
       ties += (ok[j] && key[j] == T) ? 1 : 0;
     }
     int tie_total;
-    int rank = tie_base + block_exclusive_scan<kThreads>(ties, scratch, &tie_total);
+    int rank = tie_base + block_exclusive_scan<NT>(ties, scratch, &tie_total);
     bool keep[4];
     int kept = 0;
 #pragma unroll
@@ -355,7 +357,7 @@ __device__ __forceinline__ void select_list(int n, int k, const int32_t* __restr
       kept += keep[j] ? 1 : 0;
     }
     int kept_total;
-    int pos = out_base + block_exclusive_scan<kThreads>(kept, scratch, &kept_total);
+    int pos = out_base + block_exclusive_scan<NT>(kept, scratch, &kept_total);
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       if (keep[j] && pos < k) o[pos++] = si[i0 + j];
@@ -371,10 +373,10 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(int cap, int k,
                                                         const int32_t* __restrict__ surv_count,
                                                         int32_t* __restrict__ out,
                                                         int32_t* __restrict__ out_count) {
-  __shared__ SelectLDS S;
+  __shared__ SelectLDS<kThreads> S;
   const int b = blockIdx.x;
   const int n = min(max(surv_count[b], 0), cap);
-  select_list(n, k, surv_idx + (size_t)b * cap, surv_z + (size_t)b * cap, out + (size_t)b * k,
+  select_list<kThreads>(n, k, surv_idx + (size_t)b * cap, surv_z + (size_t)b * cap, out + (size_t)b * k,
               out_count + b, S);
 }
 
@@ -402,8 +404,9 @@ constexpr int kMT = 256;               // threads per slice block
 constexpr int kMK = 16;                // scores per thread
 constexpr int kSlice = kMT * kMK;      // survivors per slice
 constexpr int kKeep = 256;             // candidates a truncating slice keeps
-constexpr int kMaxSeg = 320;           // slices the final stage can check (kMaxSeg * kKeep <= 80K)
-static_assert(kMaxSeg * kKeep <= kThreads * kReg, "the final stage holds every candidate in registers");
+constexpr int kFinalThreads = 512;    // threads of the final stage (1024: 29.7 us, 512: 28.5, 256: 32.3 at 1M context)
+// slices the final stage can check: it holds every candidate in registers
+constexpr int kMaxSeg = kFinalThreads * kReg / kKeep;
 
 __global__ __launch_bounds__(kMT) void slice_kernel(int cap, int k, int kc, int cap_c,
                                                     const int32_t* __restrict__ surv_idx,
@@ -438,7 +441,8 @@ __global__ __launch_bounds__(kMT) void slice_kernel(int cap, int k, int kc, int 
   block_select<kMT, kMK>(np, kc, kMK, sz, si, hist, scratch, &s_digit, &s_above, stage, ci, cz);
 }
 
-__global__ __launch_bounds__(kThreads) void final_kernel(int cap_c, int k, int kc, int cap,
+template <int NT>
+__global__ __launch_bounds__(NT) void final_kernel(int cap_c, int k, int kc, int cap,
                                                          const int32_t* __restrict__ cand_idx,
                                                          const float* __restrict__ cand_z,
                                                          const int32_t* __restrict__ cand_count,
@@ -447,7 +451,8 @@ __global__ __launch_bounds__(kThreads) void final_kernel(int cap_c, int k, int k
                                                          const int32_t* __restrict__ surv_count,
                                                          int32_t* __restrict__ out,
                                                          int32_t* __restrict__ out_count) {
-  __shared__ SelectLDS S;
+  static_assert(kMaxSeg * kKeep <= NT * kReg, "every candidate fits the registers");
+  __shared__ SelectLDS<NT> S;
   __shared__ int seg_kept[kMaxSeg];
   __shared__ int s_full;
   const int b = blockIdx.x, t = threadIdx.x;
@@ -457,28 +462,28 @@ __global__ __launch_bounds__(kThreads) void final_kernel(int cap_c, int k, int k
   const float* cz = cand_z + (size_t)b * cap_c;
   int32_t* o = out + (size_t)b * k;
   if (kc >= k || n <= k) {   // nothing dropped that could belong
-    select_list(n <= k ? n : nc, k, n <= k ? surv_idx + (size_t)b * cap : ci,
+    select_list<NT>(n <= k ? n : nc, k, n <= k ? surv_idx + (size_t)b * cap : ci,
                 n <= k ? surv_z + (size_t)b * cap : cz, o, out_count + b, S);
     return;
   }
   const int P = (n + kSlice - 1) / kSlice;   // <= kMaxSeg (host check)
-  for (int i = t; i < kMaxSeg; i += kThreads) seg_kept[i] = 0;
+  for (int i = t; i < kMaxSeg; i += NT) seg_kept[i] = 0;
   if (t == 0) s_full = nc <= k;   // every candidate kept while entries were dropped
   __syncthreads();
   if (nc > k) {
-    // nc <= P * kc <= kMaxSeg * kKeep = kThreads * kReg: register-resident
-    const int chunk = (nc + kThreads - 1) / kThreads;
+    // nc <= P * kc <= kMaxSeg * kKeep <= NT * kReg: register-resident
+    const int chunk = (nc + NT - 1) / NT;
     if (chunk <= 16)
-      block_select<kThreads, 16>(nc, k, chunk, cz, ci, S.hist, S.scratch, &S.digit, &S.above,
+      block_select<NT, 16>(nc, k, chunk, cz, ci, S.hist, S.scratch, &S.digit, &S.above,
                                  S.stage, o, nullptr, seg_kept, kc);
     else if (chunk <= 32)
-      block_select<kThreads, 32>(nc, k, chunk, cz, ci, S.hist, S.scratch, &S.digit, &S.above,
+      block_select<NT, 32>(nc, k, chunk, cz, ci, S.hist, S.scratch, &S.digit, &S.above,
                                  S.stage, o, nullptr, seg_kept, kc);
     else
-      block_select<kThreads, kReg>(nc, k, chunk, cz, ci, S.hist, S.scratch, &S.digit, &S.above,
+      block_select<NT, kReg>(nc, k, chunk, cz, ci, S.hist, S.scratch, &S.digit, &S.above,
                                    S.stage, o, nullptr, seg_kept, kc);
     __syncthreads();
-    for (int p = t; p < P; p += kThreads)
+    for (int p = t; p < P; p += NT)
       if (min(kSlice, n - p * kSlice) > kc && seg_kept[p] >= kc) s_full = 1;
     __syncthreads();
     if (!s_full) {
@@ -487,7 +492,7 @@ __global__ __launch_bounds__(kThreads) void final_kernel(int cap_c, int k, int k
     }
   }
   // a truncated slice may hold more of the top-k: select over the whole list
-  select_list(n, k, surv_idx + (size_t)b * cap, surv_z + (size_t)b * cap, o, out_count + b, S);
+  select_list<NT>(n, k, surv_idx + (size_t)b * cap, surv_z + (size_t)b * cap, o, out_count + b, S);
 }
 
 }  // namespace
@@ -535,7 +540,7 @@ hipError_t launch_topk(int B, int cap, int k, const int32_t* surv_idx, const flo
     hipLaunchKernelGGL(topk_kernel, dim3(B), dim3(kThreads), 0, s, cap_c, k, cand_idx, cand_z,
                        cand_count, topk_idx, topk_count);
   } else {
-    hipLaunchKernelGGL(final_kernel, dim3(B), dim3(kThreads), 0, s, cap_c, k, kc, cap, cand_idx,
+    hipLaunchKernelGGL(final_kernel<kFinalThreads>, dim3(B), dim3(kFinalThreads), 0, s, cap_c, k, kc, cap, cand_idx,
                        cand_z, cand_count, surv_idx, surv_z, surv_count, topk_idx, topk_count);
   }
   return hipGetLastError();

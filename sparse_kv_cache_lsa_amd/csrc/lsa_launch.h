@@ -23,6 +23,7 @@ struct ScoreArgs {
   float* I;                // [L][B][N] or null
   int L, B, N, H, W;       // W = ceil(N / 32)
   int nchunks;             // ceil(N / LSA_CAND_CHUNK)
+  int pairs;               // two-chunk blocks per request (set by the launcher)
 };
 
 hipError_t launch_score(int dI, lsa_key_dtype kdt, const ScoreArgs& a, hipStream_t s);

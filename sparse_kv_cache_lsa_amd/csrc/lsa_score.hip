@@ -31,6 +31,8 @@
 #include "lsa_device.h"
 #include "lsa_launch.h"
 
+#include <algorithm>
+
 namespace lsa {
 namespace {
 
@@ -169,10 +171,17 @@ __device__ __forceinline__ float score_tile(const TileRegs<KT, DI>& r, int lane,
 // their bytes.  RING: register-ring depth (RING-1 tiles in flight per wave).
 // NW = 4 wavefronts per block; 16 when the grid has fewer blocks than twice
 // the compute units (few requests, short lists), so that a short list still
-// spreads over many wavefronts.  CPB = 2 chunks per block when that still
-// leaves three blocks per compute unit: every block pays a fixed start and
+// spreads over many wavefronts.  CPB = 2 when there are at least three
+// blocks of two chunks per compute unit: every block pays a fixed start and
 // end (q~ set-up, ring fill, compaction), and halving the block count was
-// 2% faster at 1M context.
+// 2% faster at 1M context.  Then the first a.pairs chunk pairs of every
+// request go to two-chunk blocks -- as many as the compute units hold at
+// once (three each, by LDS) -- and the remaining chunks to one-chunk blocks
+// dispatched after them (request-major in both parts), so the blocks that
+// start late, as slots free up, are the short ones.  At 1M context: 768
+// two-chunk blocks, then 512 one-chunk blocks, two per compute unit;
+// 0.519 ms against 0.526 ms with two-chunk blocks only (other splits leave
+// a ragged first round and were slower).
 constexpr int kSetupW = 4;   // wavefronts that form q~ (their layout below)
 
 template <int KT, int DI, int RING, bool WZ, bool WI, int WPE, int NW, int CPB>
@@ -190,8 +199,25 @@ void score_kernel(ScoreArgs a) {
   const int lane = threadIdx.x & 63;
   const int n = lane & 31;
   const int half = lane >> 5;
-  const int b = blockIdx.y;
-  const int c = blockIdx.x;   // this block's chunks: CPB c, ..., CPB c + CPB - 1
+  int b, cf, cn;   // request, first chunk and number of chunks of this block
+  if constexpr (CPB == 2) {
+    const int P2 = a.pairs, S1 = a.nchunks - 2 * P2;
+    const int u = blockIdx.x;
+    if (u < a.B * P2) {
+      b = u / P2;
+      cf = 2 * (u - b * P2);
+      cn = 2;
+    } else {
+      const int v = u - a.B * P2;
+      b = v / S1;
+      cf = 2 * P2 + (v - b * S1);
+      cn = 1;
+    }
+  } else {
+    b = blockIdx.y;
+    cf = blockIdx.x;
+    cn = 1;
+  }
   const int L = a.L;
 
   // qt[l] = sum_h g_h q_h of (layer l, request b), fp32, in one round of
@@ -260,8 +286,8 @@ void score_kernel(ScoreArgs a) {
 
   const uint32_t N = (uint32_t)a.N;
   const int ntiles = (a.N + 31) >> 5;
-  const int c_tile0 = c * NW * kTPW;                       // first tile of the block
-  const int c_tiles = min(NW * kTPW, ntiles - c_tile0);    // tiles in this block
+  const int c_tile0 = cf * (LSA_CAND_CHUNK / 32);                     // first tile of the block
+  const int c_tiles = min(cn * (LSA_CAND_CHUNK / 32), ntiles - c_tile0);  // tiles in this block
   const int n_my = wave < c_tiles ? (c_tiles - wave + NW - 1) / NW : 0;
   const int t0 = c_tile0 + wave;
   const int t_last = t0 + NW * (n_my - 1);
@@ -328,13 +354,13 @@ void score_kernel(ScoreArgs a) {
   // chunk compaction, ascending: thread j of round r takes block entry
   // e = 64 NW r + j, held by wave (e/32) % NW at local tile (e/32) / NW; the
   // rounds of chunk cc cover block entries [cc, cc + 1) * LSA_CAND_CHUNK
-  const int b_entries = min(CPB * LSA_CAND_CHUNK, a.N - c_tile0 * 32);
+  const int b_entries = min(cn * LSA_CAND_CHUNK, a.N - c_tile0 * 32);
 #pragma unroll
   for (int cc = 0; cc < CPB; ++cc) {
     const int e_beg = cc * LSA_CAND_CHUNK;
     if (e_beg >= b_entries) break;
     const int e_end = min(e_beg + LSA_CAND_CHUNK, b_entries);
-    const size_t list = (size_t)b * a.nchunks + (size_t)c * CPB + cc;
+    const size_t list = (size_t)b * a.nchunks + cf + cc;
     int* cidx = a.cand_idx + list * LSA_CAND_CHUNK;
     float* cz = a.cand_z + list * LSA_CAND_CHUNK;
     int base = 0;
@@ -368,7 +394,8 @@ void score_kernel(ScoreArgs a) {
 
 template <int KT, int DI, int RING, int WPE, int NW, int CPB>
 hipError_t launch_nw(const ScoreArgs& a, hipStream_t s) {
-  dim3 grid((a.nchunks + CPB - 1) / CPB, a.B);
+  dim3 grid(a.nchunks, a.B);
+  if (CPB == 2) grid = dim3(a.B * a.pairs + a.B * (a.nchunks - 2 * a.pairs));
   const bool wz = a.z != nullptr, wi = a.I != nullptr;
   if (!wz && !wi)
     hipLaunchKernelGGL((score_kernel<KT, DI, RING, false, false, WPE, NW, CPB>), grid, dim3(64 * NW), 0, s, a);
@@ -382,10 +409,16 @@ hipError_t launch_nw(const ScoreArgs& a, hipStream_t s) {
 }
 
 template <int KT, int DI, int RING = 2, int WPE = 2>
-hipError_t launch_t(const ScoreArgs& a, hipStream_t s) {
+hipError_t launch_t(const ScoreArgs& a0, hipStream_t s) {
   const int64_t cus = device_cu_count();
+  ScoreArgs a = a0;
+  a.pairs = 0;
   if ((int64_t)a.nchunks * a.B < 2 * cus) return launch_nw<KT, DI, RING, 1, 16, 1>(a, s);
-  if ((int64_t)((a.nchunks + 1) / 2) * a.B >= 3 * cus) return launch_nw<KT, DI, RING, WPE, 4, 2>(a, s);
+  if ((int64_t)((a.nchunks + 1) / 2) * a.B >= 3 * cus) {
+    // two-chunk blocks for as many pairs as three blocks per compute unit hold
+    a.pairs = (int)std::min<int64_t>(a.nchunks / 2, 3 * cus / a.B);
+    return launch_nw<KT, DI, RING, WPE, 4, 2>(a, s);
+  }
   return launch_nw<KT, DI, RING, WPE, 4, 1>(a, s);
 }
 

@@ -96,6 +96,9 @@ CASES = [
     # unit): a full chunk and a ragged one; a single short chunk
     (1, 768, 4096 + 33, 8, 64, True),
     (2, 768, 300, 8, 64, False),
+    # two-chunk blocks for the first pairs of every request, one-chunk blocks
+    # for the rest (768 // 400 = 1 pair a request on 256 compute units)
+    (1, 400, 3 * 4096 + 7, 8, 64, True),
 ]
 
 

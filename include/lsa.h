@@ -96,6 +96,41 @@ lsa_status lsa_project_query(int L, int B, int D, int H, int dI,
                              hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * The same query encoder from pre-packed weights ([SUMMARY] 2.1 memory-indexer
+ * bullet, as above).  The weights are fixed parameters, so they can be laid
+ * out once, at load time, in the operand order of the matrix-core
+ * instruction the projection runs on; every weight load then reads 1 KiB of
+ * contiguous memory.  The results are those of lsa_project_query, bit for
+ * bit.
+ *
+ * Layout of one layer: its R = H*dI + H rows (the Wq rows, then the Wg rows,
+ * zero rows after them) in T = ceil(R / 16) tiles of 16 rows, the hidden
+ * dimension in D / 64 units; tile t, unit u, step s (0 or 1) and lane l
+ * (0..63) hold the 8 bf16 values of row 16 t + l % 16, columns
+ * 64 u + 32 s + 8 (l / 16) .. +7, as 16 bytes at byte offset
+ * ((t * (D / 64) + u) * 2 + s) * 1024 + 16 l.
+ *
+ * lsa_query_weights_packed_bytes: bytes of one layer's packed buffer
+ *   (T * (D / 64) * 2048); 0 for unsupported H, dI or D.
+ * lsa_pack_query_weights: writes one layer's packed buffer.
+ *   Wq, Wg   bf16 [H*dI][D] and [H][D], as for lsa_project_query
+ *   packed   out, caller-owned, lsa_query_weights_packed_bytes bytes
+ *   All three 16-byte aligned.  Enqueued on stream like every call.
+ * lsa_project_query_packed: lsa_project_query with
+ *   packed   HOST array of L device pointers, each a buffer written by
+ *            lsa_pack_query_weights for that layer
+ *   and every other argument, output and limit as for lsa_project_query.
+ */
+size_t lsa_query_weights_packed_bytes(int H, int dI, int D);
+lsa_status lsa_pack_query_weights(int H, int dI, int D, const uint16_t* Wq,
+                                  const uint16_t* Wg, void* packed,
+                                  hipStream_t stream);
+lsa_status lsa_project_query_packed(int L, int B, int D, int H, int dI,
+                                    const uint16_t* h, int64_t h_layer_stride,
+                                    const void* const* packed, uint16_t* q,
+                                    float* g, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * Lookahead index score and threshold ([SUMMARY] 2.1 scoring bullet: a
  * sigmoid, head-fused, gated match of the query against every earlier
  * compressed entry; dynamic-fetch bullet: entries with I >= 0.5 are fetched).

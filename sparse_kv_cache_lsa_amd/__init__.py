@@ -15,7 +15,8 @@ from ._abi import (LSA_CAND_CHUNK, LSA_KEY_BF16, LSA_KEY_FP8_E4M3, LSAError, che
 
 __all__ = [
     "LSAError", "LSA_KEY_BF16", "LSA_KEY_FP8_E4M3", "LSA_CAND_CHUNK", "load", "lsa_version",
-    "lsa_trigger_due", "lsa_project_query", "lsa_score", "lsa_select_or_compact",
+    "lsa_trigger_due", "lsa_project_query", "lsa_query_weights_packed_bytes",
+    "lsa_pack_query_weights", "lsa_project_query_packed", "lsa_score", "lsa_select_or_compact",
     "lsa_topk_workspace_bytes", "lsa_topk", "lsa_gather_hot",
     "lsa_label_vote_workspace_bytes", "lsa_label_vote",
     "lsa_focal_bce_grad_workspace_bytes", "lsa_focal_bce_grad",
@@ -59,6 +60,29 @@ def lsa_project_query(h, Wq, Wg, q, g, *, h_layer_stride: int = 0, stream=None):
     wg, _k2 = ptr_array([_p(w) for w in Wg])
     check(load().lsa_project_query(L, B, D, H, dI, _p(h), int(h_layer_stride), wq, wg, _p(q),
                                    _p(g), _stream(stream)))
+
+
+def lsa_query_weights_packed_bytes(H: int, dI: int, D: int) -> int:
+    return int(load().lsa_query_weights_packed_bytes(H, dI, D))
+
+
+def lsa_pack_query_weights(Wq, Wg, packed, *, stream=None):
+    """One layer: Wq bf16 [H*dI][D], Wg bf16 [H][D] -> packed (uint8 tensor of
+    lsa_query_weights_packed_bytes(H, dI, D) bytes)."""
+    _dev(Wq, Wg, packed)
+    H, D = Wg.shape
+    dI = Wq.shape[0] // H
+    check(load().lsa_pack_query_weights(H, dI, D, _p(Wq), _p(Wg), _p(packed), _stream(stream)))
+
+
+def lsa_project_query_packed(h, packed, q, g, *, h_layer_stride: int = 0, stream=None):
+    """lsa_project_query with a list of L packed weight buffers."""
+    _dev(h, q, g, *packed)
+    L, B, H, dI = q.shape
+    D = h.shape[-1]
+    wp, _k = ptr_array([_p(w) for w in packed])
+    check(load().lsa_project_query_packed(L, B, D, H, dI, _p(h), int(h_layer_stride), wp, _p(q),
+                                          _p(g), _stream(stream)))
 
 
 def lsa_score(keys, key_scale, q, g, bias, sel_mask, cand_idx, cand_z, cand_count, z=None,

@@ -28,6 +28,9 @@ SIGNATURES = {
     "lsa_version": (C.c_char_p, []),
     "lsa_trigger_due": (I32, [I64, I32]),
     "lsa_project_query": (I32, [I32, I32, I32, I32, I32, P, I64, PP, PP, P, P, P]),
+    "lsa_query_weights_packed_bytes": (SZ, [I32, I32, I32]),
+    "lsa_pack_query_weights": (I32, [I32, I32, I32, P, P, P, P]),
+    "lsa_project_query_packed": (I32, [I32, I32, I32, I32, I32, P, I64, PP, P, P, P]),
     "lsa_score": (I32, [I32, I32, I32, I32, I32, I32, PP, PP, P, P, PF, P, P, P, P, P, P, P]),
     "lsa_select_or_compact": (I32, [I32, I32, P, P, P, I32, P, P, P, P]),
     "lsa_topk_workspace_bytes": (SZ, [I32, I32, I32]),

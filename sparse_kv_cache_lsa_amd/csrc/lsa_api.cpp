@@ -50,31 +50,26 @@ int lsa_trigger_due(int64_t decode_step, int tau) {
 
 // ---------------------------------------------------------------- projection
 
-lsa_status lsa_project_query(int L, int B, int D, int H, int dI, const uint16_t* h,
-                             int64_t h_layer_stride, const uint16_t* const* Wq,
-                             const uint16_t* const* Wg, uint16_t* q, float* g,
-                             hipStream_t stream) {
-  REQUIRE(L >= 1 && L <= LSA_MAX_LAYERS, LSA_E_SHAPE, "lsa_project_query: L=%d not in [1,%d]", L,
+namespace {
+
+// Checks shared by the two projection entry points; fills everything but the
+// weights.
+lsa_status project_common(const char* fn, int L, int B, int D, int H, int dI, const uint16_t* h,
+                          int64_t h_layer_stride, uint16_t* q, float* g, lsa::ProjectArgs& a) {
+  REQUIRE(L >= 1 && L <= LSA_MAX_LAYERS, LSA_E_SHAPE, "%s: L=%d not in [1,%d]", fn, L,
           LSA_MAX_LAYERS);
-  REQUIRE(B >= 1, LSA_E_SHAPE, "lsa_project_query: B=%d < 1", B);
+  REQUIRE(B >= 1, LSA_E_SHAPE, "%s: B=%d < 1", fn, B);
   REQUIRE(D >= 64 && D <= 65536 && D % 64 == 0, LSA_E_SHAPE,
-          "lsa_project_query: D=%d not a multiple of 64 in [64,65536]", D);
+          "%s: D=%d not a multiple of 64 in [64,65536]", fn, D);
   REQUIRE((int64_t)B * D * 2 < ((int64_t)1 << 31), LSA_E_SHAPE,
-          "lsa_project_query: B*D*2 must stay below 2^31 bytes");
-  REQUIRE(H >= 1 && H <= LSA_MAX_HEADS, LSA_E_SHAPE, "lsa_project_query: H=%d not in [1,64]", H);
-  REQUIRE(dI == 64 || dI == 128, LSA_E_SHAPE, "lsa_project_query: dI=%d not 64 or 128", dI);
-  REQUIRE(h_layer_stride >= 0, LSA_E_ARG, "lsa_project_query: negative h_layer_stride");
-  REQUIRE(h && Wq && Wg && q && g, LSA_E_ARG, "lsa_project_query: null pointer argument");
+          "%s: B*D*2 must stay below 2^31 bytes", fn);
+  REQUIRE(H >= 1 && H <= LSA_MAX_HEADS, LSA_E_SHAPE, "%s: H=%d not in [1,64]", fn, H);
+  REQUIRE(dI == 64 || dI == 128, LSA_E_SHAPE, "%s: dI=%d not 64 or 128", fn, dI);
+  REQUIRE(h_layer_stride >= 0, LSA_E_ARG, "%s: negative h_layer_stride", fn);
+  REQUIRE(h && q && g, LSA_E_ARG, "%s: null pointer argument", fn);
   REQUIRE(aligned16(h) && aligned16(q) && (h_layer_stride % 8) == 0, LSA_E_ARG,
-          "lsa_project_query: h/q must be 16-byte aligned (stride multiple of 8)");
-  lsa::ProjectArgs a{};
-  for (int l = 0; l < L; ++l) {
-    REQUIRE(Wq[l] && Wg[l], LSA_E_ARG, "lsa_project_query: null weight pointer for layer %d", l);
-    REQUIRE(aligned16(Wq[l]) && aligned16(Wg[l]), LSA_E_ARG,
-            "lsa_project_query: weights of layer %d not 16-byte aligned", l);
-    a.Wq[l] = Wq[l];
-    a.Wg[l] = Wg[l];
-  }
+          "%s: h/q must be 16-byte aligned (stride multiple of 8)", fn);
+  a = lsa::ProjectArgs{};
   a.h = h;
   a.h_layer_stride = h_layer_stride;
   a.q = q;
@@ -84,7 +79,64 @@ lsa_status lsa_project_query(int L, int B, int D, int H, int dI, const uint16_t*
   a.D = D;
   a.H = H;
   a.dI = dI;
+  return LSA_OK;
+}
+
+}  // namespace
+
+lsa_status lsa_project_query(int L, int B, int D, int H, int dI, const uint16_t* h,
+                             int64_t h_layer_stride, const uint16_t* const* Wq,
+                             const uint16_t* const* Wg, uint16_t* q, float* g,
+                             hipStream_t stream) {
+  lsa::ProjectArgs a;
+  const lsa_status st =
+      project_common("lsa_project_query", L, B, D, H, dI, h, h_layer_stride, q, g, a);
+  if (st != LSA_OK) return st;
+  REQUIRE(Wq && Wg, LSA_E_ARG, "lsa_project_query: null weight array");
+  for (int l = 0; l < L; ++l) {
+    REQUIRE(Wq[l] && Wg[l], LSA_E_ARG, "lsa_project_query: null weight pointer for layer %d", l);
+    REQUIRE(aligned16(Wq[l]) && aligned16(Wg[l]), LSA_E_ARG,
+            "lsa_project_query: weights of layer %d not 16-byte aligned", l);
+    a.Wq[l] = Wq[l];
+    a.Wg[l] = Wg[l];
+  }
   return hip_status(lsa::launch_project(a, stream), "lsa_project_query launch");
+}
+
+size_t lsa_query_weights_packed_bytes(int H, int dI, int D) {
+  if (H < 1 || H > LSA_MAX_HEADS || (dI != 64 && dI != 128) || D < 64 || D > 65536 || D % 64)
+    return 0;
+  return lsa::packed_weights_bytes(H, dI, D);
+}
+
+lsa_status lsa_pack_query_weights(int H, int dI, int D, const uint16_t* Wq, const uint16_t* Wg,
+                                  void* packed, hipStream_t stream) {
+  REQUIRE(D >= 64 && D <= 65536 && D % 64 == 0, LSA_E_SHAPE,
+          "lsa_pack_query_weights: D=%d not a multiple of 64 in [64,65536]", D);
+  REQUIRE(H >= 1 && H <= LSA_MAX_HEADS, LSA_E_SHAPE, "lsa_pack_query_weights: H=%d not in [1,64]",
+          H);
+  REQUIRE(dI == 64 || dI == 128, LSA_E_SHAPE, "lsa_pack_query_weights: dI=%d not 64 or 128", dI);
+  REQUIRE(Wq && Wg && packed, LSA_E_ARG, "lsa_pack_query_weights: null pointer argument");
+  REQUIRE(aligned16(Wq) && aligned16(Wg) && aligned16(packed), LSA_E_ARG,
+          "lsa_pack_query_weights: pointers must be 16-byte aligned");
+  return hip_status(lsa::launch_pack_weights(H, dI, D, Wq, Wg, packed, stream),
+                    "lsa_pack_query_weights launch");
+}
+
+lsa_status lsa_project_query_packed(int L, int B, int D, int H, int dI, const uint16_t* h,
+                                    int64_t h_layer_stride, const void* const* packed,
+                                    uint16_t* q, float* g, hipStream_t stream) {
+  lsa::ProjectArgs a;
+  const lsa_status st =
+      project_common("lsa_project_query_packed", L, B, D, H, dI, h, h_layer_stride, q, g, a);
+  if (st != LSA_OK) return st;
+  REQUIRE(packed, LSA_E_ARG, "lsa_project_query_packed: null weight array");
+  for (int l = 0; l < L; ++l) {
+    REQUIRE(packed[l] && aligned16(packed[l]), LSA_E_ARG,
+            "lsa_project_query_packed: packed weights of layer %d null or not 16-byte aligned", l);
+    a.Wp[l] = packed[l];
+  }
+  return hip_status(lsa::launch_project(a, stream), "lsa_project_query_packed launch");
 }
 
 // --------------------------------------------------------------------- score

@@ -31,6 +31,7 @@ hipError_t launch_score(int dI, lsa_key_dtype kdt, const ScoreArgs& a, hipStream
 struct ProjectArgs {
   const uint16_t* Wq[LSA_MAX_LAYERS];
   const uint16_t* Wg[LSA_MAX_LAYERS];
+  const void* Wp[LSA_MAX_LAYERS];   // packed weights (lsa_pack_query_weights) or null
   const uint16_t* h;
   int64_t h_layer_stride;
   uint16_t* q;
@@ -38,7 +39,10 @@ struct ProjectArgs {
   int L, B, D, H, dI;
 };
 
-hipError_t launch_project(const ProjectArgs& a, hipStream_t s);
+hipError_t launch_project(const ProjectArgs& a, hipStream_t s);   // packed when a.Wp[0] is set
+size_t packed_weights_bytes(int H, int dI, int D);
+hipError_t launch_pack_weights(int H, int dI, int D, const uint16_t* Wq, const uint16_t* Wg,
+                               void* packed, hipStream_t s);
 
 // Compute units of the current device (queried once per device).
 int device_cu_count();

@@ -5,7 +5,8 @@ from __future__ import annotations
 
 from dataclasses import dataclass
 
-from . import (LSA_CAND_CHUNK, lsa_gather_hot, lsa_project_query, lsa_score,
+from . import (LSA_CAND_CHUNK, lsa_gather_hot, lsa_pack_query_weights, lsa_project_query,
+               lsa_project_query_packed, lsa_query_weights_packed_bytes, lsa_score,
                lsa_select_or_compact, lsa_topk, lsa_topk_workspace_bytes)
 
 
@@ -52,12 +53,29 @@ class TriggerBuffers:
         )
 
 
+def pack_weights(Wq, Wg, stream=None):
+    """Packed copies (one uint8 buffer per layer) of the query weights, for
+    lsa_project_query_packed; done once, when the weights are loaded."""
+    import torch
+    out = []
+    for wq, wg in zip(Wq, Wg):
+        H, D = wg.shape
+        p = torch.empty(lsa_query_weights_packed_bytes(H, wq.shape[0] // H, D), dtype=torch.uint8,
+                        device=wq.device)
+        lsa_pack_query_weights(wq, wg, p, stream=stream)
+        out.append(p)
+    return out
+
+
 def run_trigger(buf: TriggerBuffers, h, Wq, Wg, keys, key_scale, bias, pool=None, *,
-                stream=None, project=True, z_layers=None):
+                stream=None, project=True, z_layers=None, packed=None):
     """One indexer trigger.  With project=False the query buffers are used as
-    they are (the caller filled buf.q / buf.g).  z_layers: optional f32
+    they are (the caller filled buf.q / buf.g); with packed (pack_weights)
+    the projection reads the packed weights.  z_layers: optional f32
     [L][B][N] that receives every layer's logit (extra write traffic)."""
-    if project:
+    if project and packed is not None:
+        lsa_project_query_packed(h, packed, buf.q, buf.g, stream=stream)
+    elif project:
         lsa_project_query(h, Wq, Wg, buf.q, buf.g, stream=stream)
     lsa_score(keys, key_scale, buf.q, buf.g, bias, buf.mask, buf.cand_idx, buf.cand_z,
               buf.cand_count, z_layers, stream=stream)

@@ -90,6 +90,15 @@ def test_validation_errors_return_before_launch(lib):
     assert lib.lsa_gather_hot(1, 10, 4, 24, fake, fake, fake, None) == _abi.LSA_E_ARG
     # projection: hidden size not a multiple of 64
     assert lib.lsa_project_query(1, 1, 100, 8, 64, fake, 0, arr, arr, fake, fake, None) == _abi.LSA_E_SHAPE
+    # packed projection: bad D, null or misaligned packed buffers
+    assert lib.lsa_project_query_packed(1, 1, 100, 8, 64, fake, 0, arr, fake, fake, None) == _abi.LSA_E_SHAPE
+    assert lib.lsa_project_query_packed(1, 1, 128, 8, 64, fake, 0, None, fake, fake, None) == _abi.LSA_E_ARG
+    arr_bad, _keep2 = _abi.ptr_array([20])
+    assert lib.lsa_project_query_packed(1, 1, 128, 8, 64, fake, 0, arr_bad, fake, fake, None) == _abi.LSA_E_ARG
+    assert lib.lsa_pack_query_weights(8, 64, 100, fake, fake, fake, None) == _abi.LSA_E_SHAPE
+    assert lib.lsa_pack_query_weights(8, 96, 128, fake, fake, fake, None) == _abi.LSA_E_SHAPE
+    assert lib.lsa_pack_query_weights(8, 64, 128, fake, fake, None, None) == _abi.LSA_E_ARG
+    assert lib.lsa_pack_query_weights(8, 64, 128, fake, fake, C.c_void_p(20), None) == _abi.LSA_E_ARG
     # label vote: too many layers, top_p out of range, no mask and no workspace
     assert lib.lsa_label_vote(1, 33, 100, 0.6, 3, fake, fake, fake, fake, None, 0, None) == _abi.LSA_E_SHAPE
     assert lib.lsa_label_vote(1, 3, 65537, 0.6, 3, fake, fake, fake, fake, None, 0, None) == _abi.LSA_E_SHAPE
@@ -106,6 +115,14 @@ def test_validation_errors_return_before_launch(lib):
     assert F(4, 10, 128, 1, 64, g=-1.0) == _abi.LSA_E_ARG
     assert F(4, 10, 128, 1, 64, ws=C.c_void_p(256), nws=16) == _abi.LSA_E_WORKSPACE
     assert F(4, 10, 128, 1, 64, ws=C.c_void_p(16 + 256)) == _abi.LSA_E_WORKSPACE   # misaligned
+
+
+def test_packed_weight_sizes(lib):
+    # T = ceil((H*dI + H) / 16) tiles x D/64 units x 2 KiB
+    assert lib.lsa_query_weights_packed_bytes(64, 128, 4096) == 516 * 64 * 2048
+    assert lib.lsa_query_weights_packed_bytes(5, 64, 320) == 21 * 5 * 2048
+    assert lib.lsa_query_weights_packed_bytes(65, 64, 320) == 0
+    assert lib.lsa_query_weights_packed_bytes(8, 64, 100) == 0
 
 
 def test_workspace_sizes(lib):

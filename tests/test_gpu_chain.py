@@ -14,19 +14,22 @@ import lsa_inputs as gen
 import lsa_fixtures as fx
 import parity
 from gpu_util import DEV, bf16_host, host, oracle_request
-from sparse_kv_cache_lsa_amd.pipeline import TriggerBuffers, run_trigger
+from sparse_kv_cache_lsa_amd.pipeline import TriggerBuffers, pack_weights, run_trigger
 
 pytestmark = pytest.mark.gpu
 
 
-def _run(inp, pool, with_layers=False, d=None):
-    """One trigger in the benchmark's configuration (masks + merged logits
-    only); with_layers additionally returns every layer's logit."""
+def _run(inp, pool, with_layers=False, d=None, packed=False):
+    """One trigger (masks + merged logits only; with packed, the projection
+    reads packed weights, as the benchmark does); with_layers additionally
+    returns every layer's logit."""
     w = inp.w
     d = gen.to_device(inp, DEV) if d is None else d
     buf = TriggerBuffers.allocate(w.L, w.B, w.N, w.H, w.dI, w.k, w.row_elems, device=DEV)
     zl = torch.empty((w.L, w.B, w.N), dtype=torch.float32, device=DEV) if with_layers else None
-    run_trigger(buf, d["h"], d["Wq"], d["Wg"], d["keys"], d["scale"], d["bias"], pool, z_layers=zl)
+    wp = pack_weights(d["Wq"], d["Wg"]) if packed else None
+    run_trigger(buf, d["h"], d["Wq"], d["Wg"], d["keys"], d["scale"], d["bias"], pool, z_layers=zl,
+                packed=wp)
     torch.cuda.synchronize()
     return buf, zl
 
@@ -82,6 +85,11 @@ def test_chain_small_workloads(name):
         n = int(buf.surv_count[b])      # entries past the count are never written
         assert torch.equal(buf.surv_idx[b, :n], buf2.surv_idx[b, :n])
         assert torch.equal(buf.surv_z[b, :n], buf2.surv_z[b, :n])
+    # packed query weights: the same trigger, bit for bit
+    buf3, _ = _run(inp, pool, packed=True)
+    for a, c in [(buf.q, buf3.q), (buf.g, buf3.g), (buf.mask, buf3.mask),
+                 (buf.surv_count, buf3.surv_count), (buf.topk_idx, buf3.topk_idx)]:
+        assert torch.equal(a, c)
 
 
 @pytest.mark.parametrize("name", ["ctx512k", "ctx1m"])
@@ -92,7 +100,7 @@ def test_chain_full_size(name):
     print(f"{name}: inputs generated", flush=True)
     pool = gen.pool_tensor(w, DEV)
     d = gen.to_device(inp, DEV)
-    buf, _ = _run(inp, pool, d=d)
+    buf, _ = _run(inp, pool, d=d, packed=True)   # the benchmark's configuration
     print(f"{name}: GPU trigger done", flush=True)
     counts = host(buf.surv_count)
     tcounts = host(buf.topk_count)
@@ -110,7 +118,10 @@ def test_chain_full_size(name):
         for l in range(w.L):
             q_or[l, b], g_or[l, b] = fx.oracle.project(inp.h[b], inp.Wq[l], inp.Wg[l], w.H, w.dI)
         print(name, b, _check_request(inp, q_or, g_or, buf, b, pool), flush=True)
-    # per-layer logits of the same launch shape, checked on the first request
+    # per-layer logits of the same launch shape (row-major weights), checked
+    # on the first request; the packed and row-major projections agree bit
+    # for bit
     buf2, zl = _run(inp, pool, with_layers=True, d=d)
+    assert torch.equal(buf2.q, buf.q) and torch.equal(buf2.g, buf.g)
     assert torch.equal(buf2.surv_count, buf.surv_count) and torch.equal(buf2.mask, buf.mask)
     _check_request(inp, q_or, g_or, buf2, 0, pool, zl)

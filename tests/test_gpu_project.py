@@ -12,6 +12,7 @@ import lsa_inputs as gen
 import sparse_kv_cache_lsa_amd as lsa
 from gpu_util import DEV, bf16_dev, bf16_host, dev, host
 from oracle import oracle
+from sparse_kv_cache_lsa_amd.pipeline import pack_weights
 
 pytestmark = pytest.mark.gpu
 
@@ -26,13 +27,23 @@ def _bf16_boundary_distance(a):
     return np.abs(frac - 0.5) * ulp
 
 
-def _run_and_check(w: gen.Workload, h=None, stride=0):
+def _run_and_check(w: gen.Workload, h=None, stride=0, packed=False):
     h = gen.hidden(w) if h is None else h
     Wq, Wg = zip(*[gen.weights(w, l) for l in range(w.L)])
     q = torch.empty((w.L, w.B, w.H, w.dI), dtype=torch.bfloat16, device=DEV)
     g = torch.empty((w.L, w.B, w.H), dtype=torch.float32, device=DEV)
-    lsa.lsa_project_query(bf16_dev(h), [bf16_dev(x) for x in Wq], [bf16_dev(x) for x in Wg],
-                          q, g, h_layer_stride=stride)
+    wq, wg = [bf16_dev(x) for x in Wq], [bf16_dev(x) for x in Wg]
+    lsa.lsa_project_query(bf16_dev(h), wq, wg, q, g, h_layer_stride=stride)
+    if packed:
+        # packed weights: the same q and g bit for bit (then checked below)
+        wp = pack_weights(wq, wg)
+        qp = torch.full_like(q, 7.0)
+        gp = torch.full_like(g, float("nan"))
+        lsa.lsa_project_query_packed(bf16_dev(h), wp, qp, gp, h_layer_stride=stride)
+        torch.cuda.synchronize()
+        assert torch.equal(qp.view(torch.int16), q.view(torch.int16))
+        assert torch.equal(gp, g)
+        q, g = qp, gp
     torch.cuda.synchronize()
     qg, gg = bf16_host(q), host(g)
     excluded = 0
@@ -77,3 +88,48 @@ def test_project_per_layer_hidden_states():
     rng = np.random.default_rng(3)
     h = gen.to_bf16_bits(rng.standard_normal((w.L * w.B, w.D)).astype(np.float32))
     _run_and_check(w, h=h, stride=w.B * w.D)
+
+
+# Packed weights (lsa_pack_query_weights): one tile, gate tiles, a ragged last
+# tile (H*dI + H not a multiple of 16), several request groups, per-layer
+# hidden states, the largest tile count.
+@pytest.mark.parametrize("B,L,D,H,dI", [(1, 1, 64, 1, 64), (5, 2, 768, 40, 64), (7, 1, 320, 5, 64),
+                                        (40, 2, 1024, 24, 128), (65, 1, 512, 7, 64),
+                                        (32, 3, 4096, 64, 128)])
+def test_project_packed_weights(B, L, D, H, dI):
+    w = gen.custom("projp", 94, B=B, L=L, H=H, dI=dI, D=D, N=64)
+    _run_and_check(w, packed=True)
+
+
+def test_project_packed_per_layer_hidden_states():
+    w = gen.custom("projp2", 95, B=3, L=2, H=8, dI=128, D=512, N=64)
+    rng = np.random.default_rng(4)
+    h = gen.to_bf16_bits(rng.standard_normal((w.L * w.B, w.D)).astype(np.float32))
+    _run_and_check(w, h=h, stride=w.B * w.D, packed=True)
+
+
+def test_pack_layout_is_the_documented_one():
+    # the packed buffer against its definition, element by element
+    H, dI, D = 3, 64, 192
+    rng = np.random.default_rng(6)
+    Wq = rng.integers(0, 1 << 16, (H * dI, D), dtype=np.uint16)
+    Wg = rng.integers(0, 1 << 16, (H, D), dtype=np.uint16)
+    n = lsa.lsa_query_weights_packed_bytes(H, dI, D)
+    R = H * dI + H
+    T = (R + 15) // 16
+    assert n == T * (D // 64) * 2048
+    p = torch.full((n,), 0xA5, dtype=torch.uint8, device=DEV)
+    lsa.lsa_pack_query_weights(dev(Wq.view(np.int16)), dev(Wg.view(np.int16)), p)
+    torch.cuda.synchronize()
+    got = host(p).view(np.uint16).reshape(T, D // 64, 2, 64, 8)
+    W = np.zeros((16 * T, D), np.uint16)
+    W[:H * dI] = Wq
+    W[H * dI:R] = Wg
+    l = np.arange(64)
+    for t in range(T):
+        for u in range(D // 64):
+            for st in range(2):
+                rows = 16 * t + l % 16
+                cols = 64 * u + 32 * st + 8 * (l // 16)
+                want = np.stack([W[rows, cols + e] for e in range(8)], axis=1)
+                assert np.array_equal(got[t, u, st], want), (t, u, st)

@@ -13,21 +13,16 @@
 // keys with one collapsed query per row, qe_t = sum_h g_th q_th (dI wide),
 // and the backward pass goes through G_t = sum_s delta_ts k_s:
 //   d loss / d q_thi = g_th G_ti,   dW_q[(h,i)][d] = sum_t g_th G_ti h_td.
-// The two large products (projection, dW_q) split their fp32 operand three
-// ways into bf16 and run on v_mfma_f32_32x32x16_bf16 against the exactly-bf16
-// hidden states; the others run on v_mfma_f32_32x32x2_f32.
-// The operands of each product are stored with the contraction axis
-// contiguous, so a lane loads four consecutive k values of its row of A and
-// of its row of B with one vector load and feeds four MFMAs; the k order is
-// permuted identically in A and B (lane half 0 supplies k0..k0+3, half 1
-// k0+4..k0+7), which leaves every dot product unchanged.
+// Every product splits its fp32 operand three ways into bf16 and runs on
+// v_mfma_f32_32x32x16_bf16 against an exactly-bf16 operand (hidden states or
+// keys): the products are exact and only the fp32 accumulation rounds.
 //
 // Kernels (one stream, in order):
 //   1 project   partials of ([W_q; W_g] h_t)_r per slice of D (W read once)
 //   2 collapse  slice sums in order; g = softplus(gate rows), qe_t, gT[h][t]
-//   3 transpose K -> KT [dI][Np], h -> hT [D][64] in one launch (contraction axes contiguous)
-//   4 logits    z = K qe^T + b; loss terms; delta = dloss/dz -> [Q][Np]
-//   5 grad      partial G over 128-entry chunks
+//   3 transpose h -> hT [D][64] (contraction axis of dW_q contiguous)
+//   4 logits    per 128-entry chunk: z = K qe^T + b, loss terms,
+//               delta = dloss/dz (in LDS), partial G = delta K
 //   6 reduce    GT[i][t] = sum of partials, loss = sum / (Q N) (fixed orders)
 //   7 dW        dW_q = (gT * GT) hT^T, written once (nontemporal)
 #include "lsa_device.h"
@@ -39,19 +34,6 @@ namespace {
 constexpr int kQP = 64;      // padded query count (rows of the small operands)
 constexpr int kChunk = 128;  // entries per partial-gradient block
 constexpr int kProjTR = 2;   // 32-row weight tiles per projection wave
-
-__device__ __forceinline__ f32x4 bf16x4_to_f32(uint2 raw) {
-  f32x4 r;
-  r[0] = __uint_as_float(raw.x << 16);
-  r[1] = __uint_as_float(raw.x & 0xFFFF0000u);
-  r[2] = __uint_as_float(raw.y << 16);
-  r[3] = __uint_as_float(raw.y & 0xFFFF0000u);
-  return r;
-}
-
-__device__ __forceinline__ f32x4 load_bf16x4(const uint16_t* p) {
-  return bf16x4_to_f32(*(const uint2*)p);
-}
 
 // Buffer resources: loads past `bytes` return 0, so rows beyond the operand
 // (padding queries, the tail of the last tile) need no branch -- a branch
@@ -66,18 +48,7 @@ __device__ __forceinline__ f32x4 buf_f32x4(__amdgpu_buffer_rsrc_t r, uint32_t by
   return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
 }
 
-__device__ __forceinline__ f32x4 buf_bf16x4(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
-  const u32x2 v = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, byte_off, 0, 0));
-  return bf16x4_to_f32(uint2{v[0], v[1]});
-}
-
 constexpr uint32_t kFar = 0x7FFFFFF0u;   // an offset past every range used here
-
-__device__ __forceinline__ f32x16 mfma4(f32x4 a, f32x4 b, f32x16 c) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) c = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i], b[i], c, 0, 0, 0);
-  return c;
-}
 
 // Three-way bf16 split of eight fp32 values: x = hi + mid + lo exactly (each
 // residual is exact in fp32 and 3 x 8 significant bits cover fp32's 24), so
@@ -365,54 +336,77 @@ __global__ __launch_bounds__(256) void ftranspose_kernel(TransposeJob j0, Transp
   }
 }
 
-// ---------------------------------------------------------------- 4 logits + delta
-// grid: ceil(N/64); wave w takes entries 32*(2*blockIdx.x + w/2) .. +31 and
-// queries 32*(w%2) .. +31 (A = collapsed queries, B = keys), so the 32 lanes
-// of a half-wave hold consecutive entries of one query: label loads and delta
-// stores coalesce.  The epilogue (loss terms, dloss/dz) is VALU work; small
-// tiles give enough waves to hide its latency.  The collapsed queries (64 x
-// DI fp32) are first copied into LDS with contiguous loads: every wave needs
-// 32 of their rows, and fragment loads straight from memory touch 32 rows
-// per instruction.
+// ---------------------------------------------------------------- 4+5 fused
+// Logits, loss terms, dloss/dz and the partial key gradient of one chunk of
+// kChunk entries in one kernel; grid ceil(Np / kChunk), 256 threads.
+//  1. The chunk's key rows (bf16, kChunk x DI; rows past N read 0) and the
+//     collapsed queries (fp32, 64 x DI) are copied into LDS with contiguous
+//     loads.
+//  2. Logits: wave w (of 8) takes the chunk's entries 32 (w % 4) .. +31
+//     against queries 32 (w / 4) .. +31.  A = collapsed queries split exactly into three bf16
+//     parts, B = key rows (exact bf16), so the products are exact and only
+//     the fp32 accumulation rounds; lanes run over entries, so label loads
+//     coalesce.  The epilogue sums the loss terms and writes
+//     delta = dloss/dz into LDS (0 outside [0, Q) x [0, N)).
+//  3. Partial key gradient Gp[chunk][t][i] = sum over the chunk's entries of
+//     delta[t][s] K[s][i]: wave w takes queries 32 (w & 1) .. +31 and dims
+//     32 (w >> 1) .. +31; A = delta split into three bf16 parts, B = key
+//     columns gathered from the LDS rows.
+// delta never goes to memory and the keys need no transposed copy; as two
+// kernels (logits, then G over a transposed key copy) this took 34 us for the
+// label workload.
 template <int DI>
-__global__ __launch_bounds__(256) void flogits_kernel(int Q, int N, int Np, float gamma,
-                                                      float bias, float inv_qn,
-                                                      const uint16_t* __restrict__ K,
-                                                      const float* __restrict__ qe,
-                                                      const uint8_t* __restrict__ label,
-                                                      float* __restrict__ delta,
-                                                      double* __restrict__ loss_part) {
-  __shared__ double wsum[4];
-  __shared__ __attribute__((aligned(16))) float qs[kQP][DI + 4];   // rows 16 B apart in the banks
+__global__ __launch_bounds__(512) void flogits_grad_kernel(int Q, int N, float gamma, float bias,
+                                                           float inv_qn,
+                                                           const uint16_t* __restrict__ K,
+                                                           const float* __restrict__ qe,
+                                                           const uint8_t* __restrict__ label,
+                                                           float* __restrict__ Gp,
+                                                           double* __restrict__ loss_part) {
+  constexpr int NT = 512;          // 8 wavefronts
+  constexpr int KP = DI + 8;       // bf16 pitch of the key rows (16 B pad)
+  constexpr int QP = DI + 4;       // fp32 pitch of the query rows
+  constexpr int DP = kChunk + 4;   // fp32 pitch of the delta rows
+  __shared__ __attribute__((aligned(16))) uint16_t ks[kChunk][KP];
+  __shared__ __attribute__((aligned(16))) float qs[kQP][QP];
+  __shared__ __attribute__((aligned(16))) float dls[kQP][DP];
+  __shared__ double wsum[NT / 64];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int n = lane & 31, half = lane >> 5;
+  const int s_base = blockIdx.x * kChunk;
+
+  // 1. stage (K need only be 8-byte aligned: 8-byte loads)
+  const __amdgpu_buffer_rsrc_t rk = rsrc(K, (size_t)N * DI * 2);
 #pragma unroll
-  for (int i = 0; i < kQP * DI / 4 / 256; ++i) {
-    const int c = threadIdx.x + 256 * i, r = c / (DI / 4), col = 4 * (c - r * (DI / 4));
+  for (int i = 0; i < kChunk * DI / 4 / NT; ++i) {
+    const int c = threadIdx.x + NT * i, r = c / (DI / 4), col = 4 * (c - r * (DI / 4));
+    const u32x2 v = __builtin_bit_cast(
+        u32x2, __builtin_amdgcn_raw_buffer_load_b64(rk, ((uint32_t)(s_base + r) * DI + col) * 2, 0, 0));
+    *(u32x2*)&ks[r][col] = v;
+  }
+#pragma unroll
+  for (int i = 0; i < kQP * DI / 4 / NT; ++i) {
+    const int c = threadIdx.x + NT * i, r = c / (DI / 4), col = 4 * (c - r * (DI / 4));
     *(f32x4*)&qs[r][col] = *(const f32x4*)(qe + r * DI + col);
   }
   __syncthreads();
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int n = lane & 31, half = lane >> 5;
-  const int s0 = (blockIdx.x * 2 + (wave >> 1)) * 32;
-  const int t0 = 32 * (wave & 1);
-  const int s = s0 + n;
-  const __amdgpu_buffer_rsrc_t rk = rsrc(K, (size_t)N * DI * 2);
-  const uint32_t boff = s < N ? (uint32_t)s * DI * 2 : kFar;
+
+  // 2. logits and delta: wave w takes entries 32 (w % 4) .. +31 against
+  // queries 32 (w / 4) .. +31
+  const int s0 = 32 * (wave & 3), tq2 = 32 * (wave >> 2);
   f32x16 acc = {};
 #pragma unroll
-  for (int k = 0; k < DI; k += 8) {
-    const int kk = k + 4 * half;
-    const f32x4 b = buf_bf16x4(rk, boff + kk * 2);
-    const f32x4 a = *(const f32x4*)&qs[t0 + n][kk];
-    acc = mfma4(a, b, acc);
+  for (int k = 0; k < DI; k += 16) {
+    const int kk = k + 8 * half;
+    const Split3 a = split3(*(const f32x4*)&qs[tq2 + n][kk], *(const f32x4*)&qs[tq2 + n][kk + 4]);
+    acc = mfma_split(a, *(const bf16x8*)&ks[s0 + n][kk], acc);
   }
-  // labels of the lane's 16 (query, entry) pairs, all loads issued first;
-  // pairs outside [0,Q) x [0,N) read 0 and are masked below
+  const int s = s_base + s0 + n;
   const __amdgpu_buffer_rsrc_t rl = rsrc(label, (size_t)Q * N);
-  const __amdgpu_buffer_rsrc_t rdl = rsrc(delta, (size_t)Q * Np * 4);
   uint32_t yv[16];
 #pragma unroll
   for (int rr = 0; rr < 16; ++rr) {
-    const int t = t0 + acc_row(rr, half);
+    const int t = tq2 + acc_row(rr, half);
     yv[rr] = __builtin_amdgcn_raw_buffer_load_b8(rl, s < N ? (uint32_t)t * N + s : kFar, 0, 0);
   }
   // gamma as a whole number in [1, 8], else 0 (uniform)
@@ -420,7 +414,7 @@ __global__ __launch_bounds__(256) void flogits_kernel(int Q, int N, int Np, floa
   double lsum = 0.0;
 #pragma unroll
   for (int rr = 0; rr < 16; ++rr) {
-    const int t = t0 + acc_row(rr, half);
+    const int t = tq2 + acc_row(rr, half);
     const bool valid = t < Q && s < N;
     const float z = acc[rr] + bias;
     const int y = yv[rr] ? 1 : 0;
@@ -432,68 +426,38 @@ __global__ __launch_bounds__(256) void flogits_kernel(int Q, int N, int Np, floa
     if (valid) lsum += (double)nll + (double)(mod * nll);
     const float dbce = sigmoid_f(z) - (float)y;
     const float dfl_du = mod * (-gamma * pu * nll - qu);
-    const float d = valid ? (dbce + (y ? dfl_du : -dfl_du)) * inv_qn : 0.f;
-    // entries in [N, Np) get 0; rows t >= Q and entries >= Np are dropped
-    const uint32_t off = s < Np ? ((uint32_t)t * Np + s) * 4 : kFar;
-    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, d), rdl, off, 0, 0);
+    dls[t][s0 + n] = valid ? (dbce + (y ? dfl_du : -dfl_du)) * inv_qn : 0.f;
   }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) lsum += __shfl_xor(lsum, off, 64);
   if (lane == 0) wsum[wave] = lsum;
   __syncthreads();
-  if (threadIdx.x == 0) loss_part[blockIdx.x] = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
-}
-
-// ---------------------------------------------------------------- 5 partial G
-// grid: ceil(Np/kChunk) chunks; wave w: queries 32*(w&1).., dims half (w>>1).
-template <int DI>
-__global__ __launch_bounds__(256) void fgrad_kernel(int Q, int Np, const float* __restrict__ delta,
-                                                    const uint16_t* __restrict__ KT,
-                                                    float* __restrict__ Gp) {
-  constexpr int NTI = DI / 64;   // 32-dim tiles per wave
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int n = lane & 31, half = lane >> 5;
-  const int t = 32 * (wave & 1) + n;
-  const int i0 = (wave >> 1) * (DI / 2);
-  const __amdgpu_buffer_rsrc_t rd = rsrc(delta, (size_t)Q * Np * 4);
-  const uint32_t aoff = (uint32_t)t * Np * 4;   // rows t >= Q lie past the range
-  const int kbeg = blockIdx.x * kChunk, kend = min(Np, kbeg + kChunk);
-  f32x16 acc[NTI];
+  if (threadIdx.x == 0) {
+    double tot = 0.0;
 #pragma unroll
-  for (int j = 0; j < NTI; ++j) acc[j] = f32x16{};
-  const __amdgpu_buffer_rsrc_t rkt = rsrc(KT, (size_t)DI * Np * 2);
-  uint32_t boff[NTI];
-#pragma unroll
-  for (int j = 0; j < NTI; ++j) boff[j] = (uint32_t)(i0 + 32 * j + n) * Np * 2;
-  int k = kbeg;
-  for (; k + 32 <= kend; k += 32) {
-    f32x4 a[4], b[4][NTI];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int kk = k + 8 * u + 4 * half;
-      a[u] = buf_f32x4(rd, aoff + kk * 4);
-#pragma unroll
-      for (int j = 0; j < NTI; ++j) b[u][j] = buf_bf16x4(rkt, boff[j] + kk * 2);
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int j = 0; j < NTI; ++j) acc[j] = mfma4(a[u], b[u][j], acc[j]);
+    for (int w = 0; w < NT / 64; ++w) tot += wsum[w];
+    loss_part[blockIdx.x] = tot;
   }
-  for (; k < kend; k += 8) {
-    const int kk = k + 4 * half;
-    const f32x4 a = buf_f32x4(rd, aoff + kk * 4);
+
+  // 3. partial key gradient: wave w takes queries 32 (w & 1) .. +31 and dims
+  // 32 (w >> 1) .. +31 (DI = 64: waves 4-7 have no tile)
+  const int tq = 32 * (wave & 1), i0 = 32 * (wave >> 1);
+  if (i0 >= DI) return;
+  f32x16 g = {};
+  const int col = i0 + n;
 #pragma unroll
-    for (int j = 0; j < NTI; ++j) acc[j] = mfma4(a, buf_bf16x4(rkt, boff[j] + kk * 2), acc[j]);
+  for (int ss = 0; ss < kChunk; ss += 16) {
+    const int sk = ss + 8 * half;
+    const Split3 a = split3(*(const f32x4*)&dls[tq + n][sk], *(const f32x4*)&dls[tq + n][sk + 4]);
+    u32x4 w;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      w[e] = (uint32_t)ks[sk + 2 * e][col] | ((uint32_t)ks[sk + 2 * e + 1][col] << 16);
+    g = mfma_split(a, __builtin_bit_cast(bf16x8, w), g);
   }
   float* out = Gp + (size_t)blockIdx.x * kQP * DI;
 #pragma unroll
-  for (int j = 0; j < NTI; ++j)
-#pragma unroll
-    for (int rr = 0; rr < 16; ++rr) {
-      const int tt = 32 * (wave & 1) + acc_row(rr, half);
-      out[tt * DI + i0 + 32 * j + n] = acc[j][rr];
-    }
+  for (int rr = 0; rr < 16; ++rr) out[(tq + acc_row(rr, half)) * DI + col] = g[rr];
 }
 
 // ---------------------------------------------------------------- 6 reduce
@@ -580,9 +544,7 @@ struct FocalWs {
   float* qp;
   float* gT;
   float* qe;
-  uint16_t* KT;
   uint16_t* hT;
-  float* delta;
   float* Gp;
   float* GT;
   double* loss_part;
@@ -600,7 +562,7 @@ FocalWs carve(void* base, int Q, int N, int D, int H, int dI) {
   const int Np = (N + 7) & ~7;
   const size_t R = (size_t)H * dI + H;
   const int nchunks = (Np + kChunk - 1) / kChunk;
-  const int nloss = (N + 63) / 64;
+  const int nloss = nchunks;
   size_t off = 0;
   FocalWs w;
   auto take = [&](size_t bytes) {
@@ -611,9 +573,7 @@ FocalWs carve(void* base, int Q, int N, int D, int H, int dI) {
   w.qp = (float*)take((size_t)proj_slices(D) * kQP * R * 4);
   w.gT = (float*)take((size_t)64 * kQP * 4);
   w.qe = (float*)take((size_t)kQP * dI * 4);
-  w.KT = (uint16_t*)take((size_t)dI * Np * 2);
   w.hT = (uint16_t*)take((size_t)D * kQP * 2);
-  w.delta = (float*)take((size_t)kQP * Np * 4);
   w.Gp = (float*)take((size_t)nchunks * kQP * dI * 4);
   w.GT = (float*)take((size_t)dI * kQP * 4);
   w.loss_part = (double*)take((size_t)nloss * 8);
@@ -635,7 +595,7 @@ hipError_t launch_focal(int Q, int N, int D, int H, int dI, float gamma, const u
   const int HdI = H * dI;
   const int R = HdI + H;
   const int nchunks = (Np + kChunk - 1) / kChunk;
-  const int nloss = (N + 63) / 64;
+  const int nloss = nchunks;   // one loss partial per chunk
   const double inv_qn = 1.0 / ((double)Q * (double)N);
   hipError_t e;
 #define FOCAL_CHECK()                        \
@@ -656,25 +616,17 @@ hipError_t launch_focal(int Q, int N, int D, int H, int dI, float gamma, const u
                      w.qp, w.gT, w.qe);
   FOCAL_CHECK();
   {
-    const TransposeJob jk{K, w.KT, N, dI, Np, (Np + 63) / 64};
     const TransposeJob jh{h, w.hT, Q, D, kQP, 1};
-    const int nbk = jk.ntx * ((dI + 63) / 64), nbh = (D + 63) / 64;
-    hipLaunchKernelGGL(ftranspose_kernel, dim3(nbk + nbh), dim3(256), 0, s, jk, jh, nbk);
+    hipLaunchKernelGGL(ftranspose_kernel, dim3((D + 63) / 64), dim3(256), 0, s, jh, jh,
+                       (D + 63) / 64);
   }
   FOCAL_CHECK();
   if (dI == 64)
-    hipLaunchKernelGGL((flogits_kernel<64>), dim3(nloss), dim3(256), 0, s, Q, N, Np, gamma, bias,
-                       (float)inv_qn, K, w.qe, label, w.delta, w.loss_part);
+    hipLaunchKernelGGL((flogits_grad_kernel<64>), dim3(nchunks), dim3(512), 0, s, Q, N, gamma, bias,
+                       (float)inv_qn, K, w.qe, label, w.Gp, w.loss_part);
   else
-    hipLaunchKernelGGL((flogits_kernel<128>), dim3(nloss), dim3(256), 0, s, Q, N, Np, gamma, bias,
-                       (float)inv_qn, K, w.qe, label, w.delta, w.loss_part);
-  FOCAL_CHECK();
-  if (dI == 64)
-    hipLaunchKernelGGL((fgrad_kernel<64>), dim3(nchunks), dim3(256), 0, s, Q, Np, w.delta, w.KT,
-                       w.Gp);
-  else
-    hipLaunchKernelGGL((fgrad_kernel<128>), dim3(nchunks), dim3(256), 0, s, Q, Np, w.delta, w.KT,
-                       w.Gp);
+    hipLaunchKernelGGL((flogits_grad_kernel<128>), dim3(nchunks), dim3(512), 0, s, Q, N, gamma,
+                       bias, (float)inv_qn, K, w.qe, label, w.Gp, w.loss_part);
   FOCAL_CHECK();
   hipLaunchKernelGGL(freduce_kernel, dim3(kQP * dI / 64), dim3(256), 0, s, Q, dI, nchunks, w.Gp,
                      w.GT, nloss, inv_qn, w.loss_part, loss);

@@ -11,9 +11,10 @@
 //    qt = sum_h g_h q_h.  Each block forms qt (fp32) for its request and
 //    every layer once, from the bf16 queries and fp32 gates, so scoring an
 //    entry is one dI-long dot product, not H of them.
-//  * grid.y = request, grid.x = chunk of 32-entry tiles; the NW wavefronts of
-//    a block take every NW-th tile of the chunk, so a block streams one
-//    contiguous key range (the pattern HBM serves best).
+//  * A block takes one request and one or two consecutive chunks of
+//    LSA_CAND_CHUNK entries (see score_kernel for the grid); the NW
+//    wavefronts of a block take every NW-th 32-entry tile of its range, so a
+//    block streams one contiguous key range (the pattern HBM serves best).
 //  * Keys are read through a buffer resource per (layer, request): each load
 //    instruction covers 1 KiB of contiguous keys (16 B per lane, nontemporal),
 //    the lane offset is a 32-bit VGPR, and the hardware range check returns 0

@@ -43,6 +43,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="ctx1m")
     p.add_argument("--skip-cpu", action="store_true", help="do not time the CPU oracle")
+    p.add_argument("--event-every", type=int, default=5,
+                   help="bracket the roofline kernel with events in every n-th timed step")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="CPU oracle sample budget (whole requests until this much time)")
     p.add_argument("--copy-probe", type=int, default=0,
@@ -141,18 +143,21 @@ def main():
     torch.cuda.synchronize()
 
     # timed region: K steps between two synchronisations.  Two HIP events on
-    # the kernels' stream bracket every score launch (the roofline kernel).
-    # Each recorded event costs the stream a few microseconds between two
-    # kernels, so the per-call breakdown comes from a separate pass below.
-    evs = [(ev(), ev()) for _ in range(args.steps)]
+    # the kernels' stream bracket the score launch (the roofline kernel) of
+    # every --event-every-th step.  Each recorded event costs the stream a few
+    # microseconds between two kernels, so the sample keeps that overhead
+    # small, and the per-call breakdown comes from a separate pass below.
+    every = max(1, args.event_every)
+    evs = [(ev(), ev()) if i % every == 0 else None for i in range(args.steps)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for e in evs:
-        step({1: e[0], 2: e[1]})
+        step(None if e is None else {1: e[0], 2: e[1]})
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     ms_per_step = wall * 1e3 / max(args.steps, 1)
-    mean_score = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    sampled = [e for e in evs if e is not None]
+    mean_score = float(np.mean([e[0].elapsed_time(e[1]) for e in sampled]))
 
     # per-call breakdown: K more steps (untimed) with an event between calls
     bd = [[ev() for _ in range(6)] for _ in range(args.steps)]
@@ -224,7 +229,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": "lsa_score", "algorithmic_bytes_per_launch": key_bytes,
-                     "mean_launch_ms": mean_score},
+                     "mean_launch_ms": mean_score, "timed_launches_sampled": len(sampled)},
         "score_select": {"ms": score_select, "GB/s": ss_gbs, "frac_of_peak": ss_gbs / HBM_PEAK_GBS,
                          "triples_per_s": triples / (score_select * 1e-3)},
         "kernel_ms_median": per,
@@ -323,9 +328,11 @@ def bench_labels(args):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    # timed region: two events bracket every vote launch (the roofline
-    # kernel); the loss/gradient time comes from a separate pass
-    evs = [[ev(), ev()] for _ in range(args.steps)]
+    # timed region: two events bracket the vote launch (the roofline kernel)
+    # of every --event-every-th step; the loss/gradient time comes from a
+    # separate pass
+    every = max(1, args.event_every)
+    evs = [[ev(), ev()] if i % every == 0 else None for i in range(args.steps)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for e in evs:
@@ -333,7 +340,7 @@ def bench_labels(args):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     ms_per_step = wall * 1e3 / max(args.steps, 1)
-    vote_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    vote_ms = [e[0].elapsed_time(e[1]) for e in evs if e is not None]
     bd = [[ev() for _ in range(3)] for _ in range(args.steps)]
     for e in bd:
         step(e)
@@ -362,7 +369,8 @@ def bench_labels(args):
                    "head_dim": w.dI, "hidden": w.D, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": vote_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": vote_gbs / HBM_PEAK_GBS, "traffic": None, "kernel": "lsa_label_vote",
-                     "algorithmic_bytes_per_launch": vote_bytes, "mean_launch_ms": vote_mean},
+                     "algorithmic_bytes_per_launch": vote_bytes, "mean_launch_ms": vote_mean,
+                     "timed_launches_sampled": len(vote_ms)},
         "focal": {"bound": "mfma", "achieved": focal_tfs, "peak": 157.3, "unit": "TFLOP/s",
                   "frac": focal_tfs / 157.3, "kernel": "lsa_focal_bce_grad (fp32)",
                   "algorithmic_flops_per_launch": focal_flops, "mean_launch_ms": focal_mean},

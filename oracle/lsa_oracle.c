@@ -241,6 +241,50 @@ void lsa_or_gather(int64_t N, int64_t row_bytes, const uint8_t* pool,
 }
 
 /* ------------------------------------------------------------------------ */
+/* O10 cold-pool fetch                                                      */
+/* ------------------------------------------------------------------------ */
+
+int64_t lsa_or_fetch(int64_t N, int64_t S, int64_t row_bytes, const uint8_t* cold,
+                     int64_t n, const int32_t* surv, int32_t* slot_of,
+                     int32_t* entry_of, uint8_t* rows) {
+  uint8_t* is_surv = (uint8_t*)calloc((size_t)(N > 0 ? N : 1), 1);
+  for (int64_t i = 0; i < n; ++i) is_surv[surv[i]] = 1;
+
+  /* rows to copy: survivors not resident now (step 2's order) */
+  int64_t need = 0, kept = 0;
+  for (int64_t i = 0; i < n; ++i) {
+    if (slot_of[surv[i]] < 0) ++need;
+    else ++kept;
+  }
+  if (kept + need > S) {
+    free(is_surv);
+    return -1;
+  }
+
+  /* step 1: evict */
+  for (int64_t j = 0; j < S; ++j) {
+    int32_t e = entry_of[j];
+    if (e >= 0 && !is_surv[e]) {
+      slot_of[e] = -1;
+      entry_of[j] = -1;
+    }
+  }
+
+  /* steps 2 and 3: ascending survivors into ascending free slots */
+  int64_t j = 0;
+  for (int64_t i = 0; i < n; ++i) {
+    int32_t s = surv[i];
+    if (slot_of[s] >= 0) continue;
+    while (entry_of[j] >= 0) ++j;
+    entry_of[j] = s;
+    slot_of[s] = (int32_t)j;
+    memcpy(rows + j * row_bytes, cold + (int64_t)s * row_bytes, (size_t)row_bytes);
+  }
+  free(is_surv);
+  return need;
+}
+
+/* ------------------------------------------------------------------------ */
 /* O8 labels                                                                  */
 /* ------------------------------------------------------------------------ */
 

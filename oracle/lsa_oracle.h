@@ -84,6 +84,23 @@ int64_t lsa_or_topk(int64_t n, const int32_t* surv_idx, const double* surv_z,
 void lsa_or_gather(int64_t N, int64_t row_bytes, const uint8_t* pool,
                    int64_t k, const int32_t* idx, uint8_t* hot);
 
+/* ---- O10: cold-pool fetch with reuse ([SUMMARY] 2.1 dynamic-fetch bullet;
+ * [REVIEW] section 2, the step that moves entries scoring >= 0.5 from the CPU
+ * to the GPU).  One request.  A resident set of S slots holds rows of the
+ * cold pool: slot_of[N] is the slot of entry s or -1, entry_of[S] the entry in
+ * slot j or -1, rows[S][row_bytes] the bytes.  For the ascending survivor
+ * list surv[n]:
+ *   1. each resident entry that is not a survivor leaves its slot;
+ *   2. each survivor that is not resident takes a free slot: the i-th such
+ *      survivor (ascending entry) takes the i-th free slot (ascending slot);
+ *   3. its row is copied from cold[entry] into rows[slot].
+ * Survivors already resident keep their slot and are not copied again.
+ * Returns the number of rows copied, or -1 (tables unchanged) if the free
+ * slots do not suffice. */
+int64_t lsa_or_fetch(int64_t N, int64_t S, int64_t row_bytes, const uint8_t* cold,
+                     int64_t n, const int32_t* surv, int32_t* slot_of,
+                     int32_t* entry_of, uint8_t* rows);
+
 /* ---- O8: golden labels ([SUMMARY] 2.2 steps 1-3; [REVIEW] section 2,
  * training labels).  One row of raw logits x[N]:
  *   pi = softmax(x); walk entries in order (x desc, index asc) and include

@@ -62,6 +62,7 @@ def _load():
         "lsa_or_merge_compact": (i64, [i32, i64, P, P, i64, P, P]),
         "lsa_or_topk": (i64, [i64, P, P, i64, P]),
         "lsa_or_gather": (None, [i64, i64, P, i64, P, P]),
+        "lsa_or_fetch": (i64, [i64, i64, i64, P, i64, P, P, P, P]),
         "lsa_or_nucleus": (i64, [i64, P, f64, P, P]),
         "lsa_or_vote": (None, [i32, i64, P, i32, P, P]),
         "lsa_or_focal_bce_grad": (f64, [i32, i64, i32, i32, i32, f64, P, P, P, f64, P, P, P, P]),
@@ -222,6 +223,36 @@ def gather(pool, idx) -> np.ndarray:
     hot = np.empty((idx.shape[0], rb), np.uint8)
     lib.lsa_or_gather(N, rb, _p(pool), idx.shape[0], _p(idx), _p(hot))
     return hot
+
+
+# ---- O10 cold-pool fetch ------------------------------------------------------
+
+def fetch(cold, surv, slot_of, entry_of, rows) -> int:
+    """One request, in place.  cold uint8 [N][row_bytes] (the cold pool);
+    surv int32 [n] ascending survivors; slot_of int32 [N], entry_of int32 [S],
+    rows uint8 [S][row_bytes] (the resident set, updated in place).  Returns
+    the number of rows copied, or -1 if the free slots do not suffice."""
+    lib = _load()
+    cold = _c(cold, np.uint8)
+    surv = _c(surv, np.int32)
+    for a, dt in ((slot_of, np.int32), (entry_of, np.int32), (rows, np.uint8)):
+        if a.dtype != dt or not a.flags.c_contiguous:
+            raise ValueError("fetch updates slot_of/entry_of/rows in place: pass contiguous arrays")
+    N, rb = cold.shape
+    S = entry_of.shape[0]
+    assert slot_of.shape == (N,) and rows.shape == (S, rb)
+    return int(lib.lsa_or_fetch(N, S, rb, _p(cold), surv.shape[0], _p(surv), _p(slot_of),
+                                _p(entry_of), _p(rows)))
+
+
+def gather_resident(rows, slot_of, idx) -> np.ndarray:
+    """Rows of the resident set for entry indices idx (zero row for idx < 0 or
+    an entry not resident)."""
+    idx = np.asarray(idx, np.int64)
+    slot = np.full(idx.shape, -1, np.int32)
+    ok = idx >= 0
+    slot[ok] = slot_of[idx[ok]]
+    return gather(rows, slot)
 
 
 # ---- O8 labels -------------------------------------------------------------

@@ -18,7 +18,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SRC = os.path.join(ROOT, "oracle", "lsa_oracle.c")
 PINS = [os.path.join(HERE, f) for f in ("test_oracle_formats.py", "test_oracle_score.py",
-                                        "test_oracle_select.py", "test_oracle_labels.py")]
+                                        "test_oracle_select.py", "test_oracle_labels.py",
+                                        "test_oracle_fetch.py")]
 
 # (name, exact snippet of lsa_oracle.c, planted replacement)
 MUTANTS = [
@@ -47,6 +48,12 @@ MUTANTS = [
      "if (!an && a->z != b->z) return (a->z > b->z) ? 1 : -1;"),
     ("top-k ties to the higher index", "  return (a->idx < b->idx) ? -1 : (a->idx > b->idx);\n}\n\nstatic int cmp_int_asc",
      "  return (a->idx > b->idx) ? -1 : (a->idx < b->idx);\n}\n\nstatic int cmp_int_asc"),
+    ("fetch skips eviction", "if (e >= 0 && !is_surv[e]) {", "if (e >= 0 && !is_surv[e] && 0) {"),
+    ("fetch copies the slot's cold row", "cold + (int64_t)s * row_bytes", "cold + (int64_t)j * row_bytes"),
+    ("fetch takes the highest free slot", "int64_t j = 0;\n  for (int64_t i = 0; i < n; ++i) {\n    int32_t s = surv[i];\n    if (slot_of[s] >= 0) continue;\n    while (entry_of[j] >= 0) ++j;",
+     "int64_t j = S - 1;\n  for (int64_t i = 0; i < n; ++i) {\n    int32_t s = surv[i];\n    if (slot_of[s] >= 0) continue;\n    while (entry_of[j] >= 0) --j;"),
+    ("fetch re-copies resident rows", "    if (slot_of[s] >= 0) continue;\n    while",
+     "    if (slot_of[s] >= 0) {\n      memcpy(rows + (int64_t)slot_of[s] * row_bytes, cold + (int64_t)s * row_bytes, (size_t)row_bytes);\n      continue;\n    }\n    while"),
     ("gather pads with ones", "memset(hot + j * row_bytes, 0, (size_t)row_bytes);",
      "memset(hot + j * row_bytes, 1, (size_t)row_bytes);"),
     ("nucleus keeps at mass == p", "    if (A < top_p) {", "    if (A <= top_p) {"),

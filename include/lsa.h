@@ -232,6 +232,63 @@ lsa_status lsa_gather_hot(int B, int N, int k, int row_bytes, const void* pool,
                           const int32_t* idx, void* hot, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * Cold-pool fetch with reuse ([SUMMARY] 2.1 dynamic-fetch bullet: every
+ * entry with I >= 0.5 is brought from the CPU cold pool into GPU memory;
+ * [REVIEW] section 2: the move is asynchronous and overlaps compute).
+ * The GPU reads the cold pool in place over the host link into a resident
+ * set of S slots per request, on `stream` (launch it on its own stream to
+ * overlap other work).  Per request b, with n = min(surv_count[b], cap):
+ *   1. a resident entry that is not among surv_idx[b][0..n) leaves its slot
+ *      (entry_of = -1, slot_of = -1; its bytes stay);
+ *   2. the survivors that are not resident take free slots: the i-th of them
+ *      in entry order takes the i-th free slot in slot order;
+ *   3. each of those rows is copied: rows[b][slot] = cold_pool[b][entry].
+ * Survivors already resident keep their slot and are not read again.
+ * fetch_count[b] = the number of rows copied, or -1 when request b's
+ * survivors do not fit in S slots; that request's tables and rows are then
+ * left exactly as they were (raise S or lower the survivor count).
+ *
+ *   cold_pool  [B][N][row_bytes] in pinned, mapped host memory (hipHostMalloc)
+ *              or in device memory; pageable host memory is refused
+ *   surv_idx   int32 [B][cap], ascending (lsa_select_or_compact's output),
+ *   surv_count int32 [B] (may exceed cap); entries outside [0, N) are ignored
+ *   slot_of    int32 [B][N]  in/out: slot of each entry, or -1
+ *   entry_of   int32 [B][S]  in/out: entry in each slot, or -1
+ *   rows       [B][S][row_bytes] in/out device memory
+ *   fetch_count out int32 [B]
+ *   ws         device workspace of lsa_fetch_workspace_bytes(B, N, cap)
+ * The tables start with every element -1 (lsa_resident_reset) and are then
+ * owned by these calls; calls on the same tables must be stream-ordered.
+ * Limits: 1 <= B <= 65535, 0 <= N <= 2^24, cap >= 0, S >= 0, row_bytes > 0
+ * and a multiple of 16, cold_pool and rows 16-byte aligned; surv_idx holds
+ * no repeats.  Errors: LSA_E_SHAPE / LSA_E_ARG for the limits, null or
+ * misaligned pointers and a cold pool in pageable memory; LSA_E_WORKSPACE;
+ * LSA_E_HIP for a launch failure.
+ */
+size_t lsa_fetch_workspace_bytes(int B, int N, int cap);
+lsa_status lsa_resident_reset(int B, int N, int S, int32_t* slot_of, int32_t* entry_of,
+                              hipStream_t stream);
+lsa_status lsa_fetch_survivors(int B, int N, int S, int row_bytes, const void* cold_pool,
+                               int cap, const int32_t* surv_idx, const int32_t* surv_count,
+                               int32_t* slot_of, int32_t* entry_of, void* rows,
+                               int32_t* fetch_count, void* ws, size_t ws_bytes,
+                               hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Top-k rows out of the resident set ([SUMMARY] 2.1 hierarchical-selection
+ * bullet: the top-k runs inside the fetched subset and its rows feed the
+ * core attention).
+ *   hot[b][j] = rows[b][slot_of[b][idx[b][j]]], zero row when idx[b][j] is
+ *   outside [0, N) or that entry is not resident
+ *   rows [B][S][row_bytes]   slot_of int32 [B][N]   idx int32 [B][k]
+ *   hot out [B][k][row_bytes]
+ * Limits: row_bytes > 0 and a multiple of 16; rows and hot 16-byte aligned.
+ */
+lsa_status lsa_gather_resident(int B, int N, int S, int k, int row_bytes, const void* rows,
+                               const int32_t* slot_of, const int32_t* idx, void* hot,
+                               hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * Golden labels by cross-layer majority vote ([SUMMARY] 2.2 steps 1-3;
  * [REVIEW] section 2, training labels).  For every query t and teacher
  * layer l, over the N entries of the row logits[t][l]:

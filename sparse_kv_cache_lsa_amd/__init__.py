@@ -17,7 +17,8 @@ __all__ = [
     "LSAError", "LSA_KEY_BF16", "LSA_KEY_FP8_E4M3", "LSA_CAND_CHUNK", "load", "lsa_version",
     "lsa_trigger_due", "lsa_project_query", "lsa_query_weights_packed_bytes",
     "lsa_pack_query_weights", "lsa_project_query_packed", "lsa_score", "lsa_select_or_compact",
-    "lsa_topk_workspace_bytes", "lsa_topk", "lsa_gather_hot",
+    "lsa_topk_workspace_bytes", "lsa_topk", "lsa_gather_hot", "lsa_fetch_workspace_bytes",
+    "lsa_resident_reset", "lsa_fetch_survivors", "lsa_gather_resident",
     "lsa_label_vote_workspace_bytes", "lsa_label_vote",
     "lsa_focal_bce_grad_workspace_bytes", "lsa_focal_bce_grad",
 ]
@@ -138,6 +139,51 @@ def lsa_gather_hot(pool, idx, hot, *, stream=None):
     k = idx.shape[1]
     row_bytes = pool[0, 0].numel() * pool.element_size() if N > 0 else hot[0, 0].numel() * hot.element_size()
     check(load().lsa_gather_hot(B, N, k, row_bytes, _p(pool), _p(idx), _p(hot), _stream(stream)))
+
+
+def lsa_fetch_workspace_bytes(B: int, N: int, cap: int) -> int:
+    return int(load().lsa_fetch_workspace_bytes(B, N, cap))
+
+
+def lsa_resident_reset(slot_of, entry_of, *, stream=None):
+    """slot_of int32 [B][N], entry_of int32 [B][S] -> all -1 (nothing resident)."""
+    _dev(slot_of, entry_of)
+    B, N = slot_of.shape
+    check(load().lsa_resident_reset(B, N, entry_of.shape[1], _p(slot_of), _p(entry_of),
+                                    _stream(stream)))
+
+
+def lsa_fetch_survivors(cold_pool, surv_idx, surv_count, slot_of, entry_of, rows, fetch_count,
+                        ws=None, *, stream=None):
+    """cold_pool [B][N][row] in pinned host memory (or on the GPU); surv_idx
+    i32 [B][cap] ascending, surv_count i32 [B]; slot_of i32 [B][N], entry_of
+    i32 [B][S] and rows [B][S][row] (the resident set, updated in place);
+    fetch_count out i32 [B] = rows copied."""
+    if not (cold_pool.is_cuda or cold_pool.is_pinned()):
+        raise ValueError("the cold pool must be pinned host memory or a GPU tensor")
+    if not cold_pool.is_contiguous():
+        raise ValueError("LSA tensors must be contiguous")
+    _dev(surv_idx, surv_count, slot_of, entry_of, rows, fetch_count, ws)
+    B, N = cold_pool.shape[0], cold_pool.shape[1]
+    S = entry_of.shape[1]
+    cap = surv_idx.shape[1]
+    row_bytes = rows[0, 0].numel() * rows.element_size() if S > 0 else cold_pool[0, 0].numel() * cold_pool.element_size()
+    check(load().lsa_fetch_survivors(B, N, S, row_bytes, _p(cold_pool), cap, _p(surv_idx),
+                                     _p(surv_count), _p(slot_of), _p(entry_of), _p(rows),
+                                     _p(fetch_count), _p(ws),
+                                     0 if ws is None else ws.numel() * ws.element_size(),
+                                     _stream(stream)))
+
+
+def lsa_gather_resident(rows, slot_of, idx, hot, *, stream=None):
+    """rows [B][S][row], slot_of i32 [B][N], idx i32 [B][k] -> hot [B][k][row]."""
+    _dev(rows, slot_of, idx, hot)
+    B, S = rows.shape[0], rows.shape[1]
+    N = slot_of.shape[1]
+    k = idx.shape[1]
+    row_bytes = hot[0, 0].numel() * hot.element_size() if k > 0 else rows[0, 0].numel() * rows.element_size()
+    check(load().lsa_gather_resident(B, N, S, k, row_bytes, _p(rows), _p(slot_of), _p(idx),
+                                     _p(hot), _stream(stream)))
 
 
 def lsa_label_vote_workspace_bytes(Q: int, L: int, N: int) -> int:

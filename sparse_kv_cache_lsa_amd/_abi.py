@@ -36,6 +36,10 @@ SIGNATURES = {
     "lsa_topk_workspace_bytes": (SZ, [I32, I32, I32]),
     "lsa_topk": (I32, [I32, I32, I32, P, P, P, P, P, P, SZ, P]),
     "lsa_gather_hot": (I32, [I32, I32, I32, I32, P, P, P, P]),
+    "lsa_fetch_workspace_bytes": (SZ, [I32, I32, I32]),
+    "lsa_resident_reset": (I32, [I32, I32, I32, P, P, P]),
+    "lsa_fetch_survivors": (I32, [I32, I32, I32, I32, P, I32, P, P, P, P, P, P, P, SZ, P]),
+    "lsa_gather_resident": (I32, [I32, I32, I32, I32, I32, P, P, P, P, P]),
     "lsa_label_vote_workspace_bytes": (SZ, [I32, I32, I32]),
     "lsa_label_vote": (I32, [I32, I32, I32, C.c_float, I32, P, P, P, P, P, SZ, P]),
     "lsa_focal_bce_grad_workspace_bytes": (SZ, [I32, I32, I32, I32, I32]),

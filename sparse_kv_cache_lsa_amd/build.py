@@ -17,7 +17,7 @@ LIB = os.path.join(PKG, "liblsa.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["lsa_api.cpp", "lsa_score.hip", "lsa_select.hip", "lsa_topk.hip",
-           "lsa_gather.hip", "lsa_project.hip", "lsa_labels.hip", "lsa_focal.hip"]
+           "lsa_gather.hip", "lsa_fetch.hip", "lsa_project.hip", "lsa_labels.hip", "lsa_focal.hip"]
 
 # Packed fp32 VALU ops are switched off for every HIP translation unit.  MFMA
 # results are kept in ordinary VGPRs (not AGPRs), so fused epilogues read the

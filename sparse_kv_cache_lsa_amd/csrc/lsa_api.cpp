@@ -249,6 +249,103 @@ lsa_status lsa_gather_hot(int B, int N, int k, int row_bytes, const void* pool,
                     "lsa_gather_hot launch");
 }
 
+// ------------------------------------------------------- cold-pool fetch
+
+namespace {
+
+// The device-side address of the cold pool: pinned host memory is read in
+// place through its device mapping; device memory is taken as it is.  Pageable
+// host memory (or anything HIP does not know) is refused.
+lsa_status cold_pool_address(const void* cold, const void** dev) {
+  hipPointerAttribute_t at;
+  hipError_t e = hipPointerGetAttributes(&at, cold);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(LSA_E_ARG, "lsa_fetch_survivors: cold pool is neither pinned host nor device "
+                "memory (%s)", hipGetErrorString(e));
+  }
+  if (at.type == hipMemoryTypeDevice || at.type == hipMemoryTypeManaged) {
+    *dev = cold;
+    return LSA_OK;
+  }
+  if (at.type != hipMemoryTypeHost)
+    return fail(LSA_E_ARG, "lsa_fetch_survivors: cold pool is pageable host memory; allocate "
+                "it pinned (hipHostMalloc)");
+  void* d = nullptr;
+  e = hipHostGetDevicePointer(&d, const_cast<void*>(cold), 0);
+  if (e != hipSuccess || !d) {
+    (void)hipGetLastError();
+    return fail(LSA_E_ARG, "lsa_fetch_survivors: cold pool host memory is not pinned and "
+                "mapped (%s)", hipGetErrorString(e));
+  }
+  *dev = d;
+  return LSA_OK;
+}
+
+}  // namespace
+
+size_t lsa_fetch_workspace_bytes(int B, int N, int cap) {
+  if (B < 1 || N < 0 || cap < 0) return 0;
+  return lsa::fetch_workspace_bytes(B, N, cap);
+}
+
+lsa_status lsa_resident_reset(int B, int N, int S, int32_t* slot_of, int32_t* entry_of,
+                              hipStream_t stream) {
+  REQUIRE(B >= 1 && B <= 65535 && N >= 0 && S >= 0, LSA_E_SHAPE,
+          "lsa_resident_reset: bad B/N/S (%d,%d,%d)", B, N, S);
+  REQUIRE((N == 0 || slot_of) && (S == 0 || entry_of), LSA_E_ARG,
+          "lsa_resident_reset: null table");
+  return hip_status(lsa::launch_resident_reset(B, N, S, slot_of, entry_of, stream),
+                    "lsa_resident_reset launch");
+}
+
+lsa_status lsa_fetch_survivors(int B, int N, int S, int row_bytes, const void* cold_pool,
+                               int cap, const int32_t* surv_idx, const int32_t* surv_count,
+                               int32_t* slot_of, int32_t* entry_of, void* rows,
+                               int32_t* fetch_count, void* ws, size_t ws_bytes,
+                               hipStream_t stream) {
+  REQUIRE(B >= 1 && B <= 65535, LSA_E_SHAPE, "lsa_fetch_survivors: B=%d not in [1,65535]", B);
+  REQUIRE(N >= 0 && N <= (1 << 24) && cap >= 0 && S >= 0, LSA_E_SHAPE,
+          "lsa_fetch_survivors: bad N/cap/S (%d,%d,%d)", N, cap, S);
+  REQUIRE(row_bytes > 0 && row_bytes % 16 == 0, LSA_E_ARG,
+          "lsa_fetch_survivors: row_bytes=%d not a positive multiple of 16", row_bytes);
+  REQUIRE(surv_count && fetch_count, LSA_E_ARG, "lsa_fetch_survivors: null count pointer");
+  REQUIRE(cap == 0 || surv_idx, LSA_E_ARG, "lsa_fetch_survivors: null surv_idx with cap > 0");
+  REQUIRE((N == 0 || (slot_of && cold_pool)) && (S == 0 || (entry_of && rows)), LSA_E_ARG,
+          "lsa_fetch_survivors: null table, rows or cold pool");
+  REQUIRE((N == 0 || aligned16(cold_pool)) && (S == 0 || aligned16(rows)), LSA_E_ARG,
+          "lsa_fetch_survivors: cold pool/rows not 16-byte aligned");
+  const size_t need = lsa::fetch_workspace_bytes(B, N, cap);
+  REQUIRE(need == 0 || (ws && ws_bytes >= need && ((uintptr_t)ws & 15) == 0), LSA_E_WORKSPACE,
+          "lsa_fetch_survivors: workspace of %zu bytes (16-byte aligned) needed, got %zu", need,
+          ws ? ws_bytes : (size_t)0);
+  const void* cold = nullptr;
+  if (N > 0) {
+    lsa_status st = cold_pool_address(cold_pool, &cold);
+    if (st != LSA_OK) return st;
+  }
+  return hip_status(lsa::launch_fetch(B, N, S, row_bytes, cold, cap, surv_idx, surv_count,
+                                      slot_of, entry_of, rows, fetch_count, ws, stream),
+                    "lsa_fetch_survivors launch");
+}
+
+lsa_status lsa_gather_resident(int B, int N, int S, int k, int row_bytes, const void* rows,
+                               const int32_t* slot_of, const int32_t* idx, void* hot,
+                               hipStream_t stream) {
+  REQUIRE(B >= 1 && N >= 0 && S >= 0 && k >= 0, LSA_E_SHAPE,
+          "lsa_gather_resident: bad B/N/S/k (%d,%d,%d,%d)", B, N, S, k);
+  REQUIRE(row_bytes > 0 && row_bytes % 16 == 0, LSA_E_ARG,
+          "lsa_gather_resident: row_bytes=%d not a positive multiple of 16", row_bytes);
+  if (k == 0) return LSA_OK;
+  REQUIRE(idx && hot && (N == 0 || slot_of) && (S == 0 || rows), LSA_E_ARG,
+          "lsa_gather_resident: null pointer argument");
+  REQUIRE(aligned16(hot) && (S == 0 || aligned16(rows)), LSA_E_ARG,
+          "lsa_gather_resident: rows/hot not 16-byte aligned");
+  return hip_status(lsa::launch_gather_resident(B, N, S, k, row_bytes, rows, slot_of, idx, hot,
+                                                stream),
+                    "lsa_gather_resident launch");
+}
+
 // -------------------------------------------------------- label / loss calls
 
 size_t lsa_label_vote_workspace_bytes(int Q, int L, int N) {

@@ -60,6 +60,20 @@ hipError_t launch_topk(int B, int cap, int k, const int32_t* surv_idx,
 hipError_t launch_gather(int B, int N, int k, int row_bytes, const void* pool,
                          const int32_t* idx, void* hot, hipStream_t s);
 
+size_t fetch_workspace_bytes(int B, int N, int cap);
+
+hipError_t launch_resident_reset(int B, int N, int S, int32_t* slot_of, int32_t* entry_of,
+                                 hipStream_t s);
+
+hipError_t launch_fetch(int B, int N, int S, int row_bytes, const void* cold, int cap,
+                        const int32_t* surv_idx, const int32_t* surv_count, int32_t* slot_of,
+                        int32_t* entry_of, void* rows, int32_t* fetch_count, void* ws,
+                        hipStream_t s);
+
+hipError_t launch_gather_resident(int B, int N, int S, int k, int row_bytes, const void* rows,
+                                  const int32_t* slot_of, const int32_t* idx, void* hot,
+                                  hipStream_t s);
+
 hipError_t launch_label_vote(int Q, int L, int N, float top_p, int theta, const float* logits,
                              uint32_t* mask, uint8_t* count, uint8_t* label, hipStream_t s);
 

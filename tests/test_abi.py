@@ -88,6 +88,24 @@ def test_validation_errors_return_before_launch(lib):
     assert lib.lsa_topk(2, 100000, 2048, fake, fake, fake, fake, fake, None, 0, None) == _abi.LSA_E_WORKSPACE
     # gather: row size not a multiple of 16
     assert lib.lsa_gather_hot(1, 10, 4, 24, fake, fake, fake, None) == _abi.LSA_E_ARG
+    # fetch: bad sizes, bad row size, short workspace, pageable cold pool
+    Fe = lambda B, N, S, rb, cap, cold=fake, ws=fake, nws=1 << 30: lib.lsa_fetch_survivors(
+        B, N, S, rb, cold, cap, fake, fake, fake, fake, fake, fake, ws, nws, None)
+    assert Fe(2, 1000, -1, 1024, 100) == _abi.LSA_E_SHAPE
+    assert Fe(2, 1 << 25, 10, 1024, 100) == _abi.LSA_E_SHAPE
+    assert Fe(2, 1000, 100, 24, 100) == _abi.LSA_E_ARG
+    assert Fe(2, 1000, 100, 1024, 100, cold=None) == _abi.LSA_E_ARG
+    assert Fe(2, 1000, 100, 1024, 100, cold=C.c_void_p(24)) == _abi.LSA_E_ARG
+    assert Fe(2, 1000, 100, 1024, 100, ws=None, nws=0) == _abi.LSA_E_WORKSPACE
+    assert Fe(2, 1000, 100, 1024, 100, nws=8) == _abi.LSA_E_WORKSPACE
+    pageable = (C.c_uint8 * 4096)()
+    page = C.c_void_p((C.addressof(pageable) + 15) & ~15)
+    assert Fe(1, 2, 2, 1024, 2, cold=page) == _abi.LSA_E_ARG
+    assert b"cold pool" in lib.lsa_last_error()
+    assert lib.lsa_resident_reset(0, 10, 10, fake, fake, None) == _abi.LSA_E_SHAPE
+    assert lib.lsa_resident_reset(1, 10, 10, None, fake, None) == _abi.LSA_E_ARG
+    assert lib.lsa_gather_resident(1, 10, 10, 4, 24, fake, fake, fake, fake, None) == _abi.LSA_E_ARG
+    assert lib.lsa_gather_resident(1, 10, 10, 4, 32, None, fake, fake, fake, None) == _abi.LSA_E_ARG
     # projection: hidden size not a multiple of 64
     assert lib.lsa_project_query(1, 1, 100, 8, 64, fake, 0, arr, arr, fake, fake, None) == _abi.LSA_E_SHAPE
     # packed projection: bad D, null or misaligned packed buffers
@@ -126,6 +144,9 @@ def test_packed_weight_sizes(lib):
 
 
 def test_workspace_sizes(lib):
+    # fetch: survivor bitmap [B][ceil(N/32)] u32 plus two [B][cap] i32 lists
+    assert lib.lsa_fetch_workspace_bytes(32, 262144, 262144) >= 32 * 8192 * 4 + 2 * 32 * 262144 * 4
+    assert lib.lsa_fetch_workspace_bytes(0, 10, 10) == 0
     W = (32768 + 31) // 32
     assert lib.lsa_label_vote_workspace_bytes(64, 20, 32768) == 64 * 20 * W * 4
     big = lib.lsa_focal_bce_grad_workspace_bytes(64, 32768, 4096, 64, 128)

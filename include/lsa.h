@@ -259,9 +259,9 @@ lsa_status lsa_gather_hot(int B, int N, int k, int row_bytes, const void* pool,
  *   ws         device workspace of lsa_fetch_workspace_bytes(B, N, cap)
  * The tables start with every element -1 (lsa_resident_reset) and are then
  * owned by these calls; calls on the same tables must be stream-ordered.
- * Limits: 1 <= B <= 65535, 0 <= N <= 2^24, cap >= 0, S >= 0, row_bytes > 0
- * and a multiple of 16, cold_pool and rows 16-byte aligned; surv_idx holds
- * no repeats.  Errors: LSA_E_SHAPE / LSA_E_ARG for the limits, null or
+ * Limits: 1 <= B <= 65535, 0 <= N <= 2^24, cap >= 0, 0 <= S <= 2^24,
+ * B * min(cap, N, S) < 2^31, row_bytes > 0 and a multiple of 16, cold_pool
+ * and rows 16-byte aligned; surv_idx holds no repeats.  Errors: LSA_E_SHAPE / LSA_E_ARG for the limits, null or
  * misaligned pointers and a cold pool in pageable memory; LSA_E_WORKSPACE;
  * LSA_E_HIP for a launch failure.
  */

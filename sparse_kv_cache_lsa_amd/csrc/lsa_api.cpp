@@ -3,6 +3,7 @@
 // invalid call returns an error without touching device memory.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
@@ -305,10 +306,15 @@ lsa_status lsa_fetch_survivors(int B, int N, int S, int row_bytes, const void* c
                                int32_t* fetch_count, void* ws, size_t ws_bytes,
                                hipStream_t stream) {
   REQUIRE(B >= 1 && B <= 65535, LSA_E_SHAPE, "lsa_fetch_survivors: B=%d not in [1,65535]", B);
-  REQUIRE(N >= 0 && N <= (1 << 24) && cap >= 0 && S >= 0, LSA_E_SHAPE,
+  REQUIRE(N >= 0 && N <= (1 << 24) && cap >= 0 && S >= 0 && S <= (1 << 24), LSA_E_SHAPE,
           "lsa_fetch_survivors: bad N/cap/S (%d,%d,%d)", N, cap, S);
   REQUIRE(row_bytes > 0 && row_bytes % 16 == 0, LSA_E_ARG,
           "lsa_fetch_survivors: row_bytes=%d not a positive multiple of 16", row_bytes);
+  {
+    const int64_t per = std::min(std::min(cap, N), S);
+    REQUIRE((int64_t)B * per < ((int64_t)1 << 31), LSA_E_SHAPE,
+            "lsa_fetch_survivors: B*min(cap, N, S) must stay below 2^31 rows");
+  }
   REQUIRE(surv_count && fetch_count, LSA_E_ARG, "lsa_fetch_survivors: null count pointer");
   REQUIRE(cap == 0 || surv_idx, LSA_E_ARG, "lsa_fetch_survivors: null surv_idx with cap > 0");
   REQUIRE((N == 0 || (slot_of && cold_pool)) && (S == 0 || (entry_of && rows)), LSA_E_ARG,

@@ -15,14 +15,15 @@
 // entries that stopped surviving free their slots; the i-th new survivor in
 // entry order takes the i-th free slot in slot order.  A request whose
 // survivors do not fit in its S slots is left untouched (fetch count -1).
-// Five launches after the bitmap is cleared:
+// Six launches after the bitmap is cleared:
 //   mark    survivor bitmap (one bit per entry) in the workspace
 //   need    one block per request: the new survivors, compacted in entry
 //           order, and the capacity check
 //   evict   resident entries whose bit is clear leave their slots
 //   assign  one block per request: free slots, compacted in slot order, each
 //           given to the next new survivor
-//   copy    host rows -> slots
+//   offsets prefix of the per-request copy counts
+//   copy    host rows -> slots, spread over all waves across requests
 #include <algorithm>
 
 #include "lsa_device.h"
@@ -31,10 +32,27 @@
 namespace lsa {
 namespace {
 
-constexpr int kPlanThreads = 1024;
-constexpr int kCopyThreads = 256;
-constexpr int kCopyRows = 4;   // rows in flight per wavefront
+#ifndef LSA_COPY_BLOCKS
+#define LSA_COPY_BLOCKS 32
+#endif
+#ifndef LSA_COPY_ROWS
+#define LSA_COPY_ROWS 4
+#endif
 
+constexpr int kPlanThreads = 1024;
+constexpr int kPer = 4;          // list elements per thread in the planning blocks
+constexpr int kCopyThreads = 256;
+constexpr int kCopyRows = LSA_COPY_ROWS;       // rows in flight per wavefront
+// Blocks of the copy over all requests.  The host link is kept busy by well
+// under a MiB in flight (32 blocks x 4 waves x 4 rows x 1 KiB = 512 KiB): 32
+// blocks copy as fast as 2048 (about 56 GB/s measured), while a grid that
+// filled the GPU would hold every wave slot for the whole copy and keep the
+// kernels of other streams from running beside it.
+constexpr int kCopyBlocks = LSA_COPY_BLOCKS;
+
+// Survivor bitmap.  Ascending survivors put runs of lanes on the same 32-bit
+// word; each run ORs its bits together (shuffle doubling over equal words) and
+// only the run's first lane issues the atomic.
 __global__ __launch_bounds__(256) void mark_kernel(int N, int cap,
                                                    const int32_t* __restrict__ surv_idx,
                                                    const int32_t* __restrict__ surv_count,
@@ -44,9 +62,21 @@ __global__ __launch_bounds__(256) void mark_kernel(int N, int cap,
   const size_t W = ((size_t)N + 31) >> 5;
   const int32_t* sv = surv_idx + (size_t)b * cap;
   uint32_t* bw = bits + (size_t)b * W;
-  for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) {
-    const int s = sv[i];
-    if ((unsigned)s < (unsigned)N) atomicOr(&bw[s >> 5], 1u << (s & 31));
+  const int lane = lane_id();
+  for (int base = blockIdx.x * 256; base < n; base += gridDim.x * 256) {   // block-uniform
+    const int i = base + threadIdx.x;
+    const int s = i < n ? sv[i] : -1;
+    const bool ok = (unsigned)s < (unsigned)N;
+    const int word = ok ? (s >> 5) : -1;
+    uint32_t m = ok ? (1u << (s & 31)) : 0u;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const uint32_t om = __shfl_down(m, off, kWave);
+      const int ow = __shfl_down(word, off, kWave);
+      if (lane + off < kWave && ow == word) m |= om;
+    }
+    const int pw = __shfl_up(word, 1, kWave);
+    if (ok && (lane == 0 || pw != word)) atomicOr(&bw[word], m);
   }
 }
 
@@ -86,20 +116,29 @@ __global__ __launch_bounds__(kPlanThreads) void need_kernel(
   const int32_t* so = slot_of + (size_t)b * N;
   int32_t* sb = src + (size_t)b * cap;
   int nn = 0, kept = 0;
-  for (int base = 0; base < n; base += kPlanThreads) {
-    const int i = base + t;
-    bool need = false;
-    int s = -1;
-    if (i < n) {
-      s = sv[i];
-      if ((unsigned)s < (unsigned)N) {
-        need = so[s] < 0;
-        kept += need ? 0 : 1;
-      }
+  // thread t takes kPer consecutive survivors of each block-wide step, so the
+  // list keeps entry order
+  for (int base = 0; base < n; base += kPlanThreads * kPer) {
+    int s[kPer];
+    bool need[kPer];
+    int c = 0;
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int i = base + t * kPer + u;
+      s[u] = i < n ? sv[i] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const bool in = (unsigned)s[u] < (unsigned)N;
+      need[u] = in && so[s[u]] < 0;
+      kept += (in && !need[u]) ? 1 : 0;
+      c += need[u] ? 1 : 0;
     }
     int tot;
-    const int r = block_exclusive_scan<kPlanThreads>(need ? 1 : 0, scratch, &tot);
-    if (need) sb[nn + r] = s;
+    int r = block_exclusive_scan<kPlanThreads>(c, scratch, &tot);
+#pragma unroll
+    for (int u = 0; u < kPer; ++u)
+      if (need[u]) sb[nn + r++] = s[u];
     nn += tot;
   }
   int kept_all;
@@ -123,55 +162,105 @@ __global__ __launch_bounds__(kPlanThreads) void assign_kernel(
   const int32_t* sb = src + (size_t)b * cap;
   int32_t* db = dst + (size_t)b * cap;
   int placed = 0;
-  for (int base = 0; base < S && placed < nn; base += kPlanThreads) {
-    const int j = base + t;
-    const bool fr = j < S && eo[j] < 0;
+  for (int base = 0; base < S && placed < nn; base += kPlanThreads * kPer) {
+    bool fr[kPer];
+    int c = 0;
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int j = base + t * kPer + u;
+      fr[u] = j < S && eo[j] < 0;
+      c += fr[u] ? 1 : 0;
+    }
     int tot;
-    const int r = block_exclusive_scan<kPlanThreads>(fr ? 1 : 0, scratch, &tot);
-    if (fr && placed + r < nn) {
-      const int s = sb[placed + r];
-      eo[j] = s;
-      so[s] = j;
-      db[placed + r] = j;
+    int r = placed + block_exclusive_scan<kPlanThreads>(c, scratch, &tot);
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      if (fr[u]) {
+        if (r < nn) {
+          const int j = base + t * kPer + u;
+          const int sn = sb[r];
+          eo[j] = sn;
+          so[sn] = j;
+          db[r] = j;
+        }
+        ++r;
+      }
     }
     placed += tot;
   }
 }
 
-// Wave-per-row copy from the cold pool (host memory read over the host link)
-// into the resident rows; kCopyRows rows per wave are loaded before any is
-// stored.
+// Exclusive prefix of the per-request copy counts (a request that did not fit
+// counts 0): offs[0..B], so the copy can spread rows over all its waves
+// whatever the split between requests.  One block.
+__global__ __launch_bounds__(kPlanThreads) void offsets_kernel(
+    int B, const int32_t* __restrict__ fetch_count, int32_t* __restrict__ offs) {
+  __shared__ int scratch[kPlanThreads / kWave + 1];
+  int run = 0;
+  for (int base = 0; base < B; base += kPlanThreads) {
+    const int b = base + threadIdx.x;
+    const int v = b < B ? max(fetch_count[b], 0) : 0;
+    int tot;
+    const int r = block_exclusive_scan<kPlanThreads>(v, scratch, &tot);
+    if (b < B) offs[b] = run + r;
+    run += tot;
+  }
+  if (threadIdx.x == 0) offs[B] = run;
+}
+
+// Copy from the cold pool (host memory read over the host link) into the
+// resident rows.  Rows are numbered over all requests (offs); each wavefront
+// takes kCopyRows consecutive rows, loads them all, then stores them.
 __global__ __launch_bounds__(kCopyThreads) void copy_kernel(
-    int N, int S, int cap, int cpr, const unsigned char* __restrict__ cold,
+    int B, int N, int S, int cap, int cpr, const unsigned char* __restrict__ cold,
     const int32_t* __restrict__ src, const int32_t* __restrict__ dst,
-    const int32_t* __restrict__ fetch_count, unsigned char* __restrict__ rows) {
-  const int b = blockIdx.y;
-  const int nn = fetch_count[b];
+    const int32_t* __restrict__ offs, unsigned char* __restrict__ rows) {
   constexpr int kWPB = kCopyThreads / kWave;
+  const int total = offs[B];
   const int wave = blockIdx.x * kWPB + threadIdx.x / kWave;
   const int stride = gridDim.x * kWPB * kCopyRows;
   const int lane = lane_id();
   const size_t rb = 16ull * cpr;
-  const int32_t* sb = src + (size_t)b * cap;
-  const int32_t* db = dst + (size_t)b * cap;
-  const unsigned char* cb = cold + (size_t)b * N * rb;
-  unsigned char* ob = rows + (size_t)b * S * rb;
-  for (int r0 = wave * kCopyRows; r0 < nn; r0 += stride) {
-    int s[kCopyRows], d[kCopyRows];
+  // request of the wave's first row (binary search once); afterwards rows
+  // only move forward, so the request index advances in registers
+  int b = 0;
+  {
+    const int g = wave * kCopyRows;
+    int hi = B;
+    while (hi - b > 1) {
+      const int mid = (b + hi) >> 1;
+      if (offs[mid] <= g) b = mid;
+      else hi = mid;
+    }
+  }
+  int cur = offs[b], nxt = offs[b + 1];
+  for (int g0 = wave * kCopyRows; g0 < total; g0 += stride) {
+    const unsigned char* from[kCopyRows];
+    unsigned char* to[kCopyRows];
 #pragma unroll
     for (int u = 0; u < kCopyRows; ++u) {
-      const bool ok = r0 + u < nn;
-      s[u] = ok ? sb[r0 + u] : -1;
-      d[u] = ok ? db[r0 + u] : -1;
+      const int gi = g0 + u;
+      from[u] = nullptr;
+      to[u] = nullptr;
+      if (gi < total) {
+        while (gi >= nxt) {                  // gi < total = offs[B] bounds b below B
+          ++b;
+          cur = nxt;
+          nxt = offs[b + 1];
+        }
+        const size_t e = (size_t)b * cap + (gi - cur);
+        from[u] = cold + ((size_t)b * N + src[e]) * rb;
+        to[u] = rows + ((size_t)b * S + dst[e]) * rb;
+      }
     }
     for (int c = lane; c < cpr; c += kWave) {
       u32x4 v[kCopyRows];
 #pragma unroll
       for (int u = 0; u < kCopyRows; ++u)
-        if (s[u] >= 0) v[u] = *(const u32x4*)(cb + (size_t)s[u] * rb + 16ull * c);
+        if (from[u]) v[u] = *(const u32x4*)(from[u] + 16ull * c);
 #pragma unroll
       for (int u = 0; u < kCopyRows; ++u)
-        if (s[u] >= 0) *(u32x4*)(ob + (size_t)d[u] * rb + 16ull * c) = v[u];
+        if (from[u]) *(u32x4*)(to[u] + 16ull * c) = v[u];
     }
   }
 }
@@ -202,7 +291,8 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 size_t fetch_workspace_bytes(int B, int N, int cap) {
   const size_t W = ((size_t)N + 31) >> 5;
-  return align256((size_t)B * W * 4) + 2 * align256((size_t)B * cap * 4);
+  return align256((size_t)B * W * 4) + 2 * align256((size_t)B * cap * 4) +
+         align256(((size_t)B + 1) * 4);
 }
 
 hipError_t launch_resident_reset(int B, int N, int S, int32_t* slot_of, int32_t* entry_of,
@@ -220,6 +310,7 @@ hipError_t launch_fetch(int B, int N, int S, int row_bytes, const void* cold, in
   uint32_t* bits = (uint32_t*)ws;
   int32_t* src = (int32_t*)((char*)ws + align256((size_t)B * W * 4));
   int32_t* dst = (int32_t*)((char*)src + align256((size_t)B * cap * 4));
+  int32_t* offs = (int32_t*)((char*)dst + align256((size_t)B * cap * 4));
   hipError_t e = launch_fill_i32((int32_t*)bits, (int64_t)(B * W), 0, s);
   if (e != hipSuccess) return e;
   if (N > 0 && cap > 0) {
@@ -236,12 +327,9 @@ hipError_t launch_fetch(int B, int N, int S, int row_bytes, const void* cold, in
   }
   hipLaunchKernelGGL(assign_kernel, dim3(B), dim3(kPlanThreads), 0, s, N, S, cap, src,
                      fetch_count, slot_of, entry_of, dst);
-  const int rows_per_block = (kCopyThreads / kWave) * kCopyRows;
-  const int need_blocks = (int)std::min<long long>(
-      ((long long)std::min(cap, N) + rows_per_block - 1) / rows_per_block, 1 << 20);
-  const int gx = std::max(1, std::min(need_blocks, std::max(16, 2048 / B)));
-  hipLaunchKernelGGL(copy_kernel, dim3(gx, B), dim3(kCopyThreads), 0, s, N, S, cap,
-                     row_bytes / 16, (const unsigned char*)cold, src, dst, fetch_count,
+  hipLaunchKernelGGL(offsets_kernel, dim3(1), dim3(kPlanThreads), 0, s, B, fetch_count, offs);
+  hipLaunchKernelGGL(copy_kernel, dim3(kCopyBlocks), dim3(kCopyThreads), 0, s, B, N, S, cap,
+                     row_bytes / 16, (const unsigned char*)cold, src, dst, offs,
                      (unsigned char*)rows);
   return hipGetLastError();
 }

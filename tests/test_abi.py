@@ -93,6 +93,7 @@ def test_validation_errors_return_before_launch(lib):
         B, N, S, rb, cold, cap, fake, fake, fake, fake, fake, fake, ws, nws, None)
     assert Fe(2, 1000, -1, 1024, 100) == _abi.LSA_E_SHAPE
     assert Fe(2, 1 << 25, 10, 1024, 100) == _abi.LSA_E_SHAPE
+    assert Fe(65535, 1 << 20, 1 << 16, 16, 1 << 20) == _abi.LSA_E_SHAPE   # 2^32 rows
     assert Fe(2, 1000, 100, 24, 100) == _abi.LSA_E_ARG
     assert Fe(2, 1000, 100, 1024, 100, cold=None) == _abi.LSA_E_ARG
     assert Fe(2, 1000, 100, 1024, 100, cold=C.c_void_p(24)) == _abi.LSA_E_ARG

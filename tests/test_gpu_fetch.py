@@ -137,6 +137,24 @@ def test_every_entry_survives_then_none():
         p.check()
 
 
+def test_one_request_carries_every_row():
+    """Copies are spread over all requests' rows: one request with many new
+    rows next to requests with none, or with a capacity shortfall."""
+    rng = np.random.default_rng(16)
+    B, N, rb, S = 5, 30000, 1024, 9000
+    cold = rng.integers(0, 256, (B, N, rb), dtype=np.uint8)
+    p = Pair(cold, S, N, pinned=True)
+    none = np.zeros(0, np.int32)
+    many = np.sort(rng.choice(N, 8500, replace=False)).astype(np.int32)
+    over = np.sort(rng.choice(N, 9500, replace=False)).astype(np.int32)
+    few = np.sort(rng.choice(N, 3, replace=False)).astype(np.int32)
+    for sets in ([none, none, many, none, none], [over, few, many, none, many],
+                 [none, many, over, few, none]):
+        got, want = p.step(sets)
+        assert np.array_equal(got, want)
+        p.check()
+
+
 def test_gather_resident_matches_oracle():
     rng = np.random.default_rng(14)
     B, N, rb, S, k = 3, 6000, 1024, 2000, 700

@@ -32,23 +32,19 @@
 namespace lsa {
 namespace {
 
-#ifndef LSA_COPY_BLOCKS
-#define LSA_COPY_BLOCKS 32
-#endif
-#ifndef LSA_COPY_ROWS
-#define LSA_COPY_ROWS 4
-#endif
-
 constexpr int kPlanThreads = 1024;
 constexpr int kPer = 4;          // list elements per thread in the planning blocks
-constexpr int kCopyThreads = 256;
-constexpr int kCopyRows = LSA_COPY_ROWS;       // rows in flight per wavefront
-// Blocks of the copy over all requests.  The host link is kept busy by well
-// under a MiB in flight (32 blocks x 4 waves x 4 rows x 1 KiB = 512 KiB): 32
-// blocks copy as fast as 2048 (about 56 GB/s measured), while a grid that
-// filled the GPU would hold every wave slot for the whole copy and keep the
-// kernels of other streams from running beside it.
-constexpr int kCopyBlocks = LSA_COPY_BLOCKS;
+// The copy runs one single-wave block per compute unit, two rows in flight
+// per wave (256 CUs x 2 KiB = 512 KiB in flight).  Host reads take several
+// microseconds, so few bytes in flight keep the link busy (about 57 GB/s
+// measured; 32 blocks of 4 waves move as fast).  What matters is how the
+// copy shares the GPU with kernels on other streams: a wave per CU leaves
+// every CU's memory pipeline nearly free, and 64% of the shorter job is
+// hidden beside indexer triggers, against 40% with 32 blocks of 4 waves, 19%
+// with 4 waves per CU, and none with 2048 blocks of 4 waves (every wave
+// slot held for the whole copy).
+constexpr int kCopyThreads = kWave;
+constexpr int kCopyRows = 2;   // rows in flight per wavefront
 
 // Survivor bitmap.  Ascending survivors put runs of lanes on the same 32-bit
 // word; each run ORs its bits together (shuffle doubling over equal words) and
@@ -328,7 +324,8 @@ hipError_t launch_fetch(int B, int N, int S, int row_bytes, const void* cold, in
   hipLaunchKernelGGL(assign_kernel, dim3(B), dim3(kPlanThreads), 0, s, N, S, cap, src,
                      fetch_count, slot_of, entry_of, dst);
   hipLaunchKernelGGL(offsets_kernel, dim3(1), dim3(kPlanThreads), 0, s, B, fetch_count, offs);
-  hipLaunchKernelGGL(copy_kernel, dim3(kCopyBlocks), dim3(kCopyThreads), 0, s, B, N, S, cap,
+  hipLaunchKernelGGL(copy_kernel, dim3(device_cu_count()), dim3(kCopyThreads), 0, s, B, N, S,
+                     cap,
                      row_bytes / 16, (const unsigned char*)cold, src, dst, offs,
                      (unsigned char*)rows);
   return hipGetLastError();

@@ -13,7 +13,8 @@ import torch
 import lsa_inputs as gen
 import lsa_fixtures as fx
 import parity
-from gpu_util import DEV, bf16_host, host, oracle_request
+from gpu_util import DEV, bf16_host, dev, host, oracle_request
+from oracle import oracle
 from sparse_kv_cache_lsa_amd.pipeline import TriggerBuffers, pack_weights, run_trigger
 
 pytestmark = pytest.mark.gpu
@@ -125,3 +126,52 @@ def test_chain_full_size(name):
     assert torch.equal(buf2.q, buf.q) and torch.equal(buf2.g, buf.g)
     assert torch.equal(buf2.surv_count, buf.surv_count) and torch.equal(buf2.mask, buf.mask)
     _check_request(inp, q_or, g_or, buf2, 0, pool, zl)
+    _check_cold_fetch(w, buf, pool)
+
+
+def _check_cold_fetch(w, buf, pool):
+    """The trigger's survivors fetched from a pinned host copy of the pool into
+    a resident set of N/2 slots per request (the benchmark's cold-fetch
+    configuration), then a second survivor set that keeps ~80% of them; slot
+    tables and resident rows equal the oracle's, and the top-k rows gathered
+    from the resident set equal the device-pool gather."""
+    import sparse_kv_cache_lsa_amd as lsa
+    B, N, S = w.B, w.N, w.N // 2
+    cold = torch.empty(pool.shape, dtype=pool.dtype, pin_memory=True)
+    cold.copy_(pool)
+    cold_np = cold.numpy().view(np.uint8).reshape(B, N, -1)
+    so = torch.empty((B, N), dtype=torch.int32, device=DEV)
+    eo = torch.empty((B, S), dtype=torch.int32, device=DEV)
+    rows = torch.zeros((B, S, pool.shape[2]), dtype=pool.dtype, device=DEV)
+    fc = torch.empty((B,), dtype=torch.int32, device=DEV)
+    ws = torch.empty((lsa.lsa_fetch_workspace_bytes(B, N, N),), dtype=torch.uint8, device=DEV)
+    lsa.lsa_resident_reset(so, eo)
+    rng = np.random.default_rng(3)
+    counts = host(buf.surv_count)
+    first = [host(buf.surv_idx[b, :int(counts[b])]) for b in range(B)]
+    second = []
+    for s in first:
+        keep = s[rng.random(s.size) < 0.8]
+        add = rng.choice(N, s.size // 5, replace=False)
+        second.append(np.unique(np.concatenate([keep, add])).astype(np.int32))
+    o_state = [(np.full(N, -1, np.int32), np.full(S, -1, np.int32),
+                np.zeros((S, cold_np.shape[2]), np.uint8)) for _ in range(B)]
+    for t, sets in enumerate((first, second)):
+        idx = np.full((B, N), -1, np.int32)
+        cnt = np.array([x.size for x in sets], np.int32)
+        for b, x in enumerate(sets):
+            idx[b, :x.size] = x
+        lsa.lsa_fetch_survivors(cold, dev(idx), dev(cnt), so, eo, rows, fc, ws)
+        torch.cuda.synchronize()
+        got = host(fc)
+        for b in range(B):
+            o_so, o_eo, o_rows = o_state[b]
+            assert got[b] == oracle.fetch(cold_np[b], sets[b], o_so, o_eo, o_rows)
+            assert np.array_equal(host(so[b]), o_so) and np.array_equal(host(eo[b]), o_eo)
+            assert np.array_equal(host(rows[b]).view(np.uint8).reshape(S, -1), o_rows)
+        print(f"{w.name}: cold fetch {t}: {int(got.sum())} rows", flush=True)
+        if t == 0:
+            hot = torch.empty_like(buf.hot)
+            lsa.lsa_gather_resident(rows, so, buf.topk_idx, hot)
+            torch.cuda.synchronize()
+            assert torch.equal(hot, buf.hot)

@@ -15,13 +15,15 @@
 // entries that stopped surviving free their slots; the i-th new survivor in
 // entry order takes the i-th free slot in slot order.  A request whose
 // survivors do not fit in its S slots is left untouched (fetch count -1).
-// Six launches after the bitmap is cleared:
+// Seven launches after the bitmap is cleared; the planning ones run one block
+// per chunk of 4096 survivors or slots:
 //   mark    survivor bitmap (one bit per entry) in the workspace
-//   need    one block per request: the new survivors, compacted in entry
-//           order, and the capacity check
-//   evict   resident entries whose bit is clear leave their slots
-//   assign  one block per request: free slots, compacted in slot order, each
-//           given to the next new survivor
+//   need    count, then write: the new survivors compacted in entry order,
+//           and the capacity check
+//   evict   resident entries whose bit is clear leave their slots; free
+//           slots counted per chunk
+//   assign  free slots compacted in slot order, each given to the next new
+//           survivor
 //   offsets prefix of the per-request copy counts
 //   copy    host rows -> slots, spread over all waves across requests
 #include <algorithm>
@@ -34,6 +36,7 @@ namespace {
 
 constexpr int kPlanThreads = 1024;
 constexpr int kPer = 4;          // list elements per thread in the planning blocks
+constexpr int kChunk = kPlanThreads * kPer;   // list elements per planning block
 // The copy runs one single-wave block per compute unit, two rows in flight
 // per wave (256 CUs x 2 KiB = 512 KiB in flight).  Host reads take several
 // microseconds, so few bytes in flight keep the link busy (about 57 GB/s
@@ -76,113 +79,171 @@ __global__ __launch_bounds__(256) void mark_kernel(int N, int cap,
   }
 }
 
-__global__ __launch_bounds__(256) void evict_kernel(int N, int S,
-                                                    const uint32_t* __restrict__ bits,
-                                                    const int32_t* __restrict__ fetch_count,
-                                                    int32_t* __restrict__ slot_of,
-                                                    int32_t* __restrict__ entry_of) {
-  const int b = blockIdx.y;
-  if (fetch_count[b] < 0) return;
+// Sum over a request's earlier chunks of one per-chunk counter (wave 0 of the
+// block); the result is broadcast through LDS.
+__device__ __forceinline__ int earlier_chunks_sum(const int32_t* cnt, int stride, int c,
+                                                  int* slot) {
+  if (threadIdx.x < kWave) {
+    int acc = 0;
+    for (int i = lane_id(); i < c; i += kWave) acc += cnt[(size_t)i * stride];
+    acc = wave_sum(acc);
+    if (lane_id() == 0) *slot = acc;
+  }
+  __syncthreads();
+  return *slot;
+}
+
+// Survivor chunks of kChunk entries, one block each: how many are new (not
+// resident) and how many are resident.  ccnt[b][c] = {new, kept}.
+__global__ __launch_bounds__(kPlanThreads) void need_count_kernel(
+    int N, int cap, int nch, const int32_t* __restrict__ surv_idx,
+    const int32_t* __restrict__ surv_count, const int32_t* __restrict__ slot_of,
+    int32_t* __restrict__ ccnt) {
+  __shared__ int scratch[kPlanThreads / kWave + 1];
+  const int c = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
+  const int n = max(0, min(surv_count[b], cap));
+  const int32_t* sv = surv_idx + (size_t)b * cap;
+  const int32_t* so = slot_of + (size_t)b * N;
+  int nw = 0, kp = 0;
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int i = c * kChunk + t * kPer + u;
+    const int s = i < n ? sv[i] : -1;
+    if ((unsigned)s < (unsigned)N) {
+      if (so[s] < 0) ++nw;
+      else ++kp;
+    }
+  }
+  int tn, tk;
+  (void)block_exclusive_scan<kPlanThreads>(nw, scratch, &tn);
+  (void)block_exclusive_scan<kPlanThreads>(kp, scratch, &tk);
+  if (t == 0) {
+    ccnt[((size_t)b * nch + c) * 2] = tn;
+    ccnt[((size_t)b * nch + c) * 2 + 1] = tk;
+  }
+}
+
+// The new survivors of each chunk, in entry order, at the chunk's offset in
+// `src`.  Chunk 0 also writes fetch_count[b]: the number of new survivors, or
+// -1 when kept + new > S (the request is then left as it is).
+__global__ __launch_bounds__(kPlanThreads) void need_write_kernel(
+    int N, int S, int cap, int nch, const int32_t* __restrict__ surv_idx,
+    const int32_t* __restrict__ surv_count, const int32_t* __restrict__ slot_of,
+    const int32_t* __restrict__ ccnt, int32_t* __restrict__ src,
+    int32_t* __restrict__ fetch_count) {
+  __shared__ int scratch[kPlanThreads / kWave + 1];
+  __shared__ int s_base;
+  const int c = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
+  const int n = max(0, min(surv_count[b], cap));
+  const int32_t* sv = surv_idx + (size_t)b * cap;
+  const int32_t* so = slot_of + (size_t)b * N;
+  const int32_t* cb = ccnt + (size_t)b * nch * 2;
+  if (c == 0 && t < kWave) {
+    long long nn = 0, kept = 0;
+    for (int i = lane_id(); i < nch; i += kWave) {
+      nn += cb[2 * i];
+      kept += cb[2 * i + 1];
+    }
+    nn = wave_sum((int)nn);
+    kept = wave_sum((int)kept);
+    if (lane_id() == 0) fetch_count[b] = (kept + nn > S) ? -1 : (int)nn;
+  }
+  const int base = earlier_chunks_sum(cb, 2, c, &s_base);
+  int s[kPer];
+  bool need[kPer];
+  int cnt = 0;
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int i = c * kChunk + t * kPer + u;
+    s[u] = i < n ? sv[i] : -1;
+    need[u] = (unsigned)s[u] < (unsigned)N && so[s[u]] < 0;
+    cnt += need[u] ? 1 : 0;
+  }
+  int tot;
+  int r = base + block_exclusive_scan<kPlanThreads>(cnt, scratch, &tot);
+  int32_t* sb = src + (size_t)b * cap;
+#pragma unroll
+  for (int u = 0; u < kPer; ++u)
+    if (need[u]) sb[r++] = s[u];
+}
+
+// Slot chunks of kChunk slots, one block each: resident entries whose bitmap
+// bit is clear leave their slots; fcnt[b][c] = free slots of the chunk
+// afterwards.  Requests that do not fit are skipped.  Only the first
+// Ss = min(S, N) slots are scanned: new entries always take the lowest free
+// slots, so at most N entries ever occupy slots below N.
+__global__ __launch_bounds__(kPlanThreads) void evict_kernel(
+    int N, int S, int Ss, int nsc, const uint32_t* __restrict__ bits,
+    const int32_t* __restrict__ fetch_count, int32_t* __restrict__ slot_of,
+    int32_t* __restrict__ entry_of, int32_t* __restrict__ fcnt) {
+  __shared__ int scratch[kPlanThreads / kWave + 1];
+  const int c = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
+  if (fetch_count[b] < 0) return;   // block-uniform
   const size_t W = ((size_t)N + 31) >> 5;
   const uint32_t* bw = bits + (size_t)b * W;
   int32_t* so = slot_of + (size_t)b * N;
   int32_t* eo = entry_of + (size_t)b * S;
-  for (int j = blockIdx.x * 256 + threadIdx.x; j < S; j += gridDim.x * 256) {
-    const int e = eo[j];
-    if ((unsigned)e < (unsigned)N && !((bw[e >> 5] >> (e & 31)) & 1u)) {
-      so[e] = -1;
-      eo[j] = -1;
+  int fr = 0;
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int j = c * kChunk + t * kPer + u;
+    if (j < Ss) {
+      const int e = eo[j];
+      if ((unsigned)e < (unsigned)N && !((bw[e >> 5] >> (e & 31)) & 1u)) {
+        so[e] = -1;
+        eo[j] = -1;
+        ++fr;
+      } else if (e < 0) {
+        ++fr;
+      }
     }
   }
+  int tot;
+  (void)block_exclusive_scan<kPlanThreads>(fr, scratch, &tot);
+  if (t == 0) fcnt[(size_t)b * nsc + c] = tot;
 }
 
-// One block per request: the survivors that are not resident, in entry order,
-// go to `src`.  fetch_count[b] = their number, or -1 when the resident set
-// cannot hold all survivors (kept + new > S); the tables are then left as they
-// are by every later launch.
-__global__ __launch_bounds__(kPlanThreads) void need_kernel(
-    int N, int S, int cap, const int32_t* __restrict__ surv_idx,
-    const int32_t* __restrict__ surv_count, const int32_t* __restrict__ slot_of,
-    int32_t* __restrict__ src, int32_t* __restrict__ fetch_count) {
-  __shared__ int scratch[kPlanThreads / kWave + 1];
-  const int b = blockIdx.x;
-  const int t = threadIdx.x;
-  const int n = max(0, min(surv_count[b], cap));
-  const int32_t* sv = surv_idx + (size_t)b * cap;
-  const int32_t* so = slot_of + (size_t)b * N;
-  int32_t* sb = src + (size_t)b * cap;
-  int nn = 0, kept = 0;
-  // thread t takes kPer consecutive survivors of each block-wide step, so the
-  // list keeps entry order
-  for (int base = 0; base < n; base += kPlanThreads * kPer) {
-    int s[kPer];
-    bool need[kPer];
-    int c = 0;
-#pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const int i = base + t * kPer + u;
-      s[u] = i < n ? sv[i] : -1;
-    }
-#pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const bool in = (unsigned)s[u] < (unsigned)N;
-      need[u] = in && so[s[u]] < 0;
-      kept += (in && !need[u]) ? 1 : 0;
-      c += need[u] ? 1 : 0;
-    }
-    int tot;
-    int r = block_exclusive_scan<kPlanThreads>(c, scratch, &tot);
-#pragma unroll
-    for (int u = 0; u < kPer; ++u)
-      if (need[u]) sb[nn + r++] = s[u];
-    nn += tot;
-  }
-  int kept_all;
-  (void)block_exclusive_scan<kPlanThreads>(kept, scratch, &kept_all);
-  if (t == 0) fetch_count[b] = ((long long)kept_all + nn > S) ? -1 : nn;
-}
-
-// One block per request, after the evictions: free slots in slot order; the
-// r-th takes the r-th new survivor.  dst receives each new survivor's slot.
+// Slot chunks again: the free slots of the chunk, in slot order, at the
+// chunk's offset among the request's free slots; the r-th free slot takes the
+// r-th new survivor (r < fetch_count).  dst receives each new survivor's slot.
 __global__ __launch_bounds__(kPlanThreads) void assign_kernel(
-    int N, int S, int cap, const int32_t* __restrict__ src,
-    const int32_t* __restrict__ fetch_count, int32_t* __restrict__ slot_of,
-    int32_t* __restrict__ entry_of, int32_t* __restrict__ dst) {
+    int N, int S, int Ss, int cap, int nsc, const int32_t* __restrict__ src,
+    const int32_t* __restrict__ fetch_count, const int32_t* __restrict__ fcnt,
+    int32_t* __restrict__ slot_of, int32_t* __restrict__ entry_of,
+    int32_t* __restrict__ dst) {
   __shared__ int scratch[kPlanThreads / kWave + 1];
-  const int b = blockIdx.x;
-  const int t = threadIdx.x;
+  __shared__ int s_base;
+  const int c = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
   const int nn = fetch_count[b];
-  if (nn <= 0) return;
+  if (nn <= 0) return;   // block-uniform
+  const int base = earlier_chunks_sum(fcnt + (size_t)b * nsc, 1, c, &s_base);
+  if (base >= nn) return;   // block-uniform: earlier chunks hold enough slots
   int32_t* so = slot_of + (size_t)b * N;
   int32_t* eo = entry_of + (size_t)b * S;
   const int32_t* sb = src + (size_t)b * cap;
   int32_t* db = dst + (size_t)b * cap;
-  int placed = 0;
-  for (int base = 0; base < S && placed < nn; base += kPlanThreads * kPer) {
-    bool fr[kPer];
-    int c = 0;
+  bool fr[kPer];
+  int cnt = 0;
 #pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const int j = base + t * kPer + u;
-      fr[u] = j < S && eo[j] < 0;
-      c += fr[u] ? 1 : 0;
-    }
-    int tot;
-    int r = placed + block_exclusive_scan<kPlanThreads>(c, scratch, &tot);
+  for (int u = 0; u < kPer; ++u) {
+    const int j = c * kChunk + t * kPer + u;
+    fr[u] = j < Ss && eo[j] < 0;
+    cnt += fr[u] ? 1 : 0;
+  }
+  int tot;
+  int r = base + block_exclusive_scan<kPlanThreads>(cnt, scratch, &tot);
 #pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      if (fr[u]) {
-        if (r < nn) {
-          const int j = base + t * kPer + u;
-          const int sn = sb[r];
-          eo[j] = sn;
-          so[sn] = j;
-          db[r] = j;
-        }
-        ++r;
+  for (int u = 0; u < kPer; ++u) {
+    if (fr[u]) {
+      if (r < nn) {
+        const int j = c * kChunk + t * kPer + u;
+        const int sn = sb[r];
+        eo[j] = sn;
+        so[sn] = j;
+        db[r] = j;
       }
+      ++r;
     }
-    placed += tot;
   }
 }
 
@@ -285,10 +346,18 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 }  // namespace
 
+namespace {
+
+int plan_chunks(long long n) { return (int)std::max<long long>(1, (n + kChunk - 1) / kChunk); }
+
+}  // namespace
+
 size_t fetch_workspace_bytes(int B, int N, int cap) {
   const size_t W = ((size_t)N + 31) >> 5;
+  const size_t nchN = (size_t)plan_chunks(N);
   return align256((size_t)B * W * 4) + 2 * align256((size_t)B * cap * 4) +
-         align256(((size_t)B + 1) * 4);
+         align256(((size_t)B + 1) * 4) + align256((size_t)B * nchN * 2 * 4) +
+         align256((size_t)B * nchN * 4);
 }
 
 hipError_t launch_resident_reset(int B, int N, int S, int32_t* slot_of, int32_t* entry_of,
@@ -303,10 +372,22 @@ hipError_t launch_fetch(int B, int N, int S, int row_bytes, const void* cold, in
                         int32_t* entry_of, void* rows, int32_t* fetch_count, void* ws,
                         hipStream_t s) {
   const size_t W = ((size_t)N + 31) >> 5;
-  uint32_t* bits = (uint32_t*)ws;
-  int32_t* src = (int32_t*)((char*)ws + align256((size_t)B * W * 4));
-  int32_t* dst = (int32_t*)((char*)src + align256((size_t)B * cap * 4));
-  int32_t* offs = (int32_t*)((char*)dst + align256((size_t)B * cap * 4));
+  const int nch = plan_chunks(std::min(cap, N));      // survivor chunks per request
+  const int Ss = std::min(S, N);
+  const int nsc = plan_chunks(Ss);                     // slot chunks per request
+  const size_t nchN = (size_t)plan_chunks(N);
+  char* p = (char*)ws;
+  uint32_t* bits = (uint32_t*)p;
+  p += align256((size_t)B * W * 4);
+  int32_t* src = (int32_t*)p;
+  p += align256((size_t)B * cap * 4);
+  int32_t* dst = (int32_t*)p;
+  p += align256((size_t)B * cap * 4);
+  int32_t* offs = (int32_t*)p;
+  p += align256(((size_t)B + 1) * 4);
+  int32_t* ccnt = (int32_t*)p;
+  p += align256((size_t)B * nchN * 2 * 4);
+  int32_t* fcnt = (int32_t*)p;
   hipError_t e = launch_fill_i32((int32_t*)bits, (int64_t)(B * W), 0, s);
   if (e != hipSuccess) return e;
   if (N > 0 && cap > 0) {
@@ -314,19 +395,17 @@ hipError_t launch_fetch(int B, int N, int S, int row_bytes, const void* cold, in
     hipLaunchKernelGGL(mark_kernel, dim3(gx, B), dim3(256), 0, s, N, cap, surv_idx, surv_count,
                        bits);
   }
-  hipLaunchKernelGGL(need_kernel, dim3(B), dim3(kPlanThreads), 0, s, N, S, cap, surv_idx,
-                     surv_count, slot_of, src, fetch_count);
-  if (S > 0) {
-    const int gx = (int)std::min<long long>((S + 255) / 256, 64);
-    hipLaunchKernelGGL(evict_kernel, dim3(gx, B), dim3(256), 0, s, N, S, bits, fetch_count,
-                       slot_of, entry_of);
-  }
-  hipLaunchKernelGGL(assign_kernel, dim3(B), dim3(kPlanThreads), 0, s, N, S, cap, src,
-                     fetch_count, slot_of, entry_of, dst);
+  hipLaunchKernelGGL(need_count_kernel, dim3(nch, B), dim3(kPlanThreads), 0, s, N, cap, nch,
+                     surv_idx, surv_count, slot_of, ccnt);
+  hipLaunchKernelGGL(need_write_kernel, dim3(nch, B), dim3(kPlanThreads), 0, s, N, S, cap, nch,
+                     surv_idx, surv_count, slot_of, ccnt, src, fetch_count);
+  hipLaunchKernelGGL(evict_kernel, dim3(nsc, B), dim3(kPlanThreads), 0, s, N, S, Ss, nsc, bits,
+                     fetch_count, slot_of, entry_of, fcnt);
+  hipLaunchKernelGGL(assign_kernel, dim3(nsc, B), dim3(kPlanThreads), 0, s, N, S, Ss, cap, nsc,
+                     src, fetch_count, fcnt, slot_of, entry_of, dst);
   hipLaunchKernelGGL(offsets_kernel, dim3(1), dim3(kPlanThreads), 0, s, B, fetch_count, offs);
   hipLaunchKernelGGL(copy_kernel, dim3(device_cu_count()), dim3(kCopyThreads), 0, s, B, N, S,
-                     cap,
-                     row_bytes / 16, (const unsigned char*)cold, src, dst, offs,
+                     cap, row_bytes / 16, (const unsigned char*)cold, src, dst, offs,
                      (unsigned char*)rows);
   return hipGetLastError();
 }

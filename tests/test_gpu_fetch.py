@@ -225,3 +225,19 @@ def test_pageable_cold_pool_is_refused():
     with pytest.raises(ValueError):
         lsa.lsa_fetch_survivors(torch.zeros((B, N, rb), dtype=torch.uint8), idx, cnt, so, eo,
                                 rows, fc, ws)
+
+
+def test_many_requests():
+    """More requests than one planning block covers (the per-request copy
+    offsets are summed in several passes), some of them over capacity."""
+    rng = np.random.default_rng(17)
+    B, N, rb, S = 1100, 256, 16, 60
+    cold = rng.integers(0, 256, (B, N, rb), dtype=np.uint8)
+    p = Pair(cold, S, N, pinned=True)
+    for t in range(3):
+        sizes = rng.integers(0, 70, B)                 # sizes above 60 do not fit
+        sets = [np.sort(rng.choice(N, n, replace=False)).astype(np.int32) for n in sizes]
+        got, want = p.step(sets)
+        assert np.array_equal(got, want)
+        assert (got == -1).any() and (got > 0).any()
+        p.check()

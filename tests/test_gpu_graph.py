@@ -74,3 +74,61 @@ def test_trigger_graph_replays_match_eager(name):
         for key, v in want.items():
             assert torch.equal(got[key], v), (name, rep, key)
         del junk
+
+
+def test_cold_fetch_graph_replays_match_eager():
+    """Reset, two fetches from a pinned host cold pool and the resident
+    gather, captured once; every replay equals the eager run."""
+    import sparse_kv_cache_lsa_amd as lsa
+    rng = np.random.default_rng(21)
+    B, N, S, rb, k = 3, 5000, 1800, 64, 300
+    cold = torch.from_numpy(rng.integers(0, 256, (B, N, rb), dtype=np.uint8)).pin_memory()
+    sets = []
+    for t in range(2):
+        idx = np.full((B, N), -1, np.int32)
+        cnt = np.zeros(B, np.int32)
+        for b in range(B):
+            x = np.sort(rng.choice(N, 1000 + 200 * b + 100 * t, replace=False)).astype(np.int32)
+            idx[b, :x.size] = x
+            cnt[b] = x.size
+        sets.append((torch.from_numpy(idx).to(DEV), torch.from_numpy(cnt).to(DEV)))
+    top = torch.from_numpy(np.sort(rng.choice(N, (B, k)), axis=1).astype(np.int32)).to(DEV)
+    so = torch.empty((B, N), dtype=torch.int32, device=DEV)
+    eo = torch.empty((B, S), dtype=torch.int32, device=DEV)
+    rows = torch.zeros((B, S, rb), dtype=torch.uint8, device=DEV)
+    fc = torch.empty((B,), dtype=torch.int32, device=DEV)
+    hot = torch.empty((B, k, rb), dtype=torch.uint8, device=DEV)
+    ws = torch.empty((lsa.lsa_fetch_workspace_bytes(B, N, N),), dtype=torch.uint8, device=DEV)
+    outs = (so, eo, rows, fc, hot)
+
+    def run():
+        lsa.lsa_resident_reset(so, eo)
+        for s in sets:
+            lsa.lsa_fetch_survivors(cold, s[0], s[1], so, eo, rows, fc, ws)
+        lsa.lsa_gather_resident(rows, so, top, hot)
+
+    run()
+    torch.cuda.synchronize()
+    want = [t.clone() for t in outs]
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for t in outs:
+            t.view(torch.uint8).fill_(0x33 + rep)
+        junk = torch.randn(1 << 20, device=DEV).sum()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for i, t in enumerate(outs):
+            if t is rows:        # slots left free keep whatever bytes they held
+                occ = want[1] >= 0
+                assert torch.equal(t[occ], want[i][occ]), rep
+            else:
+                assert torch.equal(t, want[i]), (rep, i)
+        del junk

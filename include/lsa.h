@@ -13,9 +13,10 @@
  *
  * Conventions for every call:
  *  - All tensor arguments are DEVICE pointers owned by the caller, except
- *    where an argument is documented as a host array.  The library never
- *    allocates persistent memory and keeps no global mutable state apart from
- *    a thread-local error string.  Every call is reentrant.
+ *    where an argument is documented as a host array or as host memory.  The
+ *    library never allocates persistent memory; its only global state is a
+ *    thread-local error string and a per-device cache of the compute-unit
+ *    count (filled once, thread-safe).  Every call is reentrant.
  *  - Every compute call enqueues its kernels on `stream` and returns without
  *    synchronising.  Outputs are valid once the stream has reached that point.
  *  - Argument, shape and dtype errors are detected on the host and returned

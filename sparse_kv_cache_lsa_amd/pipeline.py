@@ -1,13 +1,15 @@
 """Device buffers for one indexer trigger and the call sequence of the hot
-path (project -> score -> select/compact -> top-k -> gather).  Allocation uses
+path (project -> score -> select/compact -> top-k -> gather), and the resident
+set that survivors are fetched into from a host cold pool.  Allocation uses
 torch; every step is one C entry point of liblsa.so."""
 from __future__ import annotations
 
 from dataclasses import dataclass
 
-from . import (LSA_CAND_CHUNK, lsa_gather_hot, lsa_pack_query_weights, lsa_project_query,
-               lsa_project_query_packed, lsa_query_weights_packed_bytes, lsa_score,
-               lsa_select_or_compact, lsa_topk, lsa_topk_workspace_bytes)
+from . import (LSA_CAND_CHUNK, lsa_fetch_survivors, lsa_fetch_workspace_bytes, lsa_gather_hot,
+               lsa_gather_resident, lsa_pack_query_weights, lsa_project_query,
+               lsa_project_query_packed, lsa_query_weights_packed_bytes, lsa_resident_reset,
+               lsa_score, lsa_select_or_compact, lsa_topk, lsa_topk_workspace_bytes)
 
 
 @dataclass
@@ -85,3 +87,43 @@ def run_trigger(buf: TriggerBuffers, h, Wq, Wg, keys, key_scale, bias, pool=None
              buf.ws_topk, stream=stream)
     if pool is not None:
         lsa_gather_hot(pool, buf.topk_idx, buf.hot, stream=stream)
+
+
+@dataclass
+class ResidentSet:
+    """GPU-resident rows of a cold pool kept in pinned host memory: S slots
+    per request and the two slot tables.  fetch() brings in the survivors of a
+    trigger (rows already resident are reused), gather() copies top-k rows
+    out of the set."""
+    slot_of: object
+    entry_of: object
+    rows: object
+    fetch_count: object
+    ws: object
+
+    @classmethod
+    def allocate(cls, B, N, S, row_elems, cap=None, dtype=None, device="cuda", stream=None):
+        import torch
+        cap = N if cap is None else cap
+        dtype = torch.int16 if dtype is None else dtype
+        r = cls(slot_of=torch.empty((B, N), dtype=torch.int32, device=device),
+                entry_of=torch.empty((B, S), dtype=torch.int32, device=device),
+                rows=torch.empty((B, S, row_elems), dtype=dtype, device=device),
+                fetch_count=torch.empty((B,), dtype=torch.int32, device=device),
+                ws=torch.empty((max(1, lsa_fetch_workspace_bytes(B, N, cap)),),
+                               dtype=torch.uint8, device=device))
+        r.reset(stream)
+        return r
+
+    def reset(self, stream=None):
+        """Nothing resident."""
+        lsa_resident_reset(self.slot_of, self.entry_of, stream=stream)
+
+    def fetch(self, cold_pool, surv_idx, surv_count, stream=None):
+        """Survivors ([B][cap] ascending, counts [B]) into the set;
+        fetch_count[b] = rows read from the cold pool, -1 if they do not fit."""
+        lsa_fetch_survivors(cold_pool, surv_idx, surv_count, self.slot_of, self.entry_of,
+                            self.rows, self.fetch_count, self.ws, stream=stream)
+
+    def gather(self, idx, hot, stream=None):
+        lsa_gather_resident(self.rows, self.slot_of, idx, hot, stream=stream)

@@ -233,7 +233,9 @@ def main():
                      "kernel": "lsa_score", "algorithmic_bytes_per_launch": key_bytes,
                      "mean_launch_ms": mean_score, "timed_launches_sampled": len(sampled)},
         "score_select": {"ms": score_select, "GB/s": ss_gbs, "frac_of_peak": ss_gbs / HBM_PEAK_GBS,
-                         "triples_per_s": triples / (score_select * 1e-3)},
+                         "triples_per_s": triples / (score_select * 1e-3),
+                         "request_entries_per_s": w.B * w.N / (score_select * 1e-3)},
+        "request_entries_per_s": w.B * w.N / (ms_per_step * 1e-3),
         "kernel_ms_median": per,
         "kernel_ms_p10_p90": pct,
         "survivor_fraction": float(counts.mean() / w.N),

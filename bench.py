@@ -298,6 +298,7 @@ def cold_fetch(w, d, pool, buf, stream, step, ms_per_step):
     import numpy as np
     import torch
     import sparse_kv_cache_lsa_amd as lsa
+    from sparse_kv_cache_lsa_amd.pipeline import ResidentSet
 
     ev = lambda: torch.cuda.Event(enable_timing=True)
     B, N = w.B, w.N
@@ -306,11 +307,7 @@ def cold_fetch(w, d, pool, buf, stream, step, ms_per_step):
     t0 = time.time()
     cold = torch.empty(pool.shape, dtype=pool.dtype, pin_memory=True)
     cold.copy_(pool)
-    so = torch.empty((B, N), dtype=torch.int32, device="cuda")
-    eo = torch.empty((B, S), dtype=torch.int32, device="cuda")
-    rows = torch.empty((B, S, w.row_elems), dtype=pool.dtype, device="cuda")
-    fc = torch.empty((B,), dtype=torch.int32, device="cuda")
-    ws = torch.empty((lsa.lsa_fetch_workspace_bytes(B, N, N),), dtype=torch.uint8, device="cuda")
+    res = ResidentSet.allocate(B, N, S, w.row_elems, dtype=pool.dtype, stream=stream)
 
     def survivors(h):
         lsa.lsa_project_query_packed(h, d["Wp"], buf.q, buf.g, stream=stream)
@@ -330,12 +327,12 @@ def cold_fetch(w, d, pool, buf, stream, step, ms_per_step):
     setup_s = time.time() - t0
 
     def fetch(s, st=stream):
-        lsa.lsa_fetch_survivors(cold, s[0], s[1], so, eo, rows, fc, ws, stream=st)
+        res.fetch(cold, s[0], s[1], stream=st)
 
     def timed(pre, s, reps=3):
         out = []
         for _ in range(reps + 1):            # the first run is a warm-up
-            lsa.lsa_resident_reset(so, eo, stream=stream)
+            res.reset(stream)
             for p in pre:
                 fetch(p)
             e0, e1 = ev(), ev()
@@ -343,7 +340,7 @@ def cold_fetch(w, d, pool, buf, stream, step, ms_per_step):
             fetch(s)
             e1.record(stream)
             torch.cuda.synchronize()
-            out.append((e0.elapsed_time(e1), int(fc.sum())))
+            out.append((e0.elapsed_time(e1), int(res.fetch_count.sum())))
         out = out[1:]
         ms = float(np.median([o[0] for o in out]))
         return ms, out[-1][1]
@@ -370,7 +367,7 @@ def cold_fetch(w, d, pool, buf, stream, step, ms_per_step):
             step()
 
     def reset_side():
-        lsa.lsa_resident_reset(so, eo, stream=side)
+        res.reset(side)
         torch.cuda.synchronize()
 
     reset_side()

@@ -43,6 +43,26 @@ def _dev(*ts):
             raise ValueError("LSA tensors must be contiguous")
 
 
+def _row_bytes(t) -> int:
+    """Bytes of one row of a [B][rows][...] tensor."""
+    n = 1
+    for d in t.shape[2:]:
+        n *= d
+    return n * t.element_size()
+
+
+def _same_rows(fn, row_tensors, row_bytes, B, batch_tensors):
+    """The row size and the batch size that a call passes to the library must
+    hold for every tensor, or a kernel would read or write past one of them."""
+    for t in row_tensors:
+        if t.dim() < 3 or _row_bytes(t) != row_bytes or t.shape[0] != B:
+            raise ValueError(f"{fn}: every row tensor must be [B={B}][rows][...] with "
+                             f"{row_bytes}-byte rows")
+    for t in batch_tensors:
+        if t.shape[0] != B:
+            raise ValueError(f"{fn}: batch size {t.shape[0]} of an index/table tensor is not B={B}")
+
+
 def lsa_version() -> str:
     return load().lsa_version().decode()
 
@@ -137,7 +157,8 @@ def lsa_gather_hot(pool, idx, hot, *, stream=None):
     _dev(pool, idx, hot)
     B, N = pool.shape[0], pool.shape[1]
     k = idx.shape[1]
-    row_bytes = pool[0, 0].numel() * pool.element_size() if N > 0 else hot[0, 0].numel() * hot.element_size()
+    row_bytes = _row_bytes(hot)
+    _same_rows("lsa_gather_hot", (pool, hot), row_bytes, B, (idx,))
     check(load().lsa_gather_hot(B, N, k, row_bytes, _p(pool), _p(idx), _p(hot), _stream(stream)))
 
 
@@ -167,7 +188,12 @@ def lsa_fetch_survivors(cold_pool, surv_idx, surv_count, slot_of, entry_of, rows
     B, N = cold_pool.shape[0], cold_pool.shape[1]
     S = entry_of.shape[1]
     cap = surv_idx.shape[1]
-    row_bytes = rows[0, 0].numel() * rows.element_size() if S > 0 else cold_pool[0, 0].numel() * cold_pool.element_size()
+    row_bytes = _row_bytes(cold_pool)
+    _same_rows("lsa_fetch_survivors", (cold_pool, rows), row_bytes, B,
+               (surv_idx, surv_count, slot_of, entry_of, fetch_count))
+    if slot_of.shape[1] != N or rows.shape[1] != S:
+        raise ValueError("lsa_fetch_survivors: slot_of must be [B][N] and rows [B][S][row] "
+                         "with S = entry_of.shape[1]")
     check(load().lsa_fetch_survivors(B, N, S, row_bytes, _p(cold_pool), cap, _p(surv_idx),
                                      _p(surv_count), _p(slot_of), _p(entry_of), _p(rows),
                                      _p(fetch_count), _p(ws),
@@ -181,7 +207,8 @@ def lsa_gather_resident(rows, slot_of, idx, hot, *, stream=None):
     B, S = rows.shape[0], rows.shape[1]
     N = slot_of.shape[1]
     k = idx.shape[1]
-    row_bytes = hot[0, 0].numel() * hot.element_size() if k > 0 else rows[0, 0].numel() * rows.element_size()
+    row_bytes = _row_bytes(hot)
+    _same_rows("lsa_gather_resident", (rows, hot), row_bytes, B, (slot_of, idx))
     check(load().lsa_gather_resident(B, N, S, k, row_bytes, _p(rows), _p(slot_of), _p(idx),
                                      _p(hot), _stream(stream)))
 

@@ -163,3 +163,19 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_abi, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="not built"):
         _abi.load()
+
+
+def test_binding_checks_row_and_batch_sizes():
+    """The binding refuses tensors whose rows or batch differ from the sizes
+    it passes to the library (a kernel would otherwise run past one of them)."""
+    import torch
+    import sparse_kv_cache_lsa_amd as lsa
+    pool = torch.zeros((2, 5, 512), dtype=torch.int16)
+    ok = torch.zeros((2, 7, 1024), dtype=torch.uint8)
+    lsa._same_rows("f", (pool, ok), 1024, 2, (torch.zeros(2, 3),))
+    with pytest.raises(ValueError):
+        lsa._same_rows("f", (pool, torch.zeros((2, 7, 512), dtype=torch.uint8)), 1024, 2, ())
+    with pytest.raises(ValueError):
+        lsa._same_rows("f", (pool, ok), 1024, 2, (torch.zeros(3, 3),))
+    with pytest.raises(ValueError):
+        lsa._same_rows("f", (pool, torch.zeros((3, 7, 1024), dtype=torch.uint8)), 1024, 2, ())

@@ -43,6 +43,11 @@ def _dev(*ts):
             raise ValueError("LSA tensors must be contiguous")
 
 
+def _expect(fn, name, t, shape):
+    if t is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{fn}: {name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
 def _row_bytes(t) -> int:
     """Bytes of one row of a [B][rows][...] tensor."""
     n = 1
@@ -77,10 +82,24 @@ def lsa_project_query(h, Wq, Wg, q, g, *, h_layer_stride: int = 0, stream=None):
     _dev(h, q, g, *Wq, *Wg)
     L, B, H, dI = q.shape
     D = h.shape[-1]
+    _check_project("lsa_project_query", h, g, L, B, H, D, h_layer_stride)
+    if len(Wq) != L or len(Wg) != L:
+        raise ValueError("lsa_project_query: one W_q and one W_g per layer")
+    for l in range(L):
+        _expect("lsa_project_query", f"Wq[{l}]", Wq[l], (H * dI, D))
+        _expect("lsa_project_query", f"Wg[{l}]", Wg[l], (H, D))
     wq, _k1 = ptr_array([_p(w) for w in Wq])
     wg, _k2 = ptr_array([_p(w) for w in Wg])
     check(load().lsa_project_query(L, B, D, H, dI, _p(h), int(h_layer_stride), wq, wg, _p(q),
                                    _p(g), _stream(stream)))
+
+
+def _check_project(fn, h, g, L, B, H, D, stride):
+    _expect(fn, "g", g, (L, B, H))
+    # the kernels read rows b*D .. of h, and layer l from l*stride on
+    if h.numel() < (L - 1) * stride + B * D:
+        raise ValueError(f"{fn}: h holds {h.numel()} elements; B*D (+ (L-1)*h_layer_stride) "
+                         f"= {(L - 1) * stride + B * D} are read")
 
 
 def lsa_query_weights_packed_bytes(H: int, dI: int, D: int) -> int:
@@ -101,6 +120,10 @@ def lsa_project_query_packed(h, packed, q, g, *, h_layer_stride: int = 0, stream
     _dev(h, q, g, *packed)
     L, B, H, dI = q.shape
     D = h.shape[-1]
+    _check_project("lsa_project_query_packed", h, g, L, B, H, D, h_layer_stride)
+    need = lsa_query_weights_packed_bytes(H, dI, D)
+    if len(packed) != L or any(p.numel() * p.element_size() < need for p in packed):
+        raise ValueError(f"lsa_project_query_packed: one packed buffer of {need} bytes per layer")
     wp, _k = ptr_array([_p(w) for w in packed])
     check(load().lsa_project_query_packed(L, B, D, H, dI, _p(h), int(h_layer_stride), wp, _p(q),
                                           _p(g), _stream(stream)))
@@ -117,6 +140,24 @@ def lsa_score(keys, key_scale, q, g, bias, sel_mask, cand_idx, cand_z, cand_coun
     _dev(q, g, sel_mask, cand_idx, cand_z, cand_count, z, I, *keys, *(key_scale or []))
     L, B, H, dI = q.shape
     N = keys[0].shape[1]
+    if N > 0:
+        fn = "lsa_score"
+        if len(keys) != L or len(bias) < L or (fp8 and len(key_scale) != L):
+            raise ValueError(f"{fn}: one key tensor, bias (and scale) per layer")
+        for l in range(L):
+            _expect(fn, f"keys[{l}]", keys[l], (B, N, dI))
+            if keys[l].element_size() != (1 if fp8 else 2):
+                raise ValueError(f"{fn}: keys must be 1-byte e4m3 codes or 2-byte bf16")
+            if fp8:
+                _expect(fn, f"key_scale[{l}]", key_scale[l], (B, N))
+        nch = (N + LSA_CAND_CHUNK - 1) // LSA_CAND_CHUNK
+        _expect(fn, "g", g, (L, B, H))
+        _expect(fn, "sel_mask", sel_mask, (L, B, (N + 31) // 32))
+        _expect(fn, "cand_idx", cand_idx, (B, nch, LSA_CAND_CHUNK))
+        _expect(fn, "cand_z", cand_z, (B, nch, LSA_CAND_CHUNK))
+        _expect(fn, "cand_count", cand_count, (B, nch))
+        _expect(fn, "z", z, (L, B, N))
+        _expect(fn, "I", I, (L, B, N))
     kp, _k1 = ptr_array([_p(k) for k in keys])
     if fp8:
         sp, _k2 = ptr_array([_p(s) for s in key_scale])
@@ -134,6 +175,13 @@ def lsa_select_or_compact(cand_idx, cand_z, cand_count, N, surv_idx, surv_z, sur
     surv_idx i32 [B][cap], surv_z f32 [B][cap], surv_count i32 [B]."""
     _dev(cand_idx, cand_z, cand_count, surv_idx, surv_z, surv_count)
     B, cap = surv_idx.shape
+    nch = (int(N) + LSA_CAND_CHUNK - 1) // LSA_CAND_CHUNK
+    fn = "lsa_select_or_compact"
+    _expect(fn, "cand_idx", cand_idx, (B, nch, LSA_CAND_CHUNK))
+    _expect(fn, "cand_z", cand_z, (B, nch, LSA_CAND_CHUNK))
+    _expect(fn, "cand_count", cand_count, (B, nch))
+    _expect(fn, "surv_z", surv_z, (B, cap))
+    _expect(fn, "surv_count", surv_count, (B,))
     check(load().lsa_select_or_compact(B, int(N), _p(cand_idx), _p(cand_z), _p(cand_count), cap,
                                        _p(surv_idx), _p(surv_z), _p(surv_count),
                                        _stream(stream)))
@@ -147,6 +195,10 @@ def lsa_topk(surv_idx, surv_z, surv_count, topk_idx, topk_count, ws=None, *, str
     _dev(surv_idx, surv_z, surv_count, topk_idx, topk_count, ws)
     B, cap = surv_idx.shape
     k = topk_idx.shape[1]
+    _expect("lsa_topk", "surv_z", surv_z, (B, cap))
+    _expect("lsa_topk", "surv_count", surv_count, (B,))
+    _expect("lsa_topk", "topk_idx", topk_idx, (B, k))
+    _expect("lsa_topk", "topk_count", topk_count, (B,))
     check(load().lsa_topk(B, cap, k, _p(surv_idx), _p(surv_z), _p(surv_count), _p(topk_idx),
                           _p(topk_count), _p(ws),
                           0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
@@ -222,6 +274,9 @@ def lsa_label_vote(logits, top_p, theta, count, label, layer_mask=None, ws=None,
     layer_mask [Q][L][ceil(N/32)]."""
     _dev(logits, count, label, layer_mask, ws)
     Q, L, N = logits.shape
+    _expect("lsa_label_vote", "count", count, (Q, N))
+    _expect("lsa_label_vote", "label", label, (Q, N))
+    _expect("lsa_label_vote", "layer_mask", layer_mask, (Q, L, (N + 31) // 32))
     check(load().lsa_label_vote(Q, L, N, float(top_p), int(theta), _p(logits), _p(layer_mask),
                                 _p(count), _p(label), _p(ws),
                                 0 if ws is None else ws.numel() * ws.element_size(),
@@ -237,6 +292,14 @@ def lsa_focal_bce_grad(h, Wq, Wg, bias, K, label, gamma, loss, dWq, ws=None, *, 
     _dev(h, Wq, Wg, K, label, loss, dWq, ws)
     Q, D = h.shape
     N = K.shape[0]
+    fn = "lsa_focal_bce_grad"
+    _expect(fn, "Wq", Wq, (H * dI, D))
+    _expect(fn, "Wg", Wg, (H, D))
+    _expect(fn, "K", K, (N, dI))
+    _expect(fn, "label", label, (Q, N))
+    _expect(fn, "dWq", dWq, (H * dI, D))
+    if loss.numel() < 1:
+        raise ValueError(f"{fn}: loss needs one element")
     check(load().lsa_focal_bce_grad(Q, N, D, H, dI, float(gamma), _p(h), _p(Wq), _p(Wg),
                                     float(bias), _p(K), _p(label), _p(loss), _p(dWq), _p(ws),
                                     0 if ws is None else ws.numel() * ws.element_size(),

@@ -275,7 +275,8 @@ int64_t lsa_or_fetch(int64_t N, int64_t S, int64_t row_bytes, const uint8_t* col
   for (int64_t i = 0; i < n; ++i) {
     int32_t s = surv[i];
     if (slot_of[s] >= 0) continue;
-    while (entry_of[j] >= 0) ++j;
+    while (j < S && entry_of[j] >= 0) ++j;
+    if (j >= S) break; /* unreachable after the capacity check */
     entry_of[j] = s;
     slot_of[s] = (int32_t)j;
     memcpy(rows + j * row_bytes, cold + (int64_t)s * row_bytes, (size_t)row_bytes);

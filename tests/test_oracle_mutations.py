@@ -50,8 +50,8 @@ MUTANTS = [
      "  return (a->idx > b->idx) ? -1 : (a->idx < b->idx);\n}\n\nstatic int cmp_int_asc"),
     ("fetch skips eviction", "if (e >= 0 && !is_surv[e]) {", "if (e >= 0 && !is_surv[e] && 0) {"),
     ("fetch copies the slot's cold row", "cold + (int64_t)s * row_bytes", "cold + (int64_t)j * row_bytes"),
-    ("fetch takes the highest free slot", "int64_t j = 0;\n  for (int64_t i = 0; i < n; ++i) {\n    int32_t s = surv[i];\n    if (slot_of[s] >= 0) continue;\n    while (entry_of[j] >= 0) ++j;",
-     "int64_t j = S - 1;\n  for (int64_t i = 0; i < n; ++i) {\n    int32_t s = surv[i];\n    if (slot_of[s] >= 0) continue;\n    while (entry_of[j] >= 0) --j;"),
+    ("fetch takes the highest free slot", "int64_t j = 0;\n  for (int64_t i = 0; i < n; ++i) {\n    int32_t s = surv[i];\n    if (slot_of[s] >= 0) continue;\n    while (j < S && entry_of[j] >= 0) ++j;\n    if (j >= S) break;",
+     "int64_t j = S - 1;\n  for (int64_t i = 0; i < n; ++i) {\n    int32_t s = surv[i];\n    if (slot_of[s] >= 0) continue;\n    while (j >= 0 && entry_of[j] >= 0) --j;\n    if (j < 0) break;"),
     ("fetch re-copies resident rows", "    if (slot_of[s] >= 0) continue;\n    while",
      "    if (slot_of[s] >= 0) {\n      memcpy(rows + (int64_t)slot_of[s] * row_bytes, cold + (int64_t)s * row_bytes, (size_t)row_bytes);\n      continue;\n    }\n    while"),
     ("gather pads with ones", "memset(hot + j * row_bytes, 0, (size_t)row_bytes);",

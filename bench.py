@@ -30,7 +30,7 @@ PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "lsa_score_ctx1m_traffic.json")
 
 def score_source_hash() -> str:
     h = hashlib.sha256()
-    for f in ("lsa_score.hip", "lsa_device.h"):
+    for f in ("lsa_score.hip", "lsa_device.h", "lsa_launch.h"):
         with open(os.path.join(ROOT, "sparse_kv_cache_lsa_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]

@@ -157,7 +157,8 @@ lsa_status lsa_project_query_packed(int L, int B, int D, int H, int dI,
  *   key_scale  HOST array of L device pointers, each fp32 [B][N]; required for
  *              LSA_KEY_FP8_E4M3, ignored (may be NULL) for bf16
  *   q, g       as written by lsa_project_query
- *   bias       HOST array of L fp32 values
+ *   bias       DEVICE fp32 [L], read by the kernels when they run (so a captured
+ *              graph picks up new values without being captured again)
  *   sel_mask   out uint32 [L][B][ceil(N/32)]: bit (s % 32) of word s / 32;
  *              bits past N are zero
  *   cand_idx   out int32 [B][nchunks][LSA_CAND_CHUNK], nchunks = ceil(N / LSA_CAND_CHUNK)
@@ -199,6 +200,36 @@ lsa_status lsa_select_or_compact(int B, int N, const int32_t* cand_idx,
                                  const float* cand_z, const int32_t* cand_count,
                                  int cap, int32_t* surv_idx, float* surv_z,
                                  int32_t* surv_count, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * The same OR merge and compaction from dense per-layer selections
+ * ([SUMMARY] 2.4: the layers' predictions are united in OR mode; [SUMMARY]
+ * 2.1 dynamic-fetch bullet: every entry a layer selects is fetched), for
+ * masks and logits from any producer -- lsa_score's sel_mask and z_opt, or
+ * another indexer.  For every request b:
+ *   surv_idx[b]   = ascending { s < N : bit s of sel_mask[l][b] is set for
+ *                   some layer l }
+ *   surv_z[b][i]  = max over ALL layers l of z[l][b][s] (NaN values ignored;
+ *                   NaN when every layer's value is NaN).  For masks that are
+ *                   z >= 0 this equals the maximum over the selecting layers.
+ *   surv_count[b] = the TRUE survivor count (only the first cap are written)
+ *
+ *   sel_mask  uint32 [L][B][ceil(N/32)], bit (s % 32) of word s / 32; bits
+ *             at or past N are ignored
+ *   z         fp32 [L][B][N]
+ *   surv_idx out int32 [B][cap]   surv_z out fp32 [B][cap]   surv_count out int32 [B]
+ *   ws        device workspace of lsa_select_or_compact_masks_workspace_bytes(B, N)
+ *             bytes, 16-byte aligned (per-chunk survivor counts)
+ * Limits: 1 <= L <= LSA_MAX_LAYERS, 1 <= B <= 65535, 0 <= N <= 2^24, cap >= 0;
+ * sel_mask and z 4-byte aligned.  Errors: LSA_E_SHAPE / LSA_E_ARG for the
+ * limits and null pointers, LSA_E_WORKSPACE for a missing or short workspace,
+ * LSA_E_HIP for a launch failure.
+ */
+size_t lsa_select_or_compact_masks_workspace_bytes(int B, int N);
+lsa_status lsa_select_or_compact_masks(int L, int B, int N, const uint32_t* sel_mask,
+                                       const float* z, int cap, int32_t* surv_idx,
+                                       float* surv_z, int32_t* surv_count, void* ws,
+                                       size_t ws_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
  * Top-k inside the fetched set ([SUMMARY] 2.1 hierarchical-selection bullet:

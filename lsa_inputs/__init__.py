@@ -331,7 +331,7 @@ def to_device(inp: IndexerInputs, device="cuda"):
         "Wg": [t(w) for w in inp.Wg],
         "keys": [t(k) for k in inp.keys],
         "scale": None if inp.scale[0] is None else [t(s) for s in inp.scale],
-        "bias": [float(b) for b in inp.bias],
+        "bias": torch.from_numpy(np.ascontiguousarray(inp.bias, np.float32)).to(device),
     }
 
 

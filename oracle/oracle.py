@@ -41,6 +41,12 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
+    # One OpenMP runtime per process: torch carries its own libgomp (soname
+    # libgomp.so.1, the one this library needs).  With torch loaded first the
+    # dynamic loader binds this library to that copy; loaded the other way
+    # round, the process maps the system libgomp as well, and two OpenMP
+    # runtimes in one process each start their own thread pools.
+    import torch  # noqa: F401
     if _ALT_LIB:
         lib = C.CDLL(_ALT_LIB)
     else:

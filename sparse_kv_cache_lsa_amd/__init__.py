@@ -17,6 +17,7 @@ __all__ = [
     "LSAError", "LSA_KEY_BF16", "LSA_KEY_FP8_E4M3", "LSA_CAND_CHUNK", "load", "lsa_version",
     "lsa_trigger_due", "lsa_project_query", "lsa_query_weights_packed_bytes",
     "lsa_pack_query_weights", "lsa_project_query_packed", "lsa_score", "lsa_select_or_compact",
+    "lsa_select_or_compact_masks_workspace_bytes", "lsa_select_or_compact_masks",
     "lsa_topk_workspace_bytes", "lsa_topk", "lsa_gather_hot", "lsa_fetch_workspace_bytes",
     "lsa_resident_reset", "lsa_fetch_survivors", "lsa_gather_resident",
     "lsa_label_vote_workspace_bytes", "lsa_label_vote",
@@ -46,6 +47,16 @@ def _dev(*ts):
 def _expect(fn, name, t, shape):
     if t is not None and tuple(t.shape) != tuple(shape):
         raise ValueError(f"{fn}: {name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _dtype(fn, name, t, *names):
+    """t's dtype must be one of the torch dtypes named (what the kernels read or write)."""
+    if t is not None and str(t.dtype).replace("torch.", "") not in names:
+        raise ValueError(f"{fn}: {name} has dtype {t.dtype}, expected {' or '.join(names)}")
+
+
+def _nbytes(t) -> int:
+    return 0 if t is None else t.numel() * t.element_size()
 
 
 def _row_bytes(t) -> int:
@@ -79,23 +90,28 @@ def lsa_trigger_due(decode_step: int, tau: int = 64) -> bool:
 def lsa_project_query(h, Wq, Wg, q, g, *, h_layer_stride: int = 0, stream=None):
     """h bf16 [B][D] (or [L][B][D] with h_layer_stride = B*D); Wq/Wg: lists of
     L bf16 tensors [H*dI][D] / [H][D]; q out bf16 [L][B][H][dI]; g out f32 [L][B][H]."""
-    _dev(h, q, g, *Wq, *Wg)
     L, B, H, dI = q.shape
     D = h.shape[-1]
-    _check_project("lsa_project_query", h, g, L, B, H, D, h_layer_stride)
+    _check_project("lsa_project_query", h, q, g, L, B, H, D, h_layer_stride)
     if len(Wq) != L or len(Wg) != L:
         raise ValueError("lsa_project_query: one W_q and one W_g per layer")
     for l in range(L):
         _expect("lsa_project_query", f"Wq[{l}]", Wq[l], (H * dI, D))
         _expect("lsa_project_query", f"Wg[{l}]", Wg[l], (H, D))
+        _dtype("lsa_project_query", f"Wq[{l}]", Wq[l], "bfloat16", "int16", "uint16")
+        _dtype("lsa_project_query", f"Wg[{l}]", Wg[l], "bfloat16", "int16", "uint16")
+    _dev(h, q, g, *Wq, *Wg)
     wq, _k1 = ptr_array([_p(w) for w in Wq])
     wg, _k2 = ptr_array([_p(w) for w in Wg])
     check(load().lsa_project_query(L, B, D, H, dI, _p(h), int(h_layer_stride), wq, wg, _p(q),
                                    _p(g), _stream(stream)))
 
 
-def _check_project(fn, h, g, L, B, H, D, stride):
+def _check_project(fn, h, q, g, L, B, H, D, stride):
     _expect(fn, "g", g, (L, B, H))
+    _dtype(fn, "h", h, "bfloat16", "int16", "uint16")
+    _dtype(fn, "q", q, "bfloat16", "int16", "uint16")
+    _dtype(fn, "g", g, "float32")
     # the kernels read rows b*D .. of h, and layer l from l*stride on
     if h.numel() < (L - 1) * stride + B * D:
         raise ValueError(f"{fn}: h holds {h.numel()} elements; B*D (+ (L-1)*h_layer_stride) "
@@ -109,21 +125,28 @@ def lsa_query_weights_packed_bytes(H: int, dI: int, D: int) -> int:
 def lsa_pack_query_weights(Wq, Wg, packed, *, stream=None):
     """One layer: Wq bf16 [H*dI][D], Wg bf16 [H][D] -> packed (uint8 tensor of
     lsa_query_weights_packed_bytes(H, dI, D) bytes)."""
-    _dev(Wq, Wg, packed)
     H, D = Wg.shape
     dI = Wq.shape[0] // H
+    _expect("lsa_pack_query_weights", "Wq", Wq, (H * dI, D))
+    need = lsa_query_weights_packed_bytes(H, dI, D)
+    if need == 0 or _nbytes(packed) < need:
+        raise ValueError(f"lsa_pack_query_weights: packed must hold {need} bytes, has "
+                         f"{_nbytes(packed)}")
+    _dtype("lsa_pack_query_weights", "Wq", Wq, "bfloat16", "int16", "uint16")
+    _dtype("lsa_pack_query_weights", "Wg", Wg, "bfloat16", "int16", "uint16")
+    _dev(Wq, Wg, packed)
     check(load().lsa_pack_query_weights(H, dI, D, _p(Wq), _p(Wg), _p(packed), _stream(stream)))
 
 
 def lsa_project_query_packed(h, packed, q, g, *, h_layer_stride: int = 0, stream=None):
     """lsa_project_query with a list of L packed weight buffers."""
-    _dev(h, q, g, *packed)
     L, B, H, dI = q.shape
     D = h.shape[-1]
-    _check_project("lsa_project_query_packed", h, g, L, B, H, D, h_layer_stride)
+    _check_project("lsa_project_query_packed", h, q, g, L, B, H, D, h_layer_stride)
     need = lsa_query_weights_packed_bytes(H, dI, D)
     if len(packed) != L or any(p.numel() * p.element_size() < need for p in packed):
         raise ValueError(f"lsa_project_query_packed: one packed buffer of {need} bytes per layer")
+    _dev(h, q, g, *packed)
     wp, _k = ptr_array([_p(w) for w in packed])
     check(load().lsa_project_query_packed(L, B, D, H, dI, _p(h), int(h_layer_stride), wp, _p(q),
                                           _p(g), _stream(stream)))
@@ -132,12 +155,12 @@ def lsa_project_query_packed(h, packed, q, g, *, h_layer_stride: int = 0, stream
 def lsa_score(keys, key_scale, q, g, bias, sel_mask, cand_idx, cand_z, cand_count, z=None,
               I=None, *, stream=None):
     """keys: list of L tensors [B][N][dI] (bf16 bits, or e4m3 codes with
-    key_scale a list of L fp32 [B][N]); bias: L host floats.  Outputs:
+    key_scale a list of L fp32 [B][N]); bias: a GPU float32 tensor [L] (or L
+    host floats, copied to the GPU by this call).  Outputs:
     sel_mask int32 [L][B][ceil(N/32)]; chunk candidate lists cand_idx int32 /
     cand_z f32 [B][nchunks][LSA_CAND_CHUNK], cand_count int32 [B][nchunks];
     optional per-layer z and I, f32 [L][B][N]."""
     fp8 = key_scale is not None
-    _dev(q, g, sel_mask, cand_idx, cand_z, cand_count, z, I, *keys, *(key_scale or []))
     L, B, H, dI = q.shape
     N = keys[0].shape[1]
     if N > 0:
@@ -158,22 +181,47 @@ def lsa_score(keys, key_scale, q, g, bias, sel_mask, cand_idx, cand_z, cand_coun
         _expect(fn, "cand_count", cand_count, (B, nch))
         _expect(fn, "z", z, (L, B, N))
         _expect(fn, "I", I, (L, B, N))
+        _dtype(fn, "q", q, "bfloat16", "int16", "uint16")
+        for name, t in (("g", g), ("cand_z", cand_z), ("z", z), ("I", I)):
+            _dtype(fn, name, t, "float32")
+        for name, t in (("sel_mask", sel_mask), ("cand_idx", cand_idx),
+                        ("cand_count", cand_count)):
+            _dtype(fn, name, t, "int32", "uint32")
+        for l in range(L if fp8 else 0):
+            _dtype(fn, f"key_scale[{l}]", key_scale[l], "float32")
+    _dev(q, g, sel_mask, cand_idx, cand_z, cand_count, z, I, *keys, *(key_scale or []))
+    bias = _bias_tensor("lsa_score", bias, L, q.device)
     kp, _k1 = ptr_array([_p(k) for k in keys])
     if fp8:
         sp, _k2 = ptr_array([_p(s) for s in key_scale])
     else:
         sp = None
-    b = (C.c_float * L)(*[float(x) for x in bias])
     check(load().lsa_score(L, B, N, H, dI, LSA_KEY_FP8_E4M3 if fp8 else LSA_KEY_BF16, kp, sp,
-                           _p(q), _p(g), b, _p(sel_mask), _p(cand_idx), _p(cand_z),
+                           _p(q), _p(g), _p(bias), _p(sel_mask), _p(cand_idx), _p(cand_z),
                            _p(cand_count), _p(z), _p(I), _stream(stream)))
+
+
+def _bias_tensor(fn, bias, L, device):
+    """The per-layer bias as the device fp32 [L] array the library reads.  A
+    GPU tensor is passed as it is (a captured graph then reads its current
+    values on every replay); a host sequence is copied to a new device tensor
+    (an allocation and a copy: not for use under graph capture)."""
+    import torch
+    if isinstance(bias, torch.Tensor) and bias.is_cuda:
+        if bias.dtype != torch.float32 or not bias.is_contiguous() or bias.numel() < L:
+            raise ValueError(f"{fn}: bias must be a contiguous float32 tensor of at least L={L} "
+                             "values")
+        return bias
+    vals = [float(x) for x in (bias.tolist() if hasattr(bias, "tolist") else bias)]
+    if len(vals) < L:
+        raise ValueError(f"{fn}: {len(vals)} bias values for L={L} layers")
+    return torch.tensor(vals[:L], dtype=torch.float32, device=device)
 
 
 def lsa_select_or_compact(cand_idx, cand_z, cand_count, N, surv_idx, surv_z, surv_count, *,
                           stream=None):
     """Chunk candidate lists of lsa_score (N entries per request) ->
     surv_idx i32 [B][cap], surv_z f32 [B][cap], surv_count i32 [B]."""
-    _dev(cand_idx, cand_z, cand_count, surv_idx, surv_z, surv_count)
     B, cap = surv_idx.shape
     nch = (int(N) + LSA_CAND_CHUNK - 1) // LSA_CAND_CHUNK
     fn = "lsa_select_or_compact"
@@ -182,9 +230,43 @@ def lsa_select_or_compact(cand_idx, cand_z, cand_count, N, surv_idx, surv_z, sur
     _expect(fn, "cand_count", cand_count, (B, nch))
     _expect(fn, "surv_z", surv_z, (B, cap))
     _expect(fn, "surv_count", surv_count, (B,))
+    for name, t in (("cand_idx", cand_idx), ("cand_count", cand_count), ("surv_idx", surv_idx),
+                    ("surv_count", surv_count)):
+        _dtype(fn, name, t, "int32")
+    _dtype(fn, "cand_z", cand_z, "float32")
+    _dtype(fn, "surv_z", surv_z, "float32")
+    _dev(cand_idx, cand_z, cand_count, surv_idx, surv_z, surv_count)
     check(load().lsa_select_or_compact(B, int(N), _p(cand_idx), _p(cand_z), _p(cand_count), cap,
                                        _p(surv_idx), _p(surv_z), _p(surv_count),
                                        _stream(stream)))
+
+
+def lsa_select_or_compact_masks_workspace_bytes(B: int, N: int) -> int:
+    return int(load().lsa_select_or_compact_masks_workspace_bytes(B, N))
+
+
+def lsa_select_or_compact_masks(sel_mask, z, surv_idx, surv_z, surv_count, ws=None, *,
+                                stream=None):
+    """Dense per-layer selections sel_mask int32/uint32 [L][B][ceil(N/32)] and
+    logits z f32 [L][B][N] -> surv_idx i32 [B][cap], surv_z f32 [B][cap],
+    surv_count i32 [B]; ws: uint8 tensor of
+    lsa_select_or_compact_masks_workspace_bytes(B, N) bytes."""
+    fn = "lsa_select_or_compact_masks"
+    L, B, N = z.shape
+    cap = surv_idx.shape[1] if surv_idx.dim() == 2 else -1
+    _expect(fn, "sel_mask", sel_mask, (L, B, (N + 31) // 32))
+    _expect(fn, "surv_idx", surv_idx, (B, cap))
+    _expect(fn, "surv_z", surv_z, (B, cap))
+    _expect(fn, "surv_count", surv_count, (B,))
+    _dtype(fn, "z", z, "float32")
+    _dtype(fn, "surv_z", surv_z, "float32")
+    _dtype(fn, "sel_mask", sel_mask, "int32", "uint32")
+    _dtype(fn, "surv_idx", surv_idx, "int32")
+    _dtype(fn, "surv_count", surv_count, "int32")
+    _dev(sel_mask, z, surv_idx, surv_z, surv_count, ws)
+    check(load().lsa_select_or_compact_masks(L, B, N, _p(sel_mask), _p(z), cap, _p(surv_idx),
+                                             _p(surv_z), _p(surv_count), _p(ws), _nbytes(ws),
+                                             _stream(stream)))
 
 
 def lsa_topk_workspace_bytes(B: int, cap: int, k: int) -> int:
@@ -192,13 +274,17 @@ def lsa_topk_workspace_bytes(B: int, cap: int, k: int) -> int:
 
 
 def lsa_topk(surv_idx, surv_z, surv_count, topk_idx, topk_count, ws=None, *, stream=None):
-    _dev(surv_idx, surv_z, surv_count, topk_idx, topk_count, ws)
     B, cap = surv_idx.shape
     k = topk_idx.shape[1]
     _expect("lsa_topk", "surv_z", surv_z, (B, cap))
     _expect("lsa_topk", "surv_count", surv_count, (B,))
     _expect("lsa_topk", "topk_idx", topk_idx, (B, k))
     _expect("lsa_topk", "topk_count", topk_count, (B,))
+    for name, t in (("surv_idx", surv_idx), ("surv_count", surv_count), ("topk_idx", topk_idx),
+                    ("topk_count", topk_count)):
+        _dtype("lsa_topk", name, t, "int32")
+    _dtype("lsa_topk", "surv_z", surv_z, "float32")
+    _dev(surv_idx, surv_z, surv_count, topk_idx, topk_count, ws)
     check(load().lsa_topk(B, cap, k, _p(surv_idx), _p(surv_z), _p(surv_count), _p(topk_idx),
                           _p(topk_count), _p(ws),
                           0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
@@ -206,11 +292,15 @@ def lsa_topk(surv_idx, surv_z, surv_count, topk_idx, topk_count, ws=None, *, str
 
 def lsa_gather_hot(pool, idx, hot, *, stream=None):
     """pool [B][N][row] (any dtype), idx i32 [B][k], hot out [B][k][row]."""
-    _dev(pool, idx, hot)
     B, N = pool.shape[0], pool.shape[1]
     k = idx.shape[1]
     row_bytes = _row_bytes(hot)
     _same_rows("lsa_gather_hot", (pool, hot), row_bytes, B, (idx,))
+    _expect("lsa_gather_hot", "idx", idx, (B, k))
+    if hot.shape[1] != k:
+        raise ValueError(f"lsa_gather_hot: hot holds {hot.shape[1]} rows per request, idx {k}")
+    _dtype("lsa_gather_hot", "idx", idx, "int32")
+    _dev(pool, idx, hot)
     check(load().lsa_gather_hot(B, N, k, row_bytes, _p(pool), _p(idx), _p(hot), _stream(stream)))
 
 
@@ -220,8 +310,12 @@ def lsa_fetch_workspace_bytes(B: int, N: int, cap: int) -> int:
 
 def lsa_resident_reset(slot_of, entry_of, *, stream=None):
     """slot_of int32 [B][N], entry_of int32 [B][S] -> all -1 (nothing resident)."""
-    _dev(slot_of, entry_of)
     B, N = slot_of.shape
+    if entry_of.dim() != 2 or entry_of.shape[0] != B:
+        raise ValueError(f"lsa_resident_reset: entry_of must be [B={B}][S]")
+    _dtype("lsa_resident_reset", "slot_of", slot_of, "int32")
+    _dtype("lsa_resident_reset", "entry_of", entry_of, "int32")
+    _dev(slot_of, entry_of)
     check(load().lsa_resident_reset(B, N, entry_of.shape[1], _p(slot_of), _p(entry_of),
                                     _stream(stream)))
 
@@ -236,7 +330,6 @@ def lsa_fetch_survivors(cold_pool, surv_idx, surv_count, slot_of, entry_of, rows
         raise ValueError("the cold pool must be pinned host memory or a GPU tensor")
     if not cold_pool.is_contiguous():
         raise ValueError("LSA tensors must be contiguous")
-    _dev(surv_idx, surv_count, slot_of, entry_of, rows, fetch_count, ws)
     B, N = cold_pool.shape[0], cold_pool.shape[1]
     S = entry_of.shape[1]
     cap = surv_idx.shape[1]
@@ -246,6 +339,10 @@ def lsa_fetch_survivors(cold_pool, surv_idx, surv_count, slot_of, entry_of, rows
     if slot_of.shape[1] != N or rows.shape[1] != S:
         raise ValueError("lsa_fetch_survivors: slot_of must be [B][N] and rows [B][S][row] "
                          "with S = entry_of.shape[1]")
+    for name, t in (("surv_idx", surv_idx), ("surv_count", surv_count), ("slot_of", slot_of),
+                    ("entry_of", entry_of), ("fetch_count", fetch_count)):
+        _dtype("lsa_fetch_survivors", name, t, "int32")
+    _dev(surv_idx, surv_count, slot_of, entry_of, rows, fetch_count, ws)
     check(load().lsa_fetch_survivors(B, N, S, row_bytes, _p(cold_pool), cap, _p(surv_idx),
                                      _p(surv_count), _p(slot_of), _p(entry_of), _p(rows),
                                      _p(fetch_count), _p(ws),
@@ -255,12 +352,16 @@ def lsa_fetch_survivors(cold_pool, surv_idx, surv_count, slot_of, entry_of, rows
 
 def lsa_gather_resident(rows, slot_of, idx, hot, *, stream=None):
     """rows [B][S][row], slot_of i32 [B][N], idx i32 [B][k] -> hot [B][k][row]."""
-    _dev(rows, slot_of, idx, hot)
     B, S = rows.shape[0], rows.shape[1]
     N = slot_of.shape[1]
     k = idx.shape[1]
     row_bytes = _row_bytes(hot)
     _same_rows("lsa_gather_resident", (rows, hot), row_bytes, B, (slot_of, idx))
+    if hot.shape[1] != k:
+        raise ValueError(f"lsa_gather_resident: hot holds {hot.shape[1]} rows per request, idx {k}")
+    _dtype("lsa_gather_resident", "slot_of", slot_of, "int32")
+    _dtype("lsa_gather_resident", "idx", idx, "int32")
+    _dev(rows, slot_of, idx, hot)
     check(load().lsa_gather_resident(B, N, S, k, row_bytes, _p(rows), _p(slot_of), _p(idx),
                                      _p(hot), _stream(stream)))
 
@@ -272,11 +373,15 @@ def lsa_label_vote_workspace_bytes(Q: int, L: int, N: int) -> int:
 def lsa_label_vote(logits, top_p, theta, count, label, layer_mask=None, ws=None, *, stream=None):
     """logits f32 [Q][L][N] -> count u8 [Q][N], label u8 [Q][N], optional
     layer_mask [Q][L][ceil(N/32)]."""
-    _dev(logits, count, label, layer_mask, ws)
     Q, L, N = logits.shape
     _expect("lsa_label_vote", "count", count, (Q, N))
     _expect("lsa_label_vote", "label", label, (Q, N))
     _expect("lsa_label_vote", "layer_mask", layer_mask, (Q, L, (N + 31) // 32))
+    _dtype("lsa_label_vote", "logits", logits, "float32")
+    _dtype("lsa_label_vote", "count", count, "uint8")
+    _dtype("lsa_label_vote", "label", label, "uint8")
+    _dtype("lsa_label_vote", "layer_mask", layer_mask, "int32", "uint32")
+    _dev(logits, count, label, layer_mask, ws)
     check(load().lsa_label_vote(Q, L, N, float(top_p), int(theta), _p(logits), _p(layer_mask),
                                 _p(count), _p(label), _p(ws),
                                 0 if ws is None else ws.numel() * ws.element_size(),
@@ -289,7 +394,6 @@ def lsa_focal_bce_grad_workspace_bytes(Q: int, N: int, D: int, H: int, dI: int) 
 
 def lsa_focal_bce_grad(h, Wq, Wg, bias, K, label, gamma, loss, dWq, ws=None, *, H: int,
                        dI: int, stream=None):
-    _dev(h, Wq, Wg, K, label, loss, dWq, ws)
     Q, D = h.shape
     N = K.shape[0]
     fn = "lsa_focal_bce_grad"
@@ -300,6 +404,12 @@ def lsa_focal_bce_grad(h, Wq, Wg, bias, K, label, gamma, loss, dWq, ws=None, *, 
     _expect(fn, "dWq", dWq, (H * dI, D))
     if loss.numel() < 1:
         raise ValueError(f"{fn}: loss needs one element")
+    _dtype(fn, "h", h, "bfloat16", "int16", "uint16")
+    _dtype(fn, "K", K, "bfloat16", "int16", "uint16")
+    for name, t in (("Wq", Wq), ("Wg", Wg), ("loss", loss), ("dWq", dWq)):
+        _dtype(fn, name, t, "float32")
+    _dtype(fn, "label", label, "uint8")
+    _dev(h, Wq, Wg, K, label, loss, dWq, ws)
     check(load().lsa_focal_bce_grad(Q, N, D, H, dI, float(gamma), _p(h), _p(Wq), _p(Wg),
                                     float(bias), _p(K), _p(label), _p(loss), _p(dWq), _p(ws),
                                     0 if ws is None else ws.numel() * ws.element_size(),

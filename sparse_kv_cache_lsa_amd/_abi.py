@@ -31,8 +31,10 @@ SIGNATURES = {
     "lsa_query_weights_packed_bytes": (SZ, [I32, I32, I32]),
     "lsa_pack_query_weights": (I32, [I32, I32, I32, P, P, P, P]),
     "lsa_project_query_packed": (I32, [I32, I32, I32, I32, I32, P, I64, PP, P, P, P]),
-    "lsa_score": (I32, [I32, I32, I32, I32, I32, I32, PP, PP, P, P, PF, P, P, P, P, P, P, P]),
+    "lsa_score": (I32, [I32, I32, I32, I32, I32, I32, PP, PP, P, P, P, P, P, P, P, P, P, P]),
     "lsa_select_or_compact": (I32, [I32, I32, P, P, P, I32, P, P, P, P]),
+    "lsa_select_or_compact_masks_workspace_bytes": (SZ, [I32, I32]),
+    "lsa_select_or_compact_masks": (I32, [I32, I32, I32, P, P, I32, P, P, P, P, SZ, P]),
     "lsa_topk_workspace_bytes": (SZ, [I32, I32, I32]),
     "lsa_topk": (I32, [I32, I32, I32, P, P, P, P, P, P, SZ, P]),
     "lsa_gather_hot": (I32, [I32, I32, I32, I32, P, P, P, P]),
@@ -56,13 +58,44 @@ class LSAError(RuntimeError):
         self.status = status
 
 
+def mapped_runtimes(names=("libamdhip64", "libhsa-runtime64", "libgomp")):
+    """Files of the HIP, HSA and OpenMP runtimes mapped into this process,
+    by runtime name (read from /proc/self/maps)."""
+    found = {n: set() for n in names}
+    try:
+        with open("/proc/self/maps") as f:
+            for ln in f:
+                parts = ln.split()
+                if len(parts) < 6:
+                    continue
+                base = os.path.basename(parts[-1])
+                for n in names:
+                    if base.startswith(n + "."):
+                        found[n].add(os.path.realpath(parts[-1]))
+    except OSError:
+        pass
+    return found
+
+
 def load():
     global _lib
     if _lib is not None:
         return _lib
     if not os.path.exists(LIB_PATH):
         raise RuntimeError(f"{LIB_PATH} is not built; run `python -m sparse_kv_cache_lsa_amd.build`")
+    # torch ships its own HIP and HSA runtimes (sonames libamdhip64.so.7 and
+    # libhsa-runtime64.so.1, the ones liblsa.so needs).  Loading torch first
+    # lets the dynamic loader bind liblsa.so to those already-loaded copies;
+    # loading liblsa.so first would map the system runtimes as well, and two
+    # HIP runtimes in one process do not share streams, devices or code
+    # objects.  So torch is imported here, and the process is checked for
+    # exactly one HIP runtime.
+    import torch  # noqa: F401
     lib = C.CDLL(LIB_PATH)
+    hip = mapped_runtimes(("libamdhip64",))["libamdhip64"]
+    if len(hip) > 1:
+        raise RuntimeError("two HIP runtimes are mapped in this process (" + ", ".join(sorted(hip)) +
+                           "): load liblsa.so only through this module, after torch")
     for name, (res, args) in SIGNATURES.items():
         fn = getattr(lib, name)
         fn.restype = res

@@ -16,7 +16,7 @@ OBJ = os.path.join(ROOT, "_build", "obj")
 LIB = os.path.join(PKG, "liblsa.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["lsa_api.cpp", "lsa_score.hip", "lsa_select.hip", "lsa_topk.hip",
+SOURCES = ["lsa_api.cpp", "lsa_score.hip", "lsa_select.hip", "lsa_select_masks.hip", "lsa_topk.hip",
            "lsa_gather.hip", "lsa_fetch.hip", "lsa_project.hip", "lsa_labels.hip", "lsa_focal.hip"]
 
 # Packed fp32 VALU ops are switched off for every HIP translation unit.  MFMA

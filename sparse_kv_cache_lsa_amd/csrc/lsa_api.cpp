@@ -158,7 +158,8 @@ lsa_status lsa_score(int L, int B, int N, int H, int dI, lsa_key_dtype kdt,
   REQUIRE((int64_t)N * dI * (kdt == LSA_KEY_BF16 ? 2 : 1) < ((int64_t)1 << 31), LSA_E_SHAPE,
           "lsa_score: keys of one (layer, request) must stay below 2^31 bytes (N=%d, dI=%d)", N,
           dI);
-  REQUIRE(bias, LSA_E_ARG, "lsa_score: null bias array");
+  REQUIRE(bias && ((uintptr_t)bias & 3u) == 0, LSA_E_ARG,
+          "lsa_score: bias must be a 4-byte aligned device array of L floats");
   if (N == 0) return LSA_OK;   // nothing to score; outputs are empty
   REQUIRE(keys && q && g && sel_mask && cand_idx && cand_z && cand_count, LSA_E_ARG,
           "lsa_score: null pointer argument");
@@ -173,8 +174,8 @@ lsa_status lsa_score(int L, int B, int N, int H, int dI, lsa_key_dtype kdt,
       REQUIRE(key_scale[l], LSA_E_ARG, "lsa_score: null key_scale pointer for layer %d", l);
       a.scale[l] = key_scale[l];
     }
-    a.bias[l] = bias[l];
   }
+  a.bias = bias;
   a.q = q;
   a.g = g;
   a.mask = sel_mask;
@@ -209,6 +210,36 @@ lsa_status lsa_select_or_compact(int B, int N, const int32_t* cand_idx, const fl
   return hip_status(lsa::launch_select(B, nchunks, cand_idx, cand_z, cand_count, cap, surv_idx,
                                        surv_z, surv_count, stream),
                     "lsa_select_or_compact launch");
+}
+
+size_t lsa_select_or_compact_masks_workspace_bytes(int B, int N) {
+  if (B < 1 || N < 0) return 0;
+  return lsa::select_masks_workspace_bytes(B, N);
+}
+
+lsa_status lsa_select_or_compact_masks(int L, int B, int N, const uint32_t* sel_mask,
+                                       const float* z, int cap, int32_t* surv_idx, float* surv_z,
+                                       int32_t* surv_count, void* ws, size_t ws_bytes,
+                                       hipStream_t stream) {
+  const char* fn = "lsa_select_or_compact_masks";
+  REQUIRE(L >= 1 && L <= LSA_MAX_LAYERS, LSA_E_SHAPE, "%s: L=%d not in [1,%d]", fn, L,
+          LSA_MAX_LAYERS);
+  REQUIRE(B >= 1 && B <= 65535, LSA_E_SHAPE, "%s: B=%d not in [1,65535]", fn, B);
+  REQUIRE(N >= 0 && N <= (1 << 24), LSA_E_SHAPE, "%s: N=%d not in [0,2^24]", fn, N);
+  REQUIRE(cap >= 0, LSA_E_ARG, "%s: cap=%d < 0", fn, cap);
+  REQUIRE(surv_count, LSA_E_ARG, "%s: null surv_count", fn);
+  REQUIRE(N == 0 || (sel_mask && z), LSA_E_ARG, "%s: null mask or logits", fn);
+  REQUIRE(((uintptr_t)sel_mask & 3u) == 0 && ((uintptr_t)z & 3u) == 0, LSA_E_ARG,
+          "%s: mask and logits must be 4-byte aligned", fn);
+  REQUIRE(cap == 0 || (surv_idx && surv_z), LSA_E_ARG, "%s: null survivor output with cap > 0",
+          fn);
+  const size_t need = lsa::select_masks_workspace_bytes(B, N);
+  REQUIRE(need == 0 || (ws && ws_bytes >= need && ((uintptr_t)ws & 15) == 0), LSA_E_WORKSPACE,
+          "%s: workspace of %zu bytes (16-byte aligned) needed, got %zu", fn, need,
+          ws ? ws_bytes : (size_t)0);
+  return hip_status(lsa::launch_select_masks(L, B, N, sel_mask, z, cap, surv_idx, surv_z,
+                                             surv_count, ws, stream),
+                    "lsa_select_or_compact_masks launch");
 }
 
 // --------------------------------------------------------------------- top-k

@@ -12,7 +12,7 @@ namespace lsa {
 struct ScoreArgs {
   const void* keys[LSA_MAX_LAYERS];
   const float* scale[LSA_MAX_LAYERS];
-  float bias[LSA_MAX_LAYERS];
+  const float* bias;       // device fp32 [L]
   const uint16_t* q;
   const float* g;
   uint32_t* mask;          // [L][B][W]
@@ -50,6 +50,12 @@ int device_cu_count();
 hipError_t launch_select(int B, int nchunks, const int32_t* cand_idx, const float* cand_z,
                          const int32_t* cand_count, int cap, int32_t* surv_idx,
                          float* surv_z, int32_t* surv_count, hipStream_t s);
+
+size_t select_masks_workspace_bytes(int B, int N);
+
+hipError_t launch_select_masks(int L, int B, int N, const uint32_t* mask, const float* z, int cap,
+                               int32_t* surv_idx, float* surv_z, int32_t* surv_count, void* ws,
+                               hipStream_t s);
 
 size_t topk_workspace_bytes(int B, int cap, int k);
 

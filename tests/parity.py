@@ -37,27 +37,74 @@ def unpack_mask(words, N):
     return bits.reshape(*w.shape[:-1], w.shape[-1] * 32)[..., :N].astype(bool)
 
 
-def check_scores(z_gpu, z_or, I_gpu=None):
-    """Returns diagnostics; raises AssertionError on a violation."""
+def bf16_boundary_distance(a):
+    """Distance of each fp64 value to the nearest bf16 rounding midpoint."""
+    a = np.asarray(a, np.float64)
+    m = np.abs(a)
+    ulp = bf16_spacing(a)
+    frac = m / ulp - np.floor(m / ulp)
+    return np.abs(frac - 0.5) * ulp
+
+
+def bf16_spacing(a):
+    """Spacing of bf16 values in the binade of |a| (an upper bound on the gap
+    between the two bf16 neighbours of a)."""
+    m = np.abs(np.asarray(a, np.float64))
+    return np.exp2(np.floor(np.log2(np.maximum(m, 1e-300))) - 7)
+
+
+def projection_flip_margin(a, S, g, k_abs, sigma=None):
+    """Bound on how far a GPU logit may move because the GPU query encoder
+    rounded a query element to the other bf16 neighbour.
+
+    The encoder sums W_q h in fp32 and rounds to bf16; the oracle sums in fp64.
+    Where the exact sum a lies within 1e-6 * S (S = sum_d |W||h|, far above the
+    fp32 error of the sum) of a rounding midpoint the two may pick different
+    neighbours, one bf16 spacing apart; elsewhere they agree bit for bit (the
+    projection tests assert both).  A flip of q[h][d] moves z_s by at most
+    g_h * spacing * |k_sd| * sigma_s, so the per-entry margin is
+      E_s = sigma_s * sum_d |k_sd| * sum_{(h,d) in band} g_h * spacing_hd.
+    a, S: fp64 [H][dI]; g [H]; k_abs: |keys| [N][dI]; sigma: [N] or None.
+    Returns (E fp64 [N], band bool [H][dI])."""
+    a = np.asarray(a, np.float64)
+    band = bf16_boundary_distance(a) <= 1e-6 * np.asarray(S, np.float64)
+    u = (band * np.asarray(g, np.float64)[:, None] * bf16_spacing(a)).sum(0)
+    if not band.any():
+        return np.zeros(k_abs.shape[0]), band
+    E = np.asarray(k_abs, np.float64) @ u
+    if sigma is not None:
+        E = E * np.asarray(sigma, np.float64)
+    return E * (1 + 1e-6), band
+
+
+def _margin(extra, like):
+    return 0.0 if extra is None else np.asarray(extra, np.float64).reshape(np.shape(like))
+
+
+def check_scores(z_gpu, z_or, I_gpu=None, extra=None):
+    """Returns diagnostics; raises AssertionError on a violation.  extra: an
+    optional per-entry margin added to the tolerance (projection_flip_margin)."""
     z_gpu = np.asarray(z_gpu, np.float64)
     z_or = np.asarray(z_or, np.float64)
+    e = _margin(extra, z_or)
     dz = np.abs(z_gpu - z_or)
     dI = np.abs(sigmoid(z_gpu) - sigmoid(z_or))
     assert np.isfinite(z_gpu).all(), "non-finite GPU score"
-    assert dz.max(initial=0) <= Z_TOL, f"max |dz| = {dz.max():.3g} > {Z_TOL}"
-    assert dI.max(initial=0) <= I_TOL, f"max |dI| = {dI.max():.3g}"
+    over = dz - e
+    assert over.max(initial=-1) <= Z_TOL, f"max |dz| - margin = {over.max():.3g} > {Z_TOL}"
+    assert (dI - e / 4).max(initial=-1) <= I_TOL, f"max |dI| = {dI.max():.3g}"
     if I_gpu is not None:
         dI2 = np.abs(np.asarray(I_gpu, np.float64) - sigmoid(z_or))
-        assert dI2.max(initial=0) <= I_TOL, f"max |I_gpu - I| = {dI2.max():.3g}"
+        assert (dI2 - e / 4).max(initial=-1) <= I_TOL, f"max |I_gpu - I| = {dI2.max():.3g}"
     return {"max_dz": float(dz.max(initial=0)), "max_dI": float(dI.max(initial=0))}
 
 
-def check_selection(sel_gpu, z_or):
-    """Per-layer threshold: exact outside the band."""
+def check_selection(sel_gpu, z_or, extra=None):
+    """Per-layer threshold: exact outside the band (widened by extra)."""
     sel_gpu = np.asarray(sel_gpu, bool)
     z_or = np.asarray(z_or, np.float64)
     want = z_or >= 0
-    band = np.abs(z_or) <= Z_BAND
+    band = np.abs(z_or) <= Z_BAND + _margin(extra, z_or)
     bad = (sel_gpu != want) & ~band
     assert not bad.any(), f"{bad.sum()} selection mismatches outside the band"
     return int(band.sum())
@@ -71,22 +118,31 @@ def flatten_candidates(cand_idx, cand_z, cand_count):
     return idx, z
 
 
-def check_merged_scores(idx_gpu, z_gpu, z_or_layers):
+def check_merged_scores(idx_gpu, z_gpu, z_or_layers, extra=None):
     """Merged logit of each listed entry: the max over the layers selecting
     it, compared where every layer's selection is outside the band."""
     z = np.asarray(z_or_layers, np.float64)
+    e = np.zeros_like(z) + _margin(extra, z)
     idx = np.asarray(idx_gpu, np.int64)
     zg = np.asarray(z_gpu, np.float64)
     sel = z >= 0
     want = np.where(sel, z, -np.inf).max(axis=0)[idx]
-    certain = (np.abs(z) > Z_BAND).all(axis=0)[idx]
+    certain = (np.abs(z) > Z_BAND + e).all(axis=0)[idx]
+    tol = Z_TOL + e.max(axis=0)[idx]
     assert np.isfinite(zg).all(), "non-finite merged logit in a survivor list"
     d = np.abs(zg[certain] - want[certain])
-    assert d.max(initial=0) <= Z_TOL, f"merged logit max |dz| = {d.max():.3g}"
+    assert (d - tol[certain]).max(initial=-1) <= 0, f"merged logit max |dz| = {d.max():.3g}"
     return float(d.max(initial=0))
 
 
-def check_survivors(idx_gpu, count_gpu, z_or_layers, cap=None):
+def uncertain_survivors(z_or_layers, extra=None):
+    """Entries whose survivor status lies inside the threshold band."""
+    z = np.asarray(z_or_layers, np.float64)
+    band = Z_BAND + _margin(extra, z)
+    return ~(z >= band).any(axis=0) & ~(z < -band).all(axis=0)
+
+
+def check_survivors(idx_gpu, count_gpu, z_or_layers, cap=None, extra=None):
     """z_or_layers: fp64 [L][N].  idx_gpu: the GPU survivor list (first
     min(count, cap) entries)."""
     z = np.asarray(z_or_layers, np.float64)
@@ -94,8 +150,9 @@ def check_survivors(idx_gpu, count_gpu, z_or_layers, cap=None):
     idx = np.asarray(idx_gpu, np.int64)
     assert (np.diff(idx) > 0).all(), "survivor list not strictly ascending"
     assert idx.size == 0 or (idx[0] >= 0 and idx[-1] < N)
-    certain_in = (z >= Z_BAND).any(axis=0)
-    certain_out = (z < -Z_BAND).all(axis=0)
+    band = Z_BAND + _margin(extra, z)
+    certain_in = (z >= band).any(axis=0)
+    certain_out = (z < -band).all(axis=0)
     uncertain = ~certain_in & ~certain_out
     n_cap = idx.size
     in_gpu = np.zeros(N, bool)
@@ -112,11 +169,13 @@ def check_survivors(idx_gpu, count_gpu, z_or_layers, cap=None):
     return int(uncertain.sum())
 
 
-def check_topk(topk_gpu, count_gpu, surv_idx_or, zstar_or, k, uncertain=None):
+def check_topk(topk_gpu, count_gpu, surv_idx_or, zstar_or, k, uncertain=None, extra=None):
     """topk_gpu: GPU top-k list [k] (ascending, -1 padded); surv_idx_or /
     zstar_or: oracle survivors and their fp64 merged logits; uncertain:
     optional bool [N] of entries whose survivor status is inside the
-    threshold band (their membership may differ)."""
+    threshold band (their membership may differ); extra: optional per-entry
+    margin [N] of the merged logit (the k-th band widens by the entry's margin
+    plus the largest margin among the survivors)."""
     t = np.asarray(topk_gpu, np.int64)
     surv = np.asarray(surv_idx_or, np.int64)
     n = surv.size
@@ -138,7 +197,8 @@ def check_topk(topk_gpu, count_gpu, surv_idx_or, zstar_or, k, uncertain=None):
     kk = min(k, n)
     order = np.lexsort((surv, -zs))
     kth = zs[order[kk - 1]]
-    band = (np.abs(zs - kth) <= TOPK_BAND) | unc_s
+    e = np.zeros(n) if extra is None else np.asarray(extra, np.float64)[surv]
+    band = (np.abs(zs - kth) <= TOPK_BAND + e + e.max(initial=0)) | unc_s
     want_in = set(int(surv[i]) for i in order[:kk] if not band[i])
     want_out = set(int(surv[i]) for i in order[kk:] if not band[i])
     assert want_in <= got, f"missing top-k members {sorted(want_in - got)[:5]}"

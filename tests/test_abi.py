@@ -52,6 +52,15 @@ def test_trigger_cadence(lib):
     assert lib.lsa_trigger_due(-64, 64) == 0 and lib.lsa_trigger_due(5, 0) == 0
 
 
+def test_trigger_due_matches_oracle(lib):
+    # the library's cadence against the oracle's, over negative steps, step 0
+    # and many windows, for several periods (tau <= 0: never due)
+    from oracle import oracle
+    for tau in (1, 2, 3, 16, 64, 100, 0, -1):
+        for t in range(-64, 10_000):
+            assert lib.lsa_trigger_due(t, tau) == int(oracle.trigger_due(t, tau)), (t, tau)
+
+
 def _status(lib, name, *args):
     return getattr(lib, name)(*args)
 
@@ -179,3 +188,66 @@ def test_binding_checks_row_and_batch_sizes():
         lsa._same_rows("f", (pool, ok), 1024, 2, (torch.zeros(3, 3),))
     with pytest.raises(ValueError):
         lsa._same_rows("f", (pool, torch.zeros((3, 7, 1024), dtype=torch.uint8)), 1024, 2, ())
+
+
+def test_binding_checks_sizes_and_dtypes_before_any_launch():
+    """Every size and dtype that a kernel relies on is checked by the binding
+    before the device check (so these CPU tensors are refused for their
+    shape or dtype, not for living on the host)."""
+    import torch
+    import sparse_kv_cache_lsa_amd as lsa
+    i32, f32, u8, bf = torch.int32, torch.float32, torch.uint8, torch.bfloat16
+    z = lambda *sh, dt=f32: torch.zeros(sh, dtype=dt)
+
+    def refused(call, what):
+        with pytest.raises(ValueError, match=what):
+            call()
+
+    # gathers: hot must hold k rows per request
+    refused(lambda: lsa.lsa_gather_hot(z(2, 10, 512, dt=torch.int16), z(2, 4, dt=i32),
+                                       z(2, 3, 512, dt=torch.int16)), "hot holds 3 rows")
+    refused(lambda: lsa.lsa_gather_resident(z(2, 6, 512, dt=torch.int16), z(2, 10, dt=i32),
+                                            z(2, 4, dt=i32), z(2, 2, 512, dt=torch.int16)),
+            "hot holds 2 rows")
+    refused(lambda: lsa.lsa_gather_hot(z(2, 10, 512, dt=torch.int16), z(2, 4, dt=torch.int64),
+                                       z(2, 4, 512, dt=torch.int16)), "idx has dtype")
+    # packed weights: the buffer must hold the whole packed layout
+    need = lsa.lsa_query_weights_packed_bytes(4, 64, 256)
+    refused(lambda: lsa.lsa_pack_query_weights(z(256, 256, dt=bf), z(4, 256, dt=bf),
+                                               z(need - 16, dt=u8)), f"hold {need} bytes")
+    # resident reset: both tables of the same batch
+    refused(lambda: lsa.lsa_resident_reset(z(3, 100, dt=i32), z(2, 50, dt=i32)), "entry_of")
+    # score: dtypes of the query, gates, outputs and scales
+    L, B, N, H, dI = 1, 2, 100, 4, 64
+    nch = 1
+    args = lambda q=z(L, B, H, dI, dt=bf), g=z(L, B, H), m=z(L, B, 4, dt=i32), ci=z(B, nch, 4096, dt=i32), cz=z(B, nch, 4096), cc=z(B, nch, dt=i32): (
+        [z(B, N, dI, dt=bf)], None, q, g, [0.0], m, ci, cz, cc)
+    refused(lambda: lsa.lsa_score(*args(g=z(L, B, H, dt=bf))), "g has dtype")
+    refused(lambda: lsa.lsa_score(*args(q=z(L, B, H, dI))), "q has dtype")
+    refused(lambda: lsa.lsa_score(*args(cz=z(B, nch, 4096, dt=torch.float64))), "cand_z has dtype")
+    refused(lambda: lsa.lsa_score(*args(ci=z(B, nch, 4096, dt=torch.int64))), "cand_idx has dtype")
+    refused(lambda: lsa.lsa_score([z(B, N, dI, dt=u8)], [z(B, N, dt=bf)], z(L, B, H, dI, dt=bf),
+                                  z(L, B, H), [0.0], z(L, B, 4, dt=i32), z(B, nch, 4096, dt=i32),
+                                  z(B, nch, 4096), z(B, nch, dt=i32)), "key_scale")
+    # select, top-k: index and logit dtypes
+    refused(lambda: lsa.lsa_select_or_compact(z(B, nch, 4096, dt=i32), z(B, nch, 4096),
+                                              z(B, nch, dt=i32), N, z(B, N, dt=torch.int64),
+                                              z(B, N), z(B, dt=i32)), "surv_idx has dtype")
+    refused(lambda: lsa.lsa_select_or_compact_masks(z(L, B, 4, dt=i32), z(L, B, N, dt=torch.float16),
+                                                    z(B, N, dt=i32), z(B, N), z(B, dt=i32)),
+            "z has dtype")
+    refused(lambda: lsa.lsa_select_or_compact_masks(z(L, B, 3, dt=i32), z(L, B, N),
+                                                    z(B, N, dt=i32), z(B, N), z(B, dt=i32)),
+            "sel_mask has shape")
+    refused(lambda: lsa.lsa_topk(z(B, N, dt=i32), z(B, N, dt=torch.float64), z(B, dt=i32),
+                                 z(B, 8, dt=i32), z(B, dt=i32)), "surv_z has dtype")
+    # projection: fp32 query output refused
+    refused(lambda: lsa.lsa_project_query(z(B, 256, dt=bf), [z(H * dI, 256, dt=bf)],
+                                          [z(H, 256, dt=bf)], z(L, B, H, dI), z(L, B, H)),
+            "q has dtype")
+    # labels: count/label are bytes
+    refused(lambda: lsa.lsa_label_vote(z(2, 3, 64), 0.6, 3, z(2, 64, dt=i32), z(2, 64, dt=u8)),
+            "count has dtype")
+    # a well-formed call on host tensors is refused for living on the host
+    refused(lambda: lsa.lsa_topk(z(B, N, dt=i32), z(B, N), z(B, dt=i32), z(B, 8, dt=i32),
+                                 z(B, dt=i32)), "on the GPU")

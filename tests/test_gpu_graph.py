@@ -132,3 +132,45 @@ def test_cold_fetch_graph_replays_match_eager():
             else:
                 assert torch.equal(t, want[i]), (rep, i)
         del junk
+
+
+def test_graph_reads_the_current_bias():
+    """The bias is a device array read when the kernels run: a graph captured
+    once follows new bias values written between replays (each replay equals
+    an eager trigger with the same bias)."""
+    w = gen.WORKLOADS["tiny"]
+    inp = gen.indexer_inputs(w, gen.load_calibration(w))
+    d = gen.to_device(inp, DEV)
+    pool = gen.pool_tensor(w, DEV)
+    buf = TriggerBuffers.allocate(w.L, w.B, w.N, w.H, w.dI, w.k, w.row_elems, device=DEV)
+    bias = d["bias"].clone()
+    base = float(inp.bias[0])
+    shifts = [0.0, 3.0, -2.0]
+    want = []
+    for sh in shifts:
+        bias.fill_(base + sh)
+        run_trigger(buf, d["h"], d["Wq"], d["Wg"], d["keys"], d["scale"], bias, pool)
+        torch.cuda.synchronize()
+        want.append(_snapshot(buf))
+    # a larger bias selects more entries
+    assert int(want[1]["surv_count"][0]) > int(want[0]["surv_count"][0]) > int(
+        want[2]["surv_count"][0])
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            run_trigger(buf, d["h"], d["Wq"], d["Wg"], d["keys"], d["scale"], bias, pool)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for rep in range(2):
+        for i, sh in enumerate(shifts):
+            bias.fill_(base + sh)
+            junk = torch.randn(1 << 20, device=DEV).sum()
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+            got = _snapshot(buf)
+            for key, v in want[i].items():
+                assert torch.equal(got[key], v), (rep, sh, key)
+            del junk

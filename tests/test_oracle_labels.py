@@ -91,16 +91,26 @@ def test_vote_special_cases(oracle):
     assert set(np.unique(c).tolist()) <= {0, L}                             # identical layers
 
 
-def test_single_layer_boost_never_votes_positive(oracle):
-    # an entry boosted in one layer only is not a golden label at theta=3
+def test_single_layer_noise_is_filtered(oracle):
+    # The vote exists to drop what one layer alone asks for: an entry that
+    # only layer 7 keeps (a large boost there, a very low logit in every other
+    # layer) is counted once and is not a golden label at theta = 3, while an
+    # entry that exactly theta layers keep is.
     rng = np.random.default_rng(71)
     L, N = 20, 2048
     x = rng.standard_normal((L, N)).astype(np.float32)
-    x[7, 100] += 40.0
+    x[:, 100] = -40.0
+    x[7, 100] = 40.0
+    x[:, 200] = -40.0
+    x[[2, 9, 15], 200] = 40.0
+    x[:, 300] = -40.0
+    x[[4, 11], 300] = 40.0
     sel = np.stack([oracle.nucleus(x[l], 0.6)[0] for l in range(L)])
-    assert sel[7, 100] == 1
     c, y = oracle.vote(sel, 3)
-    assert y[100] == 0 or sel[:, 100].sum() >= 3
+    assert sel[:, 100].tolist() == [int(l == 7) for l in range(L)]
+    assert c[100] == 1 and y[100] == 0
+    assert c[300] == 2 and y[300] == 0
+    assert c[200] == 3 and y[200] == 1
 
 
 # --------------------------------------------------------------------- loss

@@ -53,28 +53,56 @@ def bf16_spacing(a):
     return np.exp2(np.floor(np.log2(np.maximum(m, 1e-300))) - 7)
 
 
-def projection_flip_margin(a, S, g, k_abs, sigma=None):
-    """Bound on how far a GPU logit may move because the GPU query encoder
-    rounded a query element to the other bf16 neighbour.
+def other_bf16_neighbour(q_bits, a):
+    """The bf16 neighbour of the exact value a that its RNE rounding q_bits
+    is not (bit patterns, uint16)."""
+    q_bits = np.asarray(q_bits, np.uint16)
+    qv = (q_bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    away = np.abs(qv) > np.abs(np.asarray(a, np.float64))    # rounded away from zero
+    step = np.where(away, -1, 1).astype(np.int32)
+    return (q_bits.astype(np.int32) + step).astype(np.uint16)
 
-    The encoder sums W_q h in fp32 and rounds to bf16; the oracle sums in fp64.
-    Where the exact sum a lies within 1e-6 * S (S = sum_d |W||h|, far above the
-    fp32 error of the sum) of a rounding midpoint the two may pick different
-    neighbours, one bf16 spacing apart; elsewhere they agree bit for bit (the
-    projection tests assert both).  A flip of q[h][d] moves z_s by at most
-    g_h * spacing * |k_sd| * sigma_s, so the per-entry margin is
-      E_s = sigma_s * sum_d |k_sd| * sum_{(h,d) in band} g_h * spacing_hd.
-    a, S: fp64 [H][dI]; g [H]; k_abs: |keys| [N][dI]; sigma: [N] or None.
-    Returns (E fp64 [N], band bool [H][dI])."""
+
+def projection_flip_margin(q_or, q_gpu, a, S, g, k_abs, sigma=None):
+    """Margin for GPU logits computed from GPU queries that took some bf16
+    rounding decisions the other way.
+
+    The query encoder sums W_q h in fp32 and rounds to bf16; the oracle sums in
+    fp64.  Where the exact sum a lies within 1e-6 * S (S = sum_d |W||h|, far
+    above the fp32 error of the sum) of a rounding midpoint the two may round
+    differently.  Asserted here: every element where the GPU query differs
+    from the oracle's lies in that band, and the GPU value is the bf16
+    rounding of a value within 1e-6 * S of a (for elements near zero, whose
+    bf16 spacing is below the sum's error, that can be several spacings from
+    the oracle's).  Each such element moves the logit of entry s by
+    g_h * |q_gpu - q_or| * |k_sd| * sigma_s at most, so the margin is
+      E_s = sigma_s * sum_d |k_sd| * sum_h g_h * |q_gpu_hd - q_or_hd|.
+    q_or, q_gpu: bf16 bits [H][dI]; a, S: fp64 [H][dI]; g [H];
+    k_abs: |keys| [N][dI]; sigma: [N] or None.
+    Returns (E fp64 [N], number of differing elements)."""
+    q_or = np.asarray(q_or, np.uint16)
+    q_gpu = np.asarray(q_gpu, np.uint16)
     a = np.asarray(a, np.float64)
+    diff = q_gpu != q_or
     band = bf16_boundary_distance(a) <= 1e-6 * np.asarray(S, np.float64)
-    u = (band * np.asarray(g, np.float64)[:, None] * bf16_spacing(a)).sum(0)
-    if not band.any():
-        return np.zeros(k_abs.shape[0]), band
+    assert not (diff & ~band).any(), f"{(diff & ~band).sum()} query elements differ outside the band"
+    if not diff.any():
+        return np.zeros(np.shape(k_abs)[0]), 0
+    dec = lambda x: (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    # a differing element is a rounding of some value within the band's
+    # error of the exact sum (near zero that can be several bf16 spacings)
+    far = np.abs(dec(q_gpu) - a) > 1e-6 * np.asarray(S, np.float64) + bf16_spacing(a)
+    bad = diff & far
+    assert not bad.any(), (
+        f"{bad.sum()} differing query elements are not roundings of a value in the band, e.g. "
+        f"a={a[bad][0]!r} gpu={dec(q_gpu)[bad][0]!r} oracle={dec(q_or)[bad][0]!r} "
+        f"S={np.asarray(S)[bad][0]!r}")
+    dq = np.abs(dec(q_gpu) - dec(q_or)) * diff
+    u = (np.asarray(g, np.float64)[:, None] * dq).sum(0)
     E = np.asarray(k_abs, np.float64) @ u
     if sigma is not None:
         E = E * np.asarray(sigma, np.float64)
-    return E * (1 + 1e-6), band
+    return E * (1 + 1e-6), int(diff.sum())
 
 
 def _margin(extra, like):

@@ -8,14 +8,6 @@ import lsa_inputs as gen
 import parity
 
 
-def _other_neighbour(q_bits, a):
-    """The bf16 neighbour of a that q_bits (its RNE rounding) is not."""
-    qv = gen.bf16_bits_to_f32(q_bits).astype(np.float64)
-    away = np.abs(qv) > np.abs(a)                # rounded away from zero
-    step = np.where(away, -1, 1).astype(np.int32)
-    return (q_bits.astype(np.int32) + step).astype(np.uint16)
-
-
 @pytest.mark.parametrize("name", ["tiny", "ctx128k"])
 def test_flip_margin_bounds_every_rounding_flip(oracle, name):
     w = gen.WORKLOADS[name]
@@ -25,22 +17,41 @@ def test_flip_margin_bounds_every_rounding_flip(oracle, name):
         kabs = np.abs(gen.bf16_bits_to_f32(inp.keys[l][0]))
         sig = None if inp.scale[l] is None else inp.scale[l][0]
         z = oracle.score(inp.keys[l][0], sig, q, g, float(inp.bias[l]))
-        # an S this large puts every element in the band: flip them all
-        E, band = parity.projection_flip_margin(a, np.full(a.shape, 1e12), g, kabs, sig)
-        assert band.all()
-        q2 = _other_neighbour(q, a)
-        z2 = oracle.score(inp.keys[l][0], sig, q2, g, float(inp.bias[l]))
-        assert (np.abs(z2 - z) <= E).all()
-        # and half of them: the bound still holds (it is a sum over the band)
+        other = parity.other_bf16_neighbour(q, a)
+        huge = np.full(a.shape, 1e12)       # puts every element in the band
         rng = np.random.default_rng(l)
-        pick = rng.random(q.shape) < 0.5
-        z3 = oracle.score(inp.keys[l][0], sig, np.where(pick, q2, q), g, float(inp.bias[l]))
-        assert (np.abs(z3 - z) <= E).all()
-        # the real band (1e-6 sum |W||h|) holds a small fraction of the elements
-        S = np.abs(gen.bf16_bits_to_f32(inp.Wq[l])).astype(np.float64) @ np.abs(
-            gen.bf16_bits_to_f32(inp.h[0])).astype(np.float64)
-        _, band_real = parity.projection_flip_margin(a, S.reshape(a.shape), g, kabs, sig)
-        assert band_real.mean() < 0.1
+        for frac in (1.0, 0.5, 0.01):
+            pick = rng.random(q.shape) < frac
+            q2 = np.where(pick, other, q)
+            E, n = parity.projection_flip_margin(q, q2, a, huge, g, kabs, sig)
+            assert n == pick.sum()
+            z2 = oracle.score(inp.keys[l][0], sig, q2, g, float(inp.bias[l]))
+            assert (np.abs(z2 - z) <= E).all()
+        # no difference: no margin
+        E, n = parity.projection_flip_margin(q, q, a, huge, g, kabs, sig)
+        assert n == 0 and not E.any()
+
+
+def test_flip_margin_refuses_differences_outside_the_band(oracle):
+    w = gen.WORKLOADS["tiny"]
+    inp = gen.indexer_inputs(w, gen.load_calibration(w))
+    q, g, a = oracle.project(inp.h[0], inp.Wq[0], inp.Wg[0], w.H, w.dI, want_a=True)
+    kabs = np.abs(gen.bf16_bits_to_f32(inp.keys[0][0]))
+    S = (np.abs(gen.bf16_bits_to_f32(inp.Wq[0])).astype(np.float64) @ np.abs(
+        gen.bf16_bits_to_f32(inp.h[0])).astype(np.float64)).reshape(a.shape)
+    d = parity.bf16_boundary_distance(a)
+    far = np.unravel_index(np.argmax(d / S), a.shape)      # farthest from a midpoint
+    q2 = q.copy()
+    q2[far] = parity.other_bf16_neighbour(q, a)[far]
+    with pytest.raises(AssertionError, match="outside the band"):
+        parity.projection_flip_margin(q, q2, a, S, g, kabs)
+    # an element inside the band whose GPU value is far from any rounding of
+    # a value within the band's error
+    near = np.unravel_index(np.argmin(d / S), a.shape)
+    q3 = q.copy()
+    q3[near] ^= 0x0100
+    with pytest.raises(AssertionError, match="not roundings"):
+        parity.projection_flip_margin(q, q3, a, S, g, kabs)
 
 
 def test_boundary_distance_closed_form():

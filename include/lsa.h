@@ -252,6 +252,28 @@ lsa_status lsa_topk(int B, int cap, int k, const int32_t* surv_idx,
                     size_t ws_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * lsa_topk without a caller workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, hosts
+ * that forbid allocation).  Arguments, results and limits are those of
+ * lsa_topk; the candidate lists of long survivor lists go to a scratch array
+ * of LSA_TOPK_NOALLOC_MAX_BYTES that the library holds on each GPU it runs
+ * on, for the life of the process.  The call allocates nothing and
+ * synchronises nothing.
+ *  - Sizes whose lsa_topk_workspace_bytes(B, cap, k) exceeds
+ *    LSA_TOPK_NOALLOC_MAX_BYTES return LSA_E_SHAPE (use lsa_topk).
+ *  - Every call on one GPU shares that GPU's array: calls that overlap on one
+ *    GPU (different streams, or host threads) race and give wrong results.
+ *    Calls ordered on one stream are safe.
+ *  - The first call on a device resolves the array's device address
+ *    (hipGetSymbolAddress, not a stream operation); make that first call
+ *    outside graph capture.  A failure returns LSA_E_HIP.
+ */
+#define LSA_TOPK_NOALLOC_MAX_BYTES (16 << 20)
+lsa_status lsa_topk_noalloc(int B, int cap, int k, const int32_t* surv_idx,
+                            const float* surv_z, const int32_t* surv_count,
+                            int32_t* topk_idx, int32_t* topk_count, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * Hot-pool gather ([SUMMARY] 2.1 dynamic-fetch bullet: the selected
  * compressed KV entries are brought into GPU memory).
  *   hot[b][j] = pool[b][idx[b][j]]  (row_bytes bytes), zero row when

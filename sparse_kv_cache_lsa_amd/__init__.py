@@ -10,15 +10,15 @@ from __future__ import annotations
 
 import ctypes as C
 
-from ._abi import (LSA_CAND_CHUNK, LSA_KEY_BF16, LSA_KEY_FP8_E4M3, LSAError, check, load,
-                   ptr_array)
+from ._abi import (LSA_CAND_CHUNK, LSA_KEY_BF16, LSA_KEY_FP8_E4M3, LSA_TOPK_NOALLOC_MAX_BYTES,
+                   LSAError, check, load, ptr_array)
 
 __all__ = [
     "LSAError", "LSA_KEY_BF16", "LSA_KEY_FP8_E4M3", "LSA_CAND_CHUNK", "load", "lsa_version",
     "lsa_trigger_due", "lsa_project_query", "lsa_query_weights_packed_bytes",
     "lsa_pack_query_weights", "lsa_project_query_packed", "lsa_score", "lsa_select_or_compact",
     "lsa_select_or_compact_masks_workspace_bytes", "lsa_select_or_compact_masks",
-    "lsa_topk_workspace_bytes", "lsa_topk", "lsa_gather_hot", "lsa_fetch_workspace_bytes",
+    "lsa_topk_workspace_bytes", "lsa_topk", "lsa_topk_noalloc", "lsa_gather_hot", "lsa_fetch_workspace_bytes",
     "lsa_resident_reset", "lsa_fetch_survivors", "lsa_gather_resident",
     "lsa_label_vote_workspace_bytes", "lsa_label_vote",
     "lsa_focal_bce_grad_workspace_bytes", "lsa_focal_bce_grad",
@@ -288,6 +288,24 @@ def lsa_topk(surv_idx, surv_z, surv_count, topk_idx, topk_count, ws=None, *, str
     check(load().lsa_topk(B, cap, k, _p(surv_idx), _p(surv_z), _p(surv_count), _p(topk_idx),
                           _p(topk_count), _p(ws),
                           0 if ws is None else ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def lsa_topk_noalloc(surv_idx, surv_z, surv_count, topk_idx, topk_count, *, stream=None):
+    """lsa_topk with the library's own scratch instead of a workspace (for
+    callers that cannot allocate; calls that overlap on one GPU race)."""
+    B, cap = surv_idx.shape
+    k = topk_idx.shape[1]
+    _expect("lsa_topk_noalloc", "surv_z", surv_z, (B, cap))
+    _expect("lsa_topk_noalloc", "surv_count", surv_count, (B,))
+    _expect("lsa_topk_noalloc", "topk_idx", topk_idx, (B, k))
+    _expect("lsa_topk_noalloc", "topk_count", topk_count, (B,))
+    for name, t in (("surv_idx", surv_idx), ("surv_count", surv_count), ("topk_idx", topk_idx),
+                    ("topk_count", topk_count)):
+        _dtype("lsa_topk_noalloc", name, t, "int32")
+    _dtype("lsa_topk_noalloc", "surv_z", surv_z, "float32")
+    _dev(surv_idx, surv_z, surv_count, topk_idx, topk_count)
+    check(load().lsa_topk_noalloc(B, cap, k, _p(surv_idx), _p(surv_z), _p(surv_count),
+                                  _p(topk_idx), _p(topk_count), _stream(stream)))
 
 
 def lsa_gather_hot(pool, idx, hot, *, stream=None):

@@ -266,6 +266,29 @@ lsa_status lsa_topk(int B, int cap, int k, const int32_t* surv_idx, const float*
                     "lsa_topk launch");
 }
 
+lsa_status lsa_topk_noalloc(int B, int cap, int k, const int32_t* surv_idx,
+                            const float* surv_z, const int32_t* surv_count, int32_t* topk_idx,
+                            int32_t* topk_count, hipStream_t stream) {
+  REQUIRE(B >= 1 && B <= 65535, LSA_E_SHAPE, "lsa_topk_noalloc: B=%d not in [1,65535]", B);
+  REQUIRE(cap >= 0 && k >= 0, LSA_E_ARG, "lsa_topk_noalloc: negative cap or k");
+  REQUIRE(surv_count && topk_count, LSA_E_ARG, "lsa_topk_noalloc: null count pointer");
+  REQUIRE(cap == 0 || (surv_idx && surv_z), LSA_E_ARG, "lsa_topk_noalloc: null survivor input");
+  REQUIRE(k == 0 || topk_idx, LSA_E_ARG, "lsa_topk_noalloc: null topk_idx with k > 0");
+  const size_t need = lsa::topk_workspace_bytes(B, cap, k);
+  REQUIRE(need <= (size_t)LSA_TOPK_NOALLOC_MAX_BYTES, LSA_E_SHAPE,
+          "lsa_topk_noalloc: B=%d, cap=%d, k=%d need %zu scratch bytes, more than the %d the "
+          "library holds (use lsa_topk with a workspace)",
+          B, cap, k, need, (int)LSA_TOPK_NOALLOC_MAX_BYTES);
+  void* ws = nullptr;
+  if (need > 0) {
+    const lsa_status st = hip_status(lsa::topk_scratch_address(&ws), "lsa_topk_noalloc scratch");
+    if (st != LSA_OK) return st;
+  }
+  return hip_status(lsa::launch_topk(B, cap, k, surv_idx, surv_z, surv_count, topk_idx,
+                                     topk_count, ws, stream),
+                    "lsa_topk_noalloc launch");
+}
+
 // -------------------------------------------------------------------- gather
 
 lsa_status lsa_gather_hot(int B, int N, int k, int row_bytes, const void* pool,

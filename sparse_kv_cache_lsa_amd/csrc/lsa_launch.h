@@ -63,6 +63,10 @@ hipError_t launch_topk(int B, int cap, int k, const int32_t* surv_idx,
                        const float* surv_z, const int32_t* surv_count,
                        int32_t* topk_idx, int32_t* topk_count, void* ws, hipStream_t s);
 
+// Device address of the top-k scratch array on the current device (resolved
+// on the first call per device).
+hipError_t topk_scratch_address(void** out);
+
 hipError_t launch_gather(int B, int N, int k, int row_bytes, const void* pool,
                          const int32_t* idx, void* hot, hipStream_t s);
 

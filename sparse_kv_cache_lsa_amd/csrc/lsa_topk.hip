@@ -21,6 +21,8 @@
 #include "lsa_device.h"
 #include "lsa_launch.h"
 
+#include <mutex>
+
 namespace lsa {
 namespace {
 
@@ -544,6 +546,35 @@ hipError_t launch_topk(int B, int cap, int k, const int32_t* surv_idx, const flo
                        cand_z, cand_count, surv_idx, surv_z, surv_count, topk_idx, topk_count);
   }
   return hipGetLastError();
+}
+
+// ----------------------------------------------------------------------------
+// Library-owned scratch for callers that cannot allocate (lsa_topk_noalloc):
+// the candidate lists of the two-stage top-k live in this file-scope device
+// array instead of a caller workspace.  Each GPU holds its own copy for the
+// life of the process.  Host code never uses the array's name as an address:
+// the device address is resolved once per device with hipGetSymbolAddress
+// (with that device current) and kept.
+__device__ __align__(256) unsigned char scratch[LSA_TOPK_NOALLOC_MAX_BYTES];
+
+hipError_t topk_scratch_address(void** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return hipSuccess;
 }
 
 }  // namespace lsa

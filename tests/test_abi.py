@@ -95,6 +95,13 @@ def test_validation_errors_return_before_launch(lib):
     assert lib.lsa_topk(1, 10, -1, fake, fake, fake, fake, fake, None, 0, None) == _abi.LSA_E_ARG
     assert lib.lsa_topk_workspace_bytes(2, 100000, 2048) > 0
     assert lib.lsa_topk(2, 100000, 2048, fake, fake, fake, fake, fake, None, 0, None) == _abi.LSA_E_WORKSPACE
+    # top-k on the library's scratch: sizes past its capacity are refused
+    # before anything is resolved or launched
+    big = (200, 262144, 2048)
+    assert lib.lsa_topk_workspace_bytes(*big) > _abi.LSA_TOPK_NOALLOC_MAX_BYTES
+    assert lib.lsa_topk_noalloc(*big, fake, fake, fake, fake, fake, None) == _abi.LSA_E_SHAPE
+    assert b"scratch" in lib.lsa_last_error()
+    assert lib.lsa_topk_noalloc(1, 10, -1, fake, fake, fake, fake, fake, None) == _abi.LSA_E_ARG
     # gather: row size not a multiple of 16
     assert lib.lsa_gather_hot(1, 10, 4, 24, fake, fake, fake, None) == _abi.LSA_E_ARG
     # fetch: bad sizes, bad row size, short workspace, pageable cold pool

@@ -470,3 +470,49 @@ double lsa_or_focal_bce_loss64(int Q, int64_t N, int D, int H, int dI,
                                const uint8_t* y) {
   return focal_core(Q, N, D, H, dI, gamma, h, Wq, Wg, bias, K, y, NULL, NULL);
 }
+
+/* ------------------------------------------------------------------------ */
+/* O11 core attention over the selected rows                                 */
+/* ------------------------------------------------------------------------ */
+
+void lsa_or_attention(int64_t n, int D, int H, const uint16_t* q,
+                      const uint16_t* rows, double scale, double* out,
+                      double* wabs) {
+#pragma omp parallel for schedule(static)
+  for (int hh = 0; hh < H; ++hh) {
+    double* o = out + (int64_t)hh * D;
+    double* wa = wabs ? wabs + (int64_t)hh * D : NULL;
+    for (int d = 0; d < D; ++d) {
+      o[d] = 0.0;
+      if (wa) wa[d] = 0.0;
+    }
+    if (n <= 0) continue;
+    double* s = (double*)malloc((size_t)n * sizeof(double));
+    /* scores */
+    for (int64_t j = 0; j < n; ++j) {
+      double dot = 0.0;
+      for (int d = 0; d < D; ++d)
+        dot += lsa_or_bf16_to_double(q[(int64_t)hh * D + d]) *
+               lsa_or_bf16_to_double(rows[j * D + d]);
+      s[j] = scale * dot;
+    }
+    /* softmax weights, shifted by the maximum score */
+    double m = s[0];
+    for (int64_t j = 1; j < n; ++j) m = fmax(m, s[j]);
+    double sum = 0.0;
+    for (int64_t j = 0; j < n; ++j) {
+      s[j] = exp(s[j] - m);
+      sum += s[j];
+    }
+    /* weighted sum of the rows */
+    for (int64_t j = 0; j < n; ++j) {
+      double p = s[j] / sum;
+      for (int d = 0; d < D; ++d) {
+        double v = lsa_or_bf16_to_double(rows[j * D + d]);
+        o[d] += p * v;
+        if (wa) wa[d] += p * fabs(v);
+      }
+    }
+    free(s);
+  }
+}

@@ -134,6 +134,21 @@ double lsa_or_focal_bce_loss64(int Q, int64_t N, int D, int H, int dI,
                                const double* Wg, double bias, const double* K,
                                const uint8_t* y);
 
+/* ---- O11: core attention over the selected rows ([SUMMARY] 2.1
+ * hierarchical-selection bullet: once the selected subset is on the GPU, a
+ * top-k inside it feeds the final core attention).  Reading: each row is a
+ * compressed latent vector that serves as both key and value, shared by all
+ * heads; for head h over the n given rows:
+ *   s_j = scale * sum_d q[h][d] * row_j[d]
+ *   p_j = exp(s_j - max_i s_i)
+ *   out[h][d] = sum_j p_j row_j[d] / sum_j p_j
+ * q: bf16 [H][D]; rows: bf16 [n][D]; out fp64 [H][D]; n = 0 gives zeros.
+ * wabs (optional, [H][D]) receives sum_j p_j |row_j[d]| / sum_j p_j, the
+ * scale of the output's rounding error. */
+void lsa_or_attention(int64_t n, int D, int H, const uint16_t* q,
+                      const uint16_t* rows, double scale, double* out,
+                      double* wabs);
+
 /* ---- trigger cadence ([SUMMARY] 2.1 periodic-trigger bullet; [REVIEW]
  * section 2): the indexer runs at decode step t iff t is a multiple of tau,
  * counting from step 0. */

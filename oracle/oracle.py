@@ -76,6 +76,7 @@ def _load():
         "lsa_or_num_threads": (i32, []),
         "lsa_or_set_num_threads": (None, [i32]),
         "lsa_or_trigger_due": (i32, [i64, i32]),
+        "lsa_or_attention": (None, [i64, i32, i32, P, P, f64, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -314,3 +315,21 @@ def focal_bce_loss64(h, Wq, Wg, bias: float, K, y, gamma: float, H: int, dI: int
     N = K.shape[0]
     return lib.lsa_or_focal_bce_loss64(Q, N, D, H, dI, float(gamma), _p(h), _p(Wq),
                                        _p(Wg), float(bias), _p(K), _p(y))
+
+
+def attention(q, rows, scale: float, want_wabs: bool = False):
+    """Core attention of one request: q bf16 [H][D], rows bf16 [n][D] (each
+    row both key and value) -> out fp64 [H][D] (and optionally
+    sum_j p_j |row_j| / sum_j p_j, [H][D])."""
+    lib = _load()
+    q = _c(q, np.uint16)
+    rows = _c(rows, np.uint16)
+    H, D = q.shape
+    n = rows.shape[0] if rows.size else 0
+    if n:
+        assert rows.shape[1] == D
+    out = np.empty((H, D), np.float64)
+    wabs = np.empty((H, D), np.float64) if want_wabs else None
+    lib.lsa_or_attention(n, D, H, _p(q), _p(rows) if n else None, float(scale), _p(out),
+                         _p(wabs))
+    return (out, wabs) if want_wabs else out

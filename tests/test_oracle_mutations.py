@@ -19,7 +19,7 @@ ROOT = os.path.dirname(HERE)
 SRC = os.path.join(ROOT, "oracle", "lsa_oracle.c")
 PINS = [os.path.join(HERE, f) for f in ("test_oracle_formats.py", "test_oracle_score.py",
                                         "test_oracle_select.py", "test_oracle_labels.py",
-                                        "test_oracle_fetch.py")]
+                                        "test_oracle_fetch.py", "test_oracle_attention.py")]
 
 # (name, exact snippet of lsa_oracle.c, planted replacement)
 MUTANTS = [
@@ -68,6 +68,15 @@ MUTANTS = [
      "acc += G[t * dI + d] * h[(int64_t)t * D + c];"),
     ("mean over N only", "const double inv = 1.0 / ((double)Q * (double)N);", "const double inv = 1.0 / (double)N;"),
     ("trigger phase", "return (t % tau) == 0;", "return (t % tau) == 1;"),
+    ("attention without the max shift", "      s[j] = exp(s[j] - m);", "      s[j] = exp(s[j]);"),
+    ("attention unnormalised", "    double p = s[j] / sum;", "    double p = s[j];"),
+    ("attention scale applied twice", "      s[j] = scale * dot;", "      s[j] = scale * scale * dot;"),
+    ("attention transposed row index", "               lsa_or_bf16_to_double(rows[j * D + d]);\n      s[j]",
+     "               lsa_or_bf16_to_double(rows[(int64_t)d * n + j]);\n      s[j]"),
+    ("attention value from the query", "        double v = lsa_or_bf16_to_double(rows[j * D + d]);",
+     "        double v = lsa_or_bf16_to_double(q[(int64_t)hh * D + d]);"),
+    ("attention drops the last row", "    for (int64_t j = 0; j < n; ++j) {\n      double p = s[j] / sum;",
+     "    for (int64_t j = 0; j + 1 < n; ++j) {\n      double p = s[j] / sum;"),
 ]
 
 

@@ -56,6 +56,8 @@ def parse():
                         "HBM instead of the 256 MB Infinity Cache")
     p.add_argument("--no-cold-fetch", action="store_true",
                    help="skip the cold-pool fetch report")
+    p.add_argument("--no-attention", action="store_true",
+                   help="skip the core-attention report (attention over the hot rows)")
     p.add_argument("--no-stream-probe", action="store_true",
                    help="skip the plain streaming-read reference measurement")
     p.add_argument("--graph", action="store_true",
@@ -279,12 +281,81 @@ def main():
         result["copy_probe"] = {"kernel": "gather_kernel (identity index list)",
                                 "read_bytes": rows * 1024 + rows * 4, "write_bytes": rows * 1024}
 
+    if not args.no_attention and w.row_elems == 512:
+        result["attention"] = attention_report(w, buf, stream, step, ms_per_step)
+
     if not args.no_cold_fetch:
         result["cold_fetch"] = cold_fetch(w, d, pool, buf, stream, step, ms_per_step)
 
     if not args.skip_cpu:
         result["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def attention_report(w, buf, stream, step, ms_per_step, launches=20, tau=64):
+    """Core attention of one decode step (lsa_sparse_attention) over the
+    trigger's hot rows -- buf.hot, gathered by the last step, with the top-k
+    counts -- plus a local window of recent rows, for ATT_HEADS heads: mean
+    time of `launches` back-to-back launches between two events, its HBM and
+    bf16 matrix-core rooflines, and one decode window of tau steps (one
+    trigger, then tau attention steps) timed as a whole."""
+    import numpy as np
+    import torch
+    import lsa_inputs as gen
+    import sparse_kv_cache_lsa_amd as lsa
+
+    B, k, D = w.B, w.k, gen.ATT_ROW
+    H, W = gen.ATT_HEADS, gen.ATT_WINDOW
+    a = gen.attention_inputs(B, H, 0, W, wid=59)
+    dev = "cuda"
+    q = torch.from_numpy(a.q.view(np.int16)).to(dev).view(torch.bfloat16)
+    win = torch.from_numpy(a.win.view(np.int16)).to(dev).view(torch.bfloat16)
+    hot = buf.hot.view(torch.bfloat16)
+    out = torch.empty((B, H, D), dtype=torch.float32, device=dev)
+    nws = lsa.lsa_sparse_attention_workspace_bytes(B, H, D, k, W)
+    ws = torch.empty((max(nws, 1),), dtype=torch.uint8, device=dev)
+    scale = gen.att_scale()
+
+    def att():
+        lsa.lsa_sparse_attention(q, hot, out, scale, hot_count=buf.topk_count, win=win,
+                                 ws=ws, stream=stream)
+
+    for _ in range(3):
+        att()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(launches):
+        att()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / launches
+    rows = int(buf.topk_count.sum().item()) + B * W
+    nbytes = rows * D * 2 + B * H * D * 2 + B * H * D * 4
+    flops = 4.0 * H * rows * D
+    # one decode window: a trigger, then tau attention steps
+    wins = []
+    for _ in range(3):
+        f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        f0.record(stream)
+        step()
+        for _ in range(tau):
+            att()
+        f1.record(stream)
+        torch.cuda.synchronize()
+        wins.append(f0.elapsed_time(f1))
+    wms = float(np.median(wins))
+    return {"kernel": "lsa_sparse_attention", "heads": H, "row_elems": D,
+            "selected_rows": k, "window_rows": W, "rows_attended": rows,
+            "splits_workspace_bytes": nws, "ms": ms, "launches": launches,
+            "algorithmic_bytes": nbytes, "GB/s": nbytes / (ms * 1e-3) / 1e9,
+            "frac_hbm": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "flops": flops, "TFLOP/s": flops / (ms * 1e-3) / 1e12,
+            "frac_bf16_mfma": flops / (ms * 1e-3) / 1e12 / 2500.0,
+            "decode_window": {"tau": tau, "ms": wms,
+                              "decode_tokens_per_s": B * tau / (wms * 1e-3),
+                              "trigger_ms": ms_per_step, "attention_ms_x_tau": ms * tau}}
 
 
 def cold_fetch(w, d, pool, buf, stream, step, ms_per_step):

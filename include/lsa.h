@@ -286,6 +286,44 @@ lsa_status lsa_gather_hot(int B, int N, int k, int row_bytes, const void* pool,
                           const int32_t* idx, void* hot, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * Core attention of one decode step over the selected rows ([SUMMARY] 2.1
+ * hierarchical-selection bullet: the top-k chosen inside the fetched subset
+ * feeds the final core attention; [SUMMARY] 1: recent tokens carry most
+ * requests, so a local window of recent rows is attended as well).  Reading
+ * of this library: every row is a compressed latent vector of D = 512 bf16
+ * that serves as both key and value and is shared by all heads.  For every
+ * request b and head h, over the rows
+ *   R_b = hot[b][0 .. hc) followed by win[b][0 .. wc),
+ *   hc = min(hot_count[b], k) (k when hot_count is NULL; negative = 0),
+ *   wc = min(win_count[b], W) (W when win_count is NULL),
+ * the output is
+ *   s_j = scale * (q[b][h] . r_j),   out[b][h] = sum_j softmax(s)_j * r_j
+ * (fp32; both products on bf16 matrix cores with fp32 accumulation, the
+ * softmax weights carried as an exact bf16 pair).  No rows: zeros.
+ *
+ *   q          bf16 [B][H][D]
+ *   hot        bf16 [B][k][D]   (lsa_gather_hot / lsa_gather_resident output;
+ *              rows past hc are not read)
+ *   hot_count  int32 [B] or NULL (lsa_topk's topk_count)
+ *   win        bf16 [B][W][D] or NULL when W = 0;  win_count int32 [B] or NULL
+ *   out        out fp32 [B][H][D]
+ *   ws         device workspace of lsa_sparse_attention_workspace_bytes()
+ *              bytes, 256-byte aligned (per-split partial outputs; 0 bytes
+ *              when one split covers the rows)
+ * Limits: 1 <= B <= 65535, H a multiple of 16 in [16, 1024], D == LSA_ATT_ROW,
+ * k, W >= 0 and k + W <= 2^20, finite scale; q, hot, win, out 16-byte
+ * aligned.  Errors: LSA_E_SHAPE / LSA_E_ARG for the limits and null or
+ * misaligned pointers, LSA_E_WORKSPACE, LSA_E_HIP for a launch failure.
+ */
+#define LSA_ATT_ROW 512
+size_t lsa_sparse_attention_workspace_bytes(int B, int H, int D, int k, int W);
+lsa_status lsa_sparse_attention(int B, int H, int D, int k, int W, float scale,
+                                const uint16_t* q, const uint16_t* hot,
+                                const int32_t* hot_count, const uint16_t* win,
+                                const int32_t* win_count, float* out, void* ws,
+                                size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * Cold-pool fetch with reuse ([SUMMARY] 2.1 dynamic-fetch bullet: every
  * entry with I >= 0.5 is brought from the CPU cold pool into GPU memory;
  * [REVIEW] section 2: the move is asynchronous and overlaps compute).

@@ -29,7 +29,7 @@ import torch
 GENERATOR_VERSION = 4
 
 _TAGS = {"h": 1, "wq": 2, "wg": 3, "plant": 4, "keys": 5, "logits": 6,
-         "student": 7, "misc": 8}
+         "student": 7, "misc": 8, "att_q": 9, "att_rows": 10, "att_win": 11}
 _ALL = 0xFFFF  # "not per request / not per layer" slot in the seed tuple
 
 
@@ -403,3 +403,40 @@ def student(w: LabelWorkload):
     K = to_bf16_bits(r.standard_normal((w.N, w.dI), dtype=np.float32)
                      * np.float32(1.0 / math.sqrt(w.dI)))
     return h, Wq, Wg, K, 0.0
+
+
+# ---------------------------------------------------------------------------
+# core attention after the selection (decode step)
+# ---------------------------------------------------------------------------
+
+ATT_HEADS = 64      # attention heads sharing each compressed row
+ATT_WINDOW = 128    # local window: recent rows attended besides the selected ones
+ATT_ROW = 512       # compressed row width (bf16 elements), as the KV pool rows
+
+
+def att_scale(D: int = ATT_ROW) -> float:
+    return 1.0 / math.sqrt(D)
+
+
+@dataclass
+class AttentionInputs:
+    q: np.ndarray      # bf16 bits [B][H][D]
+    hot: np.ndarray    # bf16 bits [B][k][D]
+    win: np.ndarray    # bf16 bits [B][W][D]
+
+
+def attention_inputs(B: int, H: int, k: int, W: int, D: int = ATT_ROW, wid: int = 60,
+                     seed: int = 0, rows_sd: float = 1.0) -> AttentionInputs:
+    """Queries, selected rows and window rows, all N(0, 1) (rows times
+    rows_sd) rounded to bf16; one stream per (request, tensor)."""
+    q = np.empty((B, H, D), np.uint16)
+    hot = np.empty((B, k, D), np.uint16)
+    win = np.empty((B, W, D), np.uint16)
+    sd = np.float32(rows_sd)
+    for b in range(B):
+        q[b] = to_bf16_bits(stream(seed, wid, b, _ALL, "att_q").standard_normal((H, D), dtype=np.float32))
+        hot[b] = to_bf16_bits(stream(seed, wid, b, _ALL, "att_rows")
+                              .standard_normal((k, D), dtype=np.float32) * sd)
+        win[b] = to_bf16_bits(stream(seed, wid, b, _ALL, "att_win")
+                              .standard_normal((W, D), dtype=np.float32) * sd)
+    return AttentionInputs(q=q, hot=hot, win=win)

@@ -20,6 +20,7 @@ __all__ = [
     "lsa_select_or_compact_masks_workspace_bytes", "lsa_select_or_compact_masks",
     "lsa_topk_workspace_bytes", "lsa_topk", "lsa_topk_noalloc", "lsa_gather_hot", "lsa_fetch_workspace_bytes",
     "lsa_resident_reset", "lsa_fetch_survivors", "lsa_gather_resident",
+    "lsa_sparse_attention_workspace_bytes", "lsa_sparse_attention",
     "lsa_label_vote_workspace_bytes", "lsa_label_vote",
     "lsa_focal_bce_grad_workspace_bytes", "lsa_focal_bce_grad",
 ]
@@ -320,6 +321,37 @@ def lsa_gather_hot(pool, idx, hot, *, stream=None):
     _dtype("lsa_gather_hot", "idx", idx, "int32")
     _dev(pool, idx, hot)
     check(load().lsa_gather_hot(B, N, k, row_bytes, _p(pool), _p(idx), _p(hot), _stream(stream)))
+
+
+def lsa_sparse_attention_workspace_bytes(B: int, H: int, D: int, k: int, W: int) -> int:
+    return int(load().lsa_sparse_attention_workspace_bytes(B, H, D, k, W))
+
+
+def lsa_sparse_attention(q, hot, out, scale, hot_count=None, win=None, win_count=None, ws=None,
+                         *, stream=None):
+    """q bf16 [B][H][D], hot bf16 [B][k][D] (selected rows), optional
+    hot_count i32 [B], win bf16 [B][W][D] (local window) and win_count i32
+    [B] -> out f32 [B][H][D]; ws: uint8 tensor of
+    lsa_sparse_attention_workspace_bytes(B, H, D, k, W) bytes."""
+    fn = "lsa_sparse_attention"
+    B, H, D = q.shape
+    k = hot.shape[1]
+    W = 0 if win is None else win.shape[1]
+    _expect(fn, "hot", hot, (B, k, D))
+    _expect(fn, "out", out, (B, H, D))
+    _expect(fn, "hot_count", hot_count, (B,))
+    if win is not None:
+        _expect(fn, "win", win, (B, W, D))
+    _expect(fn, "win_count", win_count, (B,))
+    for name, t in (("q", q), ("hot", hot), ("win", win)):
+        _dtype(fn, name, t, "bfloat16", "int16", "uint16")
+    _dtype(fn, "out", out, "float32")
+    _dtype(fn, "hot_count", hot_count, "int32")
+    _dtype(fn, "win_count", win_count, "int32")
+    _dev(q, hot, out, hot_count, win, win_count, ws)
+    check(load().lsa_sparse_attention(B, H, D, k, W, float(scale), _p(q), _p(hot), _p(hot_count),
+                                      _p(win), _p(win_count), _p(out), _p(ws), _nbytes(ws),
+                                      _stream(stream)))
 
 
 def lsa_fetch_workspace_bytes(B: int, N: int, cap: int) -> int:

@@ -13,6 +13,7 @@ LSA_OK, LSA_E_ARG, LSA_E_SHAPE, LSA_E_DTYPE, LSA_E_HIP, LSA_E_WORKSPACE = range(
 LSA_KEY_BF16, LSA_KEY_FP8_E4M3 = 0, 1
 LSA_CAND_CHUNK = 4096
 LSA_TOPK_NOALLOC_MAX_BYTES = 16 << 20
+LSA_ATT_ROW = 512
 STATUS_NAMES = {0: "LSA_OK", 1: "LSA_E_ARG", 2: "LSA_E_SHAPE", 3: "LSA_E_DTYPE",
                 4: "LSA_E_HIP", 5: "LSA_E_WORKSPACE"}
 
@@ -40,6 +41,9 @@ SIGNATURES = {
     "lsa_topk": (I32, [I32, I32, I32, P, P, P, P, P, P, SZ, P]),
     "lsa_topk_noalloc": (I32, [I32, I32, I32, P, P, P, P, P, P]),
     "lsa_gather_hot": (I32, [I32, I32, I32, I32, P, P, P, P]),
+    "lsa_sparse_attention_workspace_bytes": (SZ, [I32, I32, I32, I32, I32]),
+    "lsa_sparse_attention": (I32, [I32, I32, I32, I32, I32, C.c_float, P, P, P, P, P, P, P, SZ,
+                                   P]),
     "lsa_fetch_workspace_bytes": (SZ, [I32, I32, I32]),
     "lsa_resident_reset": (I32, [I32, I32, I32, P, P, P]),
     "lsa_fetch_survivors": (I32, [I32, I32, I32, I32, P, I32, P, P, P, P, P, P, P, SZ, P]),

@@ -304,6 +304,39 @@ lsa_status lsa_gather_hot(int B, int N, int k, int row_bytes, const void* pool,
                     "lsa_gather_hot launch");
 }
 
+// ------------------------------------------------------------ core attention
+
+size_t lsa_sparse_attention_workspace_bytes(int B, int H, int D, int k, int W) {
+  if (B < 1 || H < 16 || H % 16 || D != LSA_ATT_ROW || k < 0 || W < 0) return 0;
+  return lsa::attention_workspace_bytes(B, H, D, k, W);
+}
+
+lsa_status lsa_sparse_attention(int B, int H, int D, int k, int W, float scale,
+                                const uint16_t* q, const uint16_t* hot, const int32_t* hot_count,
+                                const uint16_t* win, const int32_t* win_count, float* out,
+                                void* ws, size_t ws_bytes, hipStream_t stream) {
+  const char* fn = "lsa_sparse_attention";
+  REQUIRE(B >= 1 && B <= 65535, LSA_E_SHAPE, "%s: B=%d not in [1,65535]", fn, B);
+  REQUIRE(H >= 16 && H <= 1024 && H % 16 == 0, LSA_E_SHAPE,
+          "%s: H=%d not a multiple of 16 in [16,1024]", fn, H);
+  REQUIRE(D == LSA_ATT_ROW, LSA_E_SHAPE, "%s: D=%d, rows must be %d wide", fn, D, LSA_ATT_ROW);
+  REQUIRE(k >= 0 && W >= 0 && (int64_t)k + W <= (1 << 20), LSA_E_SHAPE,
+          "%s: k=%d, W=%d: need k, W >= 0 and k + W <= 2^20", fn, k, W);
+  REQUIRE(scale == scale && scale - scale == 0.f, LSA_E_ARG, "%s: scale not finite", fn);
+  REQUIRE(q && out && (k == 0 || hot) && (W == 0 || win), LSA_E_ARG, "%s: null pointer argument",
+          fn);
+  REQUIRE(aligned16(q) && aligned16(out) && (k == 0 || aligned16(hot)) &&
+              (W == 0 || aligned16(win)),
+          LSA_E_ARG, "%s: q, hot, win and out must be 16-byte aligned", fn);
+  const size_t need = lsa::attention_workspace_bytes(B, H, D, k, W);
+  REQUIRE(need == 0 || (ws && ws_bytes >= need && ((uintptr_t)ws & 255) == 0), LSA_E_WORKSPACE,
+          "%s: workspace of %zu bytes (256-byte aligned) needed, got %zu", fn, need,
+          ws ? ws_bytes : (size_t)0);
+  return hip_status(lsa::launch_attention(B, H, k, W, scale, q, hot, hot_count, win, win_count,
+                                          out, ws, stream),
+                    "lsa_sparse_attention launch");
+}
+
 // ------------------------------------------------------- cold-pool fetch
 
 namespace {

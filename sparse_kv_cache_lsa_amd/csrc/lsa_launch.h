@@ -95,4 +95,10 @@ hipError_t launch_focal(int Q, int N, int D, int H, int dI, float gamma, const u
 
 hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s);
 
+int attention_splits(int B, int H, int k, int W);
+size_t attention_workspace_bytes(int B, int H, int D, int k, int W);
+hipError_t launch_attention(int B, int H, int k, int W, float scale, const uint16_t* q,
+                            const uint16_t* hot, const int32_t* hot_count, const uint16_t* win,
+                            const int32_t* win_count, float* out, void* ws, hipStream_t s);
+
 }  // namespace lsa

@@ -333,3 +333,57 @@ def attention(q, rows, scale: float, want_wabs: bool = False):
     lib.lsa_or_attention(n, D, H, _p(q), _p(rows) if n else None, float(scale), _p(out),
                          _p(wabs))
     return (out, wabs) if want_wabs else out
+
+
+# ---- O12 decode session over a growing key cache --------------------------
+
+def stream_session(keys, scale, queries, bias, N0: int, tau: int, T: int, per_window: int,
+                   k: int, cold=None, S: int = 0):
+    """One request of a decode session (gist.science technical summary, 2.1,
+    periodic-trigger and dynamic-fetch bullets; paper.oopus.info review,
+    section 2: every tau steps the indexer looks ahead over every entry
+    compressed so far).
+
+    keys: list of L arrays [N_cap][dI] (bf16 bits or e4m3 codes) holding every
+    entry the session will have; scale: list of L fp32 [N_cap] (e4m3) or None.
+    The cache holds N0 entries at step 0 and per_window more after each
+    window of tau steps (the entries compressed from that window's tokens),
+    so at step t it holds N0 + (t // tau) * per_window entries.  At every step
+    t in [0, T) with trigger_due(t, tau) the indexer scores the entries
+    present then: queries(i) gives the i-th trigger's (q [L][H][dI] bf16 bits,
+    g [L][H] fp32); bias [L].
+
+    With cold (uint8 [N_cap][row_bytes], the cold pool) and S slots, each
+    trigger fetches its survivors into the resident set (fetch: rows still
+    resident are kept) and gathers its top-k rows from it.
+
+    Returns one dict per trigger: step, N, z (fp64 [L][N]), survivors, zstar,
+    count, topk, kcount and, with cold: fetched, slot_of, entry_of, hot."""
+    L = len(keys)
+    N_cap = keys[0].shape[0]
+    out = []
+    if cold is not None:
+        slot_of = np.full(N_cap, -1, np.int32)
+        entry_of = np.full(S, -1, np.int32)
+        rows = np.zeros((S, cold.shape[1]), np.uint8)
+    i = 0
+    for t in range(T):
+        if not trigger_due(t, tau):
+            continue
+        N = N0 + (t // tau) * per_window
+        assert N <= N_cap, "the session needs more entries than the cache holds"
+        q, g = queries(i)
+        z = np.stack([score(keys[l][:N], None if scale is None or scale[l] is None
+                            else scale[l][:N], q[l], g[l], float(bias[l])) for l in range(L)])
+        surv, zstar, count = merge_compact(threshold(z), z)
+        top, kc = topk(surv, zstar, k)
+        rec = {"step": t, "N": N, "z": z, "survivors": surv, "zstar": zstar, "count": count,
+               "topk": top, "kcount": kc}
+        if cold is not None:
+            rec["fetched"] = fetch(cold, surv, slot_of, entry_of, rows)
+            rec["slot_of"] = slot_of.copy()
+            rec["entry_of"] = entry_of.copy()
+            rec["hot"] = gather_resident(rows, slot_of, top[:kc])
+        out.append(rec)
+        i += 1
+    return out

@@ -183,6 +183,39 @@ lsa_status lsa_score(int L, int B, int N, int H, int dI, lsa_key_dtype kdt,
                      hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * lsa_score on a growing key cache ([REVIEW] section 2 and [SUMMARY] 2.1,
+ * periodic trigger: every tau decode steps the indexer scores every entry
+ * compressed so far, and entries keep being appended between triggers).  The
+ * key and scale arrays of each layer hold entry_stride entries per request
+ * (the cache capacity); the call scores the first N of each request.  Every
+ * other argument, output and limit is that of lsa_score, which is this call
+ * with entry_stride = N.  Limits: N <= entry_stride <= 2^40.
+ */
+lsa_status lsa_score_strided(int L, int B, int N, int64_t entry_stride, int H, int dI,
+                             lsa_key_dtype kdt, const void* const* keys,
+                             const float* const* key_scale, const uint16_t* q,
+                             const float* g, const float* bias, uint32_t* sel_mask,
+                             int32_t* cand_idx, float* cand_z, int32_t* cand_count,
+                             float* z_opt, float* I_opt, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Append to a per-request cache ([REVIEW] section 2: the backbone keeps
+ * compressing 4 tokens into one entry, so 16 entries arrive per 64-step
+ * trigger window; [SUMMARY] 2.3: each new entry's indexer key is computed once
+ * and then frozen).  For every request b and i < n:
+ *   dst[b][dst_start + i] = src[b][i]        (rows of row_bytes bytes)
+ * with src holding src_stride rows per request and dst dst_stride rows per
+ * request (the cache capacity).  Used for the per-layer key rows, their fp32
+ * scales and the KV pool rows.
+ * Limits: 1 <= B <= 65535, n >= 0, row_bytes > 0 and a multiple of 4,
+ * src_stride >= n, 0 <= dst_start, dst_start + n <= dst_stride; src and dst
+ * 4-byte aligned (16-byte alignment and row sizes move 16 bytes a thread).
+ */
+lsa_status lsa_append_rows(int B, int n, int row_bytes, const void* src, int64_t src_stride,
+                           void* dst, int64_t dst_stride, int64_t dst_start,
+                           hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * Survivor compaction of the OR-merged selection ([SUMMARY] 2.1 dynamic-fetch
  * bullet: every entry some indexer layer selects is fetched).  Concatenates
  * the chunk candidate lists of lsa_score, in chunk order, so for every

@@ -29,7 +29,8 @@ import torch
 GENERATOR_VERSION = 4
 
 _TAGS = {"h": 1, "wq": 2, "wg": 3, "plant": 4, "keys": 5, "logits": 6,
-         "student": 7, "misc": 8, "att_q": 9, "att_rows": 10, "att_win": 11}
+         "student": 7, "misc": 8, "att_q": 9, "att_rows": 10, "att_win": 11,
+         "h_drift": 12}
 _ALL = 0xFFFF  # "not per request / not per layer" slot in the seed tuple
 
 
@@ -440,3 +441,23 @@ def attention_inputs(B: int, H: int, k: int, W: int, D: int = ATT_ROW, wid: int 
         win[b] = to_bf16_bits(stream(seed, wid, b, _ALL, "att_win")
                               .standard_normal((W, D), dtype=np.float32) * sd)
     return AttentionInputs(q=q, hot=hot, win=win)
+
+
+# ---------------------------------------------------------------------------
+# decode session: hidden states of successive triggers
+# ---------------------------------------------------------------------------
+
+def drift_hidden(w: Workload, n: int, cosine: float = 0.97) -> np.ndarray:
+    """Hidden states of n successive triggers, bf16 bits [n][B][D]: the first
+    is hidden(w), each next one c * previous + sqrt(1 - c^2) * fresh N(0, 1)
+    noise (c = cosine), rounded to bf16 -- a decode position that moves slowly
+    away from the one the keys were planted for."""
+    h = np.empty((n, w.B, w.D), np.uint16)
+    h[0] = hidden(w)
+    s = math.sqrt(max(0.0, 1.0 - cosine * cosine))
+    for i in range(1, n):
+        prev = bf16_bits_to_f32(h[i - 1])
+        noise = np.stack([stream(w.seed, w.wid, b, i, "h_drift").standard_normal(w.D, dtype=np.float32)
+                          for b in range(w.B)])
+        h[i] = to_bf16_bits(np.float32(cosine) * prev + np.float32(s) * noise)
+    return h

@@ -16,7 +16,8 @@ from ._abi import (LSA_CAND_CHUNK, LSA_KEY_BF16, LSA_KEY_FP8_E4M3, LSA_TOPK_NOAL
 __all__ = [
     "LSAError", "LSA_KEY_BF16", "LSA_KEY_FP8_E4M3", "LSA_CAND_CHUNK", "load", "lsa_version",
     "lsa_trigger_due", "lsa_project_query", "lsa_query_weights_packed_bytes",
-    "lsa_pack_query_weights", "lsa_project_query_packed", "lsa_score", "lsa_select_or_compact",
+    "lsa_pack_query_weights", "lsa_project_query_packed", "lsa_score", "lsa_score_strided",
+    "lsa_append_rows", "lsa_select_or_compact",
     "lsa_select_or_compact_masks_workspace_bytes", "lsa_select_or_compact_masks",
     "lsa_topk_workspace_bytes", "lsa_topk", "lsa_topk_noalloc", "lsa_gather_hot", "lsa_fetch_workspace_bytes",
     "lsa_resident_reset", "lsa_fetch_survivors", "lsa_gather_resident",
@@ -161,19 +162,35 @@ def lsa_score(keys, key_scale, q, g, bias, sel_mask, cand_idx, cand_z, cand_coun
     sel_mask int32 [L][B][ceil(N/32)]; chunk candidate lists cand_idx int32 /
     cand_z f32 [B][nchunks][LSA_CAND_CHUNK], cand_count int32 [B][nchunks];
     optional per-layer z and I, f32 [L][B][N]."""
+    _score("lsa_score", keys, key_scale, q, g, bias, None, sel_mask, cand_idx, cand_z,
+           cand_count, z, I, stream)
+
+
+def lsa_score_strided(keys, key_scale, q, g, bias, N, sel_mask, cand_idx, cand_z, cand_count,
+                      z=None, I=None, *, stream=None):
+    """lsa_score over the first N entries of growing caches: keys [B][N_cap][dI]
+    (and scales [B][N_cap]) with N <= N_cap; outputs sized by N."""
+    _score("lsa_score_strided", keys, key_scale, q, g, bias, int(N), sel_mask, cand_idx,
+           cand_z, cand_count, z, I, stream)
+
+
+def _score(fn, keys, key_scale, q, g, bias, n_live, sel_mask, cand_idx, cand_z, cand_count, z,
+           I, stream):
     fp8 = key_scale is not None
     L, B, H, dI = q.shape
-    N = keys[0].shape[1]
+    cap = keys[0].shape[1]
+    N = cap if n_live is None else n_live
+    if not 0 <= N <= cap:
+        raise ValueError(f"{fn}: N={N} outside [0, {cap}] (the cache holds {cap} entries)")
     if N > 0:
-        fn = "lsa_score"
         if len(keys) != L or len(bias) < L or (fp8 and len(key_scale) != L):
             raise ValueError(f"{fn}: one key tensor, bias (and scale) per layer")
         for l in range(L):
-            _expect(fn, f"keys[{l}]", keys[l], (B, N, dI))
+            _expect(fn, f"keys[{l}]", keys[l], (B, cap, dI))
             if keys[l].element_size() != (1 if fp8 else 2):
                 raise ValueError(f"{fn}: keys must be 1-byte e4m3 codes or 2-byte bf16")
             if fp8:
-                _expect(fn, f"key_scale[{l}]", key_scale[l], (B, N))
+                _expect(fn, f"key_scale[{l}]", key_scale[l], (B, cap))
         nch = (N + LSA_CAND_CHUNK - 1) // LSA_CAND_CHUNK
         _expect(fn, "g", g, (L, B, H))
         _expect(fn, "sel_mask", sel_mask, (L, B, (N + 31) // 32))
@@ -191,15 +208,39 @@ def lsa_score(keys, key_scale, q, g, bias, sel_mask, cand_idx, cand_z, cand_coun
         for l in range(L if fp8 else 0):
             _dtype(fn, f"key_scale[{l}]", key_scale[l], "float32")
     _dev(q, g, sel_mask, cand_idx, cand_z, cand_count, z, I, *keys, *(key_scale or []))
-    bias = _bias_tensor("lsa_score", bias, L, q.device)
+    bias = _bias_tensor(fn, bias, L, q.device)
     kp, _k1 = ptr_array([_p(k) for k in keys])
     if fp8:
         sp, _k2 = ptr_array([_p(s) for s in key_scale])
     else:
         sp = None
-    check(load().lsa_score(L, B, N, H, dI, LSA_KEY_FP8_E4M3 if fp8 else LSA_KEY_BF16, kp, sp,
-                           _p(q), _p(g), _p(bias), _p(sel_mask), _p(cand_idx), _p(cand_z),
-                           _p(cand_count), _p(z), _p(I), _stream(stream)))
+    kdt = LSA_KEY_FP8_E4M3 if fp8 else LSA_KEY_BF16
+    if n_live is None:
+        check(load().lsa_score(L, B, N, H, dI, kdt, kp, sp, _p(q), _p(g), _p(bias),
+                               _p(sel_mask), _p(cand_idx), _p(cand_z), _p(cand_count), _p(z),
+                               _p(I), _stream(stream)))
+    else:
+        check(load().lsa_score_strided(L, B, N, cap, H, dI, kdt, kp, sp, _p(q), _p(g), _p(bias),
+                                       _p(sel_mask), _p(cand_idx), _p(cand_z), _p(cand_count),
+                                       _p(z), _p(I), _stream(stream)))
+
+
+def lsa_append_rows(src, dst, dst_start, n=None, *, stream=None):
+    """dst[b][dst_start + i] = src[b][i] for i < n (n = src.shape[1] by
+    default): src [B][n_src][...], dst [B][N_cap][...] with the same row."""
+    fn = "lsa_append_rows"
+    B = src.shape[0]
+    n = src.shape[1] if n is None else int(n)
+    rb = _row_bytes(src) if src.dim() >= 3 else src.element_size()
+    drb = _row_bytes(dst) if dst.dim() >= 3 else dst.element_size()
+    if dst.shape[0] != B or rb != drb:
+        raise ValueError(f"{fn}: src and dst must have the same batch and row size")
+    if not 0 <= n <= src.shape[1] or not 0 <= dst_start or dst_start + n > dst.shape[1]:
+        raise ValueError(f"{fn}: rows [{dst_start}, {dst_start + n}) do not fit the cache of "
+                         f"{dst.shape[1]} rows (or n > the {src.shape[1]} source rows)")
+    _dev(src, dst)
+    check(load().lsa_append_rows(B, n, rb, _p(src), src.shape[1], _p(dst), dst.shape[1],
+                                 int(dst_start), _stream(stream)))
 
 
 def _bias_tensor(fn, bias, L, device):

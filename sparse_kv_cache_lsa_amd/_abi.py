@@ -34,6 +34,9 @@ SIGNATURES = {
     "lsa_pack_query_weights": (I32, [I32, I32, I32, P, P, P, P]),
     "lsa_project_query_packed": (I32, [I32, I32, I32, I32, I32, P, I64, PP, P, P, P]),
     "lsa_score": (I32, [I32, I32, I32, I32, I32, I32, PP, PP, P, P, P, P, P, P, P, P, P, P]),
+    "lsa_score_strided": (I32, [I32, I32, I32, I64, I32, I32, I32, PP, PP, P, P, P, P, P, P, P, P,
+                                P, P]),
+    "lsa_append_rows": (I32, [I32, I32, I32, P, I64, P, I64, I64, P]),
     "lsa_select_or_compact": (I32, [I32, I32, P, P, P, I32, P, P, P, P]),
     "lsa_select_or_compact_masks_workspace_bytes": (SZ, [I32, I32]),
     "lsa_select_or_compact_masks": (I32, [I32, I32, I32, P, P, I32, P, P, P, P, SZ, P]),

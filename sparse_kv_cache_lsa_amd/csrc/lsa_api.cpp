@@ -142,11 +142,12 @@ lsa_status lsa_project_query_packed(int L, int B, int D, int H, int dI, const ui
 
 // --------------------------------------------------------------------- score
 
-lsa_status lsa_score(int L, int B, int N, int H, int dI, lsa_key_dtype kdt,
-                     const void* const* keys, const float* const* key_scale, const uint16_t* q,
-                     const float* g, const float* bias, uint32_t* sel_mask, int32_t* cand_idx,
-                     float* cand_z, int32_t* cand_count, float* z_opt, float* I_opt,
-                     hipStream_t stream) {
+lsa_status lsa_score_strided(int L, int B, int N, int64_t entry_stride, int H, int dI,
+                             lsa_key_dtype kdt, const void* const* keys,
+                             const float* const* key_scale, const uint16_t* q, const float* g,
+                             const float* bias, uint32_t* sel_mask, int32_t* cand_idx,
+                             float* cand_z, int32_t* cand_count, float* z_opt, float* I_opt,
+                             hipStream_t stream) {
   REQUIRE(kdt == LSA_KEY_BF16 || kdt == LSA_KEY_FP8_E4M3, LSA_E_DTYPE,
           "lsa_score: unknown key dtype %d", (int)kdt);
   REQUIRE(L >= 1 && L <= LSA_MAX_LAYERS, LSA_E_SHAPE, "lsa_score: L=%d not in [1,%d]", L,
@@ -158,6 +159,8 @@ lsa_status lsa_score(int L, int B, int N, int H, int dI, lsa_key_dtype kdt,
   REQUIRE((int64_t)N * dI * (kdt == LSA_KEY_BF16 ? 2 : 1) < ((int64_t)1 << 31), LSA_E_SHAPE,
           "lsa_score: keys of one (layer, request) must stay below 2^31 bytes (N=%d, dI=%d)", N,
           dI);
+  REQUIRE(entry_stride >= N && entry_stride <= ((int64_t)1 << 40), LSA_E_SHAPE,
+          "lsa_score: entry_stride=%lld must be at least N=%d", (long long)entry_stride, N);
   REQUIRE(bias && ((uintptr_t)bias & 3u) == 0, LSA_E_ARG,
           "lsa_score: bias must be a 4-byte aligned device array of L floats");
   if (N == 0) return LSA_OK;   // nothing to score; outputs are empty
@@ -184,6 +187,7 @@ lsa_status lsa_score(int L, int B, int N, int H, int dI, lsa_key_dtype kdt,
   a.cand_count = cand_count;
   a.z = z_opt;
   a.I = I_opt;
+  a.stride = entry_stride;
   a.L = L;
   a.B = B;
   a.N = N;
@@ -191,6 +195,36 @@ lsa_status lsa_score(int L, int B, int N, int H, int dI, lsa_key_dtype kdt,
   a.W = (N + 31) / 32;
   a.nchunks = (N + LSA_CAND_CHUNK - 1) / LSA_CAND_CHUNK;
   return hip_status(lsa::launch_score(dI, kdt, a, stream), "lsa_score launch");
+}
+
+lsa_status lsa_score(int L, int B, int N, int H, int dI, lsa_key_dtype kdt,
+                     const void* const* keys, const float* const* key_scale, const uint16_t* q,
+                     const float* g, const float* bias, uint32_t* sel_mask, int32_t* cand_idx,
+                     float* cand_z, int32_t* cand_count, float* z_opt, float* I_opt,
+                     hipStream_t stream) {
+  return lsa_score_strided(L, B, N, N, H, dI, kdt, keys, key_scale, q, g, bias, sel_mask,
+                           cand_idx, cand_z, cand_count, z_opt, I_opt, stream);
+}
+
+// ------------------------------------------------------------- cache append
+
+lsa_status lsa_append_rows(int B, int n, int row_bytes, const void* src, int64_t src_stride,
+                           void* dst, int64_t dst_stride, int64_t dst_start,
+                           hipStream_t stream) {
+  const char* fn = "lsa_append_rows";
+  REQUIRE(B >= 1 && B <= 65535 && n >= 0, LSA_E_SHAPE, "%s: B=%d, n=%d", fn, B, n);
+  REQUIRE(row_bytes > 0 && row_bytes % 4 == 0, LSA_E_ARG,
+          "%s: row_bytes=%d not a positive multiple of 4", fn, row_bytes);
+  REQUIRE(src_stride >= n && dst_start >= 0 && dst_stride >= dst_start + n, LSA_E_SHAPE,
+          "%s: strides must hold the rows (src_stride %lld, n %d, dst_start %lld, dst_stride "
+          "%lld)", fn, (long long)src_stride, n, (long long)dst_start, (long long)dst_stride);
+  if (n == 0) return LSA_OK;
+  REQUIRE(src && dst, LSA_E_ARG, "%s: null pointer argument", fn);
+  REQUIRE(((uintptr_t)src & 3u) == 0 && ((uintptr_t)dst & 3u) == 0, LSA_E_ARG,
+          "%s: src and dst must be 4-byte aligned", fn);
+  return hip_status(lsa::launch_append_rows(B, n, row_bytes, src, src_stride, dst, dst_stride,
+                                            dst_start, stream),
+                    "lsa_append_rows launch");
 }
 
 // ----------------------------------------------------------- select/compact

@@ -29,7 +29,50 @@ __global__ __launch_bounds__(256) void gather_kernel(int N, int k, int chunks_pe
   *(u32x4*)(hot + row * row_bytes + 16ll * c) = v;
 }
 
+// Cache append: dst[b][dst_start + i] = src[b][i] for i < n, rows of row_bytes
+// (a multiple of 4).  One 4-, 8- or 16-byte word per thread, as wide as the
+// rows' alignment allows (key rows and pool rows move 16 bytes a thread, the
+// per-entry fp32 scales 4).
+template <typename T>
+__global__ __launch_bounds__(256) void append_kernel(int n, int words_per_row, long long total,
+                                                     const T* __restrict__ src,
+                                                     long long src_stride_words,
+                                                     T* __restrict__ dst,
+                                                     long long dst_stride_words,
+                                                     long long dst_start_words) {
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= total) return;
+  const long long per_b = (long long)n * words_per_row;
+  const long long b = i / per_b;
+  const long long w = i - b * per_b;
+  dst[b * dst_stride_words + dst_start_words + w] = src[b * src_stride_words + w];
+}
+
+template <typename T>
+hipError_t launch_append_t(int B, int n, int row_bytes, const void* src, int64_t src_stride,
+                           void* dst, int64_t dst_stride, int64_t dst_start, hipStream_t s) {
+  const int wpr = row_bytes / (int)sizeof(T);
+  const long long total = (long long)B * n * wpr;
+  const long long blocks = (total + 255) / 256;
+  hipLaunchKernelGGL(append_kernel<T>, dim3((unsigned)blocks), dim3(256), 0, s, n, wpr, total,
+                     (const T*)src, (long long)src_stride * wpr, (T*)dst,
+                     (long long)dst_stride * wpr, (long long)dst_start * wpr);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_append_rows(int B, int n, int row_bytes, const void* src, int64_t src_stride,
+                              void* dst, int64_t dst_stride, int64_t dst_start, hipStream_t s) {
+  if ((long long)B * n == 0) return hipSuccess;
+  const uintptr_t al = (uintptr_t)src | (uintptr_t)dst;
+  if (row_bytes % 16 == 0 && al % 16 == 0)
+    return launch_append_t<u32x4>(B, n, row_bytes, src, src_stride, dst, dst_stride, dst_start, s);
+  if (row_bytes % 8 == 0 && al % 8 == 0)
+    return launch_append_t<u32x2>(B, n, row_bytes, src, src_stride, dst, dst_stride, dst_start, s);
+  return launch_append_t<uint32_t>(B, n, row_bytes, src, src_stride, dst, dst_stride, dst_start,
+                                   s);
+}
 
 hipError_t launch_gather(int B, int N, int k, int row_bytes, const void* pool,
                          const int32_t* idx, void* hot, hipStream_t s) {

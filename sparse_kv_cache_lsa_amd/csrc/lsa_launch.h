@@ -21,6 +21,7 @@ struct ScoreArgs {
   int32_t* cand_count;     // [B][nchunks]
   float* z;                // [L][B][N] or null
   float* I;                // [L][B][N] or null
+  int64_t stride;          // entries between two requests in keys / scales (>= N)
   int L, B, N, H, W;       // W = ceil(N / 32)
   int nchunks;             // ceil(N / LSA_CAND_CHUNK)
   int pairs;               // two-chunk blocks per request (set by the launcher)
@@ -94,6 +95,9 @@ hipError_t launch_focal(int Q, int N, int D, int H, int dI, float gamma, const u
                         const uint8_t* label, float* loss, float* dWq, void* ws, hipStream_t s);
 
 hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s);
+
+hipError_t launch_append_rows(int B, int n, int row_bytes, const void* src, int64_t src_stride,
+                              void* dst, int64_t dst_stride, int64_t dst_start, hipStream_t s);
 
 int attention_splits(int B, int H, int k, int W);
 size_t attention_workspace_bytes(int B, int H, int D, int k, int W);

@@ -300,9 +300,9 @@ void score_kernel(ScoreArgs a) {
 #pragma unroll
     for (int i = 0; i < G::EPC; ++i) qv[i] = qt[l][G::EPC * (lane % G::LPR) + i];
     const __amdgpu_buffer_rsrc_t kr =
-        buffer((const unsigned char*)a.keys[l] + (size_t)b * N * G::RB, N * G::RB);
+        buffer((const unsigned char*)a.keys[l] + (size_t)b * a.stride * G::RB, N * G::RB);
     const __amdgpu_buffer_rsrc_t sr =
-        buffer(KT == 1 ? (const void*)(a.scale[l] + (size_t)b * N) : a.keys[l], KT == 1 ? N * 4 : 0);
+        buffer(KT == 1 ? (const void*)(a.scale[l] + (size_t)b * a.stride) : a.keys[l], KT == 1 ? N * 4 : 0);
     const __amdgpu_buffer_rsrc_t zr = buffer(WZ ? a.z + (size_t)p * N : a.keys[l], WZ ? N * 4 : 0);
     const __amdgpu_buffer_rsrc_t ir = buffer(WI ? a.I + (size_t)p * N : a.keys[l], WI ? N * 4 : 0);
     const float bias = a.bias[l];

@@ -1,15 +1,17 @@
 """Device buffers for one indexer trigger and the call sequence of the hot
-path (project -> score -> select/compact -> top-k -> gather), and the resident
-set that survivors are fetched into from a host cold pool.  Allocation uses
-torch; every step is one C entry point of liblsa.so."""
+path (project -> score -> select/compact -> top-k -> gather), the resident set
+that survivors are fetched into from a host cold pool, and a decode session
+over caches that grow between triggers.  Allocation uses torch; every step is
+one C entry point of liblsa.so."""
 from __future__ import annotations
 
 from dataclasses import dataclass
 
-from . import (LSA_CAND_CHUNK, lsa_fetch_survivors, lsa_fetch_workspace_bytes, lsa_gather_hot,
-               lsa_gather_resident, lsa_pack_query_weights, lsa_project_query,
+from . import (LSA_CAND_CHUNK, lsa_append_rows, lsa_fetch_survivors, lsa_fetch_workspace_bytes,
+               lsa_gather_hot, lsa_gather_resident, lsa_pack_query_weights, lsa_project_query,
                lsa_project_query_packed, lsa_query_weights_packed_bytes, lsa_resident_reset,
-               lsa_score, lsa_select_or_compact, lsa_topk, lsa_topk_workspace_bytes)
+               lsa_score, lsa_score_strided, lsa_select_or_compact, lsa_topk,
+               lsa_topk_workspace_bytes)
 
 
 @dataclass
@@ -127,3 +129,109 @@ class ResidentSet:
 
     def gather(self, idx, hot, stream=None):
         lsa_gather_resident(self.rows, self.slot_of, idx, hot, stream=stream)
+
+
+class StreamingSession:
+    """Decode-time indexer state of B requests whose compressed caches keep
+    growing: per-layer key caches of N_cap entries per request (the first N
+    live), a host cold pool of KV rows and the GPU-resident set fetched from it.
+
+    append() adds entries to the caches (lsa_append_rows); trigger() runs one
+    lookahead trigger over the live entries (project -> score the first N ->
+    OR/compact -> top-k -> fetch the survivors, reusing rows already resident ->
+    gather the top-k rows into `hot`); decode() is the host loop over decode
+    steps that triggers at lsa_trigger_due(t, tau) and appends the entries of
+    each finished window before the trigger, so the trigger at step t sees
+    N0 + (t // tau) * per_window entries.  Steps between triggers reuse `hot`.
+    Every computation is a C entry point; torch only allocates."""
+
+    def __init__(self, L, B, N_cap, H, dI, k, row_elems, S, cold_pool, key_dtype="bf16",
+                 tau=64, per_window=16, device="cuda"):
+        import torch
+        from . import lsa_trigger_due  # noqa: F401  (the cadence is the library's)
+        self.L, self.B, self.N_cap, self.H, self.dI, self.k = L, B, N_cap, H, dI, k
+        self.tau, self.per_window, self.N = tau, per_window, 0
+        self.fp8 = key_dtype == "e4m3"
+        kdt = torch.uint8 if self.fp8 else torch.bfloat16
+        self.keys = [torch.zeros((B, N_cap, dI), dtype=kdt, device=device) for _ in range(L)]
+        self.scale = ([torch.zeros((B, N_cap), dtype=torch.float32, device=device)
+                       for _ in range(L)] if self.fp8 else None)
+        self.cold = cold_pool
+        W_cap = (N_cap + 31) // 32
+        nch_cap = (N_cap + LSA_CAND_CHUNK - 1) // LSA_CAND_CHUNK
+        # flat capacity buffers; each trigger views their leading part with the
+        # shapes of the live N (the kernels index them densely by N)
+        self._mask = torch.empty(L * B * W_cap, dtype=torch.int32, device=device)
+        self._cidx = torch.empty(B * nch_cap * LSA_CAND_CHUNK, dtype=torch.int32, device=device)
+        self._cz = torch.empty(B * nch_cap * LSA_CAND_CHUNK, dtype=torch.float32, device=device)
+        self._cc = torch.empty(B * nch_cap, dtype=torch.int32, device=device)
+        self.q = torch.empty((L, B, H, dI), dtype=torch.bfloat16, device=device)
+        self.g = torch.empty((L, B, H), dtype=torch.float32, device=device)
+        self.surv_idx = torch.empty((B, N_cap), dtype=torch.int32, device=device)
+        self.surv_z = torch.empty((B, N_cap), dtype=torch.float32, device=device)
+        self.surv_count = torch.empty((B,), dtype=torch.int32, device=device)
+        self.ws_topk = torch.empty((max(1, lsa_topk_workspace_bytes(B, N_cap, k)),),
+                                   dtype=torch.uint8, device=device)
+        self.topk_idx = torch.empty((B, k), dtype=torch.int32, device=device)
+        self.topk_count = torch.empty((B,), dtype=torch.int32, device=device)
+        self.hot = torch.zeros((B, k, row_elems), dtype=cold_pool.dtype, device=device)
+        self.res = ResidentSet.allocate(B, N_cap, S, row_elems, dtype=cold_pool.dtype,
+                                        device=device)
+        self.triggers = []   # (step, N, survivors per request)
+
+    def append(self, new_keys, new_scale=None, stream=None):
+        """New entries of every request: new_keys list of L [B][n][dI] (and
+        new_scale list of L [B][n] for e4m3 keys), appended after the live
+        ones."""
+        n = new_keys[0].shape[1]
+        if self.N + n > self.N_cap:
+            raise ValueError(f"the caches hold {self.N_cap} entries; {self.N} + {n} do not fit")
+        for l in range(self.L):
+            lsa_append_rows(new_keys[l], self.keys[l], self.N, stream=stream)
+            if self.fp8:
+                lsa_append_rows(new_scale[l], self.scale[l], self.N, stream=stream)
+        self.N += n
+
+    def _views(self):
+        N, L, B = self.N, self.L, self.B
+        W = (N + 31) // 32
+        nch = (N + LSA_CAND_CHUNK - 1) // LSA_CAND_CHUNK
+        return (self._mask[:L * B * W].view(L, B, W),
+                self._cidx[:B * nch * LSA_CAND_CHUNK].view(B, nch, LSA_CAND_CHUNK),
+                self._cz[:B * nch * LSA_CAND_CHUNK].view(B, nch, LSA_CAND_CHUNK),
+                self._cc[:B * nch].view(B, nch))
+
+    def trigger(self, h, packed, bias, stream=None):
+        """One lookahead trigger over the N live entries (h bf16 [B][D])."""
+        mask, cidx, cz, cc = self._views()
+        lsa_project_query_packed(h, packed, self.q, self.g, stream=stream)
+        lsa_score_strided(self.keys, self.scale, self.q, self.g, bias, self.N, mask, cidx, cz,
+                          cc, stream=stream)
+        lsa_select_or_compact(cidx, cz, cc, self.N, self.surv_idx, self.surv_z, self.surv_count,
+                              stream=stream)
+        lsa_topk(self.surv_idx, self.surv_z, self.surv_count, self.topk_idx, self.topk_count,
+                 self.ws_topk, stream=stream)
+        self.res.fetch(self.cold, self.surv_idx, self.surv_count, stream=stream)
+        self.res.gather(self.topk_idx, self.hot, stream=stream)
+
+    def decode(self, T, hidden_of, packed, bias, window_source, on_trigger=None, on_step=None,
+               stream=None):
+        """Decode steps [0, T): at every step with lsa_trigger_due(t, tau) the
+        entries of the window that just ended are appended
+        (window_source(i) -> (new_keys, new_scale) for trigger i >= 1) and the
+        trigger runs on hidden_of(i); on_trigger(i, t) after each trigger,
+        on_step(t) after every step (e.g. the core attention on `hot`)."""
+        from . import lsa_trigger_due
+        i = 0
+        for t in range(T):
+            if lsa_trigger_due(t, self.tau):
+                if i > 0:
+                    nk, ns = window_source(i)
+                    self.append(nk, ns, stream=stream)
+                self.trigger(hidden_of(i), packed, bias, stream=stream)
+                if on_trigger is not None:
+                    on_trigger(i, t)
+                i += 1
+            if on_step is not None:
+                on_step(t)
+        return i

@@ -102,7 +102,8 @@ def _check_request(inp, oq, buf, b, pool, zl=None):
                            extra=E.max(axis=0))
     _check_gather(buf, b, pool, kc)
     return {"uncertain": unc, "topk_band": nb, "band_z": band_z, "survivors": cnt,
-            "topk": kc, "q_flips": flips, "max_margin": float(E.max(initial=0))}
+            "topk": kc, "q_flips": flips, "max_margin": float(E.max(initial=0)),
+            "oracle_survivors": surv, "oracle_topk": topk[:kcount]}
 
 
 def _check_gather(buf, b, pool, kc):
@@ -121,7 +122,9 @@ def test_chain_small_workloads(name):
     pool = gen.pool_tensor(w, DEV)
     buf, _ = _run(inp, pool)
     for b in range(w.B):
-        print(name, b, _check_request(inp, oq, buf, b, pool))
+        r = _check_request(inp, oq, buf, b, pool)
+        r.pop("oracle_survivors"), r.pop("oracle_topk")
+        print(name, b, r)
     # with per-layer logits requested: the same selection, plus every z
     buf2, zl = _run(inp, pool, with_layers=True)
     for b in range(w.B):
@@ -166,23 +169,26 @@ def test_chain_full_size(name):
     tcounts = host(buf.topk_count)
     oq = OracleQueries(inp)
     totals = {"uncertain": 0, "topk_band": 0, "band_z": 0, "q_flips": 0}
+    oracle_sets = []
     for b in range(w.B):
         cnt = int(counts[b])
         assert 0 < cnt < w.N and tcounts[b] == min(w.k, cnt)
         r = _check_request(inp, oq, buf, b, pool, zl)
+        oracle_sets.append((r.pop("oracle_survivors"), r.pop("oracle_topk")))
         for key in totals:
             totals[key] += r[key]
         print(name, b, r, flush=True)
     print(name, "excluded over all requests:", totals, flush=True)
-    _check_cold_fetch(w, buf, pool)
+    _check_cold_fetch(w, oracle_sets, pool)
 
 
-def _check_cold_fetch(w, buf, pool):
-    """The trigger's survivors fetched from a pinned host copy of the pool into
-    a resident set of N/2 slots per request (the benchmark's cold-fetch
-    configuration), then a second survivor set that keeps ~80% of them; slot
-    tables and resident rows equal the oracle's, and the top-k rows gathered
-    from the resident set equal the device-pool gather."""
+def _check_cold_fetch(w, oracle_sets, pool):
+    """The oracle's survivors of every request fetched from a pinned host copy
+    of the pool into a resident set of N/2 slots per request (the benchmark's
+    cold-fetch configuration), then a second survivor set that keeps ~80% of
+    them (drawn from a seeded generator); slot tables and resident rows equal
+    the oracle's fetch, and the oracle's top-k rows gathered from the resident
+    set equal the device-pool gather of the same indices."""
     import sparse_kv_cache_lsa_amd as lsa
     B, N, S = w.B, w.N, w.N // 2
     cold = torch.empty(pool.shape, dtype=pool.dtype, pin_memory=True)
@@ -195,8 +201,7 @@ def _check_cold_fetch(w, buf, pool):
     ws = torch.empty((lsa.lsa_fetch_workspace_bytes(B, N, N),), dtype=torch.uint8, device=DEV)
     lsa.lsa_resident_reset(so, eo)
     rng = np.random.default_rng(3)
-    counts = host(buf.surv_count)
-    first = [host(buf.surv_idx[b, :int(counts[b])]) for b in range(B)]
+    first = [x[0].astype(np.int32) for x in oracle_sets]
     second = []
     for s in first:
         keep = s[rng.random(s.size) < 0.8]
@@ -219,7 +224,14 @@ def _check_cold_fetch(w, buf, pool):
             assert np.array_equal(host(rows[b]).view(np.uint8).reshape(S, -1), o_rows)
         print(f"{w.name}: cold fetch {t}: {int(got.sum())} rows", flush=True)
         if t == 0:
-            hot = torch.empty_like(buf.hot)
-            lsa.lsa_gather_resident(rows, so, buf.topk_idx, hot)
+            k = w.k
+            top = np.full((B, k), -1, np.int32)
+            for b, x in enumerate(oracle_sets):
+                top[b, :x[1].size] = x[1]
+            td = dev(top)
+            hot = torch.empty((B, k, pool.shape[2]), dtype=pool.dtype, device=DEV)
+            hot2 = torch.empty_like(hot)
+            lsa.lsa_gather_resident(rows, so, td, hot)
+            lsa.lsa_gather_hot(pool, td, hot2)
             torch.cuda.synchronize()
-            assert torch.equal(hot, buf.hot)
+            assert torch.equal(hot, hot2)

@@ -58,6 +58,9 @@ def parse():
                    help="skip the cold-pool fetch report")
     p.add_argument("--no-attention", action="store_true",
                    help="skip the core-attention report (attention over the hot rows)")
+    p.add_argument("--no-stream", action="store_true",
+                   help="skip the decode-session report (growing caches, 11 triggers) and the "
+                        "survivor-growth sweep")
     p.add_argument("--no-stream-probe", action="store_true",
                    help="skip the plain streaming-read reference measurement")
     p.add_argument("--graph", action="store_true",
@@ -287,6 +290,10 @@ def main():
     if not args.no_cold_fetch:
         result["cold_fetch"] = cold_fetch(w, d, pool, buf, stream, step, ms_per_step)
 
+    if not args.no_stream and w.name == "ctx1m":
+        result["decode_session"] = stream_report(w, d, pool, stream)
+        result["survivor_growth"] = growth_report(args.threads)
+
     if not args.skip_cpu:
         result["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)
     print(json.dumps(result), flush=True)
@@ -356,6 +363,112 @@ def attention_report(w, buf, stream, step, ms_per_step, launches=20, tau=64):
             "decode_window": {"tau": tau, "ms": wms,
                               "decode_tokens_per_s": B * tau / (wms * 1e-3),
                               "trigger_ms": ms_per_step, "attention_ms_x_tau": ms * tau}}
+
+
+def stream_report(w, d, pool, stream, triggers=11, tau=64, per_window=16):
+    """A decode session over growing caches (pipeline.StreamingSession) on the
+    workload's inputs: the caches start with all but the last
+    per_window * (triggers - 1) entries, the host loop triggers every tau steps
+    and appends each finished window's entries first; survivors are fetched
+    from a pinned host copy of the pool into N/2 resident slots with reuse.
+    Each trigger is timed with events (append + trigger + fetch + gather); the
+    first trigger's fetch is cold, the later ones are deltas."""
+    import numpy as np
+    import torch
+    import lsa_inputs as gen
+    from sparse_kv_cache_lsa_amd.pipeline import StreamingSession
+
+    N_cap, B = w.N, w.B
+    N0 = N_cap - per_window * (triggers - 1)
+    cold = torch.empty(pool.shape, dtype=pool.dtype, pin_memory=True)
+    cold.copy_(pool)
+    sess = StreamingSession(w.L, B, N_cap, w.H, w.dI, w.k, w.row_elems, N_cap // 2, cold,
+                            key_dtype=w.key_dtype, tau=tau, per_window=per_window)
+    sess.append([k[:, :N0].contiguous() for k in d["keys"]],
+                None if d["scale"] is None else [s[:, :N0].contiguous() for s in d["scale"]],
+                stream=stream)
+    hs = gen.drift_hidden(w, triggers)
+    hd = [torch.from_numpy(h.view(np.int16)).to("cuda").view(torch.bfloat16) for h in hs]
+    win = []
+    for i in range(1, triggers):
+        lo, hi = N0 + per_window * (i - 1), N0 + per_window * i
+        win.append(([k[:, lo:hi].contiguous() for k in d["keys"]],
+                    None if d["scale"] is None else [s[:, lo:hi].contiguous() for s in d["scale"]]))
+    torch.cuda.synchronize()
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    marks = []
+
+    def window_source(i):
+        e = ev()
+        e.record(stream)
+        marks.append(e)
+        return win[i - 1]
+
+    per = []
+
+    def on_trigger(i, t):
+        torch.cuda.synchronize()
+        per.append({"step": t, "N": sess.N,
+                    "survivors_mean": float(sess.surv_count.float().mean().item()),
+                    "rows_fetched": int(sess.res.fetch_count.sum().item())})
+
+    e0 = ev()
+    e0.record(stream)
+    marks.append(e0)
+    ends = []
+
+    def on_trigger_timed(i, t):
+        e = ev()
+        e.record(stream)
+        ends.append(e)
+        on_trigger(i, t)
+
+    T = tau * (triggers - 1) + 1
+    sess.decode(T, lambda i: hd[i], d["Wp"], d["bias"], window_source, on_trigger_timed,
+                stream=stream)
+    torch.cuda.synchronize()
+    starts = [marks[0]] + marks[1:]
+    ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    for r, m in zip(per, ms):
+        r["ms"] = m
+        r["survivor_fraction"] = r["survivors_mean"] / r["N"]
+    delta = [r["ms"] for r in per[1:]]
+    return {"requests": B, "triggers": triggers, "tau": tau, "entries_per_window": per_window,
+            "N_first": N0, "N_last": sess.N,
+            "cold_first_trigger_ms": per[0]["ms"],
+            "delta_trigger_ms_median": float(np.median(delta)) if delta else None,
+            "per_trigger": per}
+
+
+def growth_report(threads, lengths=(16384, 32768, 65536, 131072, 262144)):
+    """Survivors as the context grows around a fixed relevant set (workload
+    growth1m: the planted entries lie in the first 16,384 of 262,144): one
+    trigger over each prefix of the caches (lsa_score_strided), mean survivors
+    per request and their fraction of N."""
+    import numpy as np
+    import torch
+    import lsa_inputs as gen
+    import sparse_kv_cache_lsa_amd as lsa
+    from sparse_kv_cache_lsa_amd.pipeline import TriggerBuffers, pack_weights
+
+    w = gen.WORKLOADS["growth1m"]
+    inp = gen.indexer_inputs(w, gen.load_calibration(w), threads=threads)
+    d = gen.to_device(inp, "cuda")
+    wp = pack_weights(d["Wq"], d["Wg"])
+    out = []
+    for N in lengths:
+        buf = TriggerBuffers.allocate(w.L, w.B, N, w.H, w.dI, w.k, w.row_elems)
+        lsa.lsa_project_query_packed(d["h"], wp, buf.q, buf.g)
+        lsa.lsa_score_strided(d["keys"], d["scale"], buf.q, buf.g, d["bias"], N, buf.mask,
+                              buf.cand_idx, buf.cand_z, buf.cand_count)
+        lsa.lsa_select_or_compact(buf.cand_idx, buf.cand_z, buf.cand_count, N, buf.surv_idx,
+                                  buf.surv_z, buf.surv_count)
+        torch.cuda.synchronize()
+        m = float(buf.surv_count.float().mean().item())
+        out.append({"N": N, "context_tokens": 4 * N, "survivors_mean": m,
+                    "survivor_fraction": m / N})
+    return {"workload": w.name, "relevant_within_first": w.plant_within, "requests": w.B,
+            "points": out}
 
 
 def cold_fetch(w, d, pool, buf, stream, step, ms_per_step):

@@ -58,6 +58,7 @@ class Workload:
     layers: tuple = (10, 12, 20)
     calib_rows: int = 0   # rows per (layer, request) used to set the bias; 0 = all
     seed: int = 0
+    plant_within: int = 0  # planted entries only among the first this many; 0 = all N
 
     @property
     def triples(self) -> int:
@@ -89,6 +90,14 @@ WORKLOADS = {
                       key_dtype="e4m3", k=2048, row_elems=512,
                       planted=(0.10, 0.10, 0.10), core=0.05,
                       sel_frac=_sel((0.10, 0.10, 0.10)), calib_rows=8192),
+    # a fixed relevant set (10% of the first 16,384 entries, i.e. of a 64K-token
+    # context) inside a context that grows to 1M tokens: the bias passes ~2% of
+    # the other entries, as in ctx1m
+    "growth1m": Workload("growth1m", 6, B=4, L=3, N=262144, H=64, dI=128, D=4096,
+                         key_dtype="e4m3", k=2048, row_elems=512,
+                         planted=(0.10, 0.10, 0.10), core=0.05,
+                         sel_frac=_sel((0.10, 0.10, 0.10)), calib_rows=16384,
+                         plant_within=16384),
 }
 
 
@@ -162,16 +171,20 @@ def weights(w: Workload, l: int):
 
 def planted_sets(w: Workload, b: int):
     """Planted-relevant entries of request b: bool [L][N] and the cosine of
-    each entry with the planting direction, float64 [L][N] (~U(0.5, 0.7))."""
+    each entry with the planting direction, float64 [L][N] (~U(0.5, 0.7)).
+    The planted fractions apply to the first plant_within entries when the
+    workload sets it (a fixed relevant set in a context that keeps growing),
+    else to all N."""
     r = stream(w.seed, w.wid, b, _ALL, "plant")
-    n_core = int(round(w.core * w.N))
-    perm = r.permutation(w.N)
+    M = w.plant_within or w.N     # entries the planted set is drawn from
+    n_core = int(round(w.core * M))
+    perm = r.permutation(M)
     core = perm[:n_core]
     rest = perm[n_core:]
     mask = np.zeros((w.L, w.N), bool)
     for l in range(w.L):
         mask[l, core] = True
-        n_extra = max(0, int(round((w.planted[l] - w.core) * w.N)))
+        n_extra = max(0, int(round((w.planted[l] - w.core) * M)))
         extra = r.choice(rest, size=min(n_extra, rest.size), replace=False)
         mask[l, extra] = True
     cos = r.uniform(0.5, 0.7, size=(w.L, w.N))

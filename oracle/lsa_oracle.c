@@ -516,3 +516,26 @@ void lsa_or_attention(int64_t n, int D, int H, const uint16_t* q,
     free(s);
   }
 }
+
+/* ------------------------------------------------------------------------ */
+/* O13 fine-grained score inside the fetched set                             */
+/* ------------------------------------------------------------------------ */
+
+void lsa_or_lightning(int N, int H, int dI, int key_dtype, const void* keys,
+                      const float* scale, const uint16_t* q, const float* w,
+                      const int32_t* idx, int64_t n, double* out) {
+  (void)N;
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) {
+    const int64_t s = idx[i];
+    const double sigma = (key_dtype == 1 && scale) ? (double)scale[s] : 1.0;
+    double acc = 0.0;
+    for (int hh = 0; hh < H; ++hh) {
+      double dot = 0.0;
+      for (int d = 0; d < dI; ++d)
+        dot += lsa_or_bf16_to_double(q[hh * dI + d]) * key_value(key_dtype, keys, s * dI + d);
+      acc += (double)w[hh] * fmax(0.0, dot * sigma);
+    }
+    out[i] = acc;
+  }
+}

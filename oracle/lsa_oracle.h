@@ -149,6 +149,18 @@ void lsa_or_attention(int64_t n, int D, int H, const uint16_t* q,
                       const uint16_t* rows, double scale, double* out,
                       double* wabs);
 
+/* ---- O13: fine-grained score inside the fetched set ([SUMMARY] 2.1
+ * hierarchical-selection bullet: the top-k inside the fetched subset uses the
+ * model's native Lightning Indexer, which the pages name but do not define).
+ * Reading: the published form of that indexer, one score per entry from its
+ * own keys and a per-query set of heads with ReLU gates and weights:
+ *   out_i = sum_h w[h] * max(0, sum_d q[h][d] * k[s_i][d] * sigma_{s_i}),  s_i = idx[i]
+ * key_dtype 0: bf16 keys [N][dI] (sigma = 1); 1: e4m3 keys with fp32 scale
+ * [N].  q: bf16 [H][dI]; w: fp32 [H]; idx: the n entries to score. */
+void lsa_or_lightning(int N, int H, int dI, int key_dtype, const void* keys,
+                      const float* scale, const uint16_t* q, const float* w,
+                      const int32_t* idx, int64_t n, double* out);
+
 /* ---- trigger cadence ([SUMMARY] 2.1 periodic-trigger bullet; [REVIEW]
  * section 2): the indexer runs at decode step t iff t is a multiple of tau,
  * counting from step 0. */

@@ -77,6 +77,7 @@ def _load():
         "lsa_or_set_num_threads": (None, [i32]),
         "lsa_or_trigger_due": (i32, [i64, i32]),
         "lsa_or_attention": (None, [i64, i32, i32, P, P, f64, P, P]),
+        "lsa_or_lightning": (None, [i32, i32, i32, i32, P, P, P, P, P, i64, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -334,6 +335,24 @@ def attention(q, rows, scale: float, want_wabs: bool = False):
                          _p(wabs))
     return (out, wabs) if want_wabs else out
 
+
+
+def lightning(keys, scale, q, w, idx) -> np.ndarray:
+    """Fine-grained score of the entries idx: keys [N][dI] (bf16 bits, or
+    e4m3 codes with scale fp32 [N]), q bf16 [H][dI], w fp32 [H] ->
+    sum_h w_h * relu(q_h . k_s * sigma_s), fp64 [n]."""
+    lib = _load()
+    kdt = 0 if keys.dtype == np.uint16 else 1
+    keys = np.ascontiguousarray(keys)
+    q = _c(q, np.uint16)
+    w = _c(w, np.float32)
+    idx = _c(idx, np.int32)
+    H, dI = q.shape
+    out = np.empty(max(idx.shape[0], 1), np.float64)
+    sc = None if scale is None else _c(scale, np.float32)
+    lib.lsa_or_lightning(keys.shape[0], H, dI, kdt, _p(keys), _p(sc), _p(q), _p(w), _p(idx),
+                         idx.shape[0], _p(out))
+    return out[:idx.shape[0]].copy()
 
 # ---- O12 decode session over a growing key cache --------------------------
 

@@ -19,7 +19,8 @@ ROOT = os.path.dirname(HERE)
 SRC = os.path.join(ROOT, "oracle", "lsa_oracle.c")
 PINS = [os.path.join(HERE, f) for f in ("test_oracle_formats.py", "test_oracle_score.py",
                                         "test_oracle_select.py", "test_oracle_labels.py",
-                                        "test_oracle_fetch.py", "test_oracle_attention.py")]
+                                        "test_oracle_fetch.py", "test_oracle_attention.py",
+                                        "test_oracle_lightning.py")]
 
 # (name, exact snippet of lsa_oracle.c, planted replacement)
 MUTANTS = [
@@ -37,8 +38,8 @@ MUTANTS = [
      "      z += dot;\n    }\n    z_out[i]"),
     ("score drops the key scale", "z_out[i] = z * sigma + bias;", "z_out[i] = z + bias;"),
     ("score bias sign", "z_out[i] = z * sigma + bias;", "z_out[i] = z * sigma - bias;"),
-    ("score transposed key index", "key_value(key_dtype, keys, s * dI + d)",
-     "key_value(key_dtype, keys, d * (int64_t)N + s)"),
+    ("score transposed key index", "*\n               key_value(key_dtype, keys, s * dI + d)",
+     "*\n               key_value(key_dtype, keys, d * (int64_t)N + s)"),
     ("threshold exclusive", "sel[i] = (z[i] >= 0.0) ? 1 : 0;", "sel[i] = (z[i] > 0.0) ? 1 : 0;"),
     ("union reads only layer 0", "if (sel[(int64_t)l * N + s]) any = 1;",
      "if (sel[(int64_t)l * N + s] && l == 0) any = 1;"),
@@ -75,6 +76,12 @@ MUTANTS = [
      "               lsa_or_bf16_to_double(rows[(int64_t)d * n + j]);\n      s[j]"),
     ("attention value from the query", "        double v = lsa_or_bf16_to_double(rows[j * D + d]);",
      "        double v = lsa_or_bf16_to_double(q[(int64_t)hh * D + d]);"),
+    ("lightning without the relu", "acc += (double)w[hh] * fmax(0.0, dot * sigma);",
+     "acc += (double)w[hh] * (dot * sigma);"),
+    ("lightning without the head weight", "acc += (double)w[hh] * fmax(0.0, dot * sigma);",
+     "acc += fmax(0.0, dot * sigma);"),
+    ("lightning scores the list position", "    const int64_t s = idx[i];\n    const double sigma = (key_dtype == 1 && scale)",
+     "    const int64_t s = i;\n    const double sigma = (key_dtype == 1 && scale)"),
     ("attention drops the last row", "    for (int64_t j = 0; j < n; ++j) {\n      double p = s[j] / sum;",
      "    for (int64_t j = 0; j + 1 < n; ++j) {\n      double p = s[j] / sum;"),
 ]

@@ -286,6 +286,7 @@ def main():
 
     if not args.no_attention and w.row_elems == 512:
         result["attention"] = attention_report(w, buf, stream, step, ms_per_step)
+        result["fine_topk"] = fine_topk_report(w, buf, stream, args.threads)
 
     if not args.no_cold_fetch:
         result["cold_fetch"] = cold_fetch(w, d, pool, buf, stream, step, ms_per_step)
@@ -297,6 +298,60 @@ def main():
     if not args.skip_cpu:
         result["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def fine_topk_report(w, buf, stream, threads, launches=20):
+    """The top-k ranked by the fine-grained score inside the fetched set
+    (lsa_lightning_score over the last trigger's survivors, then lsa_topk over
+    those scores): 64 heads of 128 dims with their own e4m3 keys (+ fp32
+    scale) per entry.  Mean of `launches` back-to-back pairs between two
+    events; its own rooflines (each survivor's key row and scale read once)."""
+    import numpy as np
+    import torch
+    import lsa_inputs as gen
+    import sparse_kv_cache_lsa_amd as lsa
+
+    li = gen.lightning_inputs(w, key_dtype="e4m3", threads=threads)
+    dev = "cuda"
+    keys = torch.from_numpy(li.keys).to(dev)
+    scale = torch.from_numpy(li.scale).to(dev)
+    q = torch.from_numpy(li.q.view(np.int16)).to(dev).view(torch.bfloat16)
+    wt = torch.from_numpy(li.w).to(dev)
+    score = torch.empty_like(buf.surv_z)
+    ti, tc = torch.empty_like(buf.topk_idx), torch.empty_like(buf.topk_count)
+
+    def run(which):
+        if which & 1:
+            lsa.lsa_lightning_score(keys, scale, q, wt, buf.surv_idx, buf.surv_count, score,
+                                    stream=stream)
+        if which & 2:
+            lsa.lsa_topk(buf.surv_idx, score, buf.surv_count, ti, tc, buf.ws_topk, stream=stream)
+
+    def timed(which):
+        for _ in range(3):
+            run(which)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(launches):
+            run(which)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / launches
+
+    both = timed(3)
+    score_ms = timed(1)
+    surv = int(buf.surv_count.sum().item())
+    H, dI = li.q.shape[1], li.q.shape[2]
+    nbytes = surv * (dI + 4 + 4 + 4) + w.B * H * (2 * dI + 4)   # key row + scale + index + score
+    flops = 2.0 * H * dI * surv
+    return {"kernel": "lsa_lightning_score", "heads": H, "head_dim": dI, "key_dtype": "e4m3",
+            "survivors": surv, "score_ms": score_ms, "score_plus_topk_ms": both,
+            "launches": launches, "algorithmic_bytes": nbytes,
+            "GB/s": nbytes / (score_ms * 1e-3) / 1e9,
+            "frac_hbm": nbytes / (score_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "TFLOP/s": flops / (score_ms * 1e-3) / 1e12,
+            "frac_bf16_mfma": flops / (score_ms * 1e-3) / 1e12 / 2500.0}
 
 
 def attention_report(w, buf, stream, step, ms_per_step, launches=20, tau=64):

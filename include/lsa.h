@@ -307,6 +307,32 @@ lsa_status lsa_topk_noalloc(int B, int cap, int k, const int32_t* surv_idx,
                             int32_t* topk_idx, int32_t* topk_count, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * Fine-grained score inside the fetched set ([SUMMARY] 2.1 hierarchical-
+ * selection bullet: once the selected subset is on the GPU, the model's
+ * native Lightning Indexer picks the final top-k inside it; the pages name it
+ * without a formula).  This library's reading is that indexer's published
+ * form: its own key per entry, and per query H heads with ReLU gates and
+ * weights.  For every request b and i < min(surv_count[b], cap):
+ *   score[b][i] = sigma_s * sum_h w[b][h] * max(0, q[b][h] . k[b][s]),
+ *   s = surv_idx[b][i],  sigma_s = key_scale[b][s] (e4m3) or 1 (bf16)
+ * (-inf for an index outside [0, N)).  Products of bf16 values are exact
+ * (e4m3 widens exactly to bf16), sums in fp32.  Rank with lsa_topk(surv_idx,
+ * score, surv_count, ...).
+ *
+ *   keys       [B][N][dI] bf16 or e4m3 (the indexer's own keys), 16-byte aligned
+ *   key_scale  fp32 [B][N] (e4m3; positive), NULL for bf16
+ *   q          bf16 [B][H][dI]      w  fp32 [B][H]
+ *   surv_idx   int32 [B][cap]       surv_count int32 [B]
+ *   score      out fp32 [B][cap] (slots past the count are not written)
+ * Limits: 1 <= B <= 65535, 0 <= N <= 2^24, cap >= 0, H a multiple of 16 in
+ * [16, 64], dI in {64, 128}, one request's keys below 2^31 bytes.
+ */
+lsa_status lsa_lightning_score(int B, int N, int cap, int H, int dI, lsa_key_dtype kdt,
+                               const void* keys, const float* key_scale, const uint16_t* q,
+                               const float* w, const int32_t* surv_idx,
+                               const int32_t* surv_count, float* score, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * Hot-pool gather ([SUMMARY] 2.1 dynamic-fetch bullet: the selected
  * compressed KV entries are brought into GPU memory).
  *   hot[b][j] = pool[b][idx[b][j]]  (row_bytes bytes), zero row when

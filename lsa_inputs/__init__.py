@@ -30,7 +30,7 @@ GENERATOR_VERSION = 4
 
 _TAGS = {"h": 1, "wq": 2, "wg": 3, "plant": 4, "keys": 5, "logits": 6,
          "student": 7, "misc": 8, "att_q": 9, "att_rows": 10, "att_win": 11,
-         "h_drift": 12}
+         "h_drift": 12, "light_q": 13, "light_keys": 14}
 _ALL = 0xFFFF  # "not per request / not per layer" slot in the seed tuple
 
 
@@ -474,3 +474,59 @@ def drift_hidden(w: Workload, n: int, cosine: float = 0.97) -> np.ndarray:
                           for b in range(w.B)])
         h[i] = to_bf16_bits(np.float32(cosine) * prev + np.float32(s) * noise)
     return h
+
+
+# ---------------------------------------------------------------------------
+# fine-grained score inside the fetched set (its own keys and query heads)
+# ---------------------------------------------------------------------------
+
+LIGHT_HEADS = 64
+LIGHT_DIM = 128
+
+
+@dataclass
+class LightningInputs:
+    q: np.ndarray       # bf16 bits [B][H][dI]
+    w: np.ndarray       # fp32 [B][H]
+    keys: np.ndarray    # bf16 bits or e4m3 codes [B][N][dI]
+    scale: object       # fp32 [B][N] (e4m3) or None
+
+
+def lightning_inputs(w: Workload, H: int = LIGHT_HEADS, dI: int = LIGHT_DIM,
+                     key_dtype: str | None = None, threads: int = 8) -> LightningInputs:
+    """Per request: a direction u ~ N(0, I); H query heads u + N(0, I) (the
+    heads agree with u more or less); head weights U(0, 1); keys N(0, I/dI),
+    with the request's planted entries (layer 0's planted set) turned to
+    cosine U(0.5, 0.7) with u, as the indexer keys are.  Stored bf16 or e4m3
+    with a per-entry scale."""
+    from concurrent.futures import ThreadPoolExecutor
+    kdt = w.key_dtype if key_dtype is None else key_dtype
+    B, N = w.B, w.N
+    q = np.empty((B, H, dI), np.uint16)
+    wt = np.empty((B, H), np.float32)
+    keys_out = np.empty((B, N, dI), np.uint16 if kdt == "bf16" else np.uint8)
+    scale = None if kdt == "bf16" else np.empty((B, N), np.float32)
+
+    def one(b):
+        r = stream(w.seed, w.wid, b, _ALL, "light_q")
+        u = r.standard_normal(dI)
+        q[b] = to_bf16_bits((u[None, :] + r.standard_normal((H, dI))).astype(np.float32))
+        wt[b] = r.uniform(0.0, 1.0, H).astype(np.float32)
+        x = stream(w.seed, w.wid, b, _ALL, "light_keys").standard_normal((N, dI), dtype=np.float32)
+        x *= np.float32(1.0 / math.sqrt(dI))
+        mask, cos = planted_sets(w, b)
+        sel = np.nonzero(mask[0])[0]
+        uu = u / np.linalg.norm(u)
+        kp = x[sel].astype(np.float64)
+        kp -= np.outer(kp @ uu, uu)
+        c = cos[0, sel]
+        t = c / np.sqrt(1.0 - c * c) * np.linalg.norm(kp, axis=1)
+        x[sel] = (kp + np.outer(t, uu)).astype(np.float32)
+        if kdt == "bf16":
+            keys_out[b] = to_bf16_bits(x)
+        else:
+            keys_out[b], scale[b] = to_e4m3_rows(x)
+
+    with ThreadPoolExecutor(max_workers=max(1, threads)) as ex:
+        list(ex.map(one, range(B)))
+    return LightningInputs(q=q, w=wt, keys=keys_out, scale=scale)

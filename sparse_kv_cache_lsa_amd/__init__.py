@@ -19,7 +19,8 @@ __all__ = [
     "lsa_pack_query_weights", "lsa_project_query_packed", "lsa_score", "lsa_score_strided",
     "lsa_append_rows", "lsa_select_or_compact",
     "lsa_select_or_compact_masks_workspace_bytes", "lsa_select_or_compact_masks",
-    "lsa_topk_workspace_bytes", "lsa_topk", "lsa_topk_noalloc", "lsa_gather_hot", "lsa_fetch_workspace_bytes",
+    "lsa_topk_workspace_bytes", "lsa_topk", "lsa_topk_noalloc", "lsa_lightning_score",
+    "lsa_gather_hot", "lsa_fetch_workspace_bytes",
     "lsa_resident_reset", "lsa_fetch_survivors", "lsa_gather_resident",
     "lsa_sparse_attention_workspace_bytes", "lsa_sparse_attention",
     "lsa_label_vote_workspace_bytes", "lsa_label_vote",
@@ -348,6 +349,33 @@ def lsa_topk_noalloc(surv_idx, surv_z, surv_count, topk_idx, topk_count, *, stre
     _dev(surv_idx, surv_z, surv_count, topk_idx, topk_count)
     check(load().lsa_topk_noalloc(B, cap, k, _p(surv_idx), _p(surv_z), _p(surv_count),
                                   _p(topk_idx), _p(topk_count), _stream(stream)))
+
+
+def lsa_lightning_score(keys, key_scale, q, w, surv_idx, surv_count, score, *, stream=None):
+    """keys [B][N][dI] (bf16, or e4m3 codes with key_scale f32 [B][N]), q bf16
+    [B][H][dI], w f32 [B][H], surv_idx i32 [B][cap], surv_count i32 [B] ->
+    score f32 [B][cap]."""
+    fn = "lsa_lightning_score"
+    fp8 = key_scale is not None
+    B, N, dI = keys.shape
+    H = q.shape[1]
+    cap = surv_idx.shape[1]
+    _expect(fn, "q", q, (B, H, dI))
+    _expect(fn, "w", w, (B, H))
+    _expect(fn, "key_scale", key_scale, (B, N))
+    _expect(fn, "surv_count", surv_count, (B,))
+    _expect(fn, "score", score, (B, cap))
+    if keys.element_size() != (1 if fp8 else 2):
+        raise ValueError(f"{fn}: keys must be 1-byte e4m3 codes (with key_scale) or 2-byte bf16")
+    _dtype(fn, "q", q, "bfloat16", "int16", "uint16")
+    for name, t in (("w", w), ("key_scale", key_scale), ("score", score)):
+        _dtype(fn, name, t, "float32")
+    _dtype(fn, "surv_idx", surv_idx, "int32")
+    _dtype(fn, "surv_count", surv_count, "int32")
+    _dev(keys, key_scale, q, w, surv_idx, surv_count, score)
+    check(load().lsa_lightning_score(B, N, cap, H, dI, LSA_KEY_FP8_E4M3 if fp8 else LSA_KEY_BF16,
+                                     _p(keys), _p(key_scale), _p(q), _p(w), _p(surv_idx),
+                                     _p(surv_count), _p(score), _stream(stream)))
 
 
 def lsa_gather_hot(pool, idx, hot, *, stream=None):

@@ -43,6 +43,7 @@ SIGNATURES = {
     "lsa_topk_workspace_bytes": (SZ, [I32, I32, I32]),
     "lsa_topk": (I32, [I32, I32, I32, P, P, P, P, P, P, SZ, P]),
     "lsa_topk_noalloc": (I32, [I32, I32, I32, P, P, P, P, P, P]),
+    "lsa_lightning_score": (I32, [I32, I32, I32, I32, I32, I32, P, P, P, P, P, P, P, P]),
     "lsa_gather_hot": (I32, [I32, I32, I32, I32, P, P, P, P]),
     "lsa_sparse_attention_workspace_bytes": (SZ, [I32, I32, I32, I32, I32]),
     "lsa_sparse_attention": (I32, [I32, I32, I32, I32, I32, C.c_float, P, P, P, P, P, P, P, SZ,

@@ -323,6 +323,33 @@ lsa_status lsa_topk_noalloc(int B, int cap, int k, const int32_t* surv_idx,
                     "lsa_topk_noalloc launch");
 }
 
+// ------------------------------------------------- fine-grained score
+
+lsa_status lsa_lightning_score(int B, int N, int cap, int H, int dI, lsa_key_dtype kdt,
+                               const void* keys, const float* key_scale, const uint16_t* q,
+                               const float* w, const int32_t* surv_idx,
+                               const int32_t* surv_count, float* score, hipStream_t stream) {
+  const char* fn = "lsa_lightning_score";
+  REQUIRE(kdt == LSA_KEY_BF16 || kdt == LSA_KEY_FP8_E4M3, LSA_E_DTYPE, "%s: unknown key dtype %d",
+          fn, (int)kdt);
+  REQUIRE(B >= 1 && B <= 65535, LSA_E_SHAPE, "%s: B=%d not in [1,65535]", fn, B);
+  REQUIRE(N >= 0 && N <= (1 << 24) && cap >= 0, LSA_E_SHAPE, "%s: N=%d, cap=%d", fn, N, cap);
+  REQUIRE(H >= 16 && H <= 64 && H % 16 == 0, LSA_E_SHAPE,
+          "%s: H=%d not a multiple of 16 in [16,64]", fn, H);
+  REQUIRE(dI == 64 || dI == 128, LSA_E_SHAPE, "%s: dI=%d not 64 or 128", fn, dI);
+  REQUIRE((int64_t)N * dI * (kdt == LSA_KEY_BF16 ? 2 : 1) < ((int64_t)1 << 31), LSA_E_SHAPE,
+          "%s: keys of one request must stay below 2^31 bytes", fn);
+  REQUIRE(surv_count, LSA_E_ARG, "%s: null surv_count", fn);
+  if (cap == 0) return LSA_OK;
+  REQUIRE(keys && q && w && surv_idx && score, LSA_E_ARG, "%s: null pointer argument", fn);
+  REQUIRE(kdt == LSA_KEY_BF16 || key_scale, LSA_E_ARG, "%s: e4m3 keys need key_scale", fn);
+  REQUIRE(aligned16(keys) && aligned16(q) && ((uintptr_t)w & 3u) == 0, LSA_E_ARG,
+          "%s: keys and q must be 16-byte aligned, w 4-byte aligned", fn);
+  return hip_status(lsa::launch_lightning(B, N, cap, H, dI, kdt, keys, key_scale, q, w,
+                                          surv_idx, surv_count, score, stream),
+                    "lsa_lightning_score launch");
+}
+
 // -------------------------------------------------------------------- gather
 
 lsa_status lsa_gather_hot(int B, int N, int k, int row_bytes, const void* pool,

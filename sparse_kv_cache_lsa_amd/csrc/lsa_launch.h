@@ -99,6 +99,11 @@ hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s);
 hipError_t launch_append_rows(int B, int n, int row_bytes, const void* src, int64_t src_stride,
                               void* dst, int64_t dst_stride, int64_t dst_start, hipStream_t s);
 
+hipError_t launch_lightning(int B, int N, int cap, int H, int dI, lsa_key_dtype kdt,
+                            const void* keys, const float* scale, const uint16_t* q,
+                            const float* w, const int32_t* surv_idx, const int32_t* surv_count,
+                            float* score, hipStream_t s);
+
 int attention_splits(int B, int H, int k, int W);
 size_t attention_workspace_bytes(int B, int H, int D, int k, int W);
 hipError_t launch_attention(int B, int H, int k, int W, float scale, const uint16_t* q,

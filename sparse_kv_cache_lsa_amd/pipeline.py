@@ -8,7 +8,8 @@ from __future__ import annotations
 from dataclasses import dataclass
 
 from . import (LSA_CAND_CHUNK, lsa_append_rows, lsa_fetch_survivors, lsa_fetch_workspace_bytes,
-               lsa_gather_hot, lsa_gather_resident, lsa_pack_query_weights, lsa_project_query,
+               lsa_gather_hot, lsa_gather_resident, lsa_lightning_score, lsa_pack_query_weights,
+               lsa_project_query,
                lsa_project_query_packed, lsa_query_weights_packed_bytes, lsa_resident_reset,
                lsa_score, lsa_score_strided, lsa_select_or_compact, lsa_topk,
                lsa_topk_workspace_bytes)
@@ -72,11 +73,14 @@ def pack_weights(Wq, Wg, stream=None):
 
 
 def run_trigger(buf: TriggerBuffers, h, Wq, Wg, keys, key_scale, bias, pool=None, *,
-                stream=None, project=True, z_layers=None, packed=None):
+                stream=None, project=True, z_layers=None, packed=None, fine=None):
     """One indexer trigger.  With project=False the query buffers are used as
     they are (the caller filled buf.q / buf.g); with packed (pack_weights)
     the projection reads the packed weights.  z_layers: optional f32
-    [L][B][N] that receives every layer's logit (extra write traffic)."""
+    [L][B][N] that receives every layer's logit (extra write traffic).
+    fine: optional (keys, key_scale, q, w, score) of the fine-grained
+    indexer; the top-k then ranks the survivors by lsa_lightning_score
+    (written to score [B][cap]) instead of their merged logit."""
     if project and packed is not None:
         lsa_project_query_packed(h, packed, buf.q, buf.g, stream=stream)
     elif project:
@@ -85,8 +89,12 @@ def run_trigger(buf: TriggerBuffers, h, Wq, Wg, keys, key_scale, bias, pool=None
               buf.cand_count, z_layers, stream=stream)
     lsa_select_or_compact(buf.cand_idx, buf.cand_z, buf.cand_count, buf.N, buf.surv_idx,
                           buf.surv_z, buf.surv_count, stream=stream)
-    lsa_topk(buf.surv_idx, buf.surv_z, buf.surv_count, buf.topk_idx, buf.topk_count,
-             buf.ws_topk, stream=stream)
+    rank = buf.surv_z
+    if fine is not None:
+        fk, fs, fq, fw, rank = fine
+        lsa_lightning_score(fk, fs, fq, fw, buf.surv_idx, buf.surv_count, rank, stream=stream)
+    lsa_topk(buf.surv_idx, rank, buf.surv_count, buf.topk_idx, buf.topk_count, buf.ws_topk,
+             stream=stream)
     if pool is not None:
         lsa_gather_hot(pool, buf.topk_idx, buf.hot, stream=stream)
 

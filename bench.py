@@ -26,14 +26,35 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak, GB/s
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "lsa_score_ctx1m_traffic.json")
+PROFILE_TRAFFIC_LABELS = os.path.join(ROOT, "profiles", "lsa_label_vote_labels128k_traffic.json")
 
 
-def score_source_hash() -> str:
+def source_hash(files) -> str:
     h = hashlib.sha256()
-    for f in ("lsa_score.hip", "lsa_device.h", "lsa_launch.h"):
+    for f in files:
         with open(os.path.join(ROOT, "sparse_kv_cache_lsa_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
+
+
+def score_source_hash() -> str:
+    return source_hash(("lsa_score.hip", "lsa_device.h", "lsa_launch.h"))
+
+
+def labels_source_hash() -> str:
+    return source_hash(("lsa_labels.hip", "lsa_device.h", "lsa_launch.h"))
+
+
+def counter_traffic(path, source_hash_now, workload):
+    """Counter-derived HBM bytes per launch from a committed profile summary,
+    used only while the kernel sources hash the same; else None."""
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        tr = json.load(f)
+    if tr.get("kernel_source_hash") == source_hash_now and tr.get("workload") == workload:
+        return tr.get("traffic_bytes_per_launch")
+    return None
 
 
 def parse():
@@ -208,12 +229,7 @@ def main():
     achieved = key_bytes / (mean_score * 1e-3) / 1e9
     ss_gbs = key_bytes / (score_select * 1e-3) / 1e9
 
-    traffic = None
-    if os.path.exists(PROFILE_TRAFFIC):
-        with open(PROFILE_TRAFFIC) as f:
-            tr = json.load(f)
-        if tr.get("kernel_source_hash") == score_source_hash() and tr.get("workload") == w.name:
-            traffic = tr.get("traffic_bytes_per_launch")
+    traffic = counter_traffic(PROFILE_TRAFFIC, score_source_hash(), w.name)
 
     counts = buf.surv_count.cpu().numpy()
     result = {
@@ -272,17 +288,7 @@ def main():
         del x
 
     if args.copy_probe:
-        # plain copy of known size for hardware-counter calibration: the row
-        # gather with the identity index list reads and writes exactly
-        # rows * 1 KiB (plus the 4-byte indices)
-        rows = (args.copy_probe << 20) // 1024
-        src = torch.zeros((1, rows, 512), dtype=torch.int16, device=dev)
-        dst = torch.empty_like(src)
-        ident = torch.arange(rows, dtype=torch.int32, device=dev).reshape(1, rows)
-        lsa.lsa_gather_hot(src, ident, dst, stream=stream)
-        torch.cuda.synchronize()
-        result["copy_probe"] = {"kernel": "gather_kernel (identity index list)",
-                                "read_bytes": rows * 1024 + rows * 4, "write_bytes": rows * 1024}
+        result["copy_probe"] = copy_probe(args.copy_probe, stream)
 
     if not args.no_attention and w.row_elems == 512:
         result["attention"] = attention_report(w, buf, stream, step, ms_per_step)
@@ -719,7 +725,9 @@ def bench_labels(args):
                    "top_p": w.top_p, "theta": w.theta, "gamma": w.gamma, "heads": w.H,
                    "head_dim": w.dI, "hidden": w.D, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": vote_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": vote_gbs / HBM_PEAK_GBS, "traffic": None, "kernel": "lsa_label_vote",
+                     "frac": vote_gbs / HBM_PEAK_GBS,
+                     "traffic": counter_traffic(PROFILE_TRAFFIC_LABELS, labels_source_hash(), w.name),
+                     "kernel": "lsa_label_vote",
                      "algorithmic_bytes_per_launch": vote_bytes, "mean_launch_ms": vote_mean,
                      "timed_launches_sampled": len(vote_ms)},
         "focal": {"bound": "mfma", "achieved": focal_tfs, "peak": 157.3, "unit": "TFLOP/s",
@@ -730,9 +738,27 @@ def bench_labels(args):
         "loss": float(loss.item()),
         "positive_label_fraction": float(label.float().mean().item()),
     }
+    if args.copy_probe:
+        result["copy_probe"] = copy_probe(args.copy_probe, stream)
     if not args.skip_cpu:
         result["cpu_baseline"] = cpu_baseline_labels(w, x, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def copy_probe(mib, stream):
+    """A plain copy of known size for hardware-counter calibration: the row
+    gather with the identity index list reads and writes exactly rows * 1 KiB
+    (plus the 4-byte indices)."""
+    import torch
+    import sparse_kv_cache_lsa_amd as lsa
+    rows = (mib << 20) // 1024
+    src = torch.zeros((1, rows, 512), dtype=torch.int16, device="cuda")
+    dst = torch.empty_like(src)
+    ident = torch.arange(rows, dtype=torch.int32, device="cuda").reshape(1, rows)
+    lsa.lsa_gather_hot(src, ident, dst, stream=stream)
+    torch.cuda.synchronize()
+    return {"kernel": "gather_kernel (identity index list)",
+            "read_bytes": rows * 1024 + rows * 4, "write_bytes": rows * 1024}
 
 
 def cpu_baseline_labels(w, x, budget_s):

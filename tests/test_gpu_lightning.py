@@ -62,7 +62,8 @@ def _lists(rng, B, N, cap, fracs):
 
 
 @pytest.mark.parametrize("kdt,H,dI,B,N", [("e4m3", 64, 128, 3, 40000), ("bf16", 64, 128, 2, 30000),
-                                          ("bf16", 16, 64, 2, 5000), ("e4m3", 32, 64, 4, 777)])
+                                          ("bf16", 16, 64, 2, 5000), ("e4m3", 32, 64, 4, 777),
+                                          ("e4m3", 48, 128, 3, 3333), ("bf16", 48, 64, 2, 65)])
 def test_lightning_scores_and_topk_match_oracle(kdt, H, dI, B, N):
     w = gen.custom("light", 97 + H + dI, B=B, N=N, H=8, dI=64, D=256, key_dtype=kdt)
     li = gen.lightning_inputs(w, H=H, dI=dI)

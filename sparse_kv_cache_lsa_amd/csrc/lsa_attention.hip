@@ -243,23 +243,48 @@ __global__ __launch_bounds__(512) void attention_kernel(AttArgs a) {
 
 // out[b][h] = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s, M = max_s m_s;
 // no rows at all: zeros.  One block of 128 threads per (request, head), four
-// dims a thread.
+// dims a thread.  Every split's (m, l) and partial output are loaded in one
+// round (up to kCombineMax splits in registers; more in further rounds), and
+// the splits are added in split order.
+constexpr int kCombineMax = 16;
+
 __global__ __launch_bounds__(128) void attention_combine_kernel(AttArgs a) {
   const int b = blockIdx.x, h = blockIdx.y;
   float M = -__builtin_inff();
-  for (int s = 0; s < a.S; ++s)
-    M = fmaxf(M, a.part_ml[2 * (((size_t)s * a.B + b) * a.H + h)]);
   f32x4 o = f32x4{0.f, 0.f, 0.f, 0.f};
   float L = 0.f;
-  if (M != -__builtin_inff()) {
-    for (int s = 0; s < a.S; ++s) {
-      const size_t row = ((size_t)s * a.B + b) * a.H + h;
-      const float ms = a.part_ml[2 * row];
-      if (ms == -__builtin_inff()) continue;
-      const float w = exp2f(ms - M);
-      L += w * a.part_ml[2 * row + 1];
-      o += w * *(const f32x4*)(a.part_o + row * kAttD + 4 * threadIdx.x);
+  for (int s0 = 0; s0 < a.S; s0 += kCombineMax) {
+    float ms[kCombineMax], ls[kCombineMax];
+    f32x4 os[kCombineMax];
+#pragma unroll
+    for (int j = 0; j < kCombineMax; ++j) {
+      const int s = s0 + j;
+      ms[j] = -__builtin_inff();
+      ls[j] = 0.f;
+      os[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (s < a.S) {
+        const size_t row = ((size_t)s * a.B + b) * a.H + h;
+        ms[j] = a.part_ml[2 * row];
+        ls[j] = a.part_ml[2 * row + 1];
+        os[j] = *(const f32x4*)(a.part_o + row * kAttD + 4 * threadIdx.x);
+      }
     }
+    float Mn = M;
+#pragma unroll
+    for (int j = 0; j < kCombineMax; ++j) Mn = fmaxf(Mn, ms[j]);
+    if (Mn == -__builtin_inff()) continue;   // no rows yet
+    // rescale what is summed so far to the new maximum, then add these splits
+    const float r = M == -__builtin_inff() ? 0.f : exp2f(M - Mn);
+    o *= r;
+    L *= r;
+#pragma unroll
+    for (int j = 0; j < kCombineMax; ++j) {
+      if (ms[j] == -__builtin_inff()) continue;
+      const float w = exp2f(ms[j] - Mn);
+      L += w * ls[j];
+      o += w * os[j];
+    }
+    M = Mn;
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
   *(f32x4*)(a.out + ((size_t)b * a.H + h) * kAttD + 4 * threadIdx.x) = o * inv;

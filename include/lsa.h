@@ -460,7 +460,7 @@ lsa_status lsa_gather_resident(int B, int N, int S, int k, int row_bytes, const 
  * exactly in 64-bit integers, so the result is deterministic; it differs
  * from exact arithmetic only for entries whose mass ahead lies within
  * N * 2^-31 (relative) of top_p.
- * Limits: Q >= 1, 1 <= L <= LSA_MAX_VOTE_LAYERS, 1 <= N <= 65536,
+ * Limits: Q >= 1, 1 <= L <= LSA_MAX_VOTE_LAYERS, Q * L < 2^31, 1 <= N <= 65536,
  * 0 < top_p <= 1, theta >= 0.  Errors: LSA_E_SHAPE / LSA_E_ARG for the
  * limits, null or misaligned pointers; LSA_E_WORKSPACE for a missing or
  * short workspace; LSA_E_HIP for a launch failure.

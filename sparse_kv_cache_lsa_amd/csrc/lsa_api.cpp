@@ -514,6 +514,8 @@ lsa_status lsa_label_vote(int Q, int L, int N, float top_p, int theta, const flo
   REQUIRE(L >= 1 && L <= LSA_MAX_VOTE_LAYERS, LSA_E_SHAPE, "lsa_label_vote: L=%d not in [1,%d]", L,
           LSA_MAX_VOTE_LAYERS);
   REQUIRE(N >= 1 && N <= 65536, LSA_E_SHAPE, "lsa_label_vote: N=%d not in [1,65536]", N);
+  REQUIRE((int64_t)Q * L <= 0x7FFFFFFF, LSA_E_SHAPE, "lsa_label_vote: Q*L=%lld rows above 2^31-1",
+          (long long)Q * L);
   REQUIRE(top_p > 0.f && top_p <= 1.f, LSA_E_ARG, "lsa_label_vote: top_p=%g not in (0,1]",
           (double)top_p);
   REQUIRE(theta >= 0, LSA_E_ARG, "lsa_label_vote: theta=%d < 0", theta);

@@ -9,10 +9,15 @@
 // summary, section 2.2 "data curation and labelling", steps 1-3; paper.oopus.info
 // review, section 2, training labels by cross-layer majority vote.)
 //
-// Design.  One 1024-thread block per (query, layer) row; thread i holds the
-// EPT consecutive entries [i*EPT, i*EPT + EPT) in registers, so one thread
-// owns EPT/32 whole selection words and index order is (thread, register)
-// order.  No sort:
+// Design.  A row of up to 32 * 1024 entries is selected by one 1024-thread
+// block: thread i holds the 32 consecutive entries [32 i, 32 i + 32) in
+// registers, so it owns one whole selection word and index order is
+// (thread, register) order.  About one block per compute unit walks rows
+// blockIdx.x, blockIdx.x + gridDim.x, ...; the next row's logits are loaded
+// into a second register set while the current row is selected, and every
+// barrier of the selection waits for LDS only, so those loads stay in flight
+// (a plain block barrier also waits for outstanding vector memory
+// operations).  No sort:
 //  * mass in fixed point: w_s = trunc(exp(x_s - max) * 2^31), summed in 64-bit
 //    integers, so every partial sum is exact and independent of summation
 //    order -- the result is deterministic and the same as a sequential walk
@@ -20,7 +25,8 @@
 //    N * 2^-31 of the largest entry's mass);
 //  * a histogram of mass over 2048 value bins (linear in max - x, so the
 //    bins follow the logit order and hold few entries each) finds the bin in
-//    which the running mass crosses top_p * S;
+//    which the running mass crosses top_p * S (one block scan over the bins
+//    gives S and the mass ahead of every bin);
 //  * the entries of that bin (usually a handful) are compared pairwise in
 //    LDS: each gets its exact mass ahead in the walk order, so it is kept iff
 //    the mass ahead of the bin plus that is below top_p * S;
@@ -28,12 +34,16 @@
 //    instead takes three radix passes over the order key of the logit
 //    (11 + 11 + 10 bits) to find the crossing logit and the mass ahead of
 //    it, and a block prefix sum in index order over the entries with exactly
-//    that logit.
+//    that logit; this path re-reads the row from memory, so the registers
+//    of the common path hold only the two rows.
 // Every other entry is kept iff its bin is ahead of the crossing bin.
-// A second kernel adds the layers' selection words per query into the vote
-// counts and labels.
+// Longer rows (up to 64 * 1024 entries) take one block per row with 64
+// entries a thread and the same arithmetic.  A second kernel adds the
+// layers' selection words per query into the vote counts and labels.
 #include "lsa_device.h"
 #include "lsa_launch.h"
+
+#include <algorithm>
 
 namespace lsa {
 namespace {
@@ -333,6 +343,368 @@ __global__ __launch_bounds__(kNT) void nucleus_kernel(int N, int W, float top_p,
   }
 }
 
+
+// An empty asm the compiler cannot see through: values derived from the
+// result are recomputed where they are used, not kept live across phases.
+__device__ __forceinline__ float opaque(float x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+// A block barrier that waits for this thread's LDS operations only: global
+// loads of the next row stay in flight across it (__syncthreads would wait
+// for every outstanding vector memory operation).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+__device__ __forceinline__ int opaque_i(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+// The helpers below take the thread index as an argument: the row loop passes
+// a copy the compiler cannot see through, so nothing derived from it is kept
+// live across rows (the registers go to the next row's logits).
+__device__ __forceinline__ uint64_t wave_inclusive_scan_u64_t(uint64_t v, int lane) {
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    uint64_t t = __shfl_up(v, off, kWave);
+    if (lane >= off) v += t;
+  }
+  return v;
+}
+
+__device__ __forceinline__ uint64_t block_exclusive_scan_u64_l(uint64_t v, uint64_t* scratch,
+                                                               uint64_t* total, int tid) {
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const uint64_t inc = wave_inclusive_scan_u64_t(v, lane);
+  if (lane == kWave - 1) scratch[wave] = inc;
+  lds_barrier();
+  if (wave == 0) {
+    const uint64_t w = lane < kNWv ? scratch[lane] : 0ull;
+    const uint64_t wi = wave_inclusive_scan_u64_t(w, lane);
+    if (lane < kNWv) scratch[lane] = wi - w;
+    if (lane == kNWv - 1) scratch[kNWv] = wi;
+  }
+  lds_barrier();
+  const uint64_t res = scratch[wave] + inc - v;
+  *total = scratch[kNWv];
+  lds_barrier();
+  return res;
+}
+
+__device__ __forceinline__ void block_max2_l(float& a, float& b, float* scratch, int tid) {
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) {
+    a = fmaxf(a, __shfl_xor(a, off, kWave));
+    b = fmaxf(b, __shfl_xor(b, off, kWave));
+  }
+  if ((tid & (kWave - 1)) == 0) {
+    scratch[tid / kWave] = a;
+    scratch[kNWv + tid / kWave] = b;
+  }
+  lds_barrier();
+  a = scratch[0];
+  b = scratch[kNWv];
+  for (int w = 1; w < kNWv; ++w) {
+    a = fmaxf(a, scratch[w]);
+    b = fmaxf(b, scratch[kNWv + w]);
+  }
+  lds_barrier();
+}
+
+__device__ __forceinline__ void find_crossing_l(const uint64_t* hist, uint64_t M, uint64_t R,
+                                                uint64_t* scan_scratch, int* s_bin,
+                                                uint64_t* s_before, int tid) {
+  constexpr int PER = kBins / kNT;
+  const int b0 = tid * PER;
+  uint64_t local = 0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) local += hist[b0 + j];
+  if (tid == 0) *s_bin = -1;
+  uint64_t total;
+  const uint64_t excl = block_exclusive_scan_u64_l(local, scan_scratch, &total, tid);
+  uint64_t before = M + excl;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const uint64_t m = hist[b0 + j];
+    if (before < R && before + m >= R) {
+      *s_bin = b0 + j;
+      *s_before = before;
+    }
+    before += m;
+  }
+  lds_barrier();
+}
+
+// FULL rows: 16-byte loads; otherwise range-checked loads (zero past the
+// row), one path, so the registers are written in one place.  The slots past
+// the row are set to -inf by the caller (pad): done when the values are first
+// used, so the loads of the next row are not waited for when issued.
+template <int EPT, bool FULL>
+__device__ __forceinline__ void load_row(float (&v)[EPT], const float* x, int N, int e0) {
+  if (FULL) {
+#pragma unroll
+    for (int i = 0; i < EPT; i += 4) {
+      const f32x4 t = *(const f32x4*)(x + e0 + i);
+      v[i] = t[0]; v[i + 1] = t[1]; v[i + 2] = t[2]; v[i + 3] = t[3];
+    }
+  } else {
+    const __amdgpu_buffer_rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(x), (short)0, N * 4, 0x00020000);
+#pragma unroll
+    for (int i = 0; i < EPT; ++i)
+      v[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rr, (uint32_t)e0 * 4u,
+                                                                            4 * i, 0));
+  }
+}
+
+template <int EPT, bool FULL>
+__device__ __forceinline__ void pad_row(float (&v)[EPT], int nv) {
+  if (!FULL) {
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) v[i] = i < nv ? v[i] : -__builtin_inff();
+  }
+}
+
+// Persistent form: about one block per compute unit walks rows blockIdx.x,
+// blockIdx.x + gridDim.x, ...; the next row's logits are loaded into
+// registers while the current row is selected (same arithmetic as
+// nucleus_kernel, bit-identical masks).
+template <int EPT, bool FULL>
+__global__ __launch_bounds__(kNT) void nucleus_lp_kernel(int nrows, int N, int W, float top_p,
+                                                        const float* __restrict__ logits,
+                                                        uint32_t* __restrict__ mask) {
+  __shared__ uint64_t hist[kBins];
+  __shared__ uint64_t scan_scratch[kNWv + 1];
+  __shared__ float red[2 * kNWv];
+  __shared__ int s_bin;
+  __shared__ uint64_t s_before;
+  __shared__ uint32_t c_key[kCand];
+  __shared__ int c_idx[kCand];
+  __shared__ uint32_t c_w[kCand];
+  __shared__ int s_ncand;
+  __shared__ uint32_t keepbits[EPT * kNT / 32];
+
+  float v[EPT], vn[EPT];
+  int row = blockIdx.x;
+  {
+    const int e0 = threadIdx.x * EPT;
+    const int nv = FULL ? EPT : min(max(N - e0, 0), EPT);
+    if (row < nrows) {
+      load_row<EPT, FULL>(v, logits + (size_t)row * N, N, e0);
+      pad_row<EPT, FULL>(v, nv);
+    }
+  }
+  for (; row < nrows; row += gridDim.x) {
+    const int tid = opaque_i((int)threadIdx.x);
+    const int e0 = tid * EPT;
+    // entries of this thread inside the row: i < nv; slots past the row hold
+    // -inf, whose weight is 0 and whose bin is the last one
+    const int nv = FULL ? EPT : min(max(N - e0, 0), EPT);
+    const float* x = logits + (size_t)row * N;
+    lds_barrier();   // the previous row's LDS reads are done
+    if (tid == 0) { s_ncand = 0; s_bin = -1; }
+    for (int j = tid; j < W; j += kNT) keepbits[j] = 0;
+    for (int j = tid; j < kBins; j += kNT) hist[j] = 0;   // ordered by the barriers below
+
+    float m = -__builtin_inff(), nmin = -__builtin_inff();
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+      m = fmaxf(m, v[i]);
+      nmin = fmaxf(nmin, i < nv ? -v[i] : -__builtin_inff());
+    }
+    // the next row's loads are issued after the barrier that follows this
+    // row's first use of its values (a wait for this row's loads placed after
+    // them would wait for them too: the counter of outstanding loads is in
+    // order) and stay in flight while this row is selected
+    block_max2_l(m, nmin, red, tid);
+    const int nxt = row + gridDim.x;
+    if (nxt < nrows) load_row<EPT, FULL>(vn, logits + (size_t)nxt * N, N, e0);
+    const float xmin = -nmin;
+    const float range = m - xmin;
+    const float inv0 = range > 0.f ? (float)kBins / range : 0.f;
+    float mo = m, inv = inv0;
+    auto weight = [&](int i) -> uint32_t { return (uint32_t)(__expf(v[i] - mo) * kFix); };
+    auto vbin = [&](int i) -> int {
+      const float t = (mo - v[i]) * inv;
+      return t < (float)(kBins - 1) ? (int)t : kBins - 1;
+    };
+
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+      const uint32_t w = i < nv ? weight(i) : 0u;
+      if (w) atomicAdd((unsigned long long*)&hist[vbin(i)], (unsigned long long)w);
+    }
+    lds_barrier();
+    constexpr int PER = kBins / kNT;
+    const int b0 = tid * PER;
+    uint64_t local = 0;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) local += hist[b0 + j];
+    uint64_t S;
+    uint64_t before = block_exclusive_scan_u64_l(local, scan_scratch, &S, tid);
+    const double rd = (double)top_p * (double)S;
+    uint64_t R = (uint64_t)rd;
+    if ((double)R < rd) ++R;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const uint64_t mb = hist[b0 + j];
+      if (before < R && before + mb >= R) {
+        s_bin = b0 + j;
+        s_before = before;
+      }
+      before += mb;
+    }
+    lds_barrier();
+    const int cbin = s_bin;
+    uint64_t M = s_before;
+    mo = opaque(m);
+    inv = opaque(inv0);
+
+    if (cbin >= 0) {
+#pragma unroll
+      for (int i = 0; i < EPT; ++i) {
+        if ((i < nv) & (vbin(i) == cbin)) {
+          const int slot = atomicAdd(&s_ncand, 1);
+          if (slot < kCand) {
+            c_key[slot] = desc_key(v[i]);
+            c_idx[slot] = e0 + i;
+            c_w[slot] = weight(i);
+          }
+        }
+      }
+    }
+    lds_barrier();
+    const int nc = s_ncand;
+    if (cbin < 0 || nc <= kCand) {   // uniform
+      if (cbin >= 0) {
+        for (int sl = tid; sl < nc; sl += kNT) {
+          const uint32_t ks = c_key[sl];
+          const int is = c_idx[sl];
+          uint64_t ahead = 0;
+          for (int j = 0; j < nc; ++j) {
+            const uint32_t kj = c_key[j];
+            if (kj < ks || (kj == ks && c_idx[j] < is)) ahead += c_w[j];
+          }
+          if (M + ahead < R) atomicOr(&keepbits[is >> 5], 1u << (is & 31));
+        }
+        lds_barrier();
+      }
+      mo = opaque(m);
+      inv = opaque(inv0);
+      const int cb = cbin < 0 ? kBins : cbin;   // cbin < 0: every entry is kept
+#pragma unroll
+      for (int wd = 0; wd < EPT / 32; ++wd) {
+        const uint32_t kb = keepbits[tid * (EPT / 32) + wd];
+        uint32_t word = 0;
+#pragma unroll
+        for (int j = 0; j < 32; ++j) {
+          const int i = wd * 32 + j;
+          const int vb = vbin(i);
+          const bool keep = (i < nv) & ((vb < cb) | ((vb == cb) & (((kb >> j) & 1u) != 0u)));
+          word |= (keep ? 1u : 0u) << j;
+        }
+        const int widx = tid * (EPT / 32) + wd;
+        if (widx < W) mask[(size_t)row * W + widx] = word;
+      }
+    } else {
+      // heavy ties: radix passes over the order key inside the crossing bin,
+      // re-reading the row through a range-checked resource
+      const float* xr = x;
+      asm volatile("" : "+s"(xr));
+      const __amdgpu_buffer_rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<float*>(xr), (short)0, N * 4, 0x00020000);
+      auto rx = [&](int i) -> float {
+        const float t = __builtin_bit_cast(
+            float, __builtin_amdgcn_raw_buffer_load_b32(rr, (uint32_t)e0 * 4u, 4 * i, 0));
+        return i < nv ? t : -__builtin_inff();
+      };
+      auto rweight = [&](float xv, int i) -> uint32_t {
+        return (i < nv) ? (uint32_t)(__expf(xv - mo) * kFix) : 0u;
+      };
+      auto rbin = [&](float xv) -> int {
+        const float t = (mo - xv) * inv;
+        return t < (float)(kBins - 1) ? (int)t : kBins - 1;
+      };
+      bool found = true;
+      uint32_t prefix = 0;
+      constexpr int kShift[3] = {21, 10, 0};
+      constexpr int kBits[3] = {11, 11, 10};
+#pragma unroll 1
+      for (int p = 0; p < 3; ++p) {
+        for (int j = tid; j < kBins; j += kNT) hist[j] = 0;
+        lds_barrier();
+        const int sh = kShift[p];
+        const int hi = sh + kBits[p];
+        mo = opaque(m);
+        inv = opaque(inv0);
+#pragma unroll
+        for (int i = 0; i < EPT; ++i) {
+          const float xv = rx(i);
+          if (i >= nv || rbin(xv) != cbin) continue;
+          const uint32_t k = desc_key(xv);
+          if (hi < 32 && (k >> hi) != prefix) continue;
+          const uint32_t w = rweight(xv, i);
+          if (w)
+            atomicAdd((unsigned long long*)&hist[(k >> sh) & ((1u << kBits[p]) - 1u)],
+                      (unsigned long long)w);
+        }
+        lds_barrier();
+        find_crossing_l(hist, M, R, scan_scratch, &s_bin, &s_before, tid);
+        if (s_bin < 0) { found = false; break; }   // uniform: s_bin is shared
+        prefix = (prefix << kBits[p]) | (uint32_t)s_bin;
+        M = s_before;
+      }
+      const uint32_t ckey = found ? prefix : 0xFFFFFFFFu;
+      mo = opaque(m);
+      uint64_t tie_local = 0;
+      if (found) {
+#pragma unroll
+        for (int i = 0; i < EPT; ++i) {
+          const float xv = rx(i);
+          if (i < nv && desc_key(xv) == ckey) tie_local += rweight(xv, i);
+        }
+      }
+      uint64_t tie_total;
+      const uint64_t tie_excl = block_exclusive_scan_u64_l(tie_local, scan_scratch, &tie_total, tid);
+      uint64_t ahead = M + tie_excl;
+      mo = opaque(m);
+#pragma unroll
+      for (int wd = 0; wd < EPT / 32; ++wd) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int j = 0; j < 32; ++j) {
+          const int i = wd * 32 + j;
+          bool keep = false;
+          if (i < nv) {
+            if (!found) {
+              keep = true;
+            } else {
+              const float xv = rx(i);
+              const uint32_t k = desc_key(xv);
+              if (k < ckey) {
+                keep = true;
+              } else if (k == ckey) {
+                keep = ahead < R;
+                ahead += rweight(xv, i);
+              }
+            }
+          }
+          word |= (keep ? 1u : 0u) << j;
+        }
+        const int widx = tid * (EPT / 32) + wd;
+        if (widx < W) mask[(size_t)row * W + widx] = word;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) v[i] = vn[i];
+    pad_row<EPT, FULL>(v, nv);
+  }
+}
+
 // count[t][s] = sum over layers of bit s of mask[t][l]; label = count >= theta.
 // One thread per selection word: eight byte-lane accumulators of four counts.
 __global__ __launch_bounds__(256) void vote_kernel(int L, int N, int W, int theta,
@@ -386,10 +758,16 @@ hipError_t launch_label_vote(int Q, int L, int N, float top_p, int theta, const 
                              uint32_t* mask, uint8_t* count, uint8_t* label, hipStream_t s) {
   const int W = (N + 31) / 32;
   const dim3 rows((unsigned)Q * (unsigned)L);
-  if (N <= 32 * kNT)
-    hipLaunchKernelGGL((nucleus_kernel<32>), rows, dim3(kNT), 0, s, N, W, top_p, logits, mask);
-  else
+  if (N <= 32 * kNT) {
+    const int nrows = Q * L;
+    const dim3 grid((unsigned)std::min(nrows, device_cu_count()));
+    if (N == 32 * kNT)
+      hipLaunchKernelGGL((nucleus_lp_kernel<32, true>), grid, dim3(kNT), 0, s, nrows, N, W, top_p, logits, mask);
+    else
+      hipLaunchKernelGGL((nucleus_lp_kernel<32, false>), grid, dim3(kNT), 0, s, nrows, N, W, top_p, logits, mask);
+  } else {
     hipLaunchKernelGGL((nucleus_kernel<64>), rows, dim3(kNT), 0, s, N, W, top_p, logits, mask);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(vote_kernel, dim3((W + 255) / 256, Q), dim3(256), 0, s, L, N, W, theta, mask,

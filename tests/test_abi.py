@@ -137,6 +137,7 @@ def test_validation_errors_return_before_launch(lib):
     # label vote: too many layers, top_p out of range, no mask and no workspace
     assert lib.lsa_label_vote(1, 33, 100, 0.6, 3, fake, fake, fake, fake, None, 0, None) == _abi.LSA_E_SHAPE
     assert lib.lsa_label_vote(1, 3, 65537, 0.6, 3, fake, fake, fake, fake, None, 0, None) == _abi.LSA_E_SHAPE
+    assert lib.lsa_label_vote(1 << 28, 8, 100, 0.6, 3, fake, fake, fake, fake, None, 0, None) == _abi.LSA_E_SHAPE
     assert lib.lsa_label_vote(1, 3, 100, 0.0, 3, fake, fake, fake, fake, None, 0, None) == _abi.LSA_E_ARG
     assert lib.lsa_label_vote(1, 3, 100, 1.5, 3, fake, fake, fake, fake, None, 0, None) == _abi.LSA_E_ARG
     assert lib.lsa_label_vote(1, 3, 100, 0.6, 3, fake, None, fake, fake, None, 0, None) == _abi.LSA_E_WORKSPACE

@@ -469,6 +469,20 @@ __device__ __forceinline__ void pad_row(float (&v)[EPT], int nv) {
   }
 }
 
+// Weight and value bin of the persistent kernel, one fused multiply-add each:
+// w = trunc(2^(x log2(e) + 31 - max log2(e))) = trunc(exp(x - max) 2^31), the
+// fixed-point scale folded into the exponent (cw = 31 - max log2(e)); bin =
+// floor(max inv - x inv), clamped to the last bin, non-increasing in x.
+// -inf (padding) weighs 0; a NaN product converts to 0.
+constexpr float kLog2e = 1.4426950408889634f;
+__device__ __forceinline__ uint32_t lp_weight(float x, float cw) {
+  return (uint32_t)__builtin_amdgcn_exp2f(fmaf(x, kLog2e, cw));
+}
+__device__ __forceinline__ int lp_bin(float x, float ninv, float mi) {
+  const float t = fmaf(x, ninv, mi);
+  return t < (float)(kBins - 1) ? (int)t : kBins - 1;
+}
+
 // Persistent form: about one block per compute unit walks rows blockIdx.x,
 // blockIdx.x + gridDim.x, ...; the next row's logits are loaded into
 // registers while the current row is selected (same arithmetic as
@@ -482,9 +496,7 @@ __global__ __launch_bounds__(kNT) void nucleus_lp_kernel(int nrows, int N, int W
   __shared__ float red[2 * kNWv];
   __shared__ int s_bin;
   __shared__ uint64_t s_before;
-  __shared__ uint32_t c_key[kCand];
-  __shared__ int c_idx[kCand];
-  __shared__ uint32_t c_w[kCand];
+  __shared__ u32x4 cand[kCand];   // crossing-bin entries: order key, index, weight
   __shared__ int s_ncand;
   __shared__ uint32_t keepbits[EPT * kNT / 32];
 
@@ -526,17 +538,15 @@ __global__ __launch_bounds__(kNT) void nucleus_lp_kernel(int nrows, int N, int W
     const float xmin = -nmin;
     const float range = m - xmin;
     const float inv0 = range > 0.f ? (float)kBins / range : 0.f;
-    float mo = m, inv = inv0;
-    auto weight = [&](int i) -> uint32_t { return (uint32_t)(__expf(v[i] - mo) * kFix); };
-    auto vbin = [&](int i) -> int {
-      const float t = (mo - v[i]) * inv;
-      return t < (float)(kBins - 1) ? (int)t : kBins - 1;
-    };
+    const float cw0 = fmaf(-m, kLog2e, 31.f), ninv0 = -inv0, mi0 = m * inv0;
+    float cw = cw0, ninv = ninv0, mi = mi0;
+    auto weight = [&](int i) -> uint32_t { return lp_weight(v[i], cw); };
+    auto vbin = [&](int i) -> int { return lp_bin(v[i], ninv, mi); };
 
 #pragma unroll
     for (int i = 0; i < EPT; ++i) {
-      const uint32_t w = i < nv ? weight(i) : 0u;
-      if (w) atomicAdd((unsigned long long*)&hist[vbin(i)], (unsigned long long)w);
+      // padding slots add 0
+      atomicAdd((unsigned long long*)&hist[vbin(i)], (unsigned long long)weight(i));
     }
     lds_barrier();
     constexpr int PER = kBins / kNT;
@@ -561,54 +571,49 @@ __global__ __launch_bounds__(kNT) void nucleus_lp_kernel(int nrows, int N, int W
     lds_barrier();
     const int cbin = s_bin;
     uint64_t M = s_before;
-    mo = opaque(m);
-    inv = opaque(inv0);
+    cw = opaque(cw0);
+    ninv = opaque(ninv0);
+    mi = opaque(mi0);
 
-    if (cbin >= 0) {
+    // one pass: entries ahead of the crossing bin set their bit of the
+    // thread's selection word; the crossing bin's entries are collected as
+    // (order key, index, weight) records
+    const int cb = cbin < 0 ? kBins : cbin;   // cbin < 0: every entry is kept
+    uint32_t word[EPT / 32];
 #pragma unroll
-      for (int i = 0; i < EPT; ++i) {
-        if ((i < nv) & (vbin(i) == cbin)) {
-          const int slot = atomicAdd(&s_ncand, 1);
-          if (slot < kCand) {
-            c_key[slot] = desc_key(v[i]);
-            c_idx[slot] = e0 + i;
-            c_w[slot] = weight(i);
-          }
-        }
+    for (int wd = 0; wd < EPT / 32; ++wd) word[wd] = 0;
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+      const int vb = vbin(i);
+      word[i / 32] |= (((i < nv) & (vb < cb)) ? 1u : 0u) << (i % 32);
+      if ((i < nv) & (vb == cb)) {
+        const int slot = atomicAdd(&s_ncand, 1);
+        if (slot < kCand) cand[slot] = u32x4{desc_key(v[i]), (uint32_t)(e0 + i), weight(i), 0u};
       }
     }
     lds_barrier();
     const int nc = s_ncand;
-    if (cbin < 0 || nc <= kCand) {   // uniform
-      if (cbin >= 0) {
+    if (nc <= kCand) {   // uniform
+      if (nc > 0) {
+        // each candidate's exact mass ahead inside the bin, in walk order
+        // (logit descending, index ascending); kept iff the mass ahead of the
+        // bin plus that is below R
         for (int sl = tid; sl < nc; sl += kNT) {
-          const uint32_t ks = c_key[sl];
-          const int is = c_idx[sl];
+          const u32x4 me = cand[sl];
           uint64_t ahead = 0;
           for (int j = 0; j < nc; ++j) {
-            const uint32_t kj = c_key[j];
-            if (kj < ks || (kj == ks && c_idx[j] < is)) ahead += c_w[j];
+            const u32x4 o = cand[j];
+            if (o[0] < me[0] || (o[0] == me[0] && o[1] < me[1])) ahead += o[2];
           }
-          if (M + ahead < R) atomicOr(&keepbits[is >> 5], 1u << (is & 31));
+          if (M + ahead < R) atomicOr(&keepbits[me[1] >> 5], 1u << (me[1] & 31));
         }
         lds_barrier();
       }
-      mo = opaque(m);
-      inv = opaque(inv0);
-      const int cb = cbin < 0 ? kBins : cbin;   // cbin < 0: every entry is kept
 #pragma unroll
       for (int wd = 0; wd < EPT / 32; ++wd) {
-        const uint32_t kb = keepbits[tid * (EPT / 32) + wd];
-        uint32_t word = 0;
-#pragma unroll
-        for (int j = 0; j < 32; ++j) {
-          const int i = wd * 32 + j;
-          const int vb = vbin(i);
-          const bool keep = (i < nv) & ((vb < cb) | ((vb == cb) & (((kb >> j) & 1u) != 0u)));
-          word |= (keep ? 1u : 0u) << j;
-        }
         const int widx = tid * (EPT / 32) + wd;
-        if (widx < W) mask[(size_t)row * W + widx] = word;
+        if (nc > 0) word[wd] |= keepbits[widx];
+        if (widx < W) mask[(size_t)row * W + widx] = word[wd];
       }
     } else {
       // heavy ties: radix passes over the order key inside the crossing bin,
@@ -622,13 +627,8 @@ __global__ __launch_bounds__(kNT) void nucleus_lp_kernel(int nrows, int N, int W
             float, __builtin_amdgcn_raw_buffer_load_b32(rr, (uint32_t)e0 * 4u, 4 * i, 0));
         return i < nv ? t : -__builtin_inff();
       };
-      auto rweight = [&](float xv, int i) -> uint32_t {
-        return (i < nv) ? (uint32_t)(__expf(xv - mo) * kFix) : 0u;
-      };
-      auto rbin = [&](float xv) -> int {
-        const float t = (mo - xv) * inv;
-        return t < (float)(kBins - 1) ? (int)t : kBins - 1;
-      };
+      auto rweight = [&](float xv, int i) -> uint32_t { return (i < nv) ? lp_weight(xv, cw) : 0u; };
+      auto rbin = [&](float xv) -> int { return lp_bin(xv, ninv, mi); };
       bool found = true;
       uint32_t prefix = 0;
       constexpr int kShift[3] = {21, 10, 0};
@@ -639,8 +639,9 @@ __global__ __launch_bounds__(kNT) void nucleus_lp_kernel(int nrows, int N, int W
         lds_barrier();
         const int sh = kShift[p];
         const int hi = sh + kBits[p];
-        mo = opaque(m);
-        inv = opaque(inv0);
+        cw = opaque(cw0);
+        ninv = opaque(ninv0);
+        mi = opaque(mi0);
 #pragma unroll
         for (int i = 0; i < EPT; ++i) {
           const float xv = rx(i);
@@ -659,7 +660,7 @@ __global__ __launch_bounds__(kNT) void nucleus_lp_kernel(int nrows, int N, int W
         M = s_before;
       }
       const uint32_t ckey = found ? prefix : 0xFFFFFFFFu;
-      mo = opaque(m);
+      cw = opaque(cw0);
       uint64_t tie_local = 0;
       if (found) {
 #pragma unroll
@@ -671,7 +672,7 @@ __global__ __launch_bounds__(kNT) void nucleus_lp_kernel(int nrows, int N, int W
       uint64_t tie_total;
       const uint64_t tie_excl = block_exclusive_scan_u64_l(tie_local, scan_scratch, &tie_total, tid);
       uint64_t ahead = M + tie_excl;
-      mo = opaque(m);
+      cw = opaque(cw0);
 #pragma unroll
       for (int wd = 0; wd < EPT / 32; ++wd) {
         uint32_t word = 0;

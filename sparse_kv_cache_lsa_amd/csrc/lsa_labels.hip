@@ -53,6 +53,8 @@ constexpr int kNWv = kNT / kWave;      // wavefronts per row block
 constexpr int kBins = 2048;            // histogram bins per pass
 constexpr float kFix = 2147483648.f;   // 2^31: fixed-point unit of exp(x - max)
 constexpr int kCand = 1024;            // crossing-bin entries handled by direct comparison
+constexpr int kMaxVoteLayers = LSA_MAX_VOTE_LAYERS;   // layers one vote adds
+static_assert(kMaxVoteLayers <= 32, "vote counts are 8-bit byte lanes; words are kept in registers");
 
 // order key: smaller key = larger logit; -0 and +0 share a key
 __device__ __forceinline__ uint32_t desc_key(float x) {
@@ -456,8 +458,8 @@ __device__ __forceinline__ void load_row(float (&v)[EPT], const float* x, int N,
         const_cast<float*>(x), (short)0, N * 4, 0x00020000);
 #pragma unroll
     for (int i = 0; i < EPT; ++i)
-      v[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rr, (uint32_t)e0 * 4u,
-                                                                            4 * i, 0));
+      v[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                           rr, (uint32_t)(e0 + i) * 4u, 0, 0));
   }
 }
 
@@ -617,14 +619,17 @@ __global__ __launch_bounds__(kNT) void nucleus_lp_kernel(int nrows, int N, int W
       }
     } else {
       // heavy ties: radix passes over the order key inside the crossing bin,
-      // re-reading the row through a range-checked resource
+      // re-reading the row (through a pointer the compiler cannot match with
+      // x, so the row's registers are not kept for this path): full rows with
+      // plain loads, others through a range-checked resource
       const float* xr = x;
       asm volatile("" : "+s"(xr));
       const __amdgpu_buffer_rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc(
           const_cast<float*>(xr), (short)0, N * 4, 0x00020000);
       auto rx = [&](int i) -> float {
+        if constexpr (FULL) return xr[e0 + i];
         const float t = __builtin_bit_cast(
-            float, __builtin_amdgcn_raw_buffer_load_b32(rr, (uint32_t)e0 * 4u, 4 * i, 0));
+            float, __builtin_amdgcn_raw_buffer_load_b32(rr, (uint32_t)(e0 + i) * 4u, 0, 0));
         return i < nv ? t : -__builtin_inff();
       };
       auto rweight = [&](float xv, int i) -> uint32_t { return (i < nv) ? lp_weight(xv, cw) : 0u; };
@@ -715,13 +720,23 @@ __global__ __launch_bounds__(256) void vote_kernel(int L, int N, int W, int thet
   const int t = blockIdx.y;
   const int w = blockIdx.x * blockDim.x + threadIdx.x;
   if (w >= W) return;
+  // all layers' words in flight at once: a resource over this query's L * W
+  // words returns 0 for the layers past L, so the loads need no branch (the
+  // whole offset goes in the vector offset: the range check does not cover
+  // the scalar offset)
+  const __amdgpu_buffer_rsrc_t rm = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint32_t*>(mask + (size_t)t * L * W), (short)0, L * W * 4, 0x00020000);
+  uint32_t words[kMaxVoteLayers];
+#pragma unroll
+  for (int l = 0; l < kMaxVoteLayers; ++l)
+    words[l] = __builtin_amdgcn_raw_buffer_load_b32(rm, (uint32_t)(l * W + w) * 4u, 0, 0);
   uint32_t acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  for (int l = 0; l < L; ++l) {
-    const uint32_t word = mask[((size_t)t * L + l) * W + w];
+#pragma unroll
+  for (int l = 0; l < kMaxVoteLayers; ++l) {
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       // bits 4k..4k+3 of the word -> bytes 0..3 (multiply spreads, mask keeps)
-      acc[k] += (((word >> (4 * k)) & 0xFu) * 0x00204081u) & 0x01010101u;
+      acc[k] += (((words[l] >> (4 * k)) & 0xFu) * 0x00204081u) & 0x01010101u;
     }
   }
   const size_t base = (size_t)t * N + (size_t)w * 32;

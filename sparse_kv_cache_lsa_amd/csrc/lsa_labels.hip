@@ -509,15 +509,19 @@ __device__ __forceinline__ void pad_row(float (&v)[EPT], int nv) {
 // Weight and value bin of the persistent kernel, one fused multiply-add each:
 // w = trunc(2^(x log2(e) + 31 - max log2(e))) = trunc(exp(x - max) 2^31), the
 // fixed-point scale folded into the exponent (cw = 31 - max log2(e)); bin =
-// floor(max inv - x inv), clamped to the last bin, non-increasing in x.
-// -inf (padding) weighs 0; a NaN product converts to 0.
+// floor(max inv - x inv) clamped to [0, last bin], non-increasing in x.  The
+// clamp at 0 matters: max inv is rounded before the subtraction, so when the
+// row's values are large against its range the unclamped value can fall to
+// -ulp(max inv) / 2 (a few units) for the largest entries.  Any bin
+// function that is non-increasing in x partitions the row correctly (the
+// crossing bin is resolved exactly).  -inf (padding) weighs 0; a NaN product
+// converts to 0.
 constexpr float kLog2e = 1.4426950408889634f;
 __device__ __forceinline__ uint32_t lp_weight(float x, float cw) {
   return (uint32_t)__builtin_amdgcn_exp2f(fmaf(x, kLog2e, cw));
 }
 __device__ __forceinline__ int lp_bin(float x, float ninv, float mi) {
-  const float t = fmaf(x, ninv, mi);
-  return t < (float)(kBins - 1) ? (int)t : kBins - 1;
+  return (int)__builtin_amdgcn_fmed3f(fmaf(x, ninv, mi), 0.f, (float)(kBins - 1));
 }
 
 // Persistent form: about one block per compute unit walks rows blockIdx.x,

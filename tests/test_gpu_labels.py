@@ -117,3 +117,17 @@ def test_labels_heavy_ties_and_signed_zeros():
         _check(x, 0.6, theta, mask, count, label)
         if theta == 0:
             assert label.all()
+
+
+@pytest.mark.parametrize("N", [32768, 5000])
+def test_labels_large_offsets(N):
+    # rows whose values are large against their spread (3e5 + N(0,1), 1e6 + ...):
+    # the value bins come from max * inv rounded before the subtraction, so
+    # the largest entries' bin value can fall below 0 and must be clamped
+    rng = np.random.default_rng(N + 5)
+    offs = np.array([0.0, 1e3, 3e5, 1e6, -1e6, 2e7], np.float64)
+    x = np.stack([np.stack([offs[(q * 3 + l) % len(offs)] + rng.standard_normal(N) * (1 + l)
+                            for l in range(3)]) for q in range(2)]).astype(np.float32)
+    for top_p in (0.05, 0.6, 0.999):
+        mask, count, label = _gpu(x, top_p, 2)
+        _check(x, top_p, 2, mask, count, label)

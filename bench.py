@@ -42,7 +42,7 @@ def score_source_hash() -> str:
 
 
 def labels_source_hash() -> str:
-    return source_hash(("lsa_labels.hip", "lsa_device.h", "lsa_launch.h"))
+    return source_hash(("lsa_labels.hip", "lsa_device.h", "lsa_dpp.h", "lsa_launch.h"))
 
 
 def counter_traffic(path, source_hash_now, workload):

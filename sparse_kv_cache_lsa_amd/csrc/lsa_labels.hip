@@ -41,6 +41,7 @@
 // entries a thread and the same arithmetic.  A second kernel adds the
 // layers' selection words per query into the vote counts and labels.
 #include "lsa_device.h"
+#include "lsa_dpp.h"
 #include "lsa_launch.h"
 
 #include <algorithm>
@@ -397,48 +398,11 @@ __device__ __forceinline__ uint64_t block_exclusive_scan_u64_l(uint64_t v, uint6
   return res;
 }
 
-// DPP moves inside the wavefront (a lane whose source is out of range or
-// whose row is masked keeps `old`): row shifts inside 16-lane rows, then
-// broadcasts of lane 15 into rows 1 and 3 and of lane 31 into rows 2 and 3,
-// so the last lane accumulates all 64.
-template <int CTRL, int ROWS>
-__device__ __forceinline__ float dpp_f32(float old, float v) {
-  return __int_as_float(
-      __builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(v), CTRL, ROWS, 0xF, false));
-}
-__device__ __forceinline__ float wave_max_dpp(float v) {
-  const float ninf = -__builtin_inff();
-  v = fmaxf(v, dpp_f32<0x111, 0xF>(ninf, v));   // row_shr:1
-  v = fmaxf(v, dpp_f32<0x112, 0xF>(ninf, v));   // row_shr:2
-  v = fmaxf(v, dpp_f32<0x114, 0xF>(ninf, v));   // row_shr:4
-  v = fmaxf(v, dpp_f32<0x118, 0xF>(ninf, v));   // row_shr:8
-  v = fmaxf(v, dpp_f32<0x142, 0xA>(ninf, v));   // row_bcast:15
-  v = fmaxf(v, dpp_f32<0x143, 0xC>(ninf, v));   // row_bcast:31
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), kWave - 1));
-}
-
-template <int CTRL, int ROWS>
-__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
-  const uint32_t lo = __builtin_amdgcn_update_dpp(0u, (uint32_t)v, CTRL, ROWS, 0xF, false);
-  const uint32_t hi = __builtin_amdgcn_update_dpp(0u, (uint32_t)(v >> 32), CTRL, ROWS, 0xF, false);
-  return ((uint64_t)hi << 32) | lo;
-}
-// inclusive prefix sum over the wavefront (out-of-range sources add 0)
-__device__ __forceinline__ uint64_t wave_inclusive_scan_u64_dpp(uint64_t v) {
-  v += dpp_u64<0x111, 0xF>(v);
-  v += dpp_u64<0x112, 0xF>(v);
-  v += dpp_u64<0x114, 0xF>(v);
-  v += dpp_u64<0x118, 0xF>(v);
-  v += dpp_u64<0x142, 0xA>(v);
-  v += dpp_u64<0x143, 0xC>(v);
-  return v;
-}
-
 // block-wide max of a and of b; scratch: 2 * kNWv floats.  No trailing
 // barrier: the caller writes scratch again only after later barriers.
 __device__ __forceinline__ void block_max2_l(float& a, float& b, float* scratch, int tid) {
-  a = wave_max_dpp(a);
-  b = wave_max_dpp(b);
+  a = wave_max_f32_dpp(a);
+  b = wave_max_f32_dpp(b);
   if ((tid & (kWave - 1)) == 0) {
     scratch[tid / kWave] = a;
     scratch[kNWv + tid / kWave] = b;
@@ -598,7 +562,7 @@ __global__ __launch_bounds__(kNT) void nucleus_lp_kernel(int nrows, int N, int W
     uint64_t local = 0;
 #pragma unroll
     for (int j = 0; j < PER; ++j) local += hist[b0 + j];
-    const uint64_t inc = wave_inclusive_scan_u64_dpp(local);
+    const uint64_t inc = wave_inclusive_sum_u64_dpp(local);
     const int wave = tid / kWave;
     if ((tid & (kWave - 1)) == kWave - 1) scan_scratch[wave] = inc;
     lds_barrier();

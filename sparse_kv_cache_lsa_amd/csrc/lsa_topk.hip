@@ -19,6 +19,7 @@
 // every pass, and the sweep needs only two block prefix sums.  Longer lists
 // stream from memory in every pass.
 #include "lsa_device.h"
+#include "lsa_dpp.h"
 #include "lsa_launch.h"
 
 #include <mutex>
@@ -39,60 +40,47 @@ __device__ __forceinline__ uint32_t order_key(float z) {
 }
 
 // Exclusive prefix sum over a block of NT threads (thread order), total in
-// *total.  The per-wave totals are scanned by one wavefront with shuffles
-// (no serial loop).  scratch: NT/64 + 1 ints.  All threads call.
+// *total: a DPP scan inside each wavefront, then every thread adds the
+// totals of the wavefronts before its own.  scratch: NT/64 ints.  All threads
+// call; the trailing barrier lets the next call reuse scratch.
 template <int NT>
 __device__ __forceinline__ int scan_block(int v, int* scratch, int* total) {
   constexpr int NW = NT / kWave;
   const int lane = lane_id();
   const int wave = threadIdx.x / kWave;
-  const int inc = wave_inclusive_scan(v);
+  const int inc = wave_inclusive_sum_dpp(v);
   if (lane == kWave - 1) scratch[wave] = inc;
   __syncthreads();
-  if (wave == 0) {
-    const int w = lane < NW ? scratch[lane] : 0;
-    const int wi = wave_inclusive_scan(w);
-    if (lane < NW) scratch[lane] = wi - w;
-    if (lane == NW - 1) scratch[NW] = wi;
+  int pre = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const int t = scratch[w];
+    all += t;
+    pre += w < wave ? t : 0;
   }
+  *total = all;
   __syncthreads();
-  const int res = scratch[wave] + inc - v;
-  *total = scratch[NW];
-  __syncthreads();
-  return res;
+  return pre + inc - v;
 }
 
-// block-wide min of a and max of b; scratch: 2 * (NT / 64) + 2 ints.  All threads call.
+// block-wide min of a and max of b; scratch: 2 * (NT / 64) ints.  All
+// threads call.  No trailing barrier: the only caller writes scratch again
+// after two more barriers.
 template <int NT>
 __device__ __forceinline__ void block_minmax_t(uint32_t& a, uint32_t& b, int* scratch) {
   constexpr int NW = NT / kWave;
-#pragma unroll
-  for (int off = kWave / 2; off > 0; off >>= 1) {
-    a = min(a, (uint32_t)__shfl_xor((int)a, off, kWave));
-    b = max(b, (uint32_t)__shfl_xor((int)b, off, kWave));
-  }
+  a = wave_min_u32_dpp(a);
+  b = wave_max_u32_dpp(b);
   if (lane_id() == 0) {
     scratch[threadIdx.x / kWave] = (int)a;
     scratch[NW + threadIdx.x / kWave] = (int)b;
   }
   __syncthreads();
-  if (threadIdx.x < kWave) {
-    uint32_t x = threadIdx.x < NW ? (uint32_t)scratch[threadIdx.x] : 0xFFFFFFFFu;
-    uint32_t y = threadIdx.x < NW ? (uint32_t)scratch[NW + threadIdx.x] : 0u;
 #pragma unroll
-    for (int off = kWave / 2; off > 0; off >>= 1) {
-      x = min(x, (uint32_t)__shfl_xor((int)x, off, kWave));
-      y = max(y, (uint32_t)__shfl_xor((int)y, off, kWave));
-    }
-    if (threadIdx.x == 0) {
-      scratch[2 * NW] = (int)x;
-      scratch[2 * NW + 1] = (int)y;
-    }
+  for (int w = 0; w < NW; ++w) {
+    a = min(a, (uint32_t)scratch[w]);
+    b = max(b, (uint32_t)scratch[NW + w]);
   }
-  __syncthreads();
-  a = (uint32_t)scratch[2 * NW];
-  b = (uint32_t)scratch[2 * NW + 1];
-  __syncthreads();
 }
 
 // Finds, scanning bins from the highest digit down, the bin holding the

@@ -56,6 +56,9 @@ __device__ __forceinline__ uint64_t wave_inclusive_sum_u64_dpp(uint64_t v) {
 __device__ __forceinline__ uint32_t wave_last_lane(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_readlane((int)v, kWave - 1);
 }
+__device__ __forceinline__ int wave_sum_dpp(int v) {
+  return (int)wave_last_lane((uint32_t)wave_inclusive_sum_dpp(v));
+}
 __device__ __forceinline__ uint32_t wave_min_u32_dpp(uint32_t v) {
   return wave_last_lane(
       wave_scan_dpp(v, 0xFFFFFFFFu, [](uint32_t a, uint32_t b) { return a < b ? a : b; }));

@@ -8,6 +8,7 @@
 // then it copies its list with coalesced loads and stores.  Deterministic; the
 // last chunk's block writes the request's true survivor count.
 #include "lsa_device.h"
+#include "lsa_dpp.h"
 #include "lsa_launch.h"
 
 namespace lsa {
@@ -28,7 +29,7 @@ __global__ __launch_bounds__(kSelThreads) void select_concat_kernel(
   if (t < kWave) {
     int acc = 0;
     for (int i = lane_id(); i < c; i += kWave) acc += cnt[i];
-    acc = wave_sum(acc);
+    acc = wave_sum_dpp(acc);
     if (lane_id() == 0) s_base = acc;
   }
   __syncthreads();

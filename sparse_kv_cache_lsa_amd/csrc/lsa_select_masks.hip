@@ -16,6 +16,7 @@
 // Survivors come out in ascending entry order; at most cap are written and
 // the last chunk's block stores the true count.  Deterministic.
 #include "lsa_device.h"
+#include "lsa_dpp.h"
 #include "lsa_launch.h"
 
 namespace lsa {
@@ -44,7 +45,7 @@ __global__ __launch_bounds__(kWordsPerChunk) void mask_count_kernel(
   __shared__ int s_part[kWordsPerChunk / kWave];
   const int c = blockIdx.x, b = blockIdx.y;
   const int w = c * kWordsPerChunk + (int)threadIdx.x;
-  const int n = wave_sum(__popc(or_word(L, B, W, N, b, w, mask)));
+  const int n = wave_sum_dpp(__popc(or_word(L, B, W, N, b, w, mask)));
   if (lane_id() == 0) s_part[threadIdx.x / kWave] = n;
   __syncthreads();
   if (threadIdx.x == 0) counts[(size_t)b * nchunks + c] = s_part[0] + s_part[1];
@@ -63,7 +64,7 @@ __global__ __launch_bounds__(kWordsPerChunk) void mask_write_kernel(
     const int32_t* cnt = counts + (size_t)b * nchunks;
     int acc = 0;
     for (int i = lane_id(); i < c; i += kWave) acc += cnt[i];
-    acc = wave_sum(acc);
+    acc = wave_sum_dpp(acc);
     if (lane_id() == 0) s_base = acc;
   }
   uint32_t m = or_word(L, B, W, N, b, w, mask);

@@ -107,9 +107,12 @@ def test_labels_constant_logits_closed_form():
     assert np.array_equal(count[0], np.where(np.arange(N) < n_keep, 3, 0))
 
 
-def test_labels_heavy_ties_and_signed_zeros():
+@pytest.mark.parametrize("N", [9000, 50000])
+def test_labels_heavy_ties_and_signed_zeros(N):
+    # few distinct values: the crossing bin holds thousands of entries and
+    # takes the radix path (rows above 32K entries: 64 entries a thread)
     rng = np.random.default_rng(11)
-    x = (np.round(rng.standard_normal((2, 3, 9000)) * 2) / 2).astype(np.float32)
+    x = (np.round(rng.standard_normal((2, 3, N)) * 2) / 2).astype(np.float32)
     z = rng.random(x.shape) < 0.1
     x[z] = np.where(rng.random(z.sum()) < 0.5, np.float32(0.0), np.float32(-0.0))
     for theta in (0, 1, 3):
@@ -119,7 +122,7 @@ def test_labels_heavy_ties_and_signed_zeros():
             assert label.all()
 
 
-@pytest.mark.parametrize("N", [32768, 5000])
+@pytest.mark.parametrize("N", [32768, 5000, 65536])
 def test_labels_large_offsets(N):
     # rows whose values are large against their spread (3e5 + N(0,1), 1e6 + ...):
     # the value bins come from max * inv rounded before the subtraction, so

@@ -441,13 +441,18 @@ __global__ __launch_bounds__(kNT) void nucleus_lp_kernel(int nrows, int N, int W
 }
 
 // count[t][s] = sum over layers of bit s of mask[t][l]; label = count >= theta.
-// One thread per selection word: eight byte-lane accumulators of four counts.
+// One thread per quarter of a selection word: two byte-lane accumulators of
+// four counts.
 __global__ __launch_bounds__(256) void vote_kernel(int L, int N, int W, int theta,
                                                    const uint32_t* __restrict__ mask,
                                                    uint8_t* __restrict__ count,
                                                    uint8_t* __restrict__ label) {
+  // one thread per quarter word (entries 8 r .. 8 r + 7 of word w): four
+  // times the threads of one per word, so more loads are in flight per
+  // compute unit; the four threads of a word load the same addresses
   const int t = blockIdx.y;
-  const int w = blockIdx.x * blockDim.x + threadIdx.x;
+  const int u = blockIdx.x * blockDim.x + threadIdx.x;
+  const int w = u >> 2, r = u & 3;
   if (w >= W) return;
   // all layers' words in flight at once: a resource over this query's L * W
   // words returns 0 for the layers past L, so the loads need no branch (the
@@ -459,37 +464,30 @@ __global__ __launch_bounds__(256) void vote_kernel(int L, int N, int W, int thet
 #pragma unroll
   for (int l = 0; l < kMaxVoteLayers; ++l)
     words[l] = __builtin_amdgcn_raw_buffer_load_b32(rm, (uint32_t)(l * W + w) * 4u, 0, 0);
-  uint32_t acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  uint32_t acc[2] = {0, 0};
 #pragma unroll
   for (int l = 0; l < kMaxVoteLayers; ++l) {
+    const uint32_t byte = (words[l] >> (8 * r)) & 0xFFu;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      // bits 4k..4k+3 of the word -> bytes 0..3 (multiply spreads, mask keeps)
-      acc[k] += (((words[l] >> (4 * k)) & 0xFu) * 0x00204081u) & 0x01010101u;
-    }
+    for (int k = 0; k < 2; ++k)
+      // bits 4k..4k+3 of the byte -> bytes 0..3 (multiply spreads, mask keeps)
+      acc[k] += (((byte >> (4 * k)) & 0xFu) * 0x00204081u) & 0x01010101u;
   }
-  const size_t base = (size_t)t * N + (size_t)w * 32;
+  const size_t base = (size_t)t * N + (size_t)w * 32 + 8 * r;
   if ((N & 31) == 0) {
-    u32x4 c0 = {acc[0], acc[1], acc[2], acc[3]}, c1 = {acc[4], acc[5], acc[6], acc[7]};
-    u32x4 y0, y1;
+    u32x2 y;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      uint32_t a = 0, b = 0;
+    for (int k = 0; k < 2; ++k) {
+      uint32_t a = 0;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        a |= ((int)((c0[k] >> (8 * j)) & 0xFFu) >= theta ? 1u : 0u) << (8 * j);
-        b |= ((int)((c1[k] >> (8 * j)) & 0xFFu) >= theta ? 1u : 0u) << (8 * j);
-      }
-      y0[k] = a;
-      y1[k] = b;
+      for (int j = 0; j < 4; ++j) a |= ((int)((acc[k] >> (8 * j)) & 0xFFu) >= theta ? 1u : 0u) << (8 * j);
+      y[k] = a;
     }
-    *(u32x4*)(count + base) = c0;
-    *(u32x4*)(count + base + 16) = c1;
-    *(u32x4*)(label + base) = y0;
-    *(u32x4*)(label + base + 16) = y1;
+    *(u32x2*)(count + base) = u32x2{acc[0], acc[1]};
+    *(u32x2*)(label + base) = y;
   } else {
-    for (int j = 0; j < 32; ++j) {
-      if (w * 32 + j >= N) break;
+    for (int j = 0; j < 8; ++j) {
+      if (w * 32 + 8 * r + j >= N) break;
       const int c = (int)((acc[j >> 2] >> (8 * (j & 3))) & 0xFFu);
       count[base + j] = (uint8_t)c;
       label[base + j] = c >= theta ? 1 : 0;
@@ -521,8 +519,8 @@ hipError_t launch_label_vote(int Q, int L, int N, float top_p, int theta, const 
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(vote_kernel, dim3((W + 255) / 256, Q), dim3(256), 0, s, L, N, W, theta, mask,
-                     count, label);
+  hipLaunchKernelGGL(vote_kernel, dim3((4 * W + 255) / 256, Q), dim3(256), 0, s, L, N, W, theta,
+                     mask, count, label);
   return hipGetLastError();
 }
 

@@ -9,15 +9,19 @@
 // summary, section 2.2 "data curation and labelling", steps 1-3; paper.oopus.info
 // review, section 2, training labels by cross-layer majority vote.)
 //
-// Design.  A row is selected by one 1024-thread block: thread i holds the
-// EPT (32, or 64 for rows longer than 32K entries) consecutive entries
-// [EPT i, EPT i + EPT) in registers, so it owns whole selection words and
-// index order is (thread, register) order.  About one block per compute unit
-// walks rows blockIdx.x, blockIdx.x + gridDim.x, ...; with 32 entries a
-// thread the next row's logits are loaded into a second register set while
-// the current row is selected, and every barrier of the selection waits for
-// LDS only, so those loads stay in flight (a plain block barrier also waits
-// for outstanding vector memory operations).  No sort:
+// Design.  A row is selected by one block: thread i holds the EPT
+// consecutive entries [EPT i, EPT i + EPT) in registers, so it owns whole
+// selection words and index order is (thread, register) order.  Blocks walk
+// rows blockIdx.x, blockIdx.x + gridDim.x, ...; every barrier of the
+// selection waits for LDS only (a plain block barrier also waits for
+// outstanding vector memory operations).  Rows of exactly 32K entries:
+// 512-thread blocks with 64 entries a thread, two blocks per compute unit at
+// 128 VGPRs, so one block's barrier phases and row loads overlap the other's
+// arithmetic.  Shorter rows: one 1024-thread block per compute unit with 32
+// entries a thread, which loads the next row's logits into a second register
+// set while the current row is selected (the LDS-only barriers keep those
+// loads in flight).  Longer rows (up to 64K): 1024 threads, 64 entries a
+// thread, the next row loaded when the current one is done.  No sort:
 //  * mass in fixed point: w_s = trunc(exp(x_s - max) * 2^31), summed in 64-bit
 //    integers, so every partial sum is exact and independent of summation
 //    order -- the result is deterministic and the same as a sequential walk
@@ -48,8 +52,6 @@
 namespace lsa {
 namespace {
 
-constexpr int kNT = 1024;              // threads per row block
-constexpr int kNWv = kNT / kWave;      // wavefronts per row block
 constexpr int kBins = 2048;            // histogram bins per pass
 constexpr int kCand = 1024;            // crossing-bin entries handled by direct comparison
 constexpr int kMaxVoteLayers = LSA_MAX_VOTE_LAYERS;   // layers one vote adds
@@ -84,6 +86,7 @@ __device__ __forceinline__ int opaque_i(int x) {
 // The helpers below take the thread index as an argument: the row loop passes
 // a copy the compiler cannot see through, so nothing derived from it is kept
 // live across rows (the registers go to the next row's logits).
+template <int NT>
 __device__ __forceinline__ uint64_t block_exclusive_scan_u64_l(uint64_t v, uint64_t* scratch,
                                                                uint64_t* total, int tid) {
   const int lane = tid & (kWave - 1);
@@ -92,47 +95,49 @@ __device__ __forceinline__ uint64_t block_exclusive_scan_u64_l(uint64_t v, uint6
   if (lane == kWave - 1) scratch[wave] = inc;
   lds_barrier();
   if (wave == 0) {
-    const uint64_t w = lane < kNWv ? scratch[lane] : 0ull;
+    const uint64_t w = lane < (NT / kWave) ? scratch[lane] : 0ull;
     const uint64_t wi = wave_inclusive_sum_u64_dpp(w);
-    if (lane < kNWv) scratch[lane] = wi - w;
-    if (lane == kNWv - 1) scratch[kNWv] = wi;
+    if (lane < (NT / kWave)) scratch[lane] = wi - w;
+    if (lane == (NT / kWave) - 1) scratch[(NT / kWave)] = wi;
   }
   lds_barrier();
   const uint64_t res = scratch[wave] + inc - v;
-  *total = scratch[kNWv];
+  *total = scratch[(NT / kWave)];
   lds_barrier();
   return res;
 }
 
-// block-wide max of a and of b; scratch: 2 * kNWv floats.  No trailing
+// block-wide max of a and of b; scratch: 2 * (NT / kWave) floats.  No trailing
 // barrier: the caller writes scratch again only after later barriers.
+template <int NT>
 __device__ __forceinline__ void block_max2_l(float& a, float& b, float* scratch, int tid) {
   a = wave_max_f32_dpp(a);
   b = wave_max_f32_dpp(b);
   if ((tid & (kWave - 1)) == 0) {
     scratch[tid / kWave] = a;
-    scratch[kNWv + tid / kWave] = b;
+    scratch[(NT / kWave) + tid / kWave] = b;
   }
   lds_barrier();
   a = scratch[0];
-  b = scratch[kNWv];
-  for (int w = 1; w < kNWv; ++w) {
+  b = scratch[(NT / kWave)];
+  for (int w = 1; w < (NT / kWave); ++w) {
     a = fmaxf(a, scratch[w]);
-    b = fmaxf(b, scratch[kNWv + w]);
+    b = fmaxf(b, scratch[(NT / kWave) + w]);
   }
 }
 
+template <int NT>
 __device__ __forceinline__ void find_crossing_l(const uint64_t* hist, uint64_t M, uint64_t R,
                                                 uint64_t* scan_scratch, int* s_bin,
                                                 uint64_t* s_before, int tid) {
-  constexpr int PER = kBins / kNT;
+  constexpr int PER = kBins / NT;
   const int b0 = tid * PER;
   uint64_t local = 0;
 #pragma unroll
   for (int j = 0; j < PER; ++j) local += hist[b0 + j];
   if (tid == 0) *s_bin = -1;
   uint64_t total;
-  const uint64_t excl = block_exclusive_scan_u64_l(local, scan_scratch, &total, tid);
+  const uint64_t excl = block_exclusive_scan_u64_l<NT>(local, scan_scratch, &total, tid);
   uint64_t before = M + excl;
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
@@ -194,22 +199,23 @@ __device__ __forceinline__ int lp_bin(float x, float ninv, float mi) {
   return (int)__builtin_amdgcn_fmed3f(fmaf(x, ninv, mi), 0.f, (float)(kBins - 1));
 }
 
-// About one block per compute unit walks rows blockIdx.x, blockIdx.x +
-// gridDim.x, ...  EPT entries a thread; FULL: N == EPT * kNT (no padding);
-// PF: the next row is loaded into a second register set while the current
-// one is selected (otherwise when it is done).
-template <int EPT, bool FULL, bool PF>
-__global__ __launch_bounds__(kNT) void nucleus_lp_kernel(int nrows, int N, int W, float top_p,
+// NT threads a block walk rows blockIdx.x, blockIdx.x + gridDim.x, ...  EPT
+// entries a thread; FULL: N == EPT * NT (no padding); PF: the next row is
+// loaded into a second register set while the current one is selected
+// (otherwise when it is done).  At most 128 VGPRs: 16 wavefronts a compute
+// unit (one 1024-thread block or two 512-thread blocks).
+template <int NT, int EPT, bool FULL, bool PF>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void nucleus_lp_kernel(int nrows, int N, int W, float top_p,
                                                         const float* __restrict__ logits,
                                                         uint32_t* __restrict__ mask) {
   __shared__ uint64_t hist[kBins];
-  __shared__ uint64_t scan_scratch[kNWv + 1];
-  __shared__ float red[2 * kNWv];
+  __shared__ uint64_t scan_scratch[(NT / kWave) + 1];
+  __shared__ float red[2 * (NT / kWave)];
   __shared__ int s_bin;
   __shared__ uint64_t s_before;
   __shared__ u32x4 cand[kCand];   // crossing-bin entries: order key, index, weight
   __shared__ int s_ncand;
-  __shared__ uint32_t keepbits[EPT * kNT / 32];
+  __shared__ uint32_t keepbits[EPT * NT / 32];
 
   float v[EPT], vn[PF ? EPT : 1];   // PF: the next row in a second register set
   int row = blockIdx.x;
@@ -230,8 +236,8 @@ __global__ __launch_bounds__(kNT) void nucleus_lp_kernel(int nrows, int N, int W
     const float* x = logits + (size_t)row * N;
     lds_barrier();   // the previous row's LDS reads are done
     if (tid == 0) { s_ncand = 0; s_bin = -1; }
-    for (int j = tid; j < W; j += kNT) keepbits[j] = 0;
-    for (int j = tid; j < kBins; j += kNT) hist[j] = 0;   // ordered by the barriers below
+    for (int j = tid; j < W; j += NT) keepbits[j] = 0;
+    for (int j = tid; j < kBins; j += NT) hist[j] = 0;   // ordered by the barriers below
 
     float m = -__builtin_inff(), nmin = -__builtin_inff();
 #pragma unroll
@@ -243,7 +249,7 @@ __global__ __launch_bounds__(kNT) void nucleus_lp_kernel(int nrows, int N, int W
     // row's first use of its values (a wait for this row's loads placed after
     // them would wait for them too: the counter of outstanding loads is in
     // order) and stay in flight while this row is selected
-    block_max2_l(m, nmin, red, tid);
+    block_max2_l<NT>(m, nmin, red, tid);
     const int nxt = row + gridDim.x;
     if constexpr (PF)
       if (nxt < nrows) load_row<EPT, FULL>(vn, logits + (size_t)nxt * N, N, e0);
@@ -264,7 +270,7 @@ __global__ __launch_bounds__(kNT) void nucleus_lp_kernel(int nrows, int N, int W
     // mass ahead of each bin: a DPP scan inside each wavefront, then every
     // thread adds the totals of the wavefronts before its own (the sum of
     // all of them is the normaliser S: every weight went to a bin)
-    constexpr int PER = kBins / kNT;
+    constexpr int PER = kBins / NT;
     const int b0 = tid * PER;
     uint64_t local = 0;
 #pragma unroll
@@ -275,7 +281,7 @@ __global__ __launch_bounds__(kNT) void nucleus_lp_kernel(int nrows, int N, int W
     lds_barrier();
     uint64_t S = 0, pre = 0;
 #pragma unroll
-    for (int w = 0; w < kNWv; ++w) {
+    for (int w = 0; w < (NT / kWave); ++w) {
       const uint64_t t = scan_scratch[w];
       S += t;
       pre += w < wave ? t : 0ull;
@@ -323,7 +329,7 @@ __global__ __launch_bounds__(kNT) void nucleus_lp_kernel(int nrows, int N, int W
         // each candidate's exact mass ahead inside the bin, in walk order
         // (logit descending, index ascending); kept iff the mass ahead of the
         // bin plus that is below R
-        for (int sl = tid; sl < nc; sl += kNT) {
+        for (int sl = tid; sl < nc; sl += NT) {
           const u32x4 me = cand[sl];
           uint64_t ahead = 0;
 #pragma unroll 4
@@ -364,7 +370,7 @@ __global__ __launch_bounds__(kNT) void nucleus_lp_kernel(int nrows, int N, int W
       constexpr int kBits[3] = {11, 11, 10};
 #pragma unroll 1
       for (int p = 0; p < 3; ++p) {
-        for (int j = tid; j < kBins; j += kNT) hist[j] = 0;
+        for (int j = tid; j < kBins; j += NT) hist[j] = 0;
         lds_barrier();
         const int sh = kShift[p];
         const int hi = sh + kBits[p];
@@ -383,7 +389,7 @@ __global__ __launch_bounds__(kNT) void nucleus_lp_kernel(int nrows, int N, int W
                       (unsigned long long)w);
         }
         lds_barrier();
-        find_crossing_l(hist, M, R, scan_scratch, &s_bin, &s_before, tid);
+        find_crossing_l<NT>(hist, M, R, scan_scratch, &s_bin, &s_before, tid);
         if (s_bin < 0) { found = false; break; }   // uniform: s_bin is shared
         prefix = (prefix << kBits[p]) | (uint32_t)s_bin;
         M = s_before;
@@ -399,7 +405,7 @@ __global__ __launch_bounds__(kNT) void nucleus_lp_kernel(int nrows, int N, int W
         }
       }
       uint64_t tie_total;
-      const uint64_t tie_excl = block_exclusive_scan_u64_l(tie_local, scan_scratch, &tie_total, tid);
+      const uint64_t tie_excl = block_exclusive_scan_u64_l<NT>(tie_local, scan_scratch, &tie_total, tid);
       uint64_t ahead = M + tie_excl;
       cw = opaque(cw0);
 #pragma unroll
@@ -500,22 +506,24 @@ __global__ __launch_bounds__(256) void vote_kernel(int L, int N, int W, int thet
 hipError_t launch_label_vote(int Q, int L, int N, float top_p, int theta, const float* logits,
                              uint32_t* mask, uint8_t* count, uint8_t* label, hipStream_t s) {
   const int W = (N + 31) / 32;
-  if (N <= 32 * kNT) {
-    const int nrows = Q * L;
-    const dim3 grid((unsigned)std::min(nrows, device_cu_count()));
-    if (N == 32 * kNT)
-      hipLaunchKernelGGL((nucleus_lp_kernel<32, true, true>), grid, dim3(kNT), 0, s, nrows, N, W, top_p, logits, mask);
-    else
-      hipLaunchKernelGGL((nucleus_lp_kernel<32, false, true>), grid, dim3(kNT), 0, s, nrows, N, W, top_p, logits, mask);
+  const int nrows = Q * L;
+  const int cus = device_cu_count();
+  if (N == 32768) {
+    // two blocks resident per compute unit; up to eight a unit in the grid,
+    // so the rows are handed out as blocks finish
+    const dim3 grid((unsigned)std::min(nrows, 8 * cus));
+    hipLaunchKernelGGL((nucleus_lp_kernel<512, 64, true, false>), grid, dim3(512), 0, s, nrows, N, W, top_p, logits, mask);
+  } else if (N < 32768) {
+    const dim3 grid((unsigned)std::min(nrows, cus));
+    hipLaunchKernelGGL((nucleus_lp_kernel<1024, 32, false, true>), grid, dim3(1024), 0, s, nrows, N, W, top_p, logits, mask);
   } else {
     // 64 entries a thread leave no room for a second row: the next row is
     // loaded when the current one is done
-    const int nrows = Q * L;
-    const dim3 grid((unsigned)std::min(nrows, device_cu_count()));
-    if (N == 64 * kNT)
-      hipLaunchKernelGGL((nucleus_lp_kernel<64, true, false>), grid, dim3(kNT), 0, s, nrows, N, W, top_p, logits, mask);
+    const dim3 grid((unsigned)std::min(nrows, cus));
+    if (N == 65536)
+      hipLaunchKernelGGL((nucleus_lp_kernel<1024, 64, true, false>), grid, dim3(1024), 0, s, nrows, N, W, top_p, logits, mask);
     else
-      hipLaunchKernelGGL((nucleus_lp_kernel<64, false, false>), grid, dim3(kNT), 0, s, nrows, N, W, top_p, logits, mask);
+      hipLaunchKernelGGL((nucleus_lp_kernel<1024, 64, false, false>), grid, dim3(1024), 0, s, nrows, N, W, top_p, logits, mask);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

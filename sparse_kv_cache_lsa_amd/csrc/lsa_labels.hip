@@ -11,17 +11,14 @@
 //
 // Design.  A row is selected by one block: thread i holds the EPT
 // consecutive entries [EPT i, EPT i + EPT) in registers, so it owns whole
-// selection words and index order is (thread, register) order.  Blocks walk
-// rows blockIdx.x, blockIdx.x + gridDim.x, ...; every barrier of the
-// selection waits for LDS only (a plain block barrier also waits for
-// outstanding vector memory operations).  Rows of exactly 32K entries:
-// 512-thread blocks with 64 entries a thread, two blocks per compute unit at
-// 128 VGPRs, so one block's barrier phases and row loads overlap the other's
-// arithmetic.  Shorter rows: one 1024-thread block per compute unit with 32
-// entries a thread, which loads the next row's logits into a second register
-// set while the current row is selected (the LDS-only barriers keep those
-// loads in flight).  Longer rows (up to 64K): 1024 threads, 64 entries a
-// thread, the next row loaded when the current one is done.  No sort:
+// selection words and index order is (thread, register) order.  Rows of up
+// to 32K entries: 512-thread blocks with 32 (up to 16K) or 64 entries a
+// thread, two blocks per compute unit at 128 VGPRs, so one block's barrier
+// phases and row loads overlap the other's arithmetic.  Longer rows (up to
+// 64K): one 1024-thread block per compute unit, 64 entries a thread.  Blocks
+// walk rows blockIdx.x, blockIdx.x + gridDim.x, ..., loading the next row
+// when the current one is done; every barrier of the selection waits for LDS
+// only.  No sort:
 //  * mass in fixed point: w_s = trunc(exp(x_s - max) * 2^31), summed in 64-bit
 //    integers, so every partial sum is exact and independent of summation
 //    order -- the result is deterministic and the same as a sequential walk
@@ -153,8 +150,7 @@ __device__ __forceinline__ void find_crossing_l(const uint64_t* hist, uint64_t M
 
 // FULL rows: 16-byte loads; otherwise range-checked loads (zero past the
 // row), one path, so the registers are written in one place.  The slots past
-// the row are set to -inf by the caller (pad): done when the values are first
-// used, so the loads of the next row are not waited for when issued.
+// the row are then set to -inf (pad_row).
 template <int EPT, bool FULL>
 __device__ __forceinline__ void load_row(float (&v)[EPT], const float* x, int N, int e0) {
   if (FULL) {
@@ -200,11 +196,10 @@ __device__ __forceinline__ int lp_bin(float x, float ninv, float mi) {
 }
 
 // NT threads a block walk rows blockIdx.x, blockIdx.x + gridDim.x, ...  EPT
-// entries a thread; FULL: N == EPT * NT (no padding); PF: the next row is
-// loaded into a second register set while the current one is selected
-// (otherwise when it is done).  At most 128 VGPRs: 16 wavefronts a compute
-// unit (one 1024-thread block or two 512-thread blocks).
-template <int NT, int EPT, bool FULL, bool PF>
+// entries a thread; FULL: N == EPT * NT (no padding).  A block loads its next
+// row when the current one is done.  At most 128 VGPRs: 16 wavefronts a
+// compute unit (two 512-thread blocks, or one 1024-thread block).
+template <int NT, int EPT, bool FULL>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void nucleus_lp_kernel(int nrows, int N, int W, float top_p,
                                                         const float* __restrict__ logits,
                                                         uint32_t* __restrict__ mask) {
@@ -217,7 +212,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void nu
   __shared__ int s_ncand;
   __shared__ uint32_t keepbits[EPT * NT / 32];
 
-  float v[EPT], vn[PF ? EPT : 1];   // PF: the next row in a second register set
+  float v[EPT];
   int row = blockIdx.x;
   {
     const int e0 = threadIdx.x * EPT;
@@ -230,9 +225,12 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void nu
   for (; row < nrows; row += gridDim.x) {
     const int tid = opaque_i((int)threadIdx.x);
     const int e0 = tid * EPT;
-    // entries of this thread inside the row: i < nv; slots past the row hold
-    // -inf, whose weight is 0 and whose bin is the last one
+    // entries of this thread inside the row: i < nv.  Slots past the row hold
+    // -inf (weight 0).  Only one thread of a ragged row holds both kinds; the
+    // threads past the row (nv == 0) skip the histogram and candidate passes,
+    // so their padding adds nothing to any LDS word.
     const int nv = FULL ? EPT : min(max(N - e0, 0), EPT);
+    const bool any = FULL || nv > 0;
     const float* x = logits + (size_t)row * N;
     lds_barrier();   // the previous row's LDS reads are done
     if (tid == 0) { s_ncand = 0; s_bin = -1; }
@@ -240,19 +238,20 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void nu
     for (int j = tid; j < kBins; j += NT) hist[j] = 0;   // ordered by the barriers below
 
     float m = -__builtin_inff(), nmin = -__builtin_inff();
+    if (FULL || nv == EPT) {
 #pragma unroll
-    for (int i = 0; i < EPT; ++i) {
-      m = fmaxf(m, v[i]);
-      nmin = fmaxf(nmin, i < nv ? -v[i] : -__builtin_inff());
+      for (int i = 0; i < EPT; ++i) {
+        m = fmaxf(m, v[i]);
+        nmin = fmaxf(nmin, -v[i]);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < EPT; ++i) {
+        m = fmaxf(m, v[i]);
+        nmin = fmaxf(nmin, i < nv ? -v[i] : -__builtin_inff());
+      }
     }
-    // the next row's loads are issued after the barrier that follows this
-    // row's first use of its values (a wait for this row's loads placed after
-    // them would wait for them too: the counter of outstanding loads is in
-    // order) and stay in flight while this row is selected
     block_max2_l<NT>(m, nmin, red, tid);
-    const int nxt = row + gridDim.x;
-    if constexpr (PF)
-      if (nxt < nrows) load_row<EPT, FULL>(vn, logits + (size_t)nxt * N, N, e0);
     const float xmin = -nmin;
     const float range = m - xmin;
     const float inv0 = range > 0.f ? (float)kBins / range : 0.f;
@@ -261,10 +260,12 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void nu
     auto weight = [&](int i) -> uint32_t { return lp_weight(v[i], cw); };
     auto vbin = [&](int i) -> int { return lp_bin(v[i], ninv, mi); };
 
+    if (any) {
 #pragma unroll
-    for (int i = 0; i < EPT; ++i) {
-      // padding slots add 0
-      atomicAdd((unsigned long long*)&hist[vbin(i)], (unsigned long long)weight(i));
+      for (int i = 0; i < EPT; ++i) {
+        // padding slots add 0
+        atomicAdd((unsigned long long*)&hist[vbin(i)], (unsigned long long)weight(i));
+      }
     }
     lds_barrier();
     // mass ahead of each bin: a DPP scan inside each wavefront, then every
@@ -308,18 +309,23 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void nu
 
     // one pass: entries ahead of the crossing bin set their bit of the
     // thread's selection word; the crossing bin's entries are collected as
-    // (order key, index, weight) records
+    // (order key, index, weight) records.  Padding of the row's last thread
+    // may set bits past the row (masked off below) or join the candidates
+    // (weight 0 and the largest order key: never kept, and adds nothing to
+    // the mass ahead of any entry).
     const int cb = cbin < 0 ? kBins : cbin;   // cbin < 0: every entry is kept
     uint32_t word[EPT / 32];
 #pragma unroll
     for (int wd = 0; wd < EPT / 32; ++wd) word[wd] = 0;
+    if (any) {
 #pragma unroll
-    for (int i = 0; i < EPT; ++i) {
-      const int vb = vbin(i);
-      word[i / 32] |= (((i < nv) & (vb < cb)) ? 1u : 0u) << (i % 32);
-      if ((i < nv) & (vb == cb)) {
-        const int slot = atomicAdd(&s_ncand, 1);
-        if (slot < kCand) cand[slot] = u32x4{desc_key(v[i]), (uint32_t)(e0 + i), weight(i), 0u};
+      for (int i = 0; i < EPT; ++i) {
+        const int vb = vbin(i);
+        word[i / 32] |= (vb < cb ? 1u : 0u) << (i % 32);
+        if (vb == cb) {
+          const int slot = atomicAdd(&s_ncand, 1);
+          if (slot < kCand) cand[slot] = u32x4{desc_key(v[i]), (uint32_t)(e0 + i), weight(i), 0u};
+        }
       }
     }
     lds_barrier();
@@ -345,6 +351,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void nu
       for (int wd = 0; wd < EPT / 32; ++wd) {
         const int widx = tid * (EPT / 32) + wd;
         if (nc > 0) word[wd] |= keepbits[widx];
+        if (!FULL && widx == W - 1 && (N & 31)) word[wd] &= (1u << (N & 31)) - 1u;
         if (widx < W) mask[(size_t)row * W + widx] = word[wd];
       }
     } else {
@@ -435,11 +442,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void nu
         if (widx < W) mask[(size_t)row * W + widx] = word;
       }
     }
-    if constexpr (PF) {
-#pragma unroll
-      for (int i = 0; i < EPT; ++i) v[i] = vn[i];
-      pad_row<EPT, FULL>(v, nv);
-    } else if (nxt < nrows) {
+    const int nxt = row + gridDim.x;
+    if (nxt < nrows) {
       load_row<EPT, FULL>(v, logits + (size_t)nxt * N, N, e0);
       pad_row<EPT, FULL>(v, nv);
     }
@@ -508,22 +512,27 @@ hipError_t launch_label_vote(int Q, int L, int N, float top_p, int theta, const 
   const int W = (N + 31) / 32;
   const int nrows = Q * L;
   const int cus = device_cu_count();
-  if (N == 32768) {
-    // two blocks resident per compute unit; up to eight a unit in the grid,
-    // so the rows are handed out as blocks finish
-    const dim3 grid((unsigned)std::min(nrows, 8 * cus));
-    hipLaunchKernelGGL((nucleus_lp_kernel<512, 64, true, false>), grid, dim3(512), 0, s, nrows, N, W, top_p, logits, mask);
-  } else if (N < 32768) {
-    const dim3 grid((unsigned)std::min(nrows, cus));
-    hipLaunchKernelGGL((nucleus_lp_kernel<1024, 32, false, true>), grid, dim3(1024), 0, s, nrows, N, W, top_p, logits, mask);
-  } else {
-    // 64 entries a thread leave no room for a second row: the next row is
-    // loaded when the current one is done
-    const dim3 grid((unsigned)std::min(nrows, cus));
-    if (N == 65536)
-      hipLaunchKernelGGL((nucleus_lp_kernel<1024, 64, true, false>), grid, dim3(1024), 0, s, nrows, N, W, top_p, logits, mask);
+  // 512-thread blocks: up to eight a compute unit in the grid (two resident
+  // at a time), so rows are handed out as blocks finish; 1024-thread blocks:
+  // one a compute unit, each walking its rows (measured faster than a larger
+  // grid for these rows)
+  const dim3 grid((unsigned)std::min(nrows, 8 * cus));
+  const dim3 grid1((unsigned)std::min(nrows, cus));
+  if (N <= 16384) {
+    if (N == 16384)
+      hipLaunchKernelGGL((nucleus_lp_kernel<512, 32, true>), grid, dim3(512), 0, s, nrows, N, W, top_p, logits, mask);
     else
-      hipLaunchKernelGGL((nucleus_lp_kernel<1024, 64, false, false>), grid, dim3(1024), 0, s, nrows, N, W, top_p, logits, mask);
+      hipLaunchKernelGGL((nucleus_lp_kernel<512, 32, false>), grid, dim3(512), 0, s, nrows, N, W, top_p, logits, mask);
+  } else if (N <= 32768) {
+    if (N == 32768)
+      hipLaunchKernelGGL((nucleus_lp_kernel<512, 64, true>), grid, dim3(512), 0, s, nrows, N, W, top_p, logits, mask);
+    else
+      hipLaunchKernelGGL((nucleus_lp_kernel<512, 64, false>), grid, dim3(512), 0, s, nrows, N, W, top_p, logits, mask);
+  } else {
+    if (N == 65536)
+      hipLaunchKernelGGL((nucleus_lp_kernel<1024, 64, true>), grid1, dim3(1024), 0, s, nrows, N, W, top_p, logits, mask);
+    else
+      hipLaunchKernelGGL((nucleus_lp_kernel<1024, 64, false>), grid1, dim3(1024), 0, s, nrows, N, W, top_p, logits, mask);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -78,7 +78,8 @@ def test_labels_full_workload():
 
 
 @pytest.mark.parametrize("Q,L,N", [(2, 1, 1), (2, 3, 31), (1, 3, 32), (3, 5, 1000),
-                                   (2, 3, 4097), (1, 2, 32773), (1, 2, 65536)])
+                                   (2, 3, 4097), (2, 3, 16384), (1, 3, 16385), (2, 2, 30001),
+                                   (1, 2, 32773), (1, 2, 65536)])
 def test_labels_ragged_sizes(Q, L, N):
     rng = np.random.default_rng(N + 10 * L)
     x = rng.standard_normal((Q, L, N)).astype(np.float32) * 2
@@ -86,10 +87,13 @@ def test_labels_ragged_sizes(Q, L, N):
     _check(x, 0.6, min(3, L), mask, count, label)
 
 
+@pytest.mark.parametrize("N", [5000, 20000])
 @pytest.mark.parametrize("top_p", [1e-6, 0.05, 0.6, 0.999, 1.0])
-def test_labels_top_p_extremes(top_p):
+def test_labels_top_p_extremes(top_p, N):
+    # top_p near 1 puts the crossing in the last value bin, where the padding
+    # of a ragged row's last thread also falls (weight 0, never kept)
     rng = np.random.default_rng(7)
-    x = rng.standard_normal((2, 4, 5000)).astype(np.float32) * 3
+    x = rng.standard_normal((2, 4, N)).astype(np.float32) * 3
     mask, count, label = _gpu(x, top_p, 2)
     _check(x, top_p, 2, mask, count, label)
 
@@ -107,10 +111,10 @@ def test_labels_constant_logits_closed_form():
     assert np.array_equal(count[0], np.where(np.arange(N) < n_keep, 3, 0))
 
 
-@pytest.mark.parametrize("N", [9000, 50000])
+@pytest.mark.parametrize("N", [9000, 20000, 50000])
 def test_labels_heavy_ties_and_signed_zeros(N):
     # few distinct values: the crossing bin holds thousands of entries and
-    # takes the radix path (rows above 32K entries: 64 entries a thread)
+    # takes the radix path (32 entries a thread up to 16K, 64 above)
     rng = np.random.default_rng(11)
     x = (np.round(rng.standard_normal((2, 3, N)) * 2) / 2).astype(np.float32)
     z = rng.random(x.shape) < 0.1

@@ -34,6 +34,7 @@ namespace {
 constexpr int kQP = 64;      // padded query count (rows of the small operands)
 constexpr int kChunk = 128;  // entries per partial-gradient block
 constexpr int kProjTR = 2;   // 32-row weight tiles per projection wave
+constexpr int kMaxGateSlices = 32;   // gate_slices(D) <= 8 * 4
 
 // Buffer resources: loads past `bytes` return 0, so rows beyond the operand
 // (padding queries, the tail of the last tile) need no branch -- a branch
@@ -100,10 +101,16 @@ __device__ __forceinline__ float focal_mod(float qu, float gamma, int igamma) {
 __device__ __forceinline__ float softplus_f(float x) { return fmaxf(x, 0.f) + log1pf(__expf(-fabsf(x))); }
 
 // ---------------------------------------------------------------- 1 project
-// grid: (ceil(R/32) row tiles, KS slices of D), R = H*dI + H; the 4 waves of
-// a block split the block's slice again; each wave keeps a 32-row x 64-query
-// tile.  Block (tile, ks) writes its partial sums to qp[ks][t][r]; splitting D
-// over KS blocks keeps enough loads in flight to stream W at full rate.
+// 1-D grid: KSG blocks for the gate rows (W_g, H <= 64 rows), then the W_q
+// blocks: 64-row groups x KS slices of D, the slices of one group adjacent.
+// The 4 waves of a block split the block's slice again; each wave keeps a
+// 32-row x 64-query tile per 32-row tile.  A W_q block writes its partial sums
+// to qp[ks][t][r], a gate block to gp[ks][t][h]; splitting D keeps enough loads
+// in flight to stream W at full rate.  The gate rows take KSG = m KS slices
+// (m up to 4), so their blocks are m times shorter: with two blocks resident
+// per compute unit the W_q blocks fill whole rounds, and the gate blocks,
+// dispatched first, finish early in the first round instead of running as a
+// last round of their own.
 // HL: the block's slice of the hidden states (64 queries x at most
 // kProjSpan k) is first copied into LDS with contiguous 1 KiB row loads; a
 // wave's fragment loads straight from memory touch 32 rows each (32 cache
@@ -112,11 +119,12 @@ __device__ __forceinline__ float softplus_f(float x) { return fmaxf(x, 0.f) + lo
 constexpr int kProjSpan = 512;
 
 template <int TR, bool HL>   // TR: 32-row tiles per wave (they share the hidden-state loads)
-__global__ __launch_bounds__(256) void fproj_kernel(int Q, int D, int HdI, int H,
+__global__ __launch_bounds__(256) void fproj_kernel(int Q, int D, int HdI, int H, int KS, int KSG,
                                                     const float* __restrict__ Wq,
                                                     const float* __restrict__ Wg,
                                                     const uint16_t* __restrict__ h,
-                                                    float* __restrict__ qp) {
+                                                    float* __restrict__ qp,
+                                                    float* __restrict__ gp) {
   // the partial-sum exchange reuses the LDS of the staged hidden states
   constexpr int kHP = kProjSpan + 8;   // padded row: consecutive rows 16 B apart in the banks
   constexpr size_t kRedB = sizeof(float) * 4 * 2 * TR * 16 * 64;
@@ -126,23 +134,21 @@ __global__ __launch_bounds__(256) void fproj_kernel(int Q, int D, int HdI, int H
   uint16_t* hs = reinterpret_cast<uint16_t*>(smem);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n = lane & 31, half = lane >> 5;
-  const int R = HdI + H;
-  // a 32-row tile lies wholly in W_q or wholly in W_g (H*dI is a multiple of
-  // 32); rows past the gate rows read 0 through the buffer range check
-  __amdgpu_buffer_rsrc_t ra[TR];
+  // block -> (gate or W_q, slice by, first row r0b of the 32 TR rows)
+  const bool gate = (int)blockIdx.x < KSG;
+  const int b = (int)blockIdx.x - KSG;
+  const int by = gate ? (int)blockIdx.x : b % KS;
+  const int r0b = gate ? 0 : (b / KS) * 32 * TR;
+  const int nsl = gate ? KSG : KS;
+  const int nrows = gate ? H : HdI;   // rows past these read 0 through the range check
+  const __amdgpu_buffer_rsrc_t ra = gate ? rsrc(Wg, (size_t)H * D * 4) : rsrc(Wq, (size_t)HdI * D * 4);
   uint32_t aoff[TR];
 #pragma unroll
-  for (int i = 0; i < TR; ++i) {
-    const int r0 = (blockIdx.x * TR + i) * 32;
-    const bool gate_tile = r0 >= HdI;
-    ra[i] = gate_tile ? rsrc(Wg, (size_t)H * D * 4) : rsrc(Wq, (size_t)HdI * D * 4);
-    aoff[i] = (uint32_t)(r0 + n - (gate_tile ? HdI : 0)) * D * 4;
-  }
+  for (int i = 0; i < TR; ++i) aoff[i] = (uint32_t)(r0b + 32 * i + n) * D * 4;
   const __amdgpu_buffer_rsrc_t rb = rsrc(h, (size_t)Q * D * 2);
-  const int KS = gridDim.y;
-  const int kq = D / (4 * KS);
-  const int kbeg = (blockIdx.y * 4 + wave) * kq, kend = kbeg + kq;
-  const int kb0 = blockIdx.y * 4 * kq;   // the block's first k
+  const int kq = D / (4 * nsl);
+  const int kbeg = (by * 4 + wave) * kq, kend = kbeg + kq;
+  const int kb0 = by * 4 * kq;   // the block's first k
   if constexpr (HL) {
     // rows q < 64 of h for k in [kb0, kb0 + 4 kq), 16-byte chunks in row
     // order (queries past Q read 0 through the range check)
@@ -177,7 +183,7 @@ __global__ __launch_bounds__(256) void fproj_kernel(int Q, int D, int HdI, int H
 #pragma unroll
     for (int i = 0; i < TR; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) st.w[i][j] = buf_f32x4(ra[i], aoff[i] + (kk + 4 * j) * 4);
+      for (int j = 0; j < 4; ++j) st.w[i][j] = buf_f32x4(ra, aoff[i] + (kk + 4 * j) * 4);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       if constexpr (HL) {
@@ -213,34 +219,37 @@ __global__ __launch_bounds__(256) void fproj_kernel(int Q, int D, int HdI, int H
       red[wave][2 * i + 1][rr][lane] = acc[i][1][rr];
     }
   __syncthreads();
-  float* out = qp + (size_t)blockIdx.y * kQP * R;
+  const int ld = gate ? kQP : HdI;   // gp rows hold 64 gates
+  float* out = (gate ? gp : qp) + (size_t)by * kQP * ld;
   for (int e = threadIdx.x; e < 2 * TR * 16 * 64; e += 256) {
     const int ij = e >> 10, rr = (e >> 6) & 15, l = e & 63;
     const int i = ij >> 1, j = ij & 1;
     const float v = red[0][ij][rr][l] + red[1][ij][rr][l] + red[2][ij][rr][l] + red[3][ij][rr][l];
     const int t = 32 * j + (l & 31);
-    const int row = (blockIdx.x * TR + i) * 32 + acc_row(rr, l >> 5);
-    if (t < Q && row < R) out[(size_t)t * R + row] = v;
+    const int row = r0b + 32 * i + acc_row(rr, l >> 5);
+    if (t < Q && row < nrows) out[(size_t)t * ld + row] = v;
   }
 }
 
 // ---------------------------------------------------------------- 2 collapse
-// qa[t][r] = sum of the KS slice partials in slice order, formed where needed.
+// qa[t][r] = sum of the KS slice partials in slice order, formed where needed
+// (the gate rows: their KSG slices in order).
 // grid: (kQP queries, dI/32 dim groups); block: 256 threads.  Each thread sums
 // the partials of 8 (head, dim) pairs of the group with all loads in flight
 // (into LDS), then one thread per dim runs the gate-weighted sum over heads in
 // head order.  Rows t >= Q get zeros; the gates are formed by every block and
 // written by group 0.
-__global__ __launch_bounds__(256) void fcollapse_kernel(int Q, int H, int dI, int KS,
+__global__ __launch_bounds__(256) void fcollapse_kernel(int Q, int H, int dI, int KS, int KSG,
                                                         const float* __restrict__ qp,
+                                                        const float* __restrict__ gp,
                                                         float* __restrict__ gT,
                                                         float* __restrict__ qe) {
   __shared__ float gs[64];
   __shared__ float qs[64][33];
   const int t = blockIdx.x;
-  const int R = H * dI + H;
-  const size_t slice = (size_t)kQP * R;
-  const size_t rowb = (size_t)t * R;
+  const int HdI = H * dI;
+  const size_t slice = (size_t)kQP * HdI;
+  const size_t rowb = (size_t)t * HdI;
   const bool live = t < Q;
   const int i0 = blockIdx.y * 32;
   // (head, dim) pairs p = threadIdx.x + 256 u, u < 8: head p / 32, dim i0 + p % 32;
@@ -257,9 +266,20 @@ __global__ __launch_bounds__(256) void fcollapse_kernel(int Q, int H, int dI, in
         const int pr = threadIdx.x + 256 * u, hh = pr >> 5, i = i0 + (pr & 31);
         v[u] = (hh < H && i < dI) ? base[hh * dI + i] : 0.f;
       }
-      v[8] = threadIdx.x < H ? base[H * dI + threadIdx.x] : 0.f;
 #pragma unroll
-      for (int u = 0; u < 9; ++u) acc[u] = ks == 0 ? v[u] : acc[u] + v[u];
+      for (int u = 0; u < 8; ++u) acc[u] = ks == 0 ? v[u] : acc[u] + v[u];
+    }
+    if (threadIdx.x < H) {
+      // every gate slice in flight at once: slices past KSG read 0 through
+      // the range check and add nothing
+      const __amdgpu_buffer_rsrc_t rg = rsrc(gp, (size_t)KSG * kQP * kQP * 4);
+      float gv[kMaxGateSlices];
+#pragma unroll
+      for (int ks = 0; ks < kMaxGateSlices; ++ks)
+        gv[ks] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                               rg, (uint32_t)((ks * kQP + t) * kQP + threadIdx.x) * 4u, 0, 0));
+#pragma unroll
+      for (int ks = 0; ks < kMaxGateSlices; ++ks) acc[8] = ks == 0 ? gv[ks] : acc[8] + gv[ks];
     }
   }
 #pragma unroll
@@ -542,6 +562,7 @@ __global__ __launch_bounds__(256) void fdw_kernel(int D, const float* __restrict
 
 struct FocalWs {
   float* qp;
+  float* gp;
   float* gT;
   float* qe;
   uint16_t* hT;
@@ -556,11 +577,18 @@ size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
 // slices of D for the projection: each wave of a slice takes D / (4 KS)
 // columns, a multiple of 32 (two bf16 MFMA steps; D % 128 == 0)
 int proj_slices(int D) { return D % 1024 == 0 ? 8 : (D % 512 == 0 ? 4 : (D % 256 == 0 ? 2 : 1)); }
+// slices of D for the gate rows: m KS with m in {4, 2, 1}, each wave's columns
+// still a multiple of 32
+int gate_slices(int D) {
+  const int KS = proj_slices(D);   // <= 8, times at most 4: kMaxGateSlices
+  const int steps = D / (4 * KS) / 32;   // 32-column steps of a W_q wave
+  return KS * (steps % 4 == 0 ? 4 : (steps % 2 == 0 ? 2 : 1));
+}
 
 FocalWs carve(void* base, int Q, int N, int D, int H, int dI) {
   (void)Q;
   const int Np = (N + 7) & ~7;
-  const size_t R = (size_t)H * dI + H;
+  const size_t HdI = (size_t)H * dI;
   const int nchunks = (Np + kChunk - 1) / kChunk;
   const int nloss = nchunks;
   size_t off = 0;
@@ -570,7 +598,8 @@ FocalWs carve(void* base, int Q, int N, int D, int H, int dI) {
     off += up256(bytes);
     return (void*)p;
   };
-  w.qp = (float*)take((size_t)proj_slices(D) * kQP * R * 4);
+  w.qp = (float*)take((size_t)proj_slices(D) * kQP * HdI * 4);
+  w.gp = (float*)take((size_t)gate_slices(D) * kQP * kQP * 4);
   w.gT = (float*)take((size_t)64 * kQP * 4);
   w.qe = (float*)take((size_t)kQP * dI * 4);
   w.hT = (uint16_t*)take((size_t)D * kQP * 2);
@@ -593,7 +622,6 @@ hipError_t launch_focal(int Q, int N, int D, int H, int dI, float gamma, const u
   const FocalWs w = carve(ws, Q, N, D, H, dI);
   const int Np = (N + 7) & ~7;
   const int HdI = H * dI;
-  const int R = HdI + H;
   const int nchunks = (Np + kChunk - 1) / kChunk;
   const int nloss = nchunks;   // one loss partial per chunk
   const double inv_qn = 1.0 / ((double)Q * (double)N);
@@ -603,17 +631,19 @@ hipError_t launch_focal(int Q, int N, int D, int H, int dI, float gamma, const u
     e = hipGetLastError();                   \
     if (e != hipSuccess) return e;           \
   } while (0)
-  const int KS = proj_slices(D);
-  const dim3 gproj((R + 32 * kProjTR - 1) / (32 * kProjTR), KS);
+  const int KS = proj_slices(D), KSG = gate_slices(D);
+  // gate blocks, then (H dI / 64 row groups) x KS W_q blocks (H dI % 64 == 0,
+  // H <= 64: the gate rows are one group)
+  const dim3 gproj((unsigned)(KSG + HdI / (32 * kProjTR) * KS));
   if (D / KS <= kProjSpan)   // a block's slice of h fits the LDS rows
-    hipLaunchKernelGGL((fproj_kernel<kProjTR, true>), gproj, dim3(256), 0, s, Q, D, HdI, H, Wq, Wg,
-                       h, w.qp);
+    hipLaunchKernelGGL((fproj_kernel<kProjTR, true>), gproj, dim3(256), 0, s, Q, D, HdI, H, KS, KSG,
+                       Wq, Wg, h, w.qp, w.gp);
   else
-    hipLaunchKernelGGL((fproj_kernel<kProjTR, false>), gproj, dim3(256), 0, s, Q, D, HdI, H, Wq,
-                       Wg, h, w.qp);
+    hipLaunchKernelGGL((fproj_kernel<kProjTR, false>), gproj, dim3(256), 0, s, Q, D, HdI, H, KS,
+                       KSG, Wq, Wg, h, w.qp, w.gp);
   FOCAL_CHECK();
   hipLaunchKernelGGL(fcollapse_kernel, dim3(kQP, (dI + 31) / 32), dim3(256), 0, s, Q, H, dI, KS,
-                     w.qp, w.gT, w.qe);
+                     KSG, w.qp, w.gp, w.gT, w.qe);
   FOCAL_CHECK();
   {
     const TransposeJob jh{h, w.hT, Q, D, kQP, 1};

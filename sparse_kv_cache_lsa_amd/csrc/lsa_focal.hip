@@ -527,36 +527,60 @@ __global__ __launch_bounds__(256) void freduce_kernel(int Q, int DI, int nchunks
 }
 
 // ---------------------------------------------------------------- 7 dW
-// grid: (ceil(D/512), HdI/32); wave w takes 128 columns; contraction over the
-// kQP padded queries: A[(h,i)][t] = gT[h][t] GT[i][t], B[d][t] = hT[d][t].
-template <int DI>
+// grid: (ceil(D/512), HdI/(32 RT)); wave w takes 128 columns and RT 32-row
+// tiles over them; contraction over the kQP padded queries:
+// A[(h,i)][t] = gT[h][t] GT[i][t], B[d][t] = hT[d][t].  The wave loads its
+// hidden-state fragments once for all RT tiles, and the next tile's A operand
+// before the current tile's stores are issued (the counter of outstanding
+// memory operations is in order: a load issued after the stores would wait
+// for them), so each wave's products overlap its own stores.  RT = 4: one
+// round of waves (two a SIMD) writes the whole gradient; with one tile a wave
+// two rounds of four a SIMD took 38 us against 30.
+template <int DI, int RT>
 __global__ __launch_bounds__(256) void fdw_kernel(int D, const float* __restrict__ gT,
                                                   const float* __restrict__ GT,
                                                   const uint16_t* __restrict__ hT,
                                                   float* __restrict__ dW) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n = lane & 31, half = lane >> 5;
-  const int row = blockIdx.y * 32 + n;             // (h, i) = (row / DI, row % DI)
   const int c0 = blockIdx.x * 512 + wave * 128;
   if (c0 >= D) return;
-  const float* ga = gT + (row / DI) * kQP;
-  const float* Ga = GT + (row % DI) * kQP;
-  f32x16 acc[4] = {};
+  bf16x8 bq[kQP / 16][4];   // [k step][column tile]
 #pragma unroll
-  for (int k = 0; k < kQP; k += 16) {
-    const int kk = k + 8 * half;
-    const Split3 a = split3(*(const f32x4*)(ga + kk) * *(const f32x4*)(Ga + kk),
-                            *(const f32x4*)(ga + kk + 4) * *(const f32x4*)(Ga + kk + 4));
+  for (int ks = 0; ks < kQP / 16; ++ks)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      acc[j] = mfma_split(a, *(const bf16x8*)(hT + (size_t)(c0 + 32 * j + n) * kQP + kk), acc[j]);
-  }
+      bq[ks][j] = *(const bf16x8*)(hT + (size_t)(c0 + 32 * j + n) * kQP + 16 * ks + 8 * half);
+  auto load_a = [&](int rt, f32x4 (&ap)[kQP / 16][2]) {
+    const int row = (blockIdx.y * RT + rt) * 32 + n;   // (h, i) = (row / DI, row % DI)
+    const float* ga = gT + (row / DI) * kQP;
+    const float* Ga = GT + (row % DI) * kQP;
 #pragma unroll
-  for (int rr = 0; rr < 16; ++rr) {
-    const size_t r = (size_t)blockIdx.y * 32 + acc_row(rr, half);
+    for (int ks = 0; ks < kQP / 16; ++ks) {
+      const int kk = 16 * ks + 8 * half;
+      ap[ks][0] = *(const f32x4*)(ga + kk) * *(const f32x4*)(Ga + kk);
+      ap[ks][1] = *(const f32x4*)(ga + kk + 4) * *(const f32x4*)(Ga + kk + 4);
+    }
+  };
+  f32x4 ap[kQP / 16][2];
+  load_a(0, ap);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (c0 + 32 * j < D) __builtin_nontemporal_store(acc[j][rr], dW + r * D + c0 + 32 * j + n);
+  for (int rt = 0; rt < RT; ++rt) {
+    f32x16 acc[4] = {};
+#pragma unroll
+    for (int ks = 0; ks < kQP / 16; ++ks) {
+      const Split3 a = split3(ap[ks][0], ap[ks][1]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[j] = mfma_split(a, bq[ks][j], acc[j]);
+    }
+    if (rt + 1 < RT) load_a(rt + 1, ap);
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) {
+      const size_t r = (size_t)(blockIdx.y * RT + rt) * 32 + acc_row(rr, half);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (c0 + 32 * j < D) __builtin_nontemporal_store(acc[j][rr], dW + r * D + c0 + 32 * j + n);
+    }
   }
 }
 
@@ -661,11 +685,20 @@ hipError_t launch_focal(int Q, int N, int D, int H, int dI, float gamma, const u
   hipLaunchKernelGGL(freduce_kernel, dim3(kQP * dI / 64), dim3(256), 0, s, Q, dI, nchunks, w.Gp,
                      w.GT, nloss, inv_qn, w.loss_part, loss);
   FOCAL_CHECK();
-  const dim3 gdw((D + 511) / 512, HdI / 32);
-  if (dI == 64)
-    hipLaunchKernelGGL((fdw_kernel<64>), gdw, dim3(256), 0, s, D, w.gT, w.GT, w.hT, dWq);
-  else
-    hipLaunchKernelGGL((fdw_kernel<128>), gdw, dim3(256), 0, s, D, w.gT, w.GT, w.hT, dWq);
+  // HdI / 32 = 2 H or 4 H: four row tiles a wave when that divides it, else two
+  if ((HdI / 32) % 4 == 0) {
+    const dim3 gdw((D + 511) / 512, HdI / 128);
+    if (dI == 64)
+      hipLaunchKernelGGL((fdw_kernel<64, 4>), gdw, dim3(256), 0, s, D, w.gT, w.GT, w.hT, dWq);
+    else
+      hipLaunchKernelGGL((fdw_kernel<128, 4>), gdw, dim3(256), 0, s, D, w.gT, w.GT, w.hT, dWq);
+  } else {
+    const dim3 gdw((D + 511) / 512, HdI / 64);
+    if (dI == 64)
+      hipLaunchKernelGGL((fdw_kernel<64, 2>), gdw, dim3(256), 0, s, D, w.gT, w.GT, w.hT, dWq);
+    else
+      hipLaunchKernelGGL((fdw_kernel<128, 2>), gdw, dim3(256), 0, s, D, w.gT, w.GT, w.hT, dWq);
+  }
   FOCAL_CHECK();
 #undef FOCAL_CHECK
   return hipSuccess;

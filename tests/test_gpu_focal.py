@@ -64,8 +64,12 @@ def test_focal_full_label_workload():
 
 @pytest.mark.parametrize("Q,N,D,H,dI", [(1, 1, 128, 1, 64), (3, 100, 128, 3, 64), (5, 1000, 256, 8, 128),
                                          (64, 4097, 128, 64, 64), (17, 333, 384, 5, 128),
-                                         (2, 50, 640, 2, 64)])
+                                         (2, 50, 640, 2, 64), (4, 500, 2048, 6, 64),
+                                         (3, 200, 1536, 3, 128), (2, 300, 512, 7, 64)])
 def test_focal_ragged_shapes(Q, N, D, H, dI):
+    # D picks the projection's slices of D (1, 2, 4 or 8) and the gate rows'
+    # (1, 2 or 4 times as many); H dI / 32 not a multiple of 4 takes two row
+    # tiles a wave in the gradient
     rng = np.random.default_rng(Q * 1000 + N)
     h, Wq, Wg, K, y = _random_student(rng, Q, N, D, H, dI)
     _check(h, Wq, Wg, 0.37, K, y, 2.0, H, dI)

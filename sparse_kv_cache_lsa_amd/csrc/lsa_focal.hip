@@ -18,13 +18,14 @@
 // keys): the products are exact and only the fp32 accumulation rounds.
 //
 // Kernels (one stream, in order):
-//   1 project   partials of ([W_q; W_g] h_t)_r per slice of D (W read once)
+//   1 project   partials of (W_q h_t)_r and (W_g h_t)_r per slice of D (W read once)
 //   2 collapse  slice sums in order; g = softplus(gate rows), qe_t, gT[h][t]
 //   3 transpose h -> hT [D][64] (contraction axis of dW_q contiguous)
 //   4 logits    per 128-entry chunk: z = K qe^T + b, loss terms,
 //               delta = dloss/dz (in LDS), partial G = delta K
 //   6 reduce    GT[i][t] = sum of partials, loss = sum / (Q N) (fixed orders)
-//   7 dW        dW_q = (gT * GT) hT^T, written once (nontemporal)
+//   7 dW        dW_q = (gT * GT) hT^T, written once (nontemporal), four row
+//               tiles a wave over the same columns
 #include "lsa_device.h"
 #include "lsa_launch.h"
 
@@ -107,10 +108,11 @@ __device__ __forceinline__ float softplus_f(float x) { return fmaxf(x, 0.f) + lo
 // 32-row x 64-query tile per 32-row tile.  A W_q block writes its partial sums
 // to qp[ks][t][r], a gate block to gp[ks][t][h]; splitting D keeps enough loads
 // in flight to stream W at full rate.  The gate rows take KSG = m KS slices
-// (m up to 4), so their blocks are m times shorter: with two blocks resident
-// per compute unit the W_q blocks fill whole rounds, and the gate blocks,
-// dispatched first, finish early in the first round instead of running as a
-// last round of their own.
+// (m up to 4), so their blocks are m times shorter and, dispatched first,
+// finish early in the first round of blocks: for H dI = 8192 and D = 4096
+// the 1,024 W_q blocks then fill two rounds of two blocks per compute unit,
+// where the gate rows as one more 64-row group had made a third round of 8
+// blocks.
 // HL: the block's slice of the hidden states (64 queries x at most
 // kProjSpan k) is first copied into LDS with contiguous 1 KiB row loads; a
 // wave's fragment loads straight from memory touch 32 rows each (32 cache

@@ -18,16 +18,14 @@
 // block walks its rows in tiles of 32:
 //  * load: wave w reads 4 rows of the tile (K group w % 4, half w / 4: rows
 //    4 (w%4) .. +3, or 16 + 4 (w%4) .. +3), one 1 KiB row per load
-//    instruction (16 B per lane, dims 8l..8l+7), and writes them to LDS
-//    twice: row-major (for S^T = V Q^T, A operand: lane (n, g) reads row n,
-//    dims 32j + 8g .. +8) and transposed, 8 rows per dim (for O^T += V^T P^T,
-//    A operand: lane (n, g) reads dim 16t + n of K group g).  The transpose
-//    is done in registers (each lane regroups its 4 rows x 8 dims per dim,
-//    one 8-byte half of the dim's 16-byte slot).  Dim d = 8 l + e sits in
-//    slot 64 e + (l xor 9 e): for the writes (one e, consecutive lanes) and
-//    the reads (16 consecutive dims) the slots are distinct modulo 8 within
-//    every 8 lanes and modulo 16 within every 16, so no LDS bank is hit twice.  The next tile's
-//    rows are loaded into registers while the current one is worked on.
+//    instruction (16 B per lane, dims 8l..8l+7), and writes them to one
+//    row-major LDS copy whose 16-byte units are XOR-swizzled by row.  The
+//    S^T = V Q^T operand (lane (n, g): row n, dims 32j + 8g .. +8) is read
+//    from it directly; the O^T += V^T P^T operand (lane (n, g): dim 16t + n of
+//    rows 4g + i and 16 + 4g + i) is read from the same copy with
+//    ds_read_tr16_b64, which transposes 16-bit elements across each group of
+//    16 lanes.  The next tile's rows are loaded into registers while the
+//    current one is worked on.
 //  * S^T: two 16-row halves x 8 K-steps of 32 dims; B = the wave's query
 //    fragments (registers, loaded once).  Lane (n, g) gets rows 4g + i and
 //    16 + 4g + i of head n.
@@ -49,7 +47,7 @@ namespace {
 
 constexpr int kAttD = 512;                 // row width (elements)
 constexpr int kTile = 32;                  // rows per tile
-constexpr int kRowStride = 2 * kAttD + 16; // bytes per row in the row-major LDS copy (padded)
+constexpr int kRowBytes = 2 * kAttD;      // bytes per row of the LDS copy
 constexpr int kHeadsPerBlock = 64;
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -71,11 +69,23 @@ struct AttArgs {
   float scale_log2;         // scale * log2(e)
 };
 
-__device__ __forceinline__ uint32_t lo_pair(uint32_t a, uint32_t b) {
-  return (a & 0xFFFFu) | (b << 16);
+// Byte offset of 16-byte unit u (0..63) of LDS row r (0..31): the unit index
+// is XORed with an even mask for rows 0-7 (16-23) and an odd one for rows
+// 8-15 (24-31), so a row written by one instruction, 16 rows read at one
+// unit, and the transposed reads (8 rows at two adjacent units) all fall in
+// distinct banks.
+__device__ __forceinline__ uint32_t lds_off(int r, int u) {
+  const int h = ((2 * r) & 15) ^ ((r >> 3) & 1);
+  return (uint32_t)(r * kRowBytes + ((u ^ h) << 4));
 }
-__device__ __forceinline__ uint32_t hi_pair(uint32_t a, uint32_t b) {
-  return (a >> 16) | (b & 0xFFFF0000u);
+
+typedef short v4s __attribute__((ext_vector_type(4)));
+
+// ds_read_tr16_b64: in each group of 16 lanes, lane 4a + c receives element c
+// of the 8-byte pieces addressed by lanes a, a + 4, a + 8 and a + 12.
+__device__ __forceinline__ u32x2 tr_read(const unsigned char* p) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4s*)(const_cast<unsigned char*>(p))));
 }
 
 // fp32 -> bf16 bits, round to nearest even (finite inputs)
@@ -86,8 +96,7 @@ __device__ __forceinline__ uint32_t bf16_bits(float f) {
 }
 
 __global__ __launch_bounds__(512) void attention_kernel(AttArgs a) {
-  __shared__ __attribute__((aligned(16))) unsigned char rm[kTile * kRowStride];   // row-major
-  __shared__ __attribute__((aligned(16))) u32x4 tr[4][kAttD];                      // 8 rows per dim
+  __shared__ __attribute__((aligned(16))) unsigned char rm[kTile * kRowBytes];    // row-major
   __shared__ __attribute__((aligned(16))) f32x4 xs[8][2][64];                      // score halves
   // the wave index is uniform across a wavefront: keep it in a scalar
   // register so that row sources and buffer resources stay scalar
@@ -149,15 +158,7 @@ __global__ __launch_bounds__(512) void attention_kernel(AttArgs a) {
     __syncthreads();   // every wave is done with the previous tile's LDS
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      *(u32x4*)(rm + tile_row(i) * kRowStride + 16 * lane) = x[i];
-    // transposed: dim 8 lane + e, the 8-byte half dh of its slot in K group hg
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int w = e >> 1;
-      const uint32_t y0 = (e & 1) ? hi_pair(x[0][w], x[1][w]) : lo_pair(x[0][w], x[1][w]);
-      const uint32_t y1 = (e & 1) ? hi_pair(x[2][w], x[3][w]) : lo_pair(x[2][w], x[3][w]);
-      *(u32x2*)((unsigned char*)&tr[hg][64 * e + (lane ^ (9 * e))] + 8 * dh) = u32x2{y0, y1};
-    }
+      *(u32x4*)(rm + lds_off(tile_row(i), lane)) = x[i];
     if (r0 + kTile < r_end) load_tile(r0 + kTile, x);   // next tile, in flight meanwhile
     __syncthreads();
 
@@ -166,11 +167,10 @@ __global__ __launch_bounds__(512) void attention_kernel(AttArgs a) {
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       f32x4 c = f32x4{0.f, 0.f, 0.f, 0.f};
-      const unsigned char* base = rm + (16 * half + n) * kRowStride + 512 * dh + 16 * g;
 #pragma unroll
       for (int j = 0; j < 8; ++j)
-        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*(const bf16x8*)(base + 64 * j), qf[j], c, 0,
-                                                    0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            *(const bf16x8*)(rm + lds_off(16 * half + n, 32 * dh + 4 * j + g)), qf[j], c, 0, 0, 0);
       sc[half] = c;
       xs[wave][half][lane] = c;
     }
@@ -209,10 +209,17 @@ __global__ __launch_bounds__(512) void attention_kernel(AttArgs a) {
     const bf16x8 bhi = __builtin_bit_cast(bf16x8, u32x4{phi[0], phi[1], phi[2], phi[3]});
     const bf16x8 blo = __builtin_bit_cast(bf16x8, u32x4{plo[0], plo[1], plo[2], plo[3]});
     // ---- O^T (this wave's dims x heads) = alpha O^T + V^T P^T
+    // A operand: dims 256 dh + 16 t + n over rows 4g + i and 16 + 4g + i, read
+    // transposed from the row-major copy (lane (n, g) addresses row 4g + n/4,
+    // dims 256 dh + 16 t + 4 (n % 4) .. +3, and the same 16 rows on)
+    const int rr = 4 * g + (n >> 2);
+    const int uo = 32 * dh + ((n & 3) >> 1);
+    const int bo = 8 * (n & 1);
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
-      const int d = 256 * dh + 16 * t + n;
-      const bf16x8 av = __builtin_bit_cast(bf16x8, tr[g][64 * (d & 7) + ((d >> 3) ^ (9 * (d & 7)))]);
+      const u32x2 lo = tr_read(rm + lds_off(rr, uo + 2 * t) + bo);
+      const u32x2 hi = tr_read(rm + lds_off(16 + rr, uo + 2 * t) + bo);
+      const bf16x8 av = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
       f32x4 c = acc[t] * alpha;
       c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bhi, c, 0, 0, 0);
       acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, blo, c, 0, 0, 0);

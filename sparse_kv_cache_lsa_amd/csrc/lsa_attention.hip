@@ -71,9 +71,9 @@ struct AttArgs {
 
 // Byte offset of 16-byte unit u (0..63) of LDS row r (0..31): the unit index
 // is XORed with an even mask for rows 0-7 (16-23) and an odd one for rows
-// 8-15 (24-31), so a row written by one instruction, 16 rows read at one
-// unit, and the transposed reads (8 rows at two adjacent units) all fall in
-// distinct banks.
+// 8-15 (24-31), so with 64 banks of 4 bytes a row written by one instruction,
+// 16 rows read at one unit, and the transposed reads (8 rows at two adjacent
+// units) all fall in distinct banks.
 __device__ __forceinline__ uint32_t lds_off(int r, int u) {
   const int h = ((2 * r) & 15) ^ ((r >> 3) & 1);
   return (uint32_t)(r * kRowBytes + ((u ^ h) << 4));

@@ -122,6 +122,32 @@ def test_attention_large_scores_and_counts_beyond_limits():
     _check(a, 4.0, got, hc, wc)
 
 
+@pytest.mark.parametrize("peaked", [False, True])
+def test_attention_at_the_row_limit(peaked):
+    # one request at the documented limit k + W = 2^20 rows (2^20 - 64 selected
+    # rows and a 64-row window) with 16 heads: 256 splits of 4,096 rows, whose
+    # partials the combine step adds in 16 rounds; the oracle checks four
+    # sampled heads over all the rows.  At the workload's scale the weights
+    # spread over the whole list; at scale 0.5 (scores of std ~11) a few rows
+    # anywhere in the list carry most of each head's weight, so a split or a
+    # combine round that went wrong would move the output far past the bound.
+    B, H, k, W = 1, 16, (1 << 20) - 64, 64
+    a = gen.attention_inputs(B, H, k, W, wid=90)
+    scale = 0.5 if peaked else gen.att_scale()
+    got, ws_n = _run(a, scale)
+    assert ws_n == lsa.lsa_sparse_attention_workspace_bytes(B, H, gen.ATT_ROW, k, W) > 0
+    assert np.isfinite(got).all()
+    heads = [0, 5, 10, 15]
+    q = a.q[0][heads]
+    rows = np.concatenate([a.hot[0], a.win[0]])
+    want, wabs = oracle.attention(q, rows, scale, want_wabs=True)
+    tol = _bound(q, rows, scale, wabs)
+    err = np.abs(got[0][heads].astype(np.float64) - want)
+    assert (err <= tol).all(), f"max err {err.max():.3g}, worst err/tol {(err / tol).max():.3g}"
+    print("row limit, peaked" if peaked else "row limit", "worst err/tol", float((err / tol).max()),
+          "max |out|", float(np.abs(want).max()))
+
+
 def test_attention_same_inputs_same_bits():
     a = gen.attention_inputs(8, 64, 1000, 100, wid=81)
     x, _ = _run(a, gen.att_scale())

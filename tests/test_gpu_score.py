@@ -110,6 +110,51 @@ def test_score_matches_oracle(L, B, N, H, dI, e4m3):
     print(f"max |dz| = {worst:.3g}")
 
 
+def test_score_at_the_key_size_limit():
+    # one (layer, request) at the documented limit: 2^24 - 1 e4m3 entries of
+    # 128 dims, 2^31 - 128 bytes of keys, so the last rows sit just below the
+    # 32-bit signed offset limit (4,096 chunks: two-chunk and one-chunk blocks).
+    # The bulk repeats one random block of 2^20 entries; the first 2^16 and the
+    # last 2^18 entries are fresh, so a row read from a wrong offset there
+    # changes the result.  The oracle scores those two regions entry by entry.
+    N, H, dI, M = (1 << 24) - 1, 8, 128, 1 << 20
+    rng = np.random.default_rng(4242)
+    q = gen.to_bf16_bits(rng.standard_normal((1, 1, H, dI)).astype(np.float32))
+    g = rng.uniform(0.1, 1.5, (1, 1, H)).astype(np.float32)
+    bias = np.array([0.3], np.float32)
+
+    def block(n):
+        c, sc = gen.to_e4m3_rows((rng.standard_normal((n, dI)) / np.sqrt(dI)).astype(np.float32))
+        return c, sc
+
+    kb, sb = block(M)
+    keys = np.empty((1, N, dI), np.uint8)
+    scl = np.empty((1, N), np.float32)
+    for i in range(0, N, M):
+        e = min(N, i + M)
+        keys[0, i:e] = kb[:e - i]
+        scl[0, i:e] = sb[:e - i]
+    regions = [(0, 1 << 16), (N - (1 << 18), N)]
+    for lo, hi in regions:
+        keys[0, lo:hi], scl[0, lo:hi] = block(hi - lo)
+    z, I, mask, (ci, cz, cc) = _run(q, g, [keys], [scl], bias)
+    W = (N + 31) // 32
+    sel = parity.unpack_mask(mask[0, 0, :W], W * 32)
+    assert not sel[N:].any(), "selection bits set past N"
+    for lo, hi in regions:
+        z_or = oracle.score(keys[0, lo:hi], scl[0, lo:hi], q[0, 0], g[0, 0], float(bias[0]))
+        d = parity.check_scores(z[0, 0, lo:hi], z_or, I[0, 0, lo:hi])
+        parity.check_selection(sel[lo:hi], z_or)
+        # one layer: each chunk's list is exactly its set bits, with the layer's logits
+        for c in range(-(-lo // CH), hi // CH):
+            want = c * CH + np.flatnonzero(sel[c * CH:(c + 1) * CH])
+            got = ci[0, c, :cc[0, c]]
+            assert np.array_equal(got, want), f"chunk {c}"
+            assert np.array_equal(cz[0, c, :cc[0, c]].view(np.uint32), z[0, 0, want].view(np.uint32))
+        print(f"entries {lo}..{hi}: max |dz| = {d['max_dz']:.3g}")
+    assert cc[0, -1] == np.count_nonzero(sel[(N // CH) * CH:N])
+
+
 @pytest.mark.parametrize("want_z,want_I", [(False, False), (False, True), (True, False)])
 def test_score_optional_outputs(want_z, want_I):
     # the hot path writes only masks + merged logits; optional per-layer

@@ -50,6 +50,7 @@ def _topk(idx, z, counts, k):
     ([530000, 10], 2048),
     ([500, 600, 700], 1),
     ([5000, 5000, 5000], 0),
+    ([1 << 24, 7], 2048),   # a request as long as the score call allows (4,096 slices)
 ])
 @pytest.mark.parametrize("ties", [False, True])
 def test_topk_matches_oracle(ns, k, ties):

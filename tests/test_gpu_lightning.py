@@ -84,6 +84,32 @@ def test_lightning_scores_and_topk_match_oracle(kdt, H, dI, B, N):
         assert np.isnan(score[b, n:]).all()   # slots past the count are not written
 
 
+def test_lightning_at_the_key_size_limit():
+    # one request whose bf16 keys reach the documented limit: 2^23 - 1 rows of
+    # 128 dims (2^31 - 256 bytes).  Only the survivors' rows are read, so only
+    # they hold fresh N(0, 1/dI) keys; the survivors include the first and last
+    # 100 rows (the largest offsets) and 20,000 rows in between.
+    N, H, dI = (1 << 23) - 1, 64, 128
+    rng = np.random.default_rng(2323)
+    sv = np.unique(np.concatenate([np.arange(100), np.arange(N - 100, N),
+                                   rng.choice(N, 20000, replace=False)])).astype(np.int32)
+    keys = np.zeros((1, N, dI), np.uint16)
+    keys[0, sv] = gen.to_bf16_bits((rng.standard_normal((sv.size, dI)) / np.sqrt(dI))
+                                   .astype(np.float32))
+    q = gen.to_bf16_bits(rng.standard_normal((1, H, dI)).astype(np.float32))
+    wt = rng.uniform(0.0, 1.0, (1, H)).astype(np.float32)
+    li = gen.LightningInputs(q=q, w=wt, keys=keys, scale=None)
+    cap = sv.size
+    score, top, tcount, k = _run(li, sv[None, :], np.array([cap], np.int32), cap)
+    want = oracle.lightning(keys[0], None, q[0], wt[0], sv)
+    tol = _bound(keys[0, sv], None, q[0], wt[0], np.arange(cap))
+    err = np.abs(score[0].astype(np.float64) - want)
+    assert (err <= tol).all(), f"worst err/tol {(err / tol).max():.3g}"
+    extra = np.zeros(N)
+    extra[sv] = tol
+    parity.check_topk(top[0], int(tcount[0]), sv, want, k, extra=extra)
+
+
 def test_lightning_empty_and_capped_lists():
     w = gen.custom("light0", 99, B=3, N=3000, H=8, dI=64, D=256, key_dtype="e4m3")
     li = gen.lightning_inputs(w)

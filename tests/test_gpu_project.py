@@ -77,7 +77,8 @@ def test_project_request_groups(B, D, H):
 # block): one tile per block; 3-4 tiles per block; more tiles than
 # 8 x blocks, so extra blocks; ten request groups.
 @pytest.mark.parametrize("B,L,D,H,dI", [(65, 1, 512, 7, 64), (40, 2, 1024, 24, 128),
-                                        (32, 4, 768, 64, 128), (300, 3, 256, 64, 128)])
+                                        (32, 4, 768, 64, 128), (300, 3, 256, 64, 128),
+                                        (2, 1, 65536, 64, 128)])   # the largest hidden size
 def test_project_tile_split(B, L, D, H, dI):
     w = gen.custom("proj3", 93, B=B, L=L, H=H, dI=dI, D=D, N=64)
     _run_and_check(w)
@@ -95,7 +96,8 @@ def test_project_per_layer_hidden_states():
 # hidden states, the largest tile count.
 @pytest.mark.parametrize("B,L,D,H,dI", [(1, 1, 64, 1, 64), (5, 2, 768, 40, 64), (7, 1, 320, 5, 64),
                                         (40, 2, 1024, 24, 128), (65, 1, 512, 7, 64),
-                                        (32, 3, 4096, 64, 128)])
+                                        (32, 3, 4096, 64, 128),
+                                        (2, 1, 65536, 64, 128)])   # the largest hidden size
 def test_project_packed_weights(B, L, D, H, dI):
     w = gen.custom("projp", 94, B=B, L=L, H=H, dI=dI, D=D, N=64)
     _run_and_check(w, packed=True)

@@ -48,7 +48,7 @@ def _run(sel, z, cap):
 
 @pytest.mark.parametrize("L,B,N", [(3, 4, 1), (3, 4, 31), (3, 4, 4096), (3, 2, 1000),
                                    (3, 2, 8192), (3, 2, 8193), (3, 3, 40000), (1, 1, 70000),
-                                   (5, 2, 12345)])
+                                   (5, 2, 12345), (2, 1, 1 << 24)])   # the largest N: 4,096 chunks
 def test_select_matches_oracle(L, B, N):
     rng = np.random.default_rng(N * 7 + L)
     z = (rng.standard_normal((L, B, N)) * 3 - 2.5).astype(np.float32)
@@ -133,7 +133,8 @@ def test_pack_bits_layout():
 
 
 @pytest.mark.parametrize("L,B,N", [(3, 4, 1), (3, 4, 31), (2, 3, 33), (3, 4, 4096), (3, 2, 8193),
-                                   (3, 3, 40000), (1, 1, 70000), (8, 2, 12345)])
+                                   (3, 3, 40000), (1, 1, 70000), (8, 2, 12345),
+                                   (2, 1, 1 << 24)])   # the largest N
 def test_select_masks_matches_oracle(L, B, N):
     # masks independent of z (any producer), NaN and signed zeros among the
     # logits: survivors are the OR of the masks, merged logit the max over

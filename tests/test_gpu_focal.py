@@ -65,7 +65,9 @@ def test_focal_full_label_workload():
 @pytest.mark.parametrize("Q,N,D,H,dI", [(1, 1, 128, 1, 64), (3, 100, 128, 3, 64), (5, 1000, 256, 8, 128),
                                          (64, 4097, 128, 64, 64), (17, 333, 384, 5, 128),
                                          (2, 50, 640, 2, 64), (4, 500, 2048, 6, 64),
-                                         (3, 200, 1536, 3, 128), (2, 300, 512, 7, 64)])
+                                         (3, 200, 1536, 3, 128), (2, 300, 512, 7, 64),
+                                         (3, 500, 16384, 8, 64),        # the largest hidden size
+                                         (1, 4000000, 128, 1, 64)])     # the largest entry count
 def test_focal_ragged_shapes(Q, N, D, H, dI):
     # D picks the projection's slices of D (1, 2, 4 or 8) and the gate rows'
     # (1, 2 or 4 times as many); H dI / 32 not a multiple of 4 takes two row

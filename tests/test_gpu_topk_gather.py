@@ -130,3 +130,24 @@ def test_gather_matches_oracle(row_bytes):
     got = host(hot)
     for b in range(B):
         assert np.array_equal(got[b], oracle.gather(pool[b], idx[b]))
+
+
+def test_gather_from_a_pool_past_4_gib():
+    # two requests of 2^22 rows of 1 KiB: request 1's rows start at 4 GiB
+    # from the pool base, so every row offset needs 64-bit arithmetic; the
+    # rows read are random bytes (the rest of the pool is zero), the list
+    # includes the first and last rows and indices outside [0, N)
+    B, N, k, rb = 2, 1 << 22, 3000, 1024
+    rng = np.random.default_rng(4096)
+    idx = rng.integers(0, N, (B, k)).astype(np.int32)
+    idx[:, :6] = [0, N - 1, N - 2, -1, N, 1]
+    pool = np.zeros((B, N, rb), np.uint8)
+    for b in range(B):
+        rows = np.unique(idx[b][(idx[b] >= 0) & (idx[b] < N)])
+        pool[b, rows] = rng.integers(0, 256, (rows.size, rb), dtype=np.uint8)
+    hot = torch.full((B, k, rb), 0xAB, dtype=torch.uint8, device=DEV)
+    lsa.lsa_gather_hot(dev(pool), dev(idx), hot)
+    torch.cuda.synchronize()
+    got = host(hot)
+    for b in range(B):
+        assert np.array_equal(got[b], oracle.gather(pool[b], idx[b])), f"request {b}"
